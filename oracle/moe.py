@@ -1,0 +1,103 @@
+"""Oracle of one expert-parallel shard of a MoE layer (fp64).
+
+Test infrastructure only (see the package docstring).  MOE-core, technical
+summary: section 1 (routing, permutation and dynamic shapes of fine-grained
+experts), section 2.4 (grouped GEMM: all experts' products batched into one
+kernel; sync-free kernels read the dynamic shapes on the device) and section
+2.2 (memory-efficient permutation).  The router itself is an input here: the
+top-k expert ids and their weights are given.
+
+Readings: an expert is a SwiGLU FFN, ``silu(x W_g^T) * (x W_u^T)`` followed by
+``W_d``, with the gate rows first and the up rows second in ``W_gu``; the
+routing weight is applied when the expert outputs are summed back per token
+(the "unpermute with routing weights" form; the memory-efficient variant that
+applies it earlier gives the same result by linearity); the permutation lists
+the local picks expert-major, then by token, then by slot.
+"""
+
+import numpy as np
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def moe_permutation(topk_ids, e_start, e_local):
+    """Enumerate this shard's picks.
+
+    Experts ``e_start .. e_start + e_local - 1`` are local.  Returns
+    ``(counts [e_local], offsets [e_local + 1], picks [R])`` where ``picks``
+    holds the flat pick index ``t * topk + k`` of every local pick, ordered by
+    local expert, then token, then slot; ``offsets`` is the exclusive prefix
+    sum of ``counts``.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    tokens, topk = ids.shape
+    counts = np.zeros(e_local, dtype=np.int64)
+    picks = []
+    for e in range(e_local):
+        for t in range(tokens):
+            for k in range(topk):
+                if ids[t, k] == e_start + e:
+                    picks.append(t * topk + k)
+                    counts[e] += 1
+    offsets = np.zeros(e_local + 1, dtype=np.int64)
+    for e in range(e_local):
+        offsets[e + 1] = offsets[e] + counts[e]
+    return counts, offsets, np.asarray(picks, dtype=np.int64)
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_swiglu_ffn(x, w_gu, w_d):
+    """One expert on rows ``x [R, Hd]``: ``(silu(x W_g^T) * (x W_u^T)) W_d^T``
+    with ``W_g = w_gu[:Fe]``, ``W_u = w_gu[Fe:]``, ``w_d [Hd, Fe]``."""
+    x, w_gu, w_d = _f64(x), _f64(w_gu), _f64(w_d)
+    fe = w_d.shape[1]
+    gate = x @ w_gu[:fe].T
+    up = x @ w_gu[fe:].T
+    return (_silu(gate) * up) @ w_d.T
+
+
+def moe_forward_rows(x, topk_ids, topk_w, w_gu, w_d, e_start, tokens):
+    """The shard's output for the listed ``tokens`` only:
+    ``out[t] = sum_k [ids[t,k] local] w[t,k] * FFN_{ids[t,k]}(x_t)``, summed
+    over k ascending; tokens with no local pick give zeros."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    w = _f64(topk_w)
+    e_local = np.shape(w_gu)[0]
+    x = _f64(x)
+    out = np.zeros((len(tokens), x.shape[1]))
+    for i, t in enumerate(tokens):
+        for k in range(ids.shape[1]):
+            e = ids[t, k] - e_start
+            if 0 <= e < e_local:
+                out[i] += w[t, k] * expert_swiglu_ffn(x[t:t + 1], w_gu[e], w_d[e])[0]
+    return out
+
+
+def moe_forward(x, topk_ids, topk_w, w_gu, w_d, e_start):
+    """Whole-shard forward: permute by expert, run each local expert on its
+    rows, sum back per token with the routing weights.  Returns
+    ``(out [T, Hd], counts, offsets, picks, y_perm [R, Hd])``."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    tokens, topk = ids.shape
+    w = _f64(topk_w)
+    x = _f64(x)
+    e_local = np.shape(w_gu)[0]
+    counts, offsets, picks = moe_permutation(ids, e_start, e_local)
+    y_perm = np.zeros((picks.size, x.shape[1]))
+    for e in range(e_local):
+        sel = picks[offsets[e]:offsets[e + 1]]
+        if sel.size:
+            y_perm[offsets[e]:offsets[e + 1]] = expert_swiglu_ffn(x[sel // topk], w_gu[e], w_d[e])
+    out = np.zeros_like(x)
+    row_of = {int(pk): r for r, pk in enumerate(picks)}
+    for t in range(tokens):
+        for k in range(topk):
+            r = row_of.get(t * topk + k)
+            if r is not None:
+                out[t] += w[t, k] * y_perm[r]
+    return out, counts, offsets, picks, y_perm

@@ -1,0 +1,145 @@
+"""Pins for the oracle's vocab-parallel and MoE pieces (CPU only).
+
+Vocab: the split lookup sums to the full lookup exactly (MLM-notes, "Model
+Parallel Transformers", embedding paragraph); per-shard exponentials and row
+sums combine to the full softmax normaliser (output paragraph); closed forms
+(zero logits give ln V; a shift of all logits changes nothing); torch's
+float64 cross-entropy and autograd as independent library routines.
+
+MoE (MOE-core, technical summary 2.2 and 2.4): the permutation is pinned
+against numpy's stable argsort; the expert FFN against a hand-computed scalar
+case and a brute-force loop; the permuted forward against the per-token
+definition.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as tF
+
+import oracle as O
+
+RNG = np.random.default_rng(4321)
+
+
+def rnd(*shape, scale=1.0):
+    return RNG.standard_normal(shape) * scale
+
+
+@pytest.mark.parametrize("n", [1, 2, 8])
+def test_embedding_split_sums_exactly(n):
+    v, k, t = 64, 5, 40
+    emb = rnd(v, k)
+    ids = RNG.integers(0, v, size=t)
+    vi = v // n
+    parts = [O.vocab_parallel_embedding(ids, emb[i * vi:(i + 1) * vi], i * vi) for i in range(n)]
+    total = np.zeros((t, k))
+    for part in parts:
+        total = total + part
+    assert np.array_equal(total, O.embedding(ids, emb))
+    assert np.array_equal(O.embedding(ids, emb), emb[ids])
+
+
+def test_cross_entropy_matches_torch_and_closed_forms():
+    z = rnd(17, 50) * 3
+    y = RNG.integers(0, 50, size=17)
+    ref = tF.cross_entropy(torch.tensor(z), torch.tensor(y), reduction="none").numpy()
+    assert np.allclose(O.full_cross_entropy(z, y), ref, rtol=1e-13, atol=1e-13)
+    # Zero logits: loss = ln V exactly; shift invariance; a dominant label -> ~0.
+    assert np.allclose(O.full_cross_entropy(np.zeros((3, 51200)), [0, 7, 51199]), math.log(51200), atol=1e-12)
+    assert np.allclose(O.full_cross_entropy(z + 123.0, y), O.full_cross_entropy(z, y), atol=1e-11)
+    zd = z.copy()
+    zd[np.arange(17), y] = 200.0
+    assert np.all(O.full_cross_entropy(zd, y) < 1e-70 + 1e-12)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_triples_combine_equals_full(n):
+    t, v = 23, 96
+    z = rnd(t, v) * 2
+    y = RNG.integers(0, v, size=t)
+    vi = v // n
+    trip = [O.vocab_parallel_xent_triples(z[:, i * vi:(i + 1) * vi], y, i * vi) for i in range(n)]
+    loss, big_m, big_s = O.vocab_xent_combine(trip)
+    assert np.allclose(loss, O.full_cross_entropy(z, y), rtol=1e-13, atol=1e-13)
+    assert np.allclose(big_m, z.max(axis=1))
+    assert np.allclose(big_s, np.exp(z - big_m[:, None]).sum(axis=1), rtol=1e-13)
+    # Exactly one shard owns each label.
+    owners = sum((np.asarray([tr[:, 2] for tr in trip]) != 0).astype(int))
+    assert np.all(owners <= 1)
+    g = 1.0 / t
+    grads = [O.vocab_parallel_xent_bwd(z[:, i * vi:(i + 1) * vi], y, i * vi, big_m, big_s, g) for i in range(n)]
+    zt = torch.tensor(z, requires_grad=True)
+    tF.cross_entropy(zt, torch.tensor(y), reduction="mean").backward()
+    assert np.allclose(np.concatenate(grads, axis=1), zt.grad.numpy(), rtol=1e-12, atol=1e-15)
+    assert np.allclose(O.full_cross_entropy_grad(z, y, g), zt.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_triples_brute_force():
+    z = rnd(3, 7)
+    y = np.array([1, 9, 4])
+    tr = O.vocab_parallel_xent_triples(z, y, 3)
+    for r in range(3):
+        m = max(z[r])
+        assert tr[r, 0] == m
+        assert abs(tr[r, 1] - sum(math.exp(val - m) for val in z[r])) < 1e-14
+        assert tr[r, 2] == (z[r, y[r] - 3] if 3 <= y[r] < 10 else 0.0)
+
+
+# ------------------------------------------------------------------ MoE
+
+def routing(tokens, experts, topk):
+    ids = np.stack([RNG.permutation(experts)[:topk] for _ in range(tokens)])
+    w = RNG.random((tokens, topk))
+    return ids, w / w.sum(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("e_start,e_local", [(0, 4), (4, 4), (2, 3), (0, 16)])
+def test_permutation_matches_stable_argsort(e_start, e_local):
+    ids, _ = routing(50, 16, 4)
+    counts, offsets, picks = O.moe_permutation(ids, e_start, e_local)
+    flat = ids.reshape(-1)
+    local = np.nonzero((flat >= e_start) & (flat < e_start + e_local))[0]
+    order = local[np.argsort(flat[local], kind="stable")]
+    assert np.array_equal(picks, order)
+    assert counts.sum() == local.size
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(counts, np.bincount(flat[local] - e_start, minlength=e_local))
+
+
+def test_expert_ffn_scalar_closed_form():
+    # Hd = Fe = 1, gate weight 1, up weight 2, down weight 3, x = 1:
+    # y = 3 * silu(1) * 2 with silu(1) = 1 / (1 + e^-1).
+    y = O.expert_swiglu_ffn(np.array([[1.0]]), np.array([[1.0], [2.0]]), np.array([[3.0]]))
+    assert abs(y[0, 0] - 6.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+def test_expert_ffn_brute_force():
+    hd, fe, r = 4, 3, 2
+    x, wgu, wd = rnd(r, hd), rnd(2 * fe, hd), rnd(hd, fe)
+    y = O.expert_swiglu_ffn(x, wgu, wd)
+    for i in range(r):
+        act = []
+        for j in range(fe):
+            g = sum(x[i, k] * wgu[j, k] for k in range(hd))
+            u = sum(x[i, k] * wgu[fe + j, k] for k in range(hd))
+            act.append(g / (1 + math.exp(-g)) * u)
+        for o in range(hd):
+            assert abs(y[i, o] - sum(act[j] * wd[o, j] for j in range(fe))) < 1e-13
+
+
+def test_moe_forward_matches_per_token_definition():
+    t, hd, fe, experts, topk, e_start, e_local = 30, 6, 5, 12, 3, 4, 4
+    ids, w = routing(t, experts, topk)
+    x = rnd(t, hd)
+    wgu, wd = rnd(e_local, 2 * fe, hd, scale=0.5), rnd(e_local, hd, fe, scale=0.5)
+    out, counts, offsets, picks, y_perm = O.moe_forward(x, ids, w, wgu, wd, e_start)
+    ref = O.moe_forward_rows(x, ids, w, wgu, wd, e_start, list(range(t)))
+    assert np.allclose(out, ref, rtol=1e-13, atol=1e-14)
+    none_local = ~np.any((ids >= e_start) & (ids < e_start + e_local), axis=1)
+    assert np.all(out[none_local] == 0)
+    # Linearity in the routing weights: doubling every weight doubles the output.
+    out2 = O.moe_forward(x, ids, 2 * w, wgu, wd, e_start)[0]
+    assert np.allclose(out2, 2 * out, rtol=1e-14, atol=1e-14)
