@@ -1,0 +1,291 @@
+/*
+ * mp.h -- C ABI of libmp, one GPU's share of a Megatron-style tensor
+ * (intra-layer) model-parallel transformer layer, for AMD MI355X (gfx950).
+ *
+ * Pages this library follows (title, then the section on that page):
+ *   MLM-review  "[NLP Paper Review] Megatron-LM: Training Multi-Billion
+ *               Parameter Language Models Using Model Parallelism"
+ *   PAR-survey  "From GPU Engineering to Scientific Discovery: Parallelism
+ *               Techniques for Large Language Models"
+ *   MLM-notes   "GTC-2020 Megatron-LM: Training Multi-Billion Parameter
+ *               Language Models Using Model Parallelism"
+ *   MOE-core    "Scalable Training of Mixture-of-Experts Models with
+ *               Megatron Core" (technical summary, sections 1 and 2.1-2.6)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Status: every call returns MP_OK (0) or a negative MP_ERR_* code and never
+ *   throws.  mp_last_error() returns a thread-local message for the last
+ *   failing call on the calling thread.
+ * - Asynchrony: calls validate their host-visible arguments, enqueue kernels
+ *   on the caller's stream `s` (0 = the legacy default stream) and return
+ *   without synchronising.  A validation failure enqueues nothing.
+ * - Ownership: the caller owns every buffer (inputs, outputs, workspaces and
+ *   host arrays of device pointers).  Device buffers must stay alive until the
+ *   stream has executed the enqueued work; host arrays are read before the
+ *   call returns.  The library allocates no device memory and keeps no
+ *   pointer after a call returns.
+ * - Layout: row-major.  Tokens are flattened t = b*L + l, activations are
+ *   [T, features]; weights are stored [out, in] (K-contiguous).  The fused
+ *   QKV weight of a rank holds the Q rows of its heads, then the K rows, then
+ *   the V rows, d consecutive rows per head; rank i of N owns heads
+ *   [i*h, (i+1)*h) of the full model.
+ * - Dtypes: MP_BF16 (bfloat16 storage, fp32 accumulation, round-to-nearest-
+ *   even on output) or MP_F32.  Weight and bias gradients are always fp32.
+ * - Alignment: every device pointer must be 16-byte aligned (MP_ERR_ALIGN);
+ *   the contiguous dimension of every bf16 matrix must be a multiple of 8
+ *   and of every fp32 matrix a multiple of 4 (MP_ERR_SHAPE), so rows stay
+ *   16-byte aligned.
+ * - Device-data preconditions (labels in [0, V), expert ids in [0, E) and
+ *   distinct within a token) are documented, not checked.
+ * - Only gfx950 is supported; mp_device_supported() says so per device.
+ */
+#ifndef MP_H
+#define MP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ types */
+
+typedef enum { MP_F32 = 0, MP_BF16 = 1 } mp_dtype;
+
+/* Activation of the column-parallel linear.  GeLU is not defined on the
+ * pages; MP_ACT_GELU_ERF is the exact z*Phi(z) (via erf), MP_ACT_GELU_TANH the
+ * tanh approximation. */
+typedef enum { MP_ACT_NONE = 0, MP_ACT_GELU_ERF = 1, MP_ACT_GELU_TANH = 2 } mp_act;
+
+#define MP_OK              0
+#define MP_ERR_NULL       -1  /* a required pointer is NULL                     */
+#define MP_ERR_SHAPE      -2  /* non-positive / inconsistent / indivisible dims */
+#define MP_ERR_DTYPE      -3  /* dtype not supported by this call               */
+#define MP_ERR_UNSUPPORTED -4 /* e.g. head dim not in {64,128}, not gfx950      */
+#define MP_ERR_ALIGN      -5  /* a device pointer is not 16-byte aligned        */
+#define MP_ERR_WORKSPACE  -6  /* workspace NULL or smaller than required        */
+#define MP_ERR_HIP        -7  /* a HIP runtime call or kernel launch failed     */
+#define MP_ERR_ARG        -8  /* an argument value is out of range (e.g. p)     */
+
+#define MP_MAX_SHARDS 16      /* largest N accepted by the reduce/combine calls */
+
+/* ------------------------------------------------------------ utilities */
+
+/* Library version, major*10000 + minor*100 + patch. */
+int mp_version(void);
+
+/* MP_OK if device `device` is a gfx950 part, MP_ERR_UNSUPPORTED otherwise,
+ * MP_ERR_HIP if the device cannot be queried. */
+int mp_device_supported(int device);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* mp_last_error(void);
+
+/* ------------------------------------------- column- and row-parallel MLP */
+
+/* Column-parallel linear with fused bias + activation (MLM-notes, "Model
+ * Parallel Transformers", MLP paragraph; PAR-survey, "How": column parallelism
+ * splits the output dimension; MLM-review, "approach": GEMM fusion).
+ *   Y_i = act(X * A_i^T + a_i)
+ * X [T,K] (in_dtype), A_i [Fi,K] (in_dtype; the rank's rows of A), a_i [Fi]
+ * (in_dtype) or NULL, Y_i [T,Fi] (out_dtype), Z_save [T,Fi] (out_dtype) or
+ * NULL: receives the pre-activation X*A_i^T + a_i for the backward.
+ * in_dtype MP_BF16 runs on bf16 MFMA; MP_F32 on an fp32 path (out must then
+ * be MP_F32).  act = MP_ACT_NONE with out_dtype = MP_F32 is the vocab-parallel
+ * logits GEMM Z_i = H * E_i^T (MLM-notes, output paragraph). */
+int mp_column_linear_gelu(mp_dtype in_dtype, mp_dtype out_dtype, int64_t T, int64_t K,
+                          int64_t Fi, const void* X, const void* A_i, const void* a_i,
+                          int act, void* Y_i, void* Z_save, hipStream_t s);
+
+/* Workspace bytes mp_column_linear_gelu_bwd needs for these sizes. */
+size_t mp_column_linear_gelu_bwd_workspace(mp_dtype dtype, int64_t T, int64_t K, int64_t Fi);
+
+/* Backward of mp_column_linear_gelu (dtype = in_dtype = out_dtype of the
+ * forward).  dZ = dY_i * act'(Z_save);  dX_partial = dZ * A_i  [T,K] (dtype),
+ * this rank's share of the input gradient (summing the shares with
+ * mp_shard_reduce is the backward all-reduce, MLM-notes "Model Parallel
+ * Transformers", communication paragraph);  dA_i = dZ^T * X  [Fi,K] fp32;
+ * da_i = column sums of dZ [Fi] fp32 or NULL.  Z_save may be NULL only when
+ * act = MP_ACT_NONE. */
+int mp_column_linear_gelu_bwd(mp_dtype dtype, int64_t T, int64_t K, int64_t Fi,
+                              const void* X, const void* A_i, const void* Z_save,
+                              const void* dY_i, int act, void* dX_partial, float* dA_i,
+                              float* da_i, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Row-parallel linear, partial sum (MLM-notes, "Model Parallel Transformers";
+ * PAR-survey, "How": row parallelism splits the input dimension).
+ *   P_i = Y_i * B_i^T           (no bias: it is added once, after the sum)
+ * Y_i [T,Fi], B_i [K,Fi] (the rank's columns of B, contiguous), P_i [T,K]. */
+int mp_row_linear_partial(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K, const void* Y_i,
+                          const void* B_i, void* P_i, hipStream_t s);
+
+/* Workspace bytes mp_row_linear_partial_bwd needs. */
+size_t mp_row_linear_partial_bwd_workspace(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K);
+
+/* Backward of mp_row_linear_partial: dY_i = dOut * B_i [T,Fi] (dtype) and
+ * dB_i = dOut^T * Y_i [K,Fi] fp32, with dOut [T,K] the replicated upstream
+ * gradient of the reduced output. */
+int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K,
+                              const void* Y_i, const void* B_i, const void* dOut, void* dY_i,
+                              float* dB_i, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ------------------------------------------------------ reduce and dropout */
+
+/* Local N-way shard reduce standing in for the all-reduce after each
+ * partitioned block (MLM-notes, "Model Parallel Transformers": one all-reduce
+ * completes the layer), with the replicated bias, the synchronised dropout
+ * (MLM-review, "key terms") and the residual fused:
+ *   out = residual + Drop(sum_{j=0..N-1} partials[j] + bias)
+ * partials: host array of N device pointers, each [rows,cols] in dtype,
+ * summed in fp32 in order j = 0..N-1.  bias [cols] or NULL, residual
+ * [rows,cols] or NULL, out [rows,cols] (may alias residual), mask_out
+ * [rows*cols] uint8 (1 = kept) or NULL.  Dropout as mp_shared_seed_dropout with
+ * element (r,c) at flat index index_base + r*cols + c.  1 <= N <= MP_MAX_SHARDS;
+ * 0 <= p < 1 (p = 0: no dropout). */
+int mp_shard_reduce(mp_dtype dtype, int N, int64_t rows, int64_t cols,
+                    const void* const* partials, const void* bias, const void* residual,
+                    float p, uint64_t seed, uint64_t offset, uint64_t index_base, void* out,
+                    uint8_t* mask_out, hipStream_t s);
+
+/* Shared-seed dropout (MLM-review, "key terms" and "approach": every device
+ * applies the same mask).  Element j (flat index index_base + i of x[i]) is
+ * kept iff word (j mod 4) of Philox4x32-10(counter = (j div 4 as 64 bits,
+ * offset as 64 bits), key = seed) is >= floor(p * 2^32) computed from the
+ * float32 p; kept values are scaled by 1/(1-p), the rest set to 0.  The mask
+ * depends on (seed, offset, j) only, never on the rank, so every shard draws
+ * it identically; applied to an upstream gradient with the same arguments it
+ * is the backward.  x, y [n] in dtype (y may alias x), mask_out [n] or NULL. */
+int mp_shared_seed_dropout(mp_dtype dtype, int64_t n, const void* x, void* y,
+                           uint8_t* mask_out, float p, uint64_t seed, uint64_t offset,
+                           uint64_t index_base, hipStream_t s);
+
+/* Column sums of dy [rows,cols] (dtype) into db [cols] fp32: the gradient of
+ * a bias added to every row (deterministic, fixed summation order). */
+size_t mp_bias_grad_workspace(int64_t rows, int64_t cols);
+int mp_bias_grad(mp_dtype dtype, int64_t rows, int64_t cols, const void* dy, float* db,
+                 void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------- attention */
+
+/* Head-partitioned causal self-attention with the fused QKV GEMM over the
+ * rank's heads (MLM-notes, "Model Parallel Transformers", attention
+ * paragraph: heads are independent and assigned to GPUs; MLM-review,
+ * "approach": the Q, K, V products are split across GPUs).
+ *   qkv = X * Wqkv_i^T + bqkv_i;  per (batch, head):
+ *   ctx = softmax(Q K^T / sqrt(d), keys m <= l if causal) * V
+ * bf16 only; d in {64, 128}.  X [T=B*L, K], Wqkv_i [3*h*d, K], bqkv_i [3*h*d]
+ * or NULL, ctx_i [T, h*d] (head-major columns), qkv [T, 3*h*d] (written; also
+ * read by the backward), lse [B, h, L] fp32: natural-log softmax normaliser
+ * per query.  The out-projection is mp_row_linear_partial on ctx_i. */
+int mp_head_attention(mp_dtype dtype, int B, int L, int K, int h, int d, int causal,
+                      const void* X, const void* Wqkv_i, const void* bqkv_i, void* ctx_i,
+                      void* qkv, float* lse, hipStream_t s);
+
+size_t mp_head_attention_bwd_workspace(mp_dtype dtype, int B, int L, int K, int h, int d);
+
+/* Backward of mp_head_attention (P recomputed from lse).  Inputs as saved by
+ * the forward plus dctx_i [T, h*d]; outputs dX_partial [T,K] (this rank's
+ * share of the input gradient), dWqkv_i [3*h*d, K] fp32, dbqkv_i [3*h*d] fp32
+ * or NULL. */
+int mp_head_attention_bwd(mp_dtype dtype, int B, int L, int K, int h, int d, int causal,
+                          const void* X, const void* Wqkv_i, const void* qkv,
+                          const void* ctx_i, const float* lse, const void* dctx_i,
+                          void* dX_partial, float* dWqkv_i, float* dbqkv_i, void* ws,
+                          size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------- vocab-parallel path */
+
+/* Vocab-parallel embedding lookup (MLM-notes, "Model Parallel Transformers",
+ * embedding paragraph: split the embedding, replicate the ids, look up, then
+ * all-reduce).  The split is along V: out_partial[t] = E_i[ids[t] - v_start]
+ * if v_start <= ids[t] < v_start + Vi, else zeros.  ids [T] int32,
+ * E_i [Vi,K], out_partial [T,K].  Summing the N partials with
+ * mp_shard_reduce reproduces the full lookup exactly. */
+int mp_vocab_parallel_embedding(mp_dtype dtype, int64_t T, int64_t Vi, int64_t v_start,
+                                int64_t K, const int32_t* ids, const void* E_i,
+                                void* out_partial, hipStream_t s);
+
+/* Per-shard cross-entropy statistics (MLM-notes, "Model Parallel
+ * Transformers", output paragraph: each GPU computes its exponentials, then
+ * the row sums are combined).  One pass over the rank's fp32 logits
+ * Z_i [T,Vi]: triples[t] = (m, s, tgt) with m = max_v Z_i[t,v],
+ * s = sum_v exp(Z_i[t,v] - m), tgt = Z_i[t, labels[t] - v_start] if the label
+ * is owned by this shard else 0.  labels [T] int32 (global ids),
+ * triples [T,3] fp32. */
+int mp_vocab_parallel_xent(int64_t T, int64_t Vi, int64_t v_start, const float* Z_i,
+                           const int32_t* labels, float* triples, hipStream_t s);
+
+/* Combine N shards' triples into the loss: M = max_j m_j,
+ * S = sum_j s_j exp(m_j - M), loss[t] = ln S + M - sum_j tgt_j.  triples: host
+ * array of N device pointers to [T,3] fp32; loss [T] fp32; stats [T,2] fp32
+ * receives (M, S) for the backward (or NULL); mean_loss [1] fp32 receives the
+ * mean over T (or NULL). */
+int mp_vocab_xent_combine(int N, int64_t T, const float* const* triples, float* loss,
+                          float* stats, float* mean_loss, hipStream_t s);
+
+/* Backward of the loss sum scaled by g (g = 1/T for the mean) on one shard:
+ * dZ_i[t,v] = g * (exp(Z_i[t,v] - M_t) / S_t - [v_start + v == labels[t]]).
+ * stats [T,2] from mp_vocab_xent_combine; dZ_i [T,Vi] in out_dtype (fp32 may
+ * alias Z_i). */
+int mp_vocab_parallel_xent_bwd(int64_t T, int64_t Vi, int64_t v_start, const float* Z_i,
+                               const int32_t* labels, const float* stats, float g,
+                               mp_dtype out_dtype, void* dZ_i, hipStream_t s);
+
+/* ---------------------------------------------------------------- MoE shard */
+
+/* Worst-case workspace bytes of mp_grouped_expert_gemm (a bound computed from
+ * the sizes alone, so no host synchronisation is ever needed). */
+size_t mp_grouped_expert_gemm_workspace(int64_t T, int64_t Hd, int64_t Fe, int topk,
+                                        int E_loc);
+
+/* One expert-parallel shard of a MoE layer (MOE-core, technical summary: 2.4
+ * grouped GEMM and sync-free kernels, 2.2 permutation; 1: small per-expert
+ * GEMMs and dynamic shapes).  Local experts are e_start .. e_start+E_loc-1.
+ *  1. permutation: list the local picks (t,k) with topk_ids[t,k] local,
+ *     ordered by expert, then token, then slot; perm_picks[r] = t*topk + k;
+ *     expert_offsets[e] = first row of local expert e (exclusive scan of the
+ *     per-expert counts; expert_offsets[E_loc] = R).  Shapes stay on the
+ *     device: nothing is copied back to the host.
+ *  2. grouped gate/up GEMM with fused SwiGLU: for the rows of expert e,
+ *     act = silu(x W_g,e^T) * (x W_u,e^T) with W_gu[e] = [W_g,e ; W_u,e]
+ *     ([2*Fe, Hd], gate rows first).
+ *  3. grouped down GEMM: y = act * W_d,e^T, W_d [E_loc, Hd, Fe].
+ *  4. unpermute: out[t] = sum over local picks k (ascending) of
+ *     topk_w[t,k] * y(t,k), fp32 sum, zeros for tokens without local picks.
+ * X [T,Hd] bf16, topk_ids [T,topk] int32, topk_w [T,topk] fp32,
+ * out [T,Hd] bf16, perm_picks [T*min(topk,E_loc)] int32 (rows >= R untouched),
+ * expert_offsets [E_loc+1] int32; ws >= mp_grouped_expert_gemm_workspace(). */
+int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                           int e_start, const void* X, const int32_t* topk_ids,
+                           const float* topk_w, const void* W_gu, const void* W_d, void* out,
+                           int32_t* perm_picks, int32_t* expert_offsets, void* ws,
+                           size_t ws_bytes, hipStream_t s);
+
+/* --------------------------------------------------------------- LayerNorm */
+
+/* LayerNorm over the last dim (MLM-review, "approach": LayerNorm placement
+ * matters for deep BERT-like models); a replicated op, not partitioned.
+ * y = (x - mean) * rstd * gamma + beta, biased variance, fp32 statistics.
+ * x, y [T,K] dtype; gamma, beta [K] dtype; mean, rstd [T] fp32 (or NULL). */
+int mp_layernorm(mp_dtype dtype, int64_t T, int64_t K, const void* x, const void* gamma,
+                 const void* beta, float eps, void* y, float* mean, float* rstd,
+                 hipStream_t s);
+
+size_t mp_layernorm_bwd_workspace(int64_t T, int64_t K);
+
+/* Backward of mp_layernorm: dx = dres + LN'(dy) (dres [T,K] or NULL is an
+ * extra gradient added to dx, e.g. a residual branch; it may alias dx),
+ * dgamma, dbeta [K] fp32 (each may be NULL). */
+int mp_layernorm_bwd(mp_dtype dtype, int64_t T, int64_t K, const void* x, const void* gamma,
+                     const float* mean, const float* rstd, const void* dy, const void* dres,
+                     void* dx, float* dgamma, float* dbeta, void* ws, size_t ws_bytes,
+                     hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MP_H */

@@ -1,0 +1,238 @@
+// Internal helpers shared by the libmp translation units: status handling,
+// argument validation, bf16 conversion, vector types and the Philox4x32-10
+// generator used by the shared-seed dropout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <math.h>
+
+#include "mp.h"
+
+namespace mp {
+
+// ----------------------------------------------------------------- status
+
+// Records `msg` as this thread's last error and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int ok();
+
+// Translates the result of a kernel launch into a status.
+int check_launch(const char* what);
+
+#define MP_REQUIRE(cond, code, ...) \
+  do {                              \
+    if (!(cond)) return ::mp::fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define MP_REQUIRE_PTR(p) MP_REQUIRE((p) != nullptr, MP_ERR_NULL, "%s: %s is NULL", __func__, #p)
+#define MP_REQUIRE_ALIGN(p) \
+  MP_REQUIRE((reinterpret_cast<uintptr_t>(p) & 15u) == 0, MP_ERR_ALIGN, "%s: %s is not 16-byte aligned", __func__, #p)
+#define MP_REQUIRE_OPT_ALIGN(p) \
+  MP_REQUIRE((p) == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0, MP_ERR_ALIGN, \
+             "%s: %s is not 16-byte aligned", __func__, #p)
+
+inline size_t dtype_size(mp_dtype t) { return t == MP_BF16 ? 2 : 4; }
+inline bool dtype_ok(int t) { return t == MP_F32 || t == MP_BF16; }
+// Elements per 16-byte vector.
+inline int64_t vec_elems(mp_dtype t) { return t == MP_BF16 ? 8 : 4; }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+// Host-side Philox keep threshold floor(p * 2^32) from the float32 p.
+inline uint32_t dropout_threshold(float p) {
+  return static_cast<uint32_t>(floor(static_cast<double>(p) * 4294967296.0));
+}
+
+// --------------------------------------------------------------- bf16 math
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// 8 bf16 (one uint4) <-> 8 floats.
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// Loads/stores of one 16-byte vector as floats: 8 bf16 or 4 fp32.
+template <bool BF16>
+struct Vec16 {
+  static constexpr int N = BF16 ? 8 : 4;
+  __device__ __forceinline__ static void load(const void* base, int64_t elem, float* f) {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem * (BF16 ? 2 : 4));
+    if constexpr (BF16) {
+      unpack8(v, f);
+    } else {
+      f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+      f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    }
+  }
+  __device__ __forceinline__ static void store(void* base, int64_t elem, const float* f) {
+    uint4 v;
+    if constexpr (BF16) {
+      v = pack8(f);
+    } else {
+      v = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+    *reinterpret_cast<uint4*>(static_cast<char*>(base) + elem * (BF16 ? 2 : 4)) = v;
+  }
+};
+
+// ------------------------------------------------------------ Philox4x32-10
+//
+// Counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC'11).  A round multiplies counter word 0 by
+// 0xD2511F53 and word 2 by 0xCD9E8D57 (full 64-bit products) and forms
+// (hi(w2 product) ^ w1 ^ key0, lo(w2 product), hi(w0 product) ^ w3 ^ key1,
+// lo(w0 product)); the key advances by the Weyl increments 0x9E3779B9 and
+// 0xBB67AE85 between the ten rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c.x;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
+    c = make_uint4(static_cast<uint32_t>(p1 >> 32) ^ c.y ^ k0, static_cast<uint32_t>(p1),
+                   static_cast<uint32_t>(p0 >> 32) ^ c.w ^ k1, static_cast<uint32_t>(p0));
+  }
+  return c;
+}
+
+// Dropout words for the four elements 4*blk .. 4*blk+3 of a stream.
+__device__ __forceinline__ uint4 dropout_words(uint64_t blk, uint64_t seed, uint64_t offset) {
+  return philox4x32_10(make_uint4(static_cast<uint32_t>(blk), static_cast<uint32_t>(blk >> 32),
+                                  static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)),
+                       static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+}
+
+struct DropoutParams {
+  uint64_t seed, offset, index_base;
+  uint32_t threshold;  // keep iff word >= threshold
+  float scale;         // 1 / (1 - p)
+  int enabled;         // p > 0
+};
+
+inline DropoutParams make_dropout(float p, uint64_t seed, uint64_t offset, uint64_t index_base) {
+  DropoutParams d;
+  d.seed = seed;
+  d.offset = offset;
+  d.index_base = index_base;
+  d.threshold = dropout_threshold(p);
+  d.scale = 1.0f / (1.0f - p);
+  d.enabled = p > 0.0f;
+  return d;
+}
+
+// Applies dropout to `n` (4 or 8) consecutive values whose first flat index
+// `j0` is a multiple of 4; writes the keep flags to `keep`.
+template <int N>
+__device__ __forceinline__ void apply_dropout(const DropoutParams& d, uint64_t j0, float* v, uint8_t* keep) {
+  if (!d.enabled) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) keep[i] = 1;
+    return;
+  }
+#pragma unroll
+  for (int b = 0; b < N / 4; ++b) {
+    const uint4 w = dropout_words((j0 >> 2) + b, d.seed, d.offset);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool k = ws[i] >= d.threshold;
+      keep[4 * b + i] = k ? 1 : 0;
+      v[4 * b + i] = k ? v[4 * b + i] * d.scale : 0.0f;
+    }
+  }
+}
+
+// Streaming (non-temporal) 16-byte fp32 loads/stores for data read or written
+// once.
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_nt4(const float* p) {
+  const nt_f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void store_nt4(float* p, float a, float b, float c, float d) {
+  nt_f32x4 v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<nt_f32x4*>(p));
+}
+
+// ----------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace mp
+
+namespace mp {
+
+// ------------------------------------------------------------- activations
+// GeLU is not defined on the pages; MP_ACT_GELU_ERF is the exact z*Phi(z),
+// MP_ACT_GELU_TANH the usual tanh approximation.  erff/tanhf/expf are the
+// device math library's.
+
+__device__ __forceinline__ float act_fwd(float z, int act) {
+  if (act == MP_ACT_GELU_ERF) return 0.5f * z * (1.0f + erff(z * 0.7071067811865476f));
+  if (act == MP_ACT_GELU_TANH) {
+    const float u = 0.7978845608028654f * (z + 0.044715f * z * z * z);
+    return 0.5f * z * (1.0f + tanhf(u));
+  }
+  return z;
+}
+
+__device__ __forceinline__ float act_grad(float z, int act) {
+  if (act == MP_ACT_GELU_ERF) {
+    const float cdf = 0.5f * (1.0f + erff(z * 0.7071067811865476f));
+    const float pdf = 0.3989422804014327f * expf(-0.5f * z * z);
+    return cdf + z * pdf;
+  }
+  if (act == MP_ACT_GELU_TANH) {
+    const float c = 0.7978845608028654f;
+    const float t = tanhf(c * (z + 0.044715f * z * z * z));
+    return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * z * z);
+  }
+  return 1.0f;
+}
+
+inline bool act_ok(int act) { return act == MP_ACT_NONE || act == MP_ACT_GELU_ERF || act == MP_ACT_GELU_TANH; }
+
+}  // namespace mp

@@ -1,0 +1,618 @@
+// GEMM family of the tensor-parallel shard: C[M,N] = sum_k A(m,k) * B(n,k).
+//
+// Each operand is either K-contiguous (row-major [rows][K], the forward "NT"
+// case) or MN-contiguous ([K][rows], as the weight in an input-gradient GEMM
+// or both operands of a weight-gradient GEMM).  MN-contiguous tiles are
+// transposed in registers (8x8 blocks of 16-bit values) on their way into LDS,
+// so the LDS tile format and the MFMA inner loop are the same for every
+// layout and no transposed copy ever goes through HBM.
+//
+// bf16 kernel: 256 threads = 4 waves in a 2x2 grid; block tile BM x BN x 64;
+// each wave owns (BM/2) x (BN/2) of the output as 32x32 MFMA tiles
+// (v_mfma_f32_32x32x16_bf16).  The k-loop double-buffers the LDS tile and
+// prefetches the next k-tile into registers while the matrix cores work on
+// the current one (one barrier per k-tile).  Workgroups are renumbered so
+// each of the 8 XCDs takes a contiguous range of output tiles, walked in
+// groups of tile-rows, for L2 reuse of the operand panels.
+//
+// Epilogues: bias + activation (+ pre-activation save), activation gradient,
+// or fp32 split-K partials followed by a fixed-order reduce (deterministic).
+#include "mfma.h"
+
+namespace mp {
+
+int colsum(mp_dtype dt, int64_t rows, int64_t cols, const void* dy, float* out, void* ws, hipStream_t s);
+size_t colsum_workspace(int64_t rows, int64_t cols);
+
+enum Epilogue { EPI_STORE = 0, EPI_SPLITK = 1, EPI_DACT = 2 };
+
+struct GemmArgs {
+  int64_t M, N, K;
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  void* C;            // [M, ldc], bf16 or fp32 (out_bf16)
+  int64_t ldc;
+  const void* bias;   // [N] in the input dtype, or NULL
+  void* zsave;        // [M, ldc] pre-activation in the output dtype, or NULL
+  const void* zin;    // [M, ldc] pre-activation (EPI_DACT), input dtype
+  float* partial;     // [splits, M, N] fp32 (EPI_SPLITK)
+  int64_t k_split;    // k-values per split, a multiple of 64
+  int act;
+  int out_bf16;
+  int tiles_m, tiles_n, group_m;
+};
+
+// Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs;
+// renumber so XCD x gets a contiguous range of logical tiles, then walk
+// logical tiles in groups of `group_m` tile-rows (column-major inside a group).
+__device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int per = nwg >> 3, rem = nwg & 7, xcd = wg & 7, idx = wg >> 3;
+  const int lid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int width = group_m * tiles_n;
+  const int group = lid / width;
+  const int first_m = group * group_m;
+  const int gsz = min(tiles_m - first_m, group_m);
+  const int inner = lid - group * width;
+  tm = first_m + inner % gsz;
+  tn = inner / gsz;
+}
+
+// Global -> register -> LDS loader of one R x 64 operand tile.  Loads go
+// through a buffer resource whose base is the tile's first row (K-contiguous)
+// or first column (MN-contiguous); an element outside the matrix or past the
+// k-range gets an out-of-range offset, which the hardware returns as zeros.
+template <int R, bool KC>
+struct TileLoader {
+  static constexpr int NBLK = KC ? 0 : (R + 255) / 256;    // 8x8 blocks per thread
+  static constexpr int NREG = KC ? R / 32 : 8 * NBLK;
+  uint4 reg[NREG];
+
+  // Resource for rows [row0, rows) of a K-contiguous matrix with row stride
+  // `ld`, or for columns [row0, ld) of an MN-contiguous matrix of `kdim` rows.
+  __device__ __forceinline__ static BufRes resource(const uint16_t* base, int64_t ld, int64_t row0, int64_t rows,
+                                                    int64_t kdim) {
+    if constexpr (KC) return make_bufres(base + row0 * ld, (rows - row0) * ld * 2);
+    else return make_bufres(base + row0, (kdim * ld - row0) * 2);
+  }
+
+  __device__ __forceinline__ void load(const BufRes& rs, int64_t ld, int64_t row0, int64_t rows, int64_t k0,
+                                       int64_t kend, int tid) {
+    if constexpr (KC) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int idx = tid + 256 * i;
+        const int64_t r = idx >> 3;
+        const int64_t gk = k0 + (idx & 7) * 8;
+        const bool ok = row0 + r < rows && gk < kend;
+        reg[i] = buf_load16(rs, ok ? static_cast<uint32_t>((r * ld + gk) * 2) : kBufOOB);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int idx = tid + 256 * b;
+        const int64_t mm = (idx >> 3) * 8;
+        const int64_t gk = k0 + (idx & 7) * 8;
+        const bool ok = idx < R && row0 + mm < rows;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          reg[8 * b + kk] =
+              buf_load16(rs, (ok && gk + kk < kend) ? static_cast<uint32_t>(((gk + kk) * ld + mm) * 2) : kBufOOB);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint4* __restrict__ tile, int tid) const {
+    if constexpr (KC) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int idx = tid + 256 * i;
+        tile[lds_slot(idx >> 3, idx & 7)] = reg[i];
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int idx = tid + 256 * b;
+        if (idx < R) {
+          uint4 t[8];
+          transpose8x8_b16(reg + 8 * b, t);
+          const int mb = (idx >> 3) * 8, kb = idx & 7;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) tile[lds_slot(mb + i, kb)] = t[i];
+        }
+      }
+    }
+  }
+};
+
+template <int BM, int BN, bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;
+  __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tmi, tni;
+  map_tile(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, g.group_m, tmi, tni);
+  const int64_t m0 = static_cast<int64_t>(tmi) * BM, n0 = static_cast<int64_t>(tni) * BN;
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * g.k_split;
+  const int64_t kend = min(g.K, kbeg + g.k_split);
+  const int nk = kend > kbeg ? static_cast<int>((kend - kbeg + 63) / 64) : 0;
+  const uint16_t* A = static_cast<const uint16_t*>(g.A);
+  const uint16_t* B = static_cast<const uint16_t*>(g.B);
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  TileLoader<BM, AK> la;
+  TileLoader<BN, BKC> lb;
+  const BufRes ra = TileLoader<BM, AK>::resource(A, g.lda, m0, g.M, g.K);
+  const BufRes rb = TileLoader<BN, BKC>::resource(B, g.ldb, n0, g.N, g.K);
+  if (nk > 0) {
+    la.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
+    lb.load(rb, g.ldb, n0, g.N, kbeg, kend, tid);
+    la.store(lds[0], tid);
+    lb.store(lds[0] + A_SLOTS, tid);
+  }
+  __syncthreads();
+
+  const int frow = lane & 31, fgrp = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load(ra, g.lda, m0, g.M, kbeg + (kt + 1) * 64, kend, tid);
+      lb.load(rb, g.ldb, n0, g.N, kbeg + (kt + 1) * 64, kend, tid);
+    }
+    const uint4* ta = lds[cur];
+    const uint4* tb = lds[cur] + A_SLOTS;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = 2 * ks + fgrp;
+      uint4 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = ta[lds_slot(wm * WM + i * 32 + frow, ch)];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = tb[lds_slot(wn * WN + j * 32 + frow, ch)];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
+    }
+    if (more) {
+      la.store(lds[cur ^ 1], tid);
+      lb.store(lds[cur ^ 1] + A_SLOTS, tid);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue, staged through LDS one 32-row strip of the wave's tile at a
+  // time: the accumulators (register r of lane l = row mfma_row(r, l),
+  // column l % 32) are written to a wave-private LDS strip, then read back
+  // row-major so each lane finishes 8 consecutive outputs of one row with
+  // 16-byte loads (bias, saved pre-activation) and 16/32-byte stores.
+  constexpr int SP = WN + 4;  // padded strip row (floats)
+  float* strip = reinterpret_cast<float*>(&lds[0][0]) + wave * 32 * SP;
+  constexpr int VPR = WN / 8;  // 8-wide vectors per strip row
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) strip[mfma_row(r, lane) * SP + j * 32 + frow] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll 1
+    for (int v = lane; v < 32 * VPR; v += 64) {
+      const int row = v / VPR, c8 = (v - row * VPR) * 8;
+      const int64_t m = m0 + wm * WM + i * 32 + row;
+      const int64_t n = n0 + wn * WN + c8;
+      if (m >= g.M || n >= g.N) continue;
+      float val[8];
+      const float4 lo = *reinterpret_cast<const float4*>(strip + row * SP + c8);
+      const float4 hi = *reinterpret_cast<const float4*>(strip + row * SP + c8 + 4);
+      val[0] = lo.x; val[1] = lo.y; val[2] = lo.z; val[3] = lo.w;
+      val[4] = hi.x; val[5] = hi.y; val[6] = hi.z; val[7] = hi.w;
+      if constexpr (EPI == EPI_SPLITK) {
+        float* dst = g.partial + (static_cast<int64_t>(blockIdx.z) * g.M + m) * g.N + n;
+        reinterpret_cast<float4*>(dst)[0] = lo;
+        reinterpret_cast<float4*>(dst)[1] = hi;
+        continue;
+      }
+      const int64_t o = m * g.ldc + n;
+      if constexpr (EPI == EPI_DACT) {
+        float z[8];
+        unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.zin) + o), z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) val[e] *= act_grad(z[e], g.act);
+      } else {
+        if (g.bias != nullptr) {
+          float b[8];
+          unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.bias) + n), b);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val[e] += b[e];
+        }
+        if (g.zsave != nullptr) {
+          if (g.out_bf16) {
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.zsave) + o) = pack8(val);
+          } else {
+            reinterpret_cast<float4*>(static_cast<float*>(g.zsave) + o)[0] = make_float4(val[0], val[1], val[2], val[3]);
+            reinterpret_cast<float4*>(static_cast<float*>(g.zsave) + o)[1] = make_float4(val[4], val[5], val[6], val[7]);
+          }
+        }
+        if (g.act != MP_ACT_NONE) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val[e] = act_fwd(val[e], g.act);
+        }
+      }
+      if (g.out_bf16) {
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C) + o) = pack8(val);
+      } else {
+        reinterpret_cast<float4*>(static_cast<float*>(g.C) + o)[0] = make_float4(val[0], val[1], val[2], val[3]);
+        reinterpret_cast<float4*>(static_cast<float*>(g.C) + o)[1] = make_float4(val[4], val[5], val[6], val[7]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// out[m, n] = sum_z partial[z, m, n] in z order; fp32 or bf16 output.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
+                                                            int64_t N, int64_t ldc, int out_bf16, void* __restrict__ C) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // index of 4 outputs
+  const int64_t nq = N >> 2;
+  if (q >= M * nq) return;
+  const int64_t m = q / nq, n = (q - m * nq) * 4;
+  float4 s = reinterpret_cast<const float4*>(partial + m * N + n)[0];
+  for (int z = 1; z < splits; ++z) {
+    const float4 v = reinterpret_cast<const float4*>(partial + (static_cast<int64_t>(z) * M + m) * N + n)[0];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  if (out_bf16) {
+    uint2 o;
+    o.x = pack_bf16x2(s.x, s.y);
+    o.y = pack_bf16x2(s.z, s.w);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + m * ldc + n) = o;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(C) + m * ldc + n) = s;
+  }
+}
+
+// ---------------------------------------------------------- fp32 SIMT path
+// 64x64 output tile, 256 threads x (4x4) outputs, 16-deep k-tiles in LDS.
+template <bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs g) {
+  __shared__ float As[16][68], Bs[16][68];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 64, n0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * g.k_split;
+  const int64_t kend = min(g.K, kbeg + g.k_split);
+  const float* A = static_cast<const float*>(g.A);
+  const float* B = static_cast<const float*>(g.B);
+  float acc[4][4] = {};
+  for (int64_t k0 = kbeg; k0 < kend; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = AK ? idx >> 4 : idx & 63, c = AK ? idx & 15 : idx >> 6;
+      const int64_t gm = m0 + r, gk = k0 + c;
+      As[c][r] = (gm < g.M && gk < kend) ? (AK ? A[gm * g.lda + gk] : A[gk * g.lda + gm]) : 0.0f;
+      const int rb = BKC ? idx >> 4 : idx & 63, cb = BKC ? idx & 15 : idx >> 6;
+      const int64_t gn = n0 + rb, gkb = k0 + cb;
+      Bs[cb][rb] = (gn < g.N && gkb < kend) ? (BKC ? B[gn * g.ldb + gkb] : B[gkb * g.ldb + gn]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[kk][ty * 4 + i];
+        b[i] = Bs[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + ty * 4 + i;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + tx * 4 + j;
+      if (n >= g.N) continue;
+      float v = acc[i][j];
+      if constexpr (EPI == EPI_SPLITK) {
+        g.partial[(static_cast<int64_t>(blockIdx.z) * g.M + m) * g.N + n] = v;
+      } else {
+        const int64_t o = m * g.ldc + n;
+        if constexpr (EPI == EPI_DACT) {
+          v *= act_grad(static_cast<const float*>(g.zin)[o], g.act);
+        } else {
+          if (g.bias != nullptr) v += static_cast<const float*>(g.bias)[n];
+          if (g.zsave != nullptr) static_cast<float*>(g.zsave)[o] = v;
+          v = act_fwd(v, g.act);
+        }
+        static_cast<float*>(g.C)[o] = v;
+      }
+    }
+  }
+}
+
+// dZ = dY * act'(Z), element-wise over 16-byte vectors.
+template <bool BF16>
+__global__ __launch_bounds__(256) void dact_kernel(int64_t nvec, const void* __restrict__ dy, const void* __restrict__ z,
+                                                   int act, void* __restrict__ dz) {
+  using V = Vec16<BF16>;
+  constexpr int E = V::N;
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (v >= nvec) return;
+  float a[E], b[E];
+  V::load(dy, v * E, a);
+  V::load(z, v * E, b);
+#pragma unroll
+  for (int i = 0; i < E; ++i) a[i] *= act_grad(b[i], act);
+  V::store(dz, v * E, a);
+}
+
+// --------------------------------------------------------------- planning
+
+enum Layout { NT = 0, NN = 1, TN = 2 };  // (A K-contig, B K-contig), (K, MN), (MN, MN)
+
+struct Plan {
+  int bm, bn, splits;
+  int64_t k_split;
+};
+
+static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split) {
+  struct Cand { int bm, bn; double eff; };
+  const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.7}};
+  Plan best{256, 256, 1, static_cast<int64_t>(align_up(static_cast<size_t>(K > 0 ? K : 64), 64))};
+  double best_cost = 1e300;
+  const int64_t kt_total = ceil_div(K > 0 ? K : 1, 64);
+  for (const Cand& c : cands) {
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    const int max_split = allow_split ? 16 : 1;
+    for (int s = 1; s <= max_split; ++s) {
+      const int64_t kt = ceil_div(kt_total, s);
+      if (s > 1 && kt < 4) break;
+      const int64_t used = ceil_div(kt_total, kt);  // splits actually non-empty
+      if (used != s) continue;
+      const int64_t waves = ceil_div(tiles * s, 256);
+      // Time units: one 64-deep k-step of a 256x256 tile at full efficiency = 1.
+      double cost = static_cast<double>(waves) * kt * (c.bm * c.bn / 65536.0) / c.eff;
+      // fp32 partials: write + read, ~ (bytes / 6 TB/s) in the same units
+      // (a 256x256x64 k-step at 1.5 PFLOP/s is ~5.6 ns).
+      if (s > 1) cost += 2.0 * 4.0 * M * N * s / 6e12 / 5.6e-9;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = Plan{c.bm, c.bn, s, kt * 64};
+      }
+    }
+  }
+  return best;
+}
+
+template <int BM, int BN, bool AK, bool BKC, int EPI>
+static void launch_bf16_tile(const GemmArgs& g, int splits, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(g.tiles_m * g.tiles_n), 1, static_cast<unsigned>(splits));
+  gemm_bf16_kernel<BM, BN, AK, BKC, EPI><<<grid, 256, 0, s>>>(g);
+}
+
+template <bool AK, bool BKC, int EPI>
+static void launch_bf16_layout(const GemmArgs& g, const Plan& p, hipStream_t s) {
+  if (p.bm == 256 && p.bn == 256) launch_bf16_tile<256, 256, AK, BKC, EPI>(g, p.splits, s);
+  else if (p.bm == 256 && p.bn == 128) launch_bf16_tile<256, 128, AK, BKC, EPI>(g, p.splits, s);
+  else launch_bf16_tile<128, 128, AK, BKC, EPI>(g, p.splits, s);
+}
+
+template <int EPI>
+static void launch_bf16_epi(Layout lay, const GemmArgs& g, const Plan& p, hipStream_t s) {
+  if (lay == NT) launch_bf16_layout<true, true, EPI>(g, p, s);
+  else if (lay == NN) launch_bf16_layout<true, false, EPI>(g, p, s);
+  else launch_bf16_layout<false, false, EPI>(g, p, s);
+}
+
+template <int EPI>
+static void launch_f32_epi(Layout lay, const GemmArgs& g, int splits, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(g.N, 64)), static_cast<unsigned>(ceil_div(g.M, 64)),
+                  static_cast<unsigned>(splits));
+  if (lay == NT) gemm_f32_kernel<true, true, EPI><<<grid, 256, 0, s>>>(g);
+  else if (lay == NN) gemm_f32_kernel<true, false, EPI><<<grid, 256, 0, s>>>(g);
+  else gemm_f32_kernel<false, false, EPI><<<grid, 256, 0, s>>>(g);
+}
+
+// Split-K partial bytes needed for an fp32-output GEMM of this shape.
+static size_t splitk_bytes(mp_dtype dt, int64_t M, int64_t N, int64_t K) {
+  if (dt != MP_BF16) return 0;
+  const Plan p = plan_bf16(M, N, K, true);
+  return p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * M * N * sizeof(float), 256) : 0;
+}
+
+// C = A * B^T in the given layout.  `allow_split` (fp32-output GEMMs only)
+// lets the planner split K, using `ws` for the partials.
+int gemm(mp_dtype dt, Layout lay, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+         int64_t ldb, void* C, int64_t ldc, bool out_bf16, const void* bias, int act, void* zsave, bool allow_split,
+         void* ws, hipStream_t s, int epi = EPI_STORE, const void* zin = nullptr) {
+  if (M == 0 || N == 0) return MP_OK;
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K; g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
+  g.bias = bias; g.zsave = zsave; g.zin = zin; g.act = act; g.out_bf16 = out_bf16 ? 1 : 0;
+  if (dt == MP_BF16) {
+    const Plan p = plan_bf16(M, N, K, allow_split && epi == EPI_STORE && bias == nullptr && act == MP_ACT_NONE &&
+                                          zsave == nullptr);
+    g.tiles_m = static_cast<int>(ceil_div(M, p.bm));
+    g.tiles_n = static_cast<int>(ceil_div(N, p.bn));
+    g.group_m = 8;
+    g.k_split = p.k_split;
+    if (p.splits > 1) {
+      if (ws == nullptr) return fail(MP_ERR_WORKSPACE, "gemm: split-K needs a workspace");
+      g.partial = static_cast<float*>(ws);
+      launch_bf16_epi<EPI_SPLITK>(lay, g, p, s);
+      const int64_t nq = M * (N / 4);
+      splitk_reduce_kernel<<<static_cast<unsigned>(ceil_div(nq, 256)), 256, 0, s>>>(g.partial, p.splits, M, N, ldc,
+                                                                                     g.out_bf16, C);
+    } else if (epi == EPI_DACT) {
+      launch_bf16_epi<EPI_DACT>(lay, g, p, s);
+    } else {
+      launch_bf16_epi<EPI_STORE>(lay, g, p, s);
+    }
+  } else {
+    g.k_split = K > 0 ? K : 16;
+    if (epi == EPI_DACT) launch_f32_epi<EPI_DACT>(lay, g, 1, s);
+    else launch_f32_epi<EPI_STORE>(lay, g, 1, s);
+  }
+  return check_launch("gemm");
+}
+
+size_t gemm_splitk_workspace(mp_dtype dt, int64_t M, int64_t N, int64_t K) { return splitk_bytes(dt, M, N, K); }
+
+static int validate_mat(mp_dtype dt, int64_t contiguous, const char* fn, const char* what) {
+  MP_REQUIRE(contiguous % vec_elems(dt) == 0, MP_ERR_SHAPE, "%s: %s=%lld must be a multiple of %lld", fn, what,
+             (long long)contiguous, (long long)vec_elems(dt));
+  return MP_OK;
+}
+
+}  // namespace mp
+
+using namespace mp;
+
+extern "C" int mp_column_linear_gelu(mp_dtype in_dtype, mp_dtype out_dtype, int64_t T, int64_t K, int64_t Fi,
+                                     const void* X, const void* A_i, const void* a_i, int act, void* Y_i,
+                                     void* Z_save, hipStream_t s) {
+  static const char* fn = "mp_column_linear_gelu";
+  MP_REQUIRE(dtype_ok(in_dtype) && dtype_ok(out_dtype), MP_ERR_DTYPE, "%s: bad dtype", fn);
+  MP_REQUIRE(in_dtype == MP_BF16 || out_dtype == MP_F32, MP_ERR_DTYPE, "%s: fp32 input needs fp32 output", fn);
+  MP_REQUIRE(act_ok(act), MP_ERR_ARG, "%s: bad activation %d", fn, act);
+  MP_REQUIRE(T >= 0 && K > 0 && Fi > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  if (int rc = validate_mat(in_dtype, K, fn, "K")) return rc;
+  if (int rc = validate_mat(out_dtype, Fi, fn, "Fi")) return rc;
+  if (int rc = validate_mat(in_dtype, Fi, fn, "Fi")) return rc;
+  MP_REQUIRE_PTR(X);
+  MP_REQUIRE_PTR(A_i);
+  MP_REQUIRE_PTR(Y_i);
+  MP_REQUIRE_ALIGN(X);
+  MP_REQUIRE_ALIGN(A_i);
+  MP_REQUIRE_ALIGN(Y_i);
+  MP_REQUIRE_OPT_ALIGN(a_i);
+  MP_REQUIRE_OPT_ALIGN(Z_save);
+  return gemm(in_dtype, NT, T, Fi, K, X, K, A_i, K, Y_i, Fi, out_dtype == MP_BF16, a_i, act, Z_save, false, nullptr, s);
+}
+
+extern "C" size_t mp_column_linear_gelu_bwd_workspace(mp_dtype dtype, int64_t T, int64_t K, int64_t Fi) {
+  if (!dtype_ok(dtype) || T < 0 || K <= 0 || Fi <= 0) return 0;
+  const size_t dz = align_up(static_cast<size_t>(T * Fi) * dtype_size(dtype), 256);
+  const size_t sk = gemm_splitk_workspace(dtype, Fi, K, T);
+  const size_t cs = colsum_workspace(T, Fi);
+  return dz + (sk > cs ? sk : cs);
+}
+
+extern "C" int mp_column_linear_gelu_bwd(mp_dtype dtype, int64_t T, int64_t K, int64_t Fi, const void* X,
+                                         const void* A_i, const void* Z_save, const void* dY_i, int act,
+                                         void* dX_partial, float* dA_i, float* da_i, void* ws, size_t ws_bytes,
+                                         hipStream_t s) {
+  static const char* fn = "mp_column_linear_gelu_bwd";
+  MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype", fn);
+  MP_REQUIRE(act_ok(act), MP_ERR_ARG, "%s: bad activation %d", fn, act);
+  MP_REQUIRE(T >= 0 && K > 0 && Fi > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  if (int rc = validate_mat(dtype, K, fn, "K")) return rc;
+  if (int rc = validate_mat(dtype, Fi, fn, "Fi")) return rc;
+  MP_REQUIRE_PTR(X);
+  MP_REQUIRE_PTR(A_i);
+  MP_REQUIRE_PTR(dY_i);
+  MP_REQUIRE_PTR(dX_partial);
+  MP_REQUIRE_PTR(dA_i);
+  MP_REQUIRE(act == MP_ACT_NONE || Z_save != nullptr, MP_ERR_NULL, "%s: Z_save is NULL", fn);
+  MP_REQUIRE_ALIGN(X);
+  MP_REQUIRE_ALIGN(A_i);
+  MP_REQUIRE_ALIGN(dY_i);
+  MP_REQUIRE_ALIGN(dX_partial);
+  MP_REQUIRE_ALIGN(dA_i);
+  MP_REQUIRE_OPT_ALIGN(Z_save);
+  const size_t need = mp_column_linear_gelu_bwd_workspace(dtype, T, K, Fi);
+  MP_REQUIRE(ws != nullptr && ws_bytes >= need, MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  MP_REQUIRE_ALIGN(ws);
+  const size_t dz_bytes = align_up(static_cast<size_t>(T * Fi) * dtype_size(dtype), 256);
+  void* dz = ws;
+  void* ws2 = static_cast<char*>(ws) + dz_bytes;
+  const void* dZ = dY_i;
+  if (act != MP_ACT_NONE && T > 0) {
+    const int64_t nvec = T * Fi / vec_elems(dtype);
+    if (dtype == MP_BF16)
+      dact_kernel<true><<<static_cast<unsigned>(ceil_div(nvec, 256)), 256, 0, s>>>(nvec, dY_i, Z_save, act, dz);
+    else
+      dact_kernel<false><<<static_cast<unsigned>(ceil_div(nvec, 256)), 256, 0, s>>>(nvec, dY_i, Z_save, act, dz);
+    dZ = dz;
+  }
+  // dX_partial[T,K] = dZ[T,Fi] * A_i[Fi,K]
+  if (int rc = gemm(dtype, NN, T, K, Fi, dZ, Fi, A_i, K, dX_partial, K, dtype == MP_BF16, nullptr, MP_ACT_NONE,
+                    nullptr, false, nullptr, s))
+    return rc;
+  // dA_i[Fi,K] = dZ^T * X  (reduction over T), fp32
+  if (int rc = gemm(dtype, TN, Fi, K, T, dZ, Fi, X, K, dA_i, K, false, nullptr, MP_ACT_NONE, nullptr, true, ws2, s))
+    return rc;
+  if (da_i != nullptr) return colsum(dtype, T, Fi, dZ, da_i, ws2, s);
+  return MP_OK;
+}
+
+extern "C" int mp_row_linear_partial(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K, const void* Y_i,
+                                     const void* B_i, void* P_i, hipStream_t s) {
+  static const char* fn = "mp_row_linear_partial";
+  MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype", fn);
+  MP_REQUIRE(T >= 0 && K > 0 && Fi > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  if (int rc = validate_mat(dtype, K, fn, "K")) return rc;
+  if (int rc = validate_mat(dtype, Fi, fn, "Fi")) return rc;
+  MP_REQUIRE_PTR(Y_i);
+  MP_REQUIRE_PTR(B_i);
+  MP_REQUIRE_PTR(P_i);
+  MP_REQUIRE_ALIGN(Y_i);
+  MP_REQUIRE_ALIGN(B_i);
+  MP_REQUIRE_ALIGN(P_i);
+  return gemm(dtype, NT, T, K, Fi, Y_i, Fi, B_i, Fi, P_i, K, dtype == MP_BF16, nullptr, MP_ACT_NONE, nullptr, false,
+              nullptr, s);
+}
+
+extern "C" size_t mp_row_linear_partial_bwd_workspace(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K) {
+  if (!dtype_ok(dtype) || T < 0 || K <= 0 || Fi <= 0) return 0;
+  return gemm_splitk_workspace(dtype, K, Fi, T);
+}
+
+extern "C" int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K, const void* Y_i,
+                                         const void* B_i, const void* dOut, void* dY_i, float* dB_i, void* ws,
+                                         size_t ws_bytes, hipStream_t s) {
+  static const char* fn = "mp_row_linear_partial_bwd";
+  MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype", fn);
+  MP_REQUIRE(T >= 0 && K > 0 && Fi > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  if (int rc = validate_mat(dtype, K, fn, "K")) return rc;
+  if (int rc = validate_mat(dtype, Fi, fn, "Fi")) return rc;
+  MP_REQUIRE_PTR(Y_i);
+  MP_REQUIRE_PTR(B_i);
+  MP_REQUIRE_PTR(dOut);
+  MP_REQUIRE_PTR(dY_i);
+  MP_REQUIRE_PTR(dB_i);
+  MP_REQUIRE_ALIGN(Y_i);
+  MP_REQUIRE_ALIGN(B_i);
+  MP_REQUIRE_ALIGN(dOut);
+  MP_REQUIRE_ALIGN(dY_i);
+  MP_REQUIRE_ALIGN(dB_i);
+  const size_t need = mp_row_linear_partial_bwd_workspace(dtype, T, Fi, K);
+  MP_REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn,
+             need);
+  MP_REQUIRE_OPT_ALIGN(ws);
+  // dY_i[T,Fi] = dOut[T,K] * B_i[K,Fi]
+  if (int rc = gemm(dtype, NN, T, Fi, K, dOut, K, B_i, Fi, dY_i, Fi, dtype == MP_BF16, nullptr, MP_ACT_NONE, nullptr,
+                    false, nullptr, s))
+    return rc;
+  // dB_i[K,Fi] = dOut^T * Y_i (reduction over T), fp32
+  return gemm(dtype, TN, K, Fi, T, dOut, K, Y_i, Fi, dB_i, Fi, false, nullptr, MP_ACT_NONE, nullptr, true, ws, s);
+}

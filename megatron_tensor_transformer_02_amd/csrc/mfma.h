@@ -1,0 +1,74 @@
+// gfx950 matrix-core helpers: the bf16 MFMA wrappers and the LDS tile format
+// shared by the GEMM, grouped-GEMM and attention kernels.
+//
+// LDS tile format: a tile of R rows x 64 k-values (bf16) is stored as R rows
+// of eight 16-byte chunks (8 k-values each).  Chunk c of row r lives at slot
+// r*8 + (c ^ (r & 7)): the XOR swizzle puts the same chunk of 8 consecutive
+// rows in 8 different bank groups, so both the 16-byte row-wise stores and
+// the 16-byte fragment reads (32 consecutive rows, one chunk) are free of
+// bank conflicts.
+#pragma once
+
+#include "common.h"
+
+namespace mp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.  Lane l gives
+// row (l % 32) of A and column (l % 32) of B, each with 8 k-values of k-group
+// (l / 32); the result holds, in register r of lane l, element
+// (row 8*(r/4) + 4*(l/32) + r%4, column l%32).
+__device__ __forceinline__ f32x16_t mfma_32x32x16(const uint4& a, const uint4& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// ------------------------------------------------------------ buffer loads
+// A buffer resource covers [base, base + bytes); a load at an offset outside
+// it returns zeros, which the tile loaders use for every out-of-range element.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kBufOOB = 0x80000000u;  // offset past any resource (<= 2 GiB)
+
+__device__ __forceinline__ BufRes make_bufres(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(n),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(const BufRes& r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+// Row m of the MFMA result held by register r of lane `lane`.
+__device__ __forceinline__ int mfma_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// 8x8 transpose of 16-bit values: in[k] holds 8 values (columns 0..7) of row
+// k; out[c] receives the 8 values of column c (rows 0..7).
+__device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ void transpose8x8_b16(const uint4* in, uint4* out) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {      // column pair (2p, 2p+1)
+    uint32_t ev[4], od[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {    // row pair (2w, 2w+1)
+      const uint32_t r0 = u4_word(in[2 * w], p);
+      const uint32_t r1 = u4_word(in[2 * w + 1], p);
+      ev[w] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // low halves
+      od[w] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // high halves
+    }
+    out[2 * p] = make_uint4(ev[0], ev[1], ev[2], ev[3]);
+    out[2 * p + 1] = make_uint4(od[0], od[1], od[2], od[3]);
+  }
+}
+
+}  // namespace mp

@@ -1,0 +1,124 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every call that
+include/mp.h declares, and rejects bad host-visible arguments with the
+documented status codes before touching the GPU (no compute call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from megatron_tensor_transformer_02_amd import mp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mp.lib_path()):
+        from megatron_tensor_transformer_02_amd import build
+        build.build()
+    return mp.lib()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_north_star_calls():
+    names = declared_symbols()
+    for want in ["mp_column_linear_gelu", "mp_row_linear_partial", "mp_shard_reduce", "mp_head_attention",
+                 "mp_vocab_parallel_xent", "mp_shared_seed_dropout", "mp_grouped_expert_gemm"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) >= 20
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(mp.EXPORTED)
+    assert lib.mp_version() == 100
+
+
+BAD = 0xDEAD0000  # a non-NULL host-side value; never dereferenced (validation fails first)
+ALIGNED = 0x10000
+
+
+def call(lib, name, *args):
+    rc = getattr(lib, name)(*args)
+    return rc, lib.mp_last_error().decode()
+
+
+def test_shard_reduce_validation(lib):
+    arr = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED)
+    rc, msg = call(lib, "mp_shard_reduce", mp.MP_BF16, 0, 4, 8, arr, None, None, 0.0, 0, 0, 0, ALIGNED, None, None)
+    assert rc == -2 and "N=0" in msg
+    rc, _ = call(lib, "mp_shard_reduce", mp.MP_BF16, 17, 4, 8, arr, None, None, 0.0, 0, 0, 0, ALIGNED, None, None)
+    assert rc == -2
+    rc, _ = call(lib, "mp_shard_reduce", mp.MP_BF16, 2, 4, 12, arr, None, None, 0.0, 0, 0, 0, ALIGNED, None, None)
+    assert rc == -2  # cols not a multiple of 8
+    rc, _ = call(lib, "mp_shard_reduce", 7, 2, 4, 8, arr, None, None, 0.0, 0, 0, 0, ALIGNED, None, None)
+    assert rc == -3
+    rc, _ = call(lib, "mp_shard_reduce", mp.MP_BF16, 2, 4, 8, arr, None, None, 1.0, 0, 0, 0, ALIGNED, None, None)
+    assert rc == -8  # p must be < 1
+    rc, _ = call(lib, "mp_shard_reduce", mp.MP_BF16, 2, 4, 8, arr, None, None, 0.1, 0, 0, 2, ALIGNED, None, None)
+    assert rc == -8  # index_base must be a multiple of 4
+    rc, _ = call(lib, "mp_shard_reduce", mp.MP_BF16, 2, 4, 8, arr, None, None, 0.1, 0, 0, 0, None, None, None)
+    assert rc == -1
+    rc, _ = call(lib, "mp_shard_reduce", mp.MP_BF16, 2, 4, 8, arr, None, None, 0.1, 0, 0, 0, ALIGNED + 2, None, None)
+    assert rc == -5
+    bad = (ctypes.c_void_p * 2)(ALIGNED, None)
+    rc, msg = call(lib, "mp_shard_reduce", mp.MP_BF16, 2, 4, 8, bad, None, None, 0.1, 0, 0, 0, ALIGNED, None, None)
+    assert rc == -1 and "partials[1]" in msg
+    # Zero rows is a valid empty call that enqueues nothing.
+    rc, _ = call(lib, "mp_shard_reduce", mp.MP_BF16, 2, 0, 8, arr, None, None, 0.1, 0, 0, 0, ALIGNED, None, None)
+    assert rc == 0
+
+
+def test_linear_validation(lib):
+    rc, _ = call(lib, "mp_column_linear_gelu", mp.MP_BF16, mp.MP_BF16, 16, 12, 16, ALIGNED, ALIGNED, None, 1,
+                 ALIGNED, None, None)
+    assert rc == -2  # K not a multiple of 8
+    rc, _ = call(lib, "mp_column_linear_gelu", mp.MP_F32, mp.MP_BF16, 16, 16, 16, ALIGNED, ALIGNED, None, 1,
+                 ALIGNED, None, None)
+    assert rc == -3  # fp32 in, bf16 out
+    rc, _ = call(lib, "mp_column_linear_gelu", mp.MP_BF16, mp.MP_BF16, 16, 16, 16, ALIGNED, ALIGNED, None, 9,
+                 ALIGNED, None, None)
+    assert rc == -8  # bad activation
+    rc, _ = call(lib, "mp_column_linear_gelu", mp.MP_BF16, mp.MP_BF16, 16, 16, 16, None, ALIGNED, None, 1,
+                 ALIGNED, None, None)
+    assert rc == -1
+    rc, _ = call(lib, "mp_column_linear_gelu_bwd", mp.MP_BF16, 16, 16, 16, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1,
+                 ALIGNED, ALIGNED, None, None, 0, None)
+    assert rc == -6  # workspace missing
+    rc, _ = call(lib, "mp_row_linear_partial", mp.MP_BF16, 16, 16, -1, ALIGNED, ALIGNED, ALIGNED, None)
+    assert rc == -2
+
+
+def test_vocab_and_norm_validation(lib):
+    rc, _ = call(lib, "mp_vocab_parallel_xent", 8, 6, 0, ALIGNED, ALIGNED, ALIGNED, None)
+    assert rc == -2  # Vi not a multiple of 4
+    arr = (ctypes.c_void_p * 1)(ALIGNED)
+    rc, _ = call(lib, "mp_vocab_xent_combine", 0, 8, arr, ALIGNED, None, None, None)
+    assert rc == -2
+    rc, _ = call(lib, "mp_vocab_parallel_xent_bwd", 8, 8, 0, ALIGNED, ALIGNED, ALIGNED, 1.0, mp.MP_BF16, ALIGNED,
+                 None)
+    assert rc == -8  # bf16 output may not alias the fp32 logits
+    rc, _ = call(lib, "mp_layernorm", mp.MP_BF16, 4, 8, ALIGNED, ALIGNED, ALIGNED, 0.0, ALIGNED, None, None, None)
+    assert rc == -8  # eps must be positive
+    rc, _ = call(lib, "mp_layernorm_bwd", mp.MP_BF16, 4, 8, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None,
+                 ALIGNED, ALIGNED, None, None, 0, None)
+    assert rc == -6
+    rc, _ = call(lib, "mp_shared_seed_dropout", mp.MP_BF16, 12, ALIGNED, ALIGNED, None, 0.5, 1, 2, 0, None)
+    assert rc == -2  # n not a multiple of 8
+
+
+def test_workspace_queries_are_pure(lib):
+    a = lib.mp_column_linear_gelu_bwd_workspace(mp.MP_BF16, 8192, 3072, 1536)
+    assert a == lib.mp_column_linear_gelu_bwd_workspace(mp.MP_BF16, 8192, 3072, 1536)
+    assert a >= 8192 * 1536 * 2
+    assert lib.mp_bias_grad_workspace(8192, 3072) >= 3072 * 4
+    assert lib.mp_layernorm_bwd_workspace(8192, 1024) >= 2 * 1024 * 4
