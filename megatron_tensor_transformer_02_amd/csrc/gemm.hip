@@ -17,14 +17,11 @@
 //
 // Epilogues: bias + activation (+ pre-activation save), activation gradient,
 // or fp32 split-K partials followed by a fixed-order reduce (deterministic).
+#include "gemm.h"
 #include "mfma.h"
 
 namespace mp {
 
-int colsum(mp_dtype dt, int64_t rows, int64_t cols, const void* dy, float* out, void* ws, hipStream_t s);
-size_t colsum_workspace(int64_t rows, int64_t cols);
-
-enum Epilogue { EPI_STORE = 0, EPI_SPLITK = 1, EPI_DACT = 2 };
 
 struct GemmArgs {
   int64_t M, N, K;
@@ -59,73 +56,6 @@ __device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles
   tn = inner / gsz;
 }
 
-// Global -> register -> LDS loader of one R x 64 operand tile.  Loads go
-// through a buffer resource whose base is the tile's first row (K-contiguous)
-// or first column (MN-contiguous); an element outside the matrix or past the
-// k-range gets an out-of-range offset, which the hardware returns as zeros.
-template <int R, bool KC>
-struct TileLoader {
-  static constexpr int NBLK = KC ? 0 : (R + 255) / 256;    // 8x8 blocks per thread
-  static constexpr int NREG = KC ? R / 32 : 8 * NBLK;
-  uint4 reg[NREG];
-
-  // Resource for rows [row0, rows) of a K-contiguous matrix with row stride
-  // `ld`, or for columns [row0, ld) of an MN-contiguous matrix of `kdim` rows.
-  __device__ __forceinline__ static BufRes resource(const uint16_t* base, int64_t ld, int64_t row0, int64_t rows,
-                                                    int64_t kdim) {
-    if constexpr (KC) return make_bufres(base + row0 * ld, (rows - row0) * ld * 2);
-    else return make_bufres(base + row0, (kdim * ld - row0) * 2);
-  }
-
-  __device__ __forceinline__ void load(const BufRes& rs, int64_t ld, int64_t row0, int64_t rows, int64_t k0,
-                                       int64_t kend, int tid) {
-    if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int idx = tid + 256 * i;
-        const int64_t r = idx >> 3;
-        const int64_t gk = k0 + (idx & 7) * 8;
-        const bool ok = row0 + r < rows && gk < kend;
-        reg[i] = buf_load16(rs, ok ? static_cast<uint32_t>((r * ld + gk) * 2) : kBufOOB);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NBLK; ++b) {
-        const int idx = tid + 256 * b;
-        const int64_t mm = (idx >> 3) * 8;
-        const int64_t gk = k0 + (idx & 7) * 8;
-        const bool ok = idx < R && row0 + mm < rows;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          reg[8 * b + kk] =
-              buf_load16(rs, (ok && gk + kk < kend) ? static_cast<uint32_t>(((gk + kk) * ld + mm) * 2) : kBufOOB);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint4* __restrict__ tile, int tid) const {
-    if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int idx = tid + 256 * i;
-        tile[lds_slot(idx >> 3, idx & 7)] = reg[i];
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NBLK; ++b) {
-        const int idx = tid + 256 * b;
-        if (idx < R) {
-          uint4 t[8];
-          transpose8x8_b16(reg + 8 * b, t);
-          const int mb = (idx >> 3) * 8, kb = idx & 7;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) tile[lds_slot(mb + i, kb)] = t[i];
-        }
-      }
-    }
-  }
-};
-
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
@@ -151,10 +81,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  TileLoader<BM, AK> la;
-  TileLoader<BN, BKC> lb;
-  const BufRes ra = TileLoader<BM, AK>::resource(A, g.lda, m0, g.M, g.K);
-  const BufRes rb = TileLoader<BN, BKC>::resource(B, g.ldb, n0, g.N, g.K);
+  TileLoader<BM, AK, 256> la;
+  TileLoader<BN, BKC, 256> lb;
+  const BufRes ra = TileLoader<BM, AK, 256>::resource(A, g.lda, m0, g.M, g.K);
+  const BufRes rb = TileLoader<BN, BKC, 256>::resource(B, g.ldb, n0, g.N, g.K);
   if (nk > 0) {
     la.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
     lb.load(rb, g.ldb, n0, g.N, kbeg, kend, tid);
@@ -367,7 +297,6 @@ __global__ __launch_bounds__(256) void dact_kernel(int64_t nvec, const void* __r
 
 // --------------------------------------------------------------- planning
 
-enum Layout { NT = 0, NN = 1, TN = 2 };  // (A K-contig, B K-contig), (K, MN), (MN, MN)
 
 struct Plan {
   int bm, bn, splits;
@@ -443,7 +372,7 @@ static size_t splitk_bytes(mp_dtype dt, int64_t M, int64_t N, int64_t K) {
 // lets the planner split K, using `ws` for the partials.
 int gemm(mp_dtype dt, Layout lay, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
          int64_t ldb, void* C, int64_t ldc, bool out_bf16, const void* bias, int act, void* zsave, bool allow_split,
-         void* ws, hipStream_t s, int epi = EPI_STORE, const void* zin = nullptr) {
+         void* ws, hipStream_t s, int epi, const void* zin) {
   if (M == 0 || N == 0) return MP_OK;
   GemmArgs g{};
   g.M = M; g.N = N; g.K = K; g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;

@@ -71,4 +71,73 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4* in, uint4* out) {
   }
 }
 
+// Global -> register -> LDS loader of one R x 64 operand tile, NT threads.  Loads go
+// through a buffer resource whose base is the tile's first row (K-contiguous)
+// or first column (MN-contiguous); an element outside the matrix or past the
+// k-range gets an out-of-range offset, which the hardware returns as zeros.
+template <int R, bool KC, int NT>
+struct TileLoader {
+  static constexpr int NBLK = KC ? 0 : (R + NT - 1) / NT;  // 8x8 blocks per thread
+  static constexpr int NREG = KC ? R * 8 / NT : 8 * NBLK;
+  static_assert(!KC || (R * 8) % NT == 0, "tile rows must cover the threads");
+  uint4 reg[NREG];
+
+  // Resource for rows [row0, rows) of a K-contiguous matrix with row stride
+  // `ld`, or for columns [row0, ld) of an MN-contiguous matrix of `kdim` rows.
+  __device__ __forceinline__ static BufRes resource(const uint16_t* base, int64_t ld, int64_t row0, int64_t rows,
+                                                    int64_t kdim) {
+    if constexpr (KC) return make_bufres(base + row0 * ld, (rows - row0) * ld * 2);
+    else return make_bufres(base + row0, (kdim * ld - row0) * 2);
+  }
+
+  // `res_row` = rows between the resource base and row0 (K-contiguous only).
+  __device__ __forceinline__ void load(const BufRes& rs, int64_t ld, int64_t row0, int64_t rows, int64_t k0,
+                                       int64_t kend, int tid, int64_t res_row = 0) {
+    if constexpr (KC) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int idx = tid + NT * i;
+        const int64_t r = idx >> 3;
+        const int64_t gk = k0 + (idx & 7) * 8;
+        const bool ok = row0 + r < rows && gk < kend;
+        reg[i] = buf_load16(rs, ok ? static_cast<uint32_t>(((res_row + r) * ld + gk) * 2) : kBufOOB);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int idx = tid + NT * b;
+        const int64_t mm = (idx >> 3) * 8;
+        const int64_t gk = k0 + (idx & 7) * 8;
+        const bool ok = idx < R && row0 + mm < rows;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          reg[8 * b + kk] =
+              buf_load16(rs, (ok && gk + kk < kend) ? static_cast<uint32_t>(((gk + kk) * ld + mm) * 2) : kBufOOB);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint4* __restrict__ tile, int tid) const {
+    if constexpr (KC) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int idx = tid + NT * i;
+        tile[lds_slot(idx >> 3, idx & 7)] = reg[i];
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int idx = tid + NT * b;
+        if (idx < R) {
+          uint4 t[8];
+          transpose8x8_b16(reg + 8 * b, t);
+          const int mb = (idx >> 3) * 8, kb = idx & 7;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) tile[lds_slot(mb + i, kb)] = t[i];
+        }
+      }
+    }
+  }
+};
+
 }  // namespace mp
