@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the tensor-parallel shard's hot path on one MI355X.
+
+One step = one pass of the whole hot path on synthetic inputs already
+resident in HBM:
+
+* layer -- one rank's share (3 of 24 heads of 128, FFN 12288/8) of the
+  8.3B-config layer at N=8, forward + backward: LayerNorm, fused-QKV
+  attention, out-projection partial, 8-way shard reduce (+bias, shared-seed
+  dropout, residual), LayerNorm, column GEMM + GeLU, row GEMM partial, 8-way
+  reduce, then the backward of all of it including the two 8-way reduces of
+  the input-gradient partials.  The other 7 ranks' partials are computed
+  once in setup by emulating those ranks (untimed);
+* vocab -- one vocab shard of N=8 (6400 of 51200 rows, K=3072, 8x1024
+  tokens): embedding lookup + 8-way reduce, logits GEMM (fp32 out), per-shard
+  cross-entropy statistics, combine with the 7 sibling shards' statistics,
+  cross-entropy backward;
+* moe   -- the hottest expert-parallel shard (experts 0-7 of 256, Zipf(1.1)
+  top-8 routing of 4096 tokens, hidden 7168, expert FFN 2048 SwiGLU).
+
+``value`` is the layer's model TFLOP/s (forward + backward = 3x the forward
+FLOPs, attention counted on the causal half); the vocab cross-entropy's GB/s
+is reported beside it.  Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_flops(B, L, K, h, d, Fi):
+    """Forward FLOPs of one rank's layer share; attention on the causal half."""
+    T = B * L
+    qkv = 2 * T * K * 3 * h * d
+    attn = 2 * 2 * B * h * (L * (L + 1) / 2) * d
+    oproj = 2 * T * h * d * K
+    mlp = 2 * 2 * T * K * Fi
+    return qkv + attn + oproj + mlp
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--parts", default="layer,vocab,moe")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from megatron_tensor_transformer_02_amd import mp, synthetic as S
+    from megatron_tensor_transformer_02_amd.layer import VocabShard, make_ranks, run_ranks
+
+    torch.cuda.set_device(0)
+    rc = mp.mp_device_supported(0)
+    if rc != 0:
+        raise SystemExit(f"device 0 is not supported: {mp.mp_last_error()}")
+    cu = lambda t: t.to("cuda").contiguous()  # noqa: E731
+    parts = args.parts.split(",")
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------- layer setup
+    wl = S.WORKLOADS["mlm8b"]
+    B, L, K, H, d, n = wl.B, wl.L, wl.K, wl.heads, wl.d, wl.N
+    hi, Fi = H // n, wl.F // n
+    if "layer" in parts:
+        t0 = time.time()
+        prm = S.layer_params(wl)
+        x, dout = S.layer_activations(wl)
+        shared = {k: cu(prm[k]) for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "b_o", "b_b")}
+        shards = []
+        for i in range(n):
+            sh = S.rank_shard(prm, i, n, H, d)
+            shards.append({k: cu(v) for k, v in sh.items() if k != "heads"})
+        ranks = make_ranks(shards, shared, B, L, hi, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+        xd, dd = cu(x), cu(dout)
+        sib = run_ranks(ranks, xd, dd)  # the other ranks' partials stay in their buffers
+        r0 = ranks[0]
+        torch.cuda.synchronize()
+        log(f"layer setup {time.time() - t0:.1f}s")
+
+        def layer_step():
+            pa = r0.attn_partial(xd)
+            r0.attn_reduce([pa] + sib["attn"][1:], xd)
+            pm = r0.mlp_partial()
+            r0.mlp_reduce([pm] + sib["mlp"][1:])
+            pb = r0.mlp_bwd_partial(dd)
+            r0.mlp_bwd_reduce([pb] + sib["mlp_bwd"][1:], dd)
+            pq = r0.attn_bwd_partial()
+            r0.attn_bwd_reduce([pq] + sib["attn_bwd"][1:], xd)
+
+    # ------------------------------------------------------------- vocab setup
+    wv = S.WORKLOADS["vocab"]
+    Tv, V, Kv, nv = wv.T, wv.V, wv.K, wv.N
+    Vi = V // nv
+    if "vocab" in parts:
+        t0 = time.time()
+        vin = S.vocab_inputs(wv)
+        emb = cu(vin["emb"])
+        hidden, ids, labels = cu(vin["hidden"]), cu(vin["ids"]), cu(vin["labels"])
+        vshards = [VocabShard(emb[j * Vi:(j + 1) * Vi].contiguous(), j * Vi, Tv) for j in range(nv)]
+        emb_sib = [vs.embed_partial(ids) for vs in vshards]
+        tri_sib = []
+        for vs in vshards:
+            vs.logits(hidden)
+            tri_sib.append(vs.triples(labels))
+        del emb
+        v0 = vshards[0]
+        torch.cuda.synchronize()
+        log(f"vocab setup {time.time() - t0:.1f}s")
+
+        def vocab_step(ev=None):
+            e0 = v0.embed_partial(ids)
+            v0.embed_reduce([e0] + emb_sib[1:])
+            v0.logits(hidden)
+            if ev is not None:
+                ev[0].record(stream)
+            t0_ = v0.triples(labels)
+            if ev is not None:
+                ev[1].record(stream)
+            v0.combine([t0_] + tri_sib[1:])
+            v0.xent_bwd(labels, 1.0 / Tv)
+
+    # --------------------------------------------------------------- moe setup
+    wm = S.WORKLOADS["moe"]
+    if "moe" in parts:
+        t0 = time.time()
+        min_ = S.moe_inputs(wm)
+        mx, mids, mw = cu(min_["x"]), cu(min_["topk_ids"]), cu(min_["topk_w"])
+        mwgu, mwd = cu(min_["w_gu"]), cu(min_["w_d"])
+        ids_np = min_["topk_ids"].numpy()
+        R_hot = int(((ids_np >= 0) & (ids_np < wm.e_local)).sum())
+        del min_
+        mout = torch.empty((wm.T, wm.K), dtype=torch.bfloat16, device="cuda")
+        mperm = torch.empty(wm.T * wm.topk, dtype=torch.int32, device="cuda")
+        moffs = torch.empty(wm.e_local + 1, dtype=torch.int32, device="cuda")
+        mws = torch.empty(mp.lib().mp_grouped_expert_gemm_workspace(wm.T, wm.K, wm.Fe, wm.topk, wm.e_local),
+                          dtype=torch.uint8, device="cuda")
+        log(f"moe setup {time.time() - t0:.1f}s (hot shard rows R={R_hot})")
+
+        def moe_step():
+            mp.mp_grouped_expert_gemm(mx, mids, mw, mwgu, mwd, 0, mout, mperm, moffs, mws)
+
+    # ------------------------------------------------------------ timed steps
+    EV = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    col_events = []
+
+    def probe(tag):
+        e = EV()
+        e.record(stream)
+        col_events.append((tag, e))
+
+    def step(rec):
+        if "layer" in parts:
+            rec["layer"][0].record(stream)
+            layer_step()
+            rec["layer"][1].record(stream)
+        if "vocab" in parts:
+            rec["vocab"][0].record(stream)
+            vocab_step(rec["xent"])
+            rec["vocab"][1].record(stream)
+        if "moe" in parts:
+            rec["moe"][0].record(stream)
+            moe_step()
+            rec["moe"][1].record(stream)
+
+    mk = lambda: {k: (EV(), EV()) for k in ("layer", "vocab", "moe", "xent")}  # noqa: E731
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    if "layer" in parts:
+        r0.probe = probe
+    recs = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        rec = mk()
+        step(rec)
+        recs.append(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    if "layer" in parts:
+        r0.probe = None
+
+    def seg_ms(name):
+        return float(np.mean([r[name][0].elapsed_time(r[name][1]) for r in recs]))
+
+    ms_step = wall * 1e3 / args.steps
+    out = {"metric": "TP-shard layer fwd+bwd TFLOPS (% bf16 MFMA peak); vocab-xent GB/s (% HBM)",
+           "value": None, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "8.3B-config TP layer rank share (hidden 3072, 3 of 24 heads x 128, FFN 12288/8, "
+                                  "seq 1024, micro-batch 8, N=8) fwd+bwd; vocab-parallel xent shard (V 51200/8, "
+                                  "K 3072, 8x1024 tokens); MoE hot expert shard (8 of 256 experts, hidden 7168, "
+                                  "FFN 2048, 4096 tokens top-8 Zipf 1.1)",
+                      "global_batch": B, "seq_len": L, "parallelism": "one rank of tp8 (N=8 emulated by the shard "
+                                                                        "reduce)"}}
+    roofs = []
+    if "layer" in parts:
+        fl = 3 * layer_flops(B, L, K, hi, d, Fi)
+        lay_ms = seg_ms("layer")
+        out["value"] = round(fl / (lay_ms * 1e-3) / 1e12, 2)
+        out["layer_ms"] = round(lay_ms, 4)
+        out["layer_pct_bf16_peak"] = round(100 * out["value"] / PEAK_BF16_TFLOPS, 2)
+        col = [b.elapsed_time(e) for (tb, b), (te, e) in zip(col_events[0::2], col_events[1::2])]
+        col_ms = float(np.mean(col))
+        col_fl = 2.0 * B * L * K * Fi
+        ach = col_fl / (col_ms * 1e-3) / 1e12
+        roofs.append({"kernel": "column-parallel GEMM + GeLU (gemm_bf16_kernel, act=erf) [8192x3072]x[1536x3072]^T",
+                      "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                      "avg_launch_us": round(col_ms * 1e3, 2), "algorithmic_per_launch": col_fl})
+    if "vocab" in parts:
+        xs = [r["xent"][0].elapsed_time(r["xent"][1]) for r in recs]
+        x_ms = float(np.mean(xs))
+        xbytes = Tv * Vi * 4.0 + Tv * 4 + Tv * 12
+        gbps = xbytes / (x_ms * 1e-3) / 1e9
+        out["vocab_ms"] = round(seg_ms("vocab"), 4)
+        out["xent_GBps"] = round(gbps, 1)
+        out["xent_pct_hbm"] = round(100 * gbps / PEAK_HBM_GBPS, 2)
+        # The logits (210 MB) are written just before by the logits GEMM and may be
+        # served from the 256 MB Infinity Cache; also time the pass cold.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = []
+        for _ in range(10):
+            flush.fill_(1)
+            b_, e_ = EV(), EV()
+            b_.record(stream)
+            v0.triples(labels)
+            e_.record(stream)
+            torch.cuda.synchronize()
+            cold.append(b_.elapsed_time(e_))
+        del flush
+        cold_ms = float(np.median(cold))
+        out["xent_cold_GBps"] = round(xbytes / (cold_ms * 1e-3) / 1e9, 1)
+        roofs.append({"kernel": "vocab xent triples (xent_triples_kernel) [8192x6400] fp32", "bound": "hbm",
+                      "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "avg_launch_us": round(x_ms * 1e3, 2),
+                      "cold_GBps": out["xent_cold_GBps"], "algorithmic_per_launch": xbytes})
+    if "moe" in parts:
+        moe_ms = seg_ms("moe")
+        moe_fl = R_hot * 2.0 * (wm.K * 2 * wm.Fe + wm.Fe * wm.K)
+        out["moe_ms"] = round(moe_ms, 4)
+        out["moe_TFLOPS"] = round(moe_fl / (moe_ms * 1e-3) / 1e12, 2)
+        out["moe_rows"] = R_hot
+    if roofs:
+        out["roofline"] = roofs[0]
+        out["rooflines"] = roofs
+
+    if not args.no_cpu_baseline and "layer" in parts:
+        out["cpu_baseline"] = cpu_baseline(wl, hi, Fi)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, hi, Fi, budget_s=20.0):
+    """The fp64 oracle's layer forward + backward on the same rank-share shape,
+    over a bounded number of sequences (sized to ~budget_s), in TFLOP/s."""
+    import oracle as O
+    from megatron_tensor_transformer_02_amd import synthetic as S
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    L, K, d = wl.L, wl.K, wl.d
+    prm = S.layer_params(wl, heads=hi, d=d, F=Fi)
+    op = {k: v.double().numpy() for k, v in prm.items()}
+
+    def run(nseq):
+        x, dout = S.layer_activations(wl, T=nseq * L)
+        x, dout = x.double().numpy(), dout.double().numpy()
+        t0 = time.perf_counter()
+        c = O.layer_forward(op, x, nseq, L, hi, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+        O.layer_backward(op, x, c, dout, nseq, L, hi, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nseq = int(max(1, min(wl.B, math.floor(budget_s / max(t1, 1e-3)))))
+    t = run(nseq) if nseq > 1 else t1
+    fl = 3 * layer_flops(nseq, L, K, hi, d, Fi)
+    return {"value": round(fl / t / 1e12, 4), "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"rank-share layer fwd+bwd on {nseq} of {wl.B} sequences (L={L}), fp64 numpy, {t:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

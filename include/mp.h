@@ -256,8 +256,9 @@ size_t mp_grouped_expert_gemm_workspace(int64_t T, int64_t Hd, int64_t Fe, int t
  *  4. unpermute: out[t] = sum over local picks k (ascending) of
  *     topk_w[t,k] * y(t,k), fp32 sum, zeros for tokens without local picks.
  * X [T,Hd] bf16, topk_ids [T,topk] int32, topk_w [T,topk] fp32,
- * out [T,Hd] bf16, perm_picks [T*min(topk,E_loc)] int32 (rows >= R untouched),
- * expert_offsets [E_loc+1] int32; ws >= mp_grouped_expert_gemm_workspace(). */
+ * out [T,Hd] bf16, perm_picks [T*topk] int32 or NULL (entries >= R untouched;
+ * with distinct ids per token R <= T*min(topk,E_loc)), expert_offsets
+ * [E_loc+1] int32 or NULL; ws >= mp_grouped_expert_gemm_workspace(). */
 int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
                            int e_start, const void* X, const int32_t* topk_ids,
                            const float* topk_w, const void* W_gu, const void* W_d, void* out,

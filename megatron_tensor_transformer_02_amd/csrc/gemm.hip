@@ -56,7 +56,7 @@ __device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles
   tn = inner / gsz;
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int ACT>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
         float z[8];
         unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.zin) + o), z);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) val[e] *= act_grad(z[e], g.act);
+        for (int e = 0; e < 8; ++e) val[e] *= act_grad(z[e], ACT);
       } else {
         if (g.bias != nullptr) {
           float b[8];
@@ -176,9 +176,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
             reinterpret_cast<float4*>(static_cast<float*>(g.zsave) + o)[1] = make_float4(val[4], val[5], val[6], val[7]);
           }
         }
-        if (g.act != MP_ACT_NONE) {
+        if constexpr (ACT != MP_ACT_NONE) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) val[e] = act_fwd(val[e], g.act);
+          for (int e = 0; e < 8; ++e) val[e] = act_fwd(val[e], ACT);
         }
       }
       if (g.out_bf16) {
@@ -332,24 +332,33 @@ static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split) {
   return best;
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int ACT>
 static void launch_bf16_tile(const GemmArgs& g, int splits, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(g.tiles_m * g.tiles_n), 1, static_cast<unsigned>(splits));
-  gemm_bf16_kernel<BM, BN, AK, BKC, EPI><<<grid, 256, 0, s>>>(g);
+  gemm_bf16_kernel<BM, BN, AK, BKC, EPI, ACT><<<grid, 256, 0, s>>>(g);
 }
 
-template <bool AK, bool BKC, int EPI>
+template <bool AK, bool BKC, int EPI, int ACT>
 static void launch_bf16_layout(const GemmArgs& g, const Plan& p, hipStream_t s) {
-  if (p.bm == 256 && p.bn == 256) launch_bf16_tile<256, 256, AK, BKC, EPI>(g, p.splits, s);
-  else if (p.bm == 256 && p.bn == 128) launch_bf16_tile<256, 128, AK, BKC, EPI>(g, p.splits, s);
-  else launch_bf16_tile<128, 128, AK, BKC, EPI>(g, p.splits, s);
+  if (p.bm == 256 && p.bn == 256) launch_bf16_tile<256, 256, AK, BKC, EPI, ACT>(g, p.splits, s);
+  else if (p.bm == 256 && p.bn == 128) launch_bf16_tile<256, 128, AK, BKC, EPI, ACT>(g, p.splits, s);
+  else launch_bf16_tile<128, 128, AK, BKC, EPI, ACT>(g, p.splits, s);
 }
 
-template <int EPI>
-static void launch_bf16_epi(Layout lay, const GemmArgs& g, const Plan& p, hipStream_t s) {
-  if (lay == NT) launch_bf16_layout<true, true, EPI>(g, p, s);
-  else if (lay == NN) launch_bf16_layout<true, false, EPI>(g, p, s);
-  else launch_bf16_layout<false, false, EPI>(g, p, s);
+// Instantiated combinations: the forward (NT) with each activation, the
+// input-gradient (NN) and weight-gradient (TN, plain or split-K) GEMMs.
+static void launch_bf16(Layout lay, int epi, int act, const GemmArgs& g, const Plan& p, hipStream_t s) {
+  if (lay == NT) {
+    if (act == MP_ACT_GELU_ERF) launch_bf16_layout<true, true, EPI_STORE, MP_ACT_GELU_ERF>(g, p, s);
+    else if (act == MP_ACT_GELU_TANH) launch_bf16_layout<true, true, EPI_STORE, MP_ACT_GELU_TANH>(g, p, s);
+    else launch_bf16_layout<true, true, EPI_STORE, MP_ACT_NONE>(g, p, s);
+  } else if (lay == NN) {
+    launch_bf16_layout<true, false, EPI_STORE, MP_ACT_NONE>(g, p, s);
+  } else if (epi == EPI_SPLITK) {
+    launch_bf16_layout<false, false, EPI_SPLITK, MP_ACT_NONE>(g, p, s);
+  } else {
+    launch_bf16_layout<false, false, EPI_STORE, MP_ACT_NONE>(g, p, s);
+  }
 }
 
 template <int EPI>
@@ -386,15 +395,16 @@ int gemm(mp_dtype dt, Layout lay, int64_t M, int64_t N, int64_t K, const void* A
     g.k_split = p.k_split;
     if (p.splits > 1) {
       if (ws == nullptr) return fail(MP_ERR_WORKSPACE, "gemm: split-K needs a workspace");
+      if (lay != TN) return fail(MP_ERR_UNSUPPORTED, "gemm: split-K is built for the weight-gradient layout only");
       g.partial = static_cast<float*>(ws);
-      launch_bf16_epi<EPI_SPLITK>(lay, g, p, s);
+      launch_bf16(lay, EPI_SPLITK, MP_ACT_NONE, g, p, s);
       const int64_t nq = M * (N / 4);
       splitk_reduce_kernel<<<static_cast<unsigned>(ceil_div(nq, 256)), 256, 0, s>>>(g.partial, p.splits, M, N, ldc,
                                                                                      g.out_bf16, C);
-    } else if (epi == EPI_DACT) {
-      launch_bf16_epi<EPI_DACT>(lay, g, p, s);
     } else {
-      launch_bf16_epi<EPI_STORE>(lay, g, p, s);
+      if (epi != EPI_STORE || (lay != NT && act != MP_ACT_NONE))
+        return fail(MP_ERR_UNSUPPORTED, "gemm: epilogue not built for this layout");
+      launch_bf16(lay, EPI_STORE, act, g, p, s);
     }
   } else {
     g.k_split = K > 0 ? K : 16;

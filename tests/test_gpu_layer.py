@@ -1,0 +1,165 @@
+"""GPU parity of whole chains against the oracle's unpartitioned computation.
+
+* tiny: the MLP split in two column/row shards plus the vocab-parallel
+  cross-entropy split in two, fp32, forward and backward (the partition
+  identities of MLM-notes "Model Parallel Transformers" at N=2);
+* gpt2m: the full pre-LN layer at N=1 in bf16, forward and backward;
+* mlm8b: the 8.3B-config layer with all 8 ranks emulated on the GPU and the
+  shard reduce standing in for the all-reduce; the reduced output and input
+  gradient must equal the oracle's unpartitioned layer.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import TOL, XENT_ABS, cu, f64, rel_frobenius, say, sync
+from megatron_tensor_transformer_02_amd import mp, synthetic as S
+from megatron_tensor_transformer_02_amd.layer import RankLayer, make_ranks, run_ranks
+
+pytestmark = pytest.mark.gpu
+
+
+def shared_params(prm):
+    return {k: cu(prm[k]) for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "b_o", "b_b")}
+
+
+def test_tiny_mlp_xent_chain_n2():
+    say("tiny chain")
+    wl = S.WORKLOADS["tiny"]
+    T, K, F, V, n, p = wl.T, wl.K, wl.F, wl.V, wl.N, wl.p
+    prm = S.layer_params(wl, heads=1, d=8)
+    x, _ = S.layer_activations(wl)
+    voc = S.vocab_inputs(wl)
+    emb, labels = voc["emb"], voc["labels"]
+    fi, vi = F // n, V // n
+    seed, off = wl.seed, 3
+    xd, ld = cu(x), cu(labels)
+    # forward: column -> row partials -> reduce (+bias, dropout) -> vocab shards
+    ys, zs, parts = [], [], []
+    for i in range(n):
+        a_i, ab_i = cu(prm["w_a"][i * fi:(i + 1) * fi]), cu(prm["b_a"][i * fi:(i + 1) * fi])
+        b_i = cu(prm["w_b"][:, i * fi:(i + 1) * fi])
+        y = torch.empty((T, fi), device="cuda")
+        z = torch.empty((T, fi), device="cuda")
+        mp.mp_column_linear_gelu(xd, a_i, ab_i, "erf", y, z)
+        pp = torch.empty((T, K), device="cuda")
+        mp.mp_row_linear_partial(y, b_i, pp)
+        ys.append(y), zs.append(z), parts.append(pp)
+    o = torch.empty((T, K), device="cuda")
+    mp.mp_shard_reduce(parts, o, cu(prm["b_b"]), None, p, seed, off)
+    e_sh = [cu(emb[j * vi:(j + 1) * vi]) for j in range(n)]
+    zl = [torch.empty((T, vi), device="cuda") for _ in range(n)]
+    tr = [torch.empty((T, 3), device="cuda") for _ in range(n)]
+    for j in range(n):
+        mp.mp_column_linear_gelu(o, e_sh[j], None, "none", zl[j])
+        mp.mp_vocab_parallel_xent(zl[j], ld, j * vi, tr[j])
+    loss = torch.empty(T, device="cuda")
+    stats = torch.empty((T, 2), device="cuda")
+    mp.mp_vocab_xent_combine(tr, loss, stats)
+    # backward
+    g = 1.0 / T
+    do_parts, de = [], []
+    for j in range(n):
+        mp.mp_vocab_parallel_xent_bwd(zl[j], ld, j * vi, stats, g, zl[j])
+        dop = torch.empty((T, K), device="cuda")
+        dej = torch.empty((vi, K), device="cuda")
+        mp.mp_column_linear_gelu_bwd(o, e_sh[j], None, zl[j], "none", dop, dej)
+        do_parts.append(dop), de.append(dej)
+    do = torch.empty((T, K), device="cuda")
+    mp.mp_shard_reduce(do_parts, do)
+    dpre = torch.empty((T, K), device="cuda")
+    mp.mp_shared_seed_dropout(do, dpre, p, seed, off)
+    db = torch.empty(K, device="cuda")
+    mp.mp_bias_grad(dpre, db)
+    dx_parts, da, dab, dbw = [], [], [], []
+    for i in range(n):
+        a_i, b_i = cu(prm["w_a"][i * fi:(i + 1) * fi]), cu(prm["w_b"][:, i * fi:(i + 1) * fi])
+        dy = torch.empty((T, fi), device="cuda")
+        dbi = torch.empty((K, fi), device="cuda")
+        mp.mp_row_linear_partial_bwd(ys[i], b_i, dpre, dy, dbi)
+        dxp = torch.empty((T, K), device="cuda")
+        dai = torch.empty((fi, K), device="cuda")
+        dabi = torch.empty(fi, device="cuda")
+        mp.mp_column_linear_gelu_bwd(xd, a_i, zs[i], dy, "erf", dxp, dai, dabi)
+        dx_parts.append(dxp), da.append(dai), dab.append(dabi), dbw.append(dbi)
+    dx = torch.empty((T, K), device="cuda")
+    mp.mp_shard_reduce(dx_parts, dx)
+    sync()
+    # oracle: the unpartitioned chain
+    A, a, B, b = (f64(prm[k]) for k in ("w_a", "b_a", "w_b", "b_b"))
+    X, E = f64(x), f64(emb)
+    Y, Z1 = O.column_linear(X, A, a)
+    Ow, _ = O.shard_reduce([O.row_linear_partial(Y, B)], b, None, p, seed, off)
+    assert rel_frobenius(f64(o), Ow) <= TOL["f32"]
+    Zl = Ow @ E.T
+    want_loss = O.full_cross_entropy(Zl, labels.numpy())
+    assert np.max(np.abs(f64(loss) - want_loss)) <= XENT_ABS
+    dZl = O.full_cross_entropy_grad(Zl, labels.numpy(), g)
+    dO = dZl @ E
+    assert rel_frobenius(f64(do), dO) <= TOL["f32"]
+    assert rel_frobenius(np.concatenate([f64(t) for t in de]), dZl.T @ Ow) <= TOL["f32"]
+    dP, wdb = O.shard_reduce_bwd(dO, p, seed, off)
+    assert rel_frobenius(f64(db), wdb) <= TOL["f32"]
+    dY, wdB = O.row_linear_partial_bwd(Y, B, dP)
+    assert rel_frobenius(np.concatenate([f64(t) for t in dbw], axis=1), wdB) <= TOL["f32"]
+    wdx, wdA, wda = O.column_linear_bwd(X, A, Z1, dY)
+    assert rel_frobenius(np.concatenate([f64(t) for t in da]), wdA) <= TOL["f32"]
+    assert rel_frobenius(np.concatenate([f64(t) for t in dab]), wda) <= TOL["f32"]
+    assert rel_frobenius(f64(dx), wdx) <= TOL["f32"]
+
+
+def _oracle_params(prm):
+    return {k: f64(v) for k, v in prm.items()}
+
+
+@pytest.mark.parametrize("B", [2, 8])
+def test_gpt2m_full_layer_n1(B):
+    say("gpt2m layer", B)
+    wl = S.WORKLOADS["gpt2m"]
+    L, K, H, d = wl.L, wl.K, wl.heads, wl.d
+    prm = S.layer_params(wl)
+    x, dout = S.layer_activations(wl, T=B * L)
+    shard = {k: cu(v) for k, v in S.rank_shard(prm, 0, 1, H, d).items() if k != "heads"}
+    r = RankLayer(shard, shared_params(prm), B, L, H, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+    xd, dd = cu(x), cu(dout)
+    run_ranks([r], xd, dd)
+    sync()
+    seqs = B if B <= 2 else 1  # whole batch, or sequence 0 of the full batch
+    rows = slice(0, seqs * L)
+    op = _oracle_params(prm)
+    c = O.layer_forward(op, f64(x)[rows], seqs, L, H, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+    assert rel_frobenius(f64(r.out)[rows], c["out"]) <= TOL["bf16"]
+    gr = O.layer_backward(op, f64(x)[rows], c, f64(dout)[rows], seqs, L, H, d, p=wl.p, seed=wl.seed,
+                          offsets=(1, 2))
+    assert rel_frobenius(f64(r.dx)[rows], gr["x"]) <= TOL["bf16"]
+    if seqs == B:
+        for k in ("w_qkv", "b_qkv", "w_o", "b_o", "w_a", "b_a", "w_b", "b_b", "ln1_g", "ln1_b", "ln2_g", "ln2_b"):
+            assert rel_frobenius(f64(r.g[k]), gr[k]) <= TOL["bf16"], k
+
+
+@pytest.mark.slow
+def test_mlm8b_eight_ranks_compose_to_full_layer():
+    say("mlm8b 8 ranks")
+    wl = S.WORKLOADS["mlm8b"]
+    B, L, K, H, d, n = wl.B, wl.L, wl.K, wl.heads, wl.d, wl.N
+    prm = S.layer_params(wl)
+    x, dout = S.layer_activations(wl)
+    shared = shared_params(prm)
+    shards = []
+    for i in range(n):
+        sh = S.rank_shard(prm, i, n, H, d)
+        shards.append({k: cu(v) for k, v in sh.items() if k != "heads"})
+    ranks = make_ranks(shards, shared, B, L, H // n, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+    xd, dd = cu(x), cu(dout)
+    run_ranks(ranks, xd, dd)
+    sync()
+    for r in ranks[1:]:
+        assert torch.equal(r.out, ranks[0].out) and torch.equal(r.dx, ranks[0].dx)
+    rows = slice(0, L)  # sequence 0 through the unpartitioned oracle
+    op = _oracle_params(prm)
+    c = O.layer_forward(op, f64(x)[rows], 1, L, H, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+    assert rel_frobenius(f64(ranks[0].out)[rows], c["out"]) <= TOL["bf16"]
+    gr = O.layer_backward(op, f64(x)[rows], c, f64(dout)[rows], 1, L, H, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+    assert rel_frobenius(f64(ranks[0].dx)[rows], gr["x"]) <= TOL["bf16"]
