@@ -81,45 +81,72 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  TileLoader<BM, AK, 256> la;
-  TileLoader<BN, BKC, 256> lb;
+  // Two register stages of prefetch: while tile kt is multiplied out of
+  // LDS[kt & 1], tile kt+1 waits in one register set (it is written to the
+  // other LDS buffer halfway through tile kt's MFMAs) and tile kt+2 is in
+  // flight into the other set.  Each load thus has two k-steps of MFMA work
+  // to arrive.  The loop is unrolled by two so the register sets keep fixed
+  // names.
+  TileLoader<BM, AK, 256> la0, la1;
+  TileLoader<BN, BKC, 256> lb0, lb1;
   const BufRes ra = TileLoader<BM, AK, 256>::resource(A, g.lda, m0, g.M, g.K);
   const BufRes rb = TileLoader<BN, BKC, 256>::resource(B, g.ldb, n0, g.N, g.K);
   if (nk > 0) {
-    la.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
-    lb.load(rb, g.ldb, n0, g.N, kbeg, kend, tid);
-    la.store(lds[0], tid);
-    lb.store(lds[0] + A_SLOTS, tid);
+    la0.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
+    lb0.load(rb, g.ldb, n0, g.N, kbeg, kend, tid);
+  }
+  if (nk > 1) {
+    la1.load(ra, g.lda, m0, g.M, kbeg + 64, kend, tid);
+    lb1.load(rb, g.ldb, n0, g.N, kbeg + 64, kend, tid);
+  }
+  if (nk > 0) {
+    la0.store(lds[0], tid);
+    lb0.store(lds[0] + A_SLOTS, tid);
   }
   __syncthreads();
 
   const int frow = lane & 31, fgrp = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(ra, g.lda, m0, g.M, kbeg + (kt + 1) * 64, kend, tid);
-      lb.load(rb, g.ldb, n0, g.N, kbeg + (kt + 1) * 64, kend, tid);
+  auto mma = [&](const uint4* tile, int ks) {
+    const int ch = 2 * ks + fgrp;
+    uint4 af[TM], bfr[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = tile[lds_slot(wm * WM + i * 32 + frow, ch)];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[j] = tile[A_SLOTS + lds_slot(wn * WN + j * 32 + frow, ch)];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    // even step: tile kt in LDS[0]; la1/lb1 hold tile kt+1; la0/lb0 refill.
+    if (kt + 2 < nk) {
+      la0.load(ra, g.lda, m0, g.M, kbeg + (kt + 2) * 64, kend, tid);
+      lb0.load(rb, g.ldb, n0, g.N, kbeg + (kt + 2) * 64, kend, tid);
     }
-    const uint4* ta = lds[cur];
-    const uint4* tb = lds[cur] + A_SLOTS;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = 2 * ks + fgrp;
-      uint4 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = ta[lds_slot(wm * WM + i * 32 + frow, ch)];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = tb[lds_slot(wn * WN + j * 32 + frow, ch)];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
+    mma(lds[0], 0);
+    mma(lds[0], 1);
+    if (kt + 1 < nk) {
+      la1.store(lds[1], tid);
+      lb1.store(lds[1] + A_SLOTS, tid);
     }
-    if (more) {
-      la.store(lds[cur ^ 1], tid);
-      lb.store(lds[cur ^ 1] + A_SLOTS, tid);
+    mma(lds[0], 2);
+    mma(lds[0], 3);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    // odd step: tile kt+1 in LDS[1]; la0/lb0 hold tile kt+2; la1/lb1 refill.
+    if (kt + 3 < nk) {
+      la1.load(ra, g.lda, m0, g.M, kbeg + (kt + 3) * 64, kend, tid);
+      lb1.load(rb, g.ldb, n0, g.N, kbeg + (kt + 3) * 64, kend, tid);
     }
+    mma(lds[1], 0);
+    mma(lds[1], 1);
+    if (kt + 2 < nk) {
+      la0.store(lds[0], tid);
+      lb0.store(lds[0] + A_SLOTS, tid);
+    }
+    mma(lds[1], 2);
+    mma(lds[1], 3);
     __syncthreads();
   }
 

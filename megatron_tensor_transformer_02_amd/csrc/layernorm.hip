@@ -176,17 +176,36 @@ __global__ __launch_bounds__(256) void layernorm_bwd_param_kernel(int64_t T, int
   }
 }
 
+// Sums the slab partials of dgamma (columns [0, K)) and dbeta ([K, 2K)):
+// the same deterministic 4-group scheme as the column-sum final pass.
 __global__ __launch_bounds__(256) void layernorm_param_final_kernel(const float* __restrict__ partial, int64_t slabs,
                                                                     int64_t K, float* __restrict__ dgamma,
                                                                     float* __restrict__ dbeta) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (c >= 2 * K) return;
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
+  const int64_t w = 2 * K;
   float t = 0.0f;
-  for (int64_t s = 0; s < slabs; ++s) t += partial[s * 2 * K + c];
+  if (c < w) {
+    int64_t s = q;
+    for (; s + 12 < slabs; s += 16) {
+      const float a0 = partial[s * w + c], a1 = partial[(s + 4) * w + c];
+      const float a2 = partial[(s + 8) * w + c], a3 = partial[(s + 12) * w + c];
+      t += a0;
+      t += a1;
+      t += a2;
+      t += a3;
+    }
+    for (; s < slabs; s += 4) t += partial[s * w + c];
+  }
+  red[q][cl] = t;
+  __syncthreads();
+  if (q != 0 || c >= w) return;
+  const float v = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
   if (c < K) {
-    if (dgamma) dgamma[c] = t;
+    if (dgamma) dgamma[c] = v;
   } else if (dbeta) {
-    dbeta[c - K] = t;
+    dbeta[c - K] = v;
   }
 }
 
@@ -226,8 +245,6 @@ struct LnBwd {
     return check_launch("mp_layernorm_bwd");
   }
 };
-
-static constexpr int64_t kMaxLnK = 64 * 16 * 8;  // 16 vectors of 8 bf16 per lane
 
 }  // namespace mp
 
@@ -298,7 +315,7 @@ extern "C" int mp_layernorm_bwd(mp_dtype dtype, int64_t T, int64_t K, const void
     else
       layernorm_bwd_param_kernel<false><<<grid, 256, 0, s>>>(T, K, x, mean, rstd, dy, slab_rows, static_cast<float*>(ws));
   }
-  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(2 * K, 256)), 256, 0, s>>>(
+  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(2 * K, 64)), 256, 0, s>>>(
       static_cast<const float*>(ws), slabs, K, dgamma, dbeta);
   return check_launch("mp_layernorm_bwd");
 }
