@@ -460,7 +460,7 @@ extern "C" int mp_head_attention(mp_dtype dtype, int B, int L, int K, int h, int
   MP_REQUIRE_ALIGN(qkv);
   const int64_t T = static_cast<int64_t>(B) * L, N3 = 3LL * h * d;
   if (int rc = gemm(MP_BF16, NT, T, N3, K, X, K, Wqkv_i, K, qkv, N3, true, bqkv_i, MP_ACT_NONE, nullptr, false,
-                    nullptr, s))
+                    nullptr, 0, s))
     return rc;
   AttnArgs a = make_args(B, L, h, d, causal);
   a.qkv = static_cast<const uint16_t*>(qkv);
@@ -532,11 +532,11 @@ extern "C" int mp_head_attention_bwd(mp_dtype dtype, int B, int L, int K, int h,
   if (int rc = check_launch(fn)) return rc;
   // dX_partial[T,K] = dqkv[T,N3] * Wqkv_i[N3,K]
   if (int rc = gemm(MP_BF16, NN, T, K, N3, dqkv, N3, Wqkv_i, K, dX_partial, K, true, nullptr, MP_ACT_NONE, nullptr,
-                    false, nullptr, s))
+                    false, nullptr, 0, s))
     return rc;
   // dWqkv_i[N3,K] = dqkv^T * X
   if (int rc = gemm(MP_BF16, TN, N3, K, T, dqkv, N3, X, K, dWqkv_i, K, false, nullptr, MP_ACT_NONE, nullptr, true,
-                    ws2, s))
+                    ws2, ws_bytes - dqkv_bytes - dvec_bytes, s))
     return rc;
   if (dbqkv_i != nullptr) return colsum(MP_BF16, T, N3, dqkv, dbqkv_i, ws2, s);
   return MP_OK;

@@ -17,7 +17,7 @@ enum Layout { NT = 0, NN = 1, TN = 2 };
 // (gemm_splitk_workspace bytes) for the partials.
 int gemm(mp_dtype dt, Layout lay, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
          int64_t ldb, void* C, int64_t ldc, bool out_bf16, const void* bias, int act, void* zsave, bool allow_split,
-         void* ws, hipStream_t s, int epi = EPI_STORE, const void* zin = nullptr);
+         void* ws, size_t ws_bytes, hipStream_t s, int epi = EPI_STORE, const void* zin = nullptr);
 size_t gemm_splitk_workspace(mp_dtype dt, int64_t M, int64_t N, int64_t K);
 
 // Deterministic column sums of a [rows, cols] matrix into out[cols] (fp32).

@@ -17,6 +17,9 @@
 //
 // Epilogues: bias + activation (+ pre-activation save), activation gradient,
 // or fp32 split-K partials followed by a fixed-order reduce (deterministic).
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "gemm.h"
 #include "mfma.h"
 
@@ -56,14 +59,17 @@ __device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles
   tn = inner / gsz;
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int ACT>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+template <int BM, int BN, int NW, bool AK, bool BKC, int EPI, int ACT>
+__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
+  // NW = 8: 2 x 4 waves (two waves per SIMD, so one wave's LDS/memory waits
+  // overlap the other's MFMAs); NW = 4: 2 x 2 waves.
+  constexpr int NT = 64 * NW, WCOLS = NW == 8 ? 4 : 2, WROWS = NW / WCOLS;
+  constexpr int WM = BM / WROWS, WN = BN / WCOLS, TM = WM / 32, TN = WN / 32;
   constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;
   __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WCOLS, wn = wave % WCOLS;
   int tmi, tni;
   map_tile(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, g.group_m, tmi, tni);
   const int64_t m0 = static_cast<int64_t>(tmi) * BM, n0 = static_cast<int64_t>(tni) * BN;
@@ -81,72 +87,52 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Two register stages of prefetch: while tile kt is multiplied out of
-  // LDS[kt & 1], tile kt+1 waits in one register set (it is written to the
-  // other LDS buffer halfway through tile kt's MFMAs) and tile kt+2 is in
-  // flight into the other set.  Each load thus has two k-steps of MFMA work
-  // to arrive.  The loop is unrolled by two so the register sets keep fixed
-  // names.
-  TileLoader<BM, AK, 256> la0, la1;
-  TileLoader<BN, BKC, 256> lb0, lb1;
-  const BufRes ra = TileLoader<BM, AK, 256>::resource(A, g.lda, m0, g.M, g.K);
-  const BufRes rb = TileLoader<BN, BKC, 256>::resource(B, g.ldb, n0, g.N, g.K);
+  // One register stage of prefetch: tile kt+1 is loaded from global memory
+  // into registers while tile kt is multiplied out of LDS[kt & 1], then
+  // written to the other LDS buffer; one barrier per k-tile.
+  TileLoader<BM, AK, NT> la;
+  TileLoader<BN, BKC, NT> lb;
+  const BufRes ra = TileLoader<BM, AK, NT>::resource(A, g.lda, m0, g.M, g.K);
+  const BufRes rb = TileLoader<BN, BKC, NT>::resource(B, g.ldb, n0, g.N, g.K);
+  // A transposing (MN-contiguous) loader keeps one 8x8 block per thread for
+  // only 256 of the 512 threads of an 8-wave tile; operand B's blocks go to
+  // the other half so both halves share the load and transpose work.
+  const int tid_b = (!BKC && NT == 512) ? (tid + 256) & 511 : tid;
   if (nk > 0) {
-    la0.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
-    lb0.load(rb, g.ldb, n0, g.N, kbeg, kend, tid);
-  }
-  if (nk > 1) {
-    la1.load(ra, g.lda, m0, g.M, kbeg + 64, kend, tid);
-    lb1.load(rb, g.ldb, n0, g.N, kbeg + 64, kend, tid);
-  }
-  if (nk > 0) {
-    la0.store(lds[0], tid);
-    lb0.store(lds[0] + A_SLOTS, tid);
+    la.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
+    lb.load(rb, g.ldb, n0, g.N, kbeg, kend, tid_b);
+    la.store(lds[0], tid);
+    lb.store(lds[0] + A_SLOTS, tid_b);
   }
   __syncthreads();
 
   const int frow = lane & 31, fgrp = lane >> 5;
-  auto mma = [&](const uint4* tile, int ks) {
-    const int ch = 2 * ks + fgrp;
-    uint4 af[TM], bfr[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = tile[lds_slot(wm * WM + i * 32 + frow, ch)];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[j] = tile[A_SLOTS + lds_slot(wn * WN + j * 32 + frow, ch)];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
-  };
-  for (int kt = 0; kt < nk; kt += 2) {
-    // even step: tile kt in LDS[0]; la1/lb1 hold tile kt+1; la0/lb0 refill.
-    if (kt + 2 < nk) {
-      la0.load(ra, g.lda, m0, g.M, kbeg + (kt + 2) * 64, kend, tid);
-      lb0.load(rb, g.ldb, n0, g.N, kbeg + (kt + 2) * 64, kend, tid);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load(ra, g.lda, m0, g.M, kbeg + (kt + 1) * 64, kend, tid);
+      lb.load(rb, g.ldb, n0, g.N, kbeg + (kt + 1) * 64, kend, tid_b);
     }
-    mma(lds[0], 0);
-    mma(lds[0], 1);
-    if (kt + 1 < nk) {
-      la1.store(lds[1], tid);
-      lb1.store(lds[1] + A_SLOTS, tid);
+    const uint4* ta = lds[cur];
+    const uint4* tb = lds[cur] + A_SLOTS;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = 2 * ks + fgrp;
+      uint4 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = ta[lds_slot(wm * WM + i * 32 + frow, ch)];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = tb[lds_slot(wn * WN + j * 32 + frow, ch)];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
     }
-    mma(lds[0], 2);
-    mma(lds[0], 3);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    // odd step: tile kt+1 in LDS[1]; la0/lb0 hold tile kt+2; la1/lb1 refill.
-    if (kt + 3 < nk) {
-      la1.load(ra, g.lda, m0, g.M, kbeg + (kt + 3) * 64, kend, tid);
-      lb1.load(rb, g.ldb, n0, g.N, kbeg + (kt + 3) * 64, kend, tid);
+    if (more) {
+      la.store(lds[cur ^ 1], tid);
+      lb.store(lds[cur ^ 1] + A_SLOTS, tid_b);
     }
-    mma(lds[1], 0);
-    mma(lds[1], 1);
-    if (kt + 2 < nk) {
-      la0.store(lds[0], tid);
-      lb0.store(lds[0] + A_SLOTS, tid);
-    }
-    mma(lds[1], 2);
-    mma(lds[1], 3);
     __syncthreads();
   }
 
@@ -330,26 +316,38 @@ struct Plan {
   int64_t k_split;
 };
 
-static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split) {
-  struct Cand { int bm, bn; double eff; };
-  const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.7}};
-  Plan best{256, 256, 1, static_cast<int64_t>(align_up(static_cast<size_t>(K > 0 ? K : 64), 64))};
-  double best_cost = 1e300;
+// Chooses the tile shape and the K split by estimated time (microseconds):
+// waves of workgroups x k-steps x the measured time of one 64-deep k-step of
+// that tile, plus, for a split, writing and re-reading the fp32 partials.
+// MP_GEMM_PLAN="bm,bn,splits" forces a plan (for tuning sweeps).
+static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split, Layout lay) {
+  // Measured on MI355X: one 64-deep k-step of a tile when every CU holds
+  // `slots / 256` workgroups, for the forward (NT) and weight-gradient (TN)
+  // layouts; the input-gradient layout (NN) runs ~10% slower than NT.
+  struct Cand { int bm, bn, slots; double t_nt_us, t_tn_us; };
+  const Cand cands[] = {{256, 256, 256, 2.1, 3.8}, {256, 128, 256, 1.5, 2.7}, {128, 128, 512, 1.0, 1.9}};
   const int64_t kt_total = ceil_div(K > 0 ? K : 1, 64);
+  if (const char* env = getenv("MP_GEMM_PLAN")) {
+    int bm = 0, bn = 0, sp = 1;
+    if (sscanf(env, "%d,%d,%d", &bm, &bn, &sp) == 3 && sp >= 1 && (allow_split || sp == 1) &&
+        ((bm == 256 && bn == 256) || (bm == 256 && bn == 128) || (bm == 128 && bn == 128))) {
+      const int64_t kt = ceil_div(kt_total, sp);
+      return Plan{bm, bn, static_cast<int>(ceil_div(kt_total, kt)), kt * 64};
+    }
+  }
+  Plan best{256, 256, 1, kt_total * 64};
+  double best_cost = 1e300;
   for (const Cand& c : cands) {
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     const int max_split = allow_split ? 16 : 1;
     for (int s = 1; s <= max_split; ++s) {
       const int64_t kt = ceil_div(kt_total, s);
       if (s > 1 && kt < 4) break;
-      const int64_t used = ceil_div(kt_total, kt);  // splits actually non-empty
-      if (used != s) continue;
-      const int64_t waves = ceil_div(tiles * s, 256);
-      // Time units: one 64-deep k-step of a 256x256 tile at full efficiency = 1.
-      double cost = static_cast<double>(waves) * kt * (c.bm * c.bn / 65536.0) / c.eff;
-      // fp32 partials: write + read, ~ (bytes / 6 TB/s) in the same units
-      // (a 256x256x64 k-step at 1.5 PFLOP/s is ~5.6 ns).
-      if (s > 1) cost += 2.0 * 4.0 * M * N * s / 6e12 / 5.6e-9;
+      if (ceil_div(kt_total, kt) != s) continue;  // every split non-empty
+      const int64_t waves = ceil_div(tiles * s, c.slots);
+      const double t_step = lay == TN ? c.t_tn_us : (lay == NN ? 1.1 * c.t_nt_us : c.t_nt_us);
+      double cost = static_cast<double>(waves) * kt * t_step;
+      if (s > 1) cost += 2.0 * 4.0 * M * N * s / 5e12 * 1e6 + 3.0;
       if (cost < best_cost) {
         best_cost = cost;
         best = Plan{c.bm, c.bn, s, kt * 64};
@@ -361,8 +359,9 @@ static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split) {
 
 template <int BM, int BN, bool AK, bool BKC, int EPI, int ACT>
 static void launch_bf16_tile(const GemmArgs& g, int splits, hipStream_t s) {
+  constexpr int NW = (BM == 256 && BN == 256) ? 8 : 4;
   const dim3 grid(static_cast<unsigned>(g.tiles_m * g.tiles_n), 1, static_cast<unsigned>(splits));
-  gemm_bf16_kernel<BM, BN, AK, BKC, EPI, ACT><<<grid, 256, 0, s>>>(g);
+  gemm_bf16_kernel<BM, BN, NW, AK, BKC, EPI, ACT><<<grid, 64 * NW, 0, s>>>(g);
 }
 
 template <bool AK, bool BKC, int EPI, int ACT>
@@ -400,7 +399,7 @@ static void launch_f32_epi(Layout lay, const GemmArgs& g, int splits, hipStream_
 // Split-K partial bytes needed for an fp32-output GEMM of this shape.
 static size_t splitk_bytes(mp_dtype dt, int64_t M, int64_t N, int64_t K) {
   if (dt != MP_BF16) return 0;
-  const Plan p = plan_bf16(M, N, K, true);
+  const Plan p = plan_bf16(M, N, K, true, TN);
   return p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * M * N * sizeof(float), 256) : 0;
 }
 
@@ -408,20 +407,22 @@ static size_t splitk_bytes(mp_dtype dt, int64_t M, int64_t N, int64_t K) {
 // lets the planner split K, using `ws` for the partials.
 int gemm(mp_dtype dt, Layout lay, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
          int64_t ldb, void* C, int64_t ldc, bool out_bf16, const void* bias, int act, void* zsave, bool allow_split,
-         void* ws, hipStream_t s, int epi, const void* zin) {
+         void* ws, size_t ws_bytes, hipStream_t s, int epi, const void* zin) {
   if (M == 0 || N == 0) return MP_OK;
   GemmArgs g{};
   g.M = M; g.N = N; g.K = K; g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.bias = bias; g.zsave = zsave; g.zin = zin; g.act = act; g.out_bf16 = out_bf16 ? 1 : 0;
   if (dt == MP_BF16) {
     const Plan p = plan_bf16(M, N, K, allow_split && epi == EPI_STORE && bias == nullptr && act == MP_ACT_NONE &&
-                                          zsave == nullptr);
+                                          zsave == nullptr && lay == TN, lay);
     g.tiles_m = static_cast<int>(ceil_div(M, p.bm));
     g.tiles_n = static_cast<int>(ceil_div(N, p.bn));
     g.group_m = 8;
     g.k_split = p.k_split;
     if (p.splits > 1) {
-      if (ws == nullptr) return fail(MP_ERR_WORKSPACE, "gemm: split-K needs a workspace");
+      const size_t need = static_cast<size_t>(p.splits) * M * N * sizeof(float);
+      if (ws == nullptr || ws_bytes < need)
+        return fail(MP_ERR_WORKSPACE, "gemm: split-K needs %zu workspace bytes, got %zu", need, ws_bytes);
       if (lay != TN) return fail(MP_ERR_UNSUPPORTED, "gemm: split-K is built for the weight-gradient layout only");
       g.partial = static_cast<float*>(ws);
       launch_bf16(lay, EPI_SPLITK, MP_ACT_NONE, g, p, s);
@@ -472,7 +473,8 @@ extern "C" int mp_column_linear_gelu(mp_dtype in_dtype, mp_dtype out_dtype, int6
   MP_REQUIRE_ALIGN(Y_i);
   MP_REQUIRE_OPT_ALIGN(a_i);
   MP_REQUIRE_OPT_ALIGN(Z_save);
-  return gemm(in_dtype, NT, T, Fi, K, X, K, A_i, K, Y_i, Fi, out_dtype == MP_BF16, a_i, act, Z_save, false, nullptr, s);
+  return gemm(in_dtype, NT, T, Fi, K, X, K, A_i, K, Y_i, Fi, out_dtype == MP_BF16, a_i, act, Z_save, false, nullptr, 0,
+              s);
 }
 
 extern "C" size_t mp_column_linear_gelu_bwd_workspace(mp_dtype dtype, int64_t T, int64_t K, int64_t Fi) {
@@ -522,10 +524,11 @@ extern "C" int mp_column_linear_gelu_bwd(mp_dtype dtype, int64_t T, int64_t K, i
   }
   // dX_partial[T,K] = dZ[T,Fi] * A_i[Fi,K]
   if (int rc = gemm(dtype, NN, T, K, Fi, dZ, Fi, A_i, K, dX_partial, K, dtype == MP_BF16, nullptr, MP_ACT_NONE,
-                    nullptr, false, nullptr, s))
+                    nullptr, false, nullptr, 0, s))
     return rc;
   // dA_i[Fi,K] = dZ^T * X  (reduction over T), fp32
-  if (int rc = gemm(dtype, TN, Fi, K, T, dZ, Fi, X, K, dA_i, K, false, nullptr, MP_ACT_NONE, nullptr, true, ws2, s))
+  if (int rc = gemm(dtype, TN, Fi, K, T, dZ, Fi, X, K, dA_i, K, false, nullptr, MP_ACT_NONE, nullptr, true, ws2,
+                    ws_bytes - dz_bytes, s))
     return rc;
   if (da_i != nullptr) return colsum(dtype, T, Fi, dZ, da_i, ws2, s);
   return MP_OK;
@@ -545,7 +548,7 @@ extern "C" int mp_row_linear_partial(mp_dtype dtype, int64_t T, int64_t Fi, int6
   MP_REQUIRE_ALIGN(B_i);
   MP_REQUIRE_ALIGN(P_i);
   return gemm(dtype, NT, T, K, Fi, Y_i, Fi, B_i, Fi, P_i, K, dtype == MP_BF16, nullptr, MP_ACT_NONE, nullptr, false,
-              nullptr, s);
+              nullptr, 0, s);
 }
 
 extern "C" size_t mp_row_linear_partial_bwd_workspace(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K) {
@@ -577,8 +580,9 @@ extern "C" int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, 
   MP_REQUIRE_OPT_ALIGN(ws);
   // dY_i[T,Fi] = dOut[T,K] * B_i[K,Fi]
   if (int rc = gemm(dtype, NN, T, Fi, K, dOut, K, B_i, Fi, dY_i, Fi, dtype == MP_BF16, nullptr, MP_ACT_NONE, nullptr,
-                    false, nullptr, s))
+                    false, nullptr, 0, s))
     return rc;
   // dB_i[K,Fi] = dOut^T * Y_i (reduction over T), fp32
-  return gemm(dtype, TN, K, Fi, T, dOut, K, Y_i, Fi, dB_i, Fi, false, nullptr, MP_ACT_NONE, nullptr, true, ws, s);
+  return gemm(dtype, TN, K, Fi, T, dOut, K, Y_i, Fi, dB_i, Fi, false, nullptr, MP_ACT_NONE, nullptr, true, ws, ws_bytes,
+              s);
 }
