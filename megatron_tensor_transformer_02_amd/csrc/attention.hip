@@ -8,8 +8,13 @@
 // other 16).  The online softmax therefore needs only a lane-pair exchange
 // for the running max.  The probabilities' registers 8s..8s+7 are, as they
 // stand, the B operand of O^T += V^T P^T for keys {16s+4g..+3, 16s+8+4g..+3}
-// (g = lane / 32); V^T is read from LDS in that same key order (two 8-byte
-// reads), so P never leaves registers.
+// (g = lane / 32); the V^T fragments come from the plain V row tile through
+// two LDS transpose reads (4 consecutive keys each) in that same key order,
+// so P never leaves registers and no transposed tile is ever stored.
+//
+// Every kernel streams 64-row tiles through two LDS buffers: the next tile is
+// loaded into registers while the current one is multiplied, then written to
+// the other buffer (one barrier per tile).
 //
 // Backward (P recomputed from the saved log-sum-exp, no atomics):
 //  * dQ kernel -- lanes own queries: S^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
@@ -41,52 +46,55 @@ __device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
   return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
 }
 
-// A-operand fragment of a transposed ([D rows][64 keys]) LDS tile for key
-// tile `kt` (32 keys) and k-step `s2`: keys {16*s2 + 4g .. +3} and
-// {16*s2 + 8 + 4g .. +3} of the tile, matching the register order of a
-// 32x32 result used as the B operand.
-__device__ __forceinline__ uint4 lds_t_frag(const uint4* tile, int row, int kt, int s2, int g) {
-  const uint2* t2 = reinterpret_cast<const uint2*>(tile);
-  const int c = kt * 4 + 2 * s2;
-  const uint2 lo = t2[lds_slot(row, c) * 2 + g];
-  const uint2 hi = t2[lds_slot(row, c + 1) * 2 + g];
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
 // Packs registers 8*s2 .. 8*s2+7 of a 32x32 result into a bf16 B operand.
 __device__ __forceinline__ uint4 pack_half(const float* v, int s2) { return pack8(v + 8 * s2); }
 
-// Loads rows [r0, r0+64) x D of the head slice at `col` of a [L, ld] bf16
-// matrix into KH = D/64 LDS tiles in the GEMM tile format.
+// A 64-row x D-column tile of a [L, ld] bf16 matrix (a head slice), held in
+// KH = D/64 LDS sub-tiles of the GEMM tile format (64 rows x 64 columns,
+// rows of eight swizzled 16-byte chunks).  load() fetches rows r0..r0+63
+// into registers (rows >= L read as zeros), store() writes them to LDS.
 template <int D, int NT>
-__device__ __forceinline__ void load_rows_tile(const BufRes& rs, int64_t ld, int r0, int L, uint4* lds, int tid) {
-  TileLoader<64, true, NT> ld_rows;
+struct RowTile {
+  TileLoader<64, true, NT> part[D / 64];
+  __device__ __forceinline__ void load(const BufRes& rs, int64_t ld, int r0, int L, int tid) {
 #pragma unroll
-  for (int hf = 0; hf < D / 64; ++hf) {
-    ld_rows.load(rs, ld, r0, L, 64 * hf, D, tid, r0);
-    ld_rows.store(lds + hf * 512, tid);
+    for (int hf = 0; hf < D / 64; ++hf) part[hf].load(rs, ld, r0, L, 64 * hf, D, tid, r0);
   }
-}
+  __device__ __forceinline__ void store(uint4* lds, int tid) const {
+#pragma unroll
+    for (int hf = 0; hf < D / 64; ++hf) part[hf].store(lds + hf * 512, tid);
+  }
+};
 
-// Loads the transposed tile [D rows][keys r0 .. r0+63] of the head slice.
-template <int D, int NT>
-__device__ __forceinline__ void load_cols_tile(const BufRes& rs, int64_t ld, int r0, int L, uint4* lds, int tid) {
-  TileLoader<D, false, NT> ld_cols;
-  ld_cols.load(rs, ld, 0, D, r0, L, tid);
-  ld_cols.store(lds, tid);
-}
-
-// Element (row, k) of a row tile loaded by load_rows_tile, as an MFMA A/B
-// fragment: row `row`, k-step `st` (16 columns), lane group g.
+// Row fragment (A or B operand) of a row tile: row `row`, k-step `st`
+// (16 columns), lane group g.
 __device__ __forceinline__ uint4 lds_row_frag(const uint4* tile, int row, int st, int g) {
   return tile[(st >> 2) * 512 + lds_slot(row, 2 * (st & 3) + g)];
 }
 
+// Byte address of element (r, d) of a row tile.
+__device__ __forceinline__ const char* tile_elem(const uint4* tile, int r, int d) {
+  return reinterpret_cast<const char*>(tile + (d >> 6) * 512 + lds_slot(r, (d & 63) >> 3)) + (d & 7) * 2;
+}
+
+// Transposed A-operand fragment from a row tile: operand row = tile column
+// d = dt*32 + lane%32; its 8 k-slots are tile rows {kt*32 + 16*s2 + 4g .. +3}
+// and {kt*32 + 16*s2 + 8 + 4g .. +3} (g = lane / 32), the register order of a
+// 32x32 result used as the B operand.  Two transpose reads of 4 rows each.
+__device__ __forceinline__ uint4 lds_tr_frag(const uint4* tile, int dt, int kt, int s2, int lane) {
+  const int grp = lane >> 4, i = lane & 15;
+  const int r = kt * 32 + 16 * s2 + 4 * (grp >> 1) + (i >> 2);
+  const int d = dt * 32 + 16 * (grp & 1) + 4 * (i & 3);
+  const uint2 lo = lds_read_tr16(tile_elem(tile, r, d));
+  const uint2 hi = lds_read_tr16(tile_elem(tile, r + 8, d));
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
-  constexpr int NT = 64 * NW, BQ = 32 * NW, DT = D / 32, KS = D / 16;
-  __shared__ uint4 lds_k[D / 64 * 512];
-  __shared__ uint4 lds_vt[D * 8];
+  constexpr int NT = 64 * NW, BQ = 32 * NW, DT = D / 32, KS = D / 16, TS = D / 64 * 512;
+  __shared__ uint4 lds_k[2][TS];
+  __shared__ uint4 lds_v[2][TS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, frow = lane & 31, g = lane >> 5;
   const int nbh = a.B * a.h;
   const int bh = blockIdx.x % nbh;
@@ -113,58 +121,75 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
 
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += 64) {
-    __syncthreads();
-    load_rows_tile<D, NT>(rk, S3, kv0, a.L, lds_k, tid);
-    load_cols_tile<D, NT>(rv, S3, kv0, a.L, lds_vt, tid);
-    __syncthreads();
-    if (a.causal && kv0 > qw0 + 31) continue;  // every key of the block is in this wave's future
-    f32x16_t s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
-#pragma unroll
-      for (int st = 0; st < KS; ++st) s[kt] = mfma_32x32x16(lds_row_frag(lds_k, kt * 32 + frow, st, g), qf[st], s[kt]);
+  const int nkb = (kv_end + 63) / 64;
+  RowTile<D, NT> tk, tv;
+  tk.load(rk, S3, 0, a.L, tid);
+  tv.load(rv, S3, 0, a.L, tid);
+  tk.store(lds_k[0], tid);
+  tv.store(lds_v[0], tid);
+  __syncthreads();
+  for (int it = 0; it < nkb; ++it) {
+    const int kv0 = it * 64, cur = it & 1;
+    const bool more = it + 1 < nkb;
+    if (more) {
+      tk.load(rk, S3, kv0 + 64, a.L, tid);
+      tv.load(rv, S3, kv0 + 64, a.L, tid);
     }
-    float mx = -INFINITY;
+    if (!(a.causal && kv0 > qw0 + 31)) {  // else every key of the block is in this wave's future
+      const uint4* kt_ = lds_k[cur];
+      const uint4* vt_ = lds_v[cur];
+      f32x16_t s[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + kt * 32 + mfma_row(r, lane);
-        const bool vis = key < a.L && (!a.causal || key <= qi);
-        if (!vis) s[kt][r] = -INFINITY;
-        mx = fmaxf(mx, s[kt][r]);
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) s[kt] = mfma_32x32x16(lds_row_frag(kt_, kt * 32 + frow, st, g), qf[st], s[kt]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float ms = mn == -INFINITY ? 0.0f : mn;
-    const float alpha = exp2f((m - ms) * a.scale_log2);
-    float ps = 0.0f;
-    uint4 pb[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f((s[kt][r] - ms) * a.scale_log2);
-        ps += p[r];
-      }
-      pb[kt][0] = pack_half(p, 0);
-      pb[kt][1] = pack_half(p, 1);
-    }
-    l = l * alpha + ps;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma_32x32x16(lds_t_frag(lds_vt, dt * 32 + frow, kt, s2, g), pb[kt][s2], o[dt]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kt * 32 + mfma_row(r, lane);
+          const bool vis = key < a.L && (!a.causal || key <= qi);
+          if (!vis) s[kt][r] = -INFINITY;
+          mx = fmaxf(mx, s[kt][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float ms = mn == -INFINITY ? 0.0f : mn;
+      const float alpha = exp2f((m - ms) * a.scale_log2);
+      float ps = 0.0f;
+      uint4 pb[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = exp2f((s[kt][r] - ms) * a.scale_log2);
+          ps += p[r];
+        }
+        pb[kt][0] = pack_half(p, 0);
+        pb[kt][1] = pack_half(p, 1);
+      }
+      l = l * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma_32x32x16(lds_tr_frag(vt_, dt, kt, s2, lane), pb[kt][s2], o[dt]);
+      }
+      m = mn;
     }
-    m = mn;
+    if (more) {
+      tk.store(lds_k[cur ^ 1], tid);
+      tv.store(lds_v[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
   const float lt = l + __shfl_xor(l, 32, 64);
   if (!qvalid) return;
@@ -209,10 +234,9 @@ __global__ __launch_bounds__(256) void attn_dvec_kernel(const AttnArgs a) {
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) {
-  constexpr int NT = 64 * NW, BQ = 32 * NW, DT = D / 32, KS = D / 16;
-  __shared__ uint4 lds_k[D / 64 * 512];
-  __shared__ uint4 lds_kt[D * 8];
-  __shared__ uint4 lds_v[D / 64 * 512];
+  constexpr int NT = 64 * NW, BQ = 32 * NW, DT = D / 32, KS = D / 16, TS = D / 64 * 512;
+  __shared__ uint4 lds_k[2][TS];
+  __shared__ uint4 lds_v[2][TS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, frow = lane & 31, g = lane >> 5;
   const int nbh = a.B * a.h;
   const int bh = blockIdx.x % nbh;
@@ -245,41 +269,57 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
     for (int r = 0; r < 16; ++r) dq[dt][r] = 0.0f;
 
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += 64) {
-    __syncthreads();
-    load_rows_tile<D, NT>(rk, S3, kv0, a.L, lds_k, tid);
-    load_cols_tile<D, NT>(rk, S3, kv0, a.L, lds_kt, tid);
-    load_rows_tile<D, NT>(rv, S3, kv0, a.L, lds_v, tid);
-    __syncthreads();
-    if (a.causal && kv0 > qw0 + 31) continue;
-    uint4 dsb[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x16_t s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        s = mfma_32x32x16(lds_row_frag(lds_k, kt * 32 + frow, st, g), qf[st], s);
-        dp = mfma_32x32x16(lds_row_frag(lds_v, kt * 32 + frow, st, g), dof[st], dp);
-      }
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + kt * 32 + mfma_row(r, lane);
-        const bool vis = qvalid && key < a.L && (!a.causal || key <= qi);
-        const float p = vis ? exp2f(s[r] * a.scale_log2 - lse2) : 0.0f;
-        ds[r] = p * (dp[r] - dq_d);
-      }
-      dsb[kt][0] = pack_half(ds, 0);
-      dsb[kt][1] = pack_half(ds, 1);
+  const int nkb = (kv_end + 63) / 64;
+  RowTile<D, NT> tk, tv;
+  tk.load(rk, S3, 0, a.L, tid);
+  tv.load(rv, S3, 0, a.L, tid);
+  tk.store(lds_k[0], tid);
+  tv.store(lds_v[0], tid);
+  __syncthreads();
+  for (int it = 0; it < nkb; ++it) {
+    const int kv0 = it * 64, cur = it & 1;
+    const bool more = it + 1 < nkb;
+    if (more) {
+      tk.load(rk, S3, kv0 + 64, a.L, tid);
+      tv.load(rv, S3, kv0 + 64, a.L, tid);
     }
+    if (!(a.causal && kv0 > qw0 + 31)) {
+      const uint4* kt_ = lds_k[cur];
+      const uint4* vt_ = lds_v[cur];
+      uint4 dsb[2][2];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16_t sv, dp;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.0f;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) dq[dt] = mfma_32x32x16(lds_t_frag(lds_kt, dt * 32 + frow, kt, s2, g), dsb[kt][s2], dq[dt]);
+        for (int st = 0; st < KS; ++st) {
+          sv = mfma_32x32x16(lds_row_frag(kt_, kt * 32 + frow, st, g), qf[st], sv);
+          dp = mfma_32x32x16(lds_row_frag(vt_, kt * 32 + frow, st, g), dof[st], dp);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kt * 32 + mfma_row(r, lane);
+          const bool vis = qvalid && key < a.L && (!a.causal || key <= qi);
+          const float p = vis ? exp2f(sv[r] * a.scale_log2 - lse2) : 0.0f;
+          ds[r] = p * (dp[r] - dq_d);
+        }
+        dsb[kt][0] = pack_half(ds, 0);
+        dsb[kt][1] = pack_half(ds, 1);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) dq[dt] = mfma_32x32x16(lds_tr_frag(kt_, dt, kt, s2, lane), dsb[kt][s2], dq[dt]);
+    }
+    if (more) {
+      tk.store(lds_k[cur ^ 1], tid);
+      tv.store(lds_v[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
   if (!qvalid) return;
   uint16_t* row = a.dqkv + trow * S3 + hh * D;
@@ -297,12 +337,10 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a) {
-  constexpr int NT = 64 * NW, BK = 32 * NW, DT = D / 32, KS = D / 16;
-  __shared__ uint4 lds_q[D / 64 * 512];
-  __shared__ uint4 lds_qt[D * 8];
-  __shared__ uint4 lds_do[D / 64 * 512];
-  __shared__ uint4 lds_dot[D * 8];
-  __shared__ float lds_lse[64], lds_dv[64];
+  constexpr int NT = 64 * NW, BK = 32 * NW, DT = D / 32, KS = D / 16, TS = D / 64 * 512;
+  __shared__ uint4 lds_q[2][TS];
+  __shared__ uint4 lds_do[2][TS];
+  __shared__ float lds_lse[2][64], lds_dv[2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, frow = lane & 31, g = lane >> 5;
   const int nbh = a.B * a.h;
   const int bh = blockIdx.x % nbh;
@@ -332,53 +370,75 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a)
     for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.0f;
 
   const int q_begin = a.causal ? (k0 / 64) * 64 : 0;
-  for (int q0 = q_begin; q0 < a.L; q0 += 64) {
-    __syncthreads();
-    load_rows_tile<D, NT>(rq, S3, q0, a.L, lds_q, tid);
-    load_cols_tile<D, NT>(rq, S3, q0, a.L, lds_qt, tid);
-    load_rows_tile<D, NT>(rdo, HD, q0, a.L, lds_do, tid);
-    load_cols_tile<D, NT>(rdo, HD, q0, a.L, lds_dot, tid);
+  const int nqb = (a.L - q_begin + 63) / 64;
+  RowTile<D, NT> tq, tdo;
+  float lse_r = 0.0f, dv_r = 0.0f;
+  auto fetch = [&](int q0) {
+    tq.load(rq, S3, q0, a.L, tid);
+    tdo.load(rdo, HD, q0, a.L, tid);
     if (tid < 64) {
       const int q = q0 + tid;
-      lds_lse[tid] = q < a.L ? a.lse[sbase + q] * kLog2eA : 0.0f;
-      lds_dv[tid] = q < a.L ? a.dvec[sbase + q] : 0.0f;
+      lse_r = q < a.L ? a.lse[sbase + q] * kLog2eA : 0.0f;
+      dv_r = q < a.L ? a.dvec[sbase + q] : 0.0f;
     }
-    __syncthreads();
-    if (a.causal && q0 + 63 < kw0) continue;  // every query of the block precedes this wave's keys
-    uint4 pb[2][2], dsb[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      f32x16_t s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.0f;
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        s = mfma_32x32x16(lds_row_frag(lds_q, qt * 32 + frow, st, g), kf[st], s);
-        dp = mfma_32x32x16(lds_row_frag(lds_do, qt * 32 + frow, st, g), vf[st], dp);
-      }
-      float p[16], ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = qt * 32 + mfma_row(r, lane);
-        const int q = q0 + ql;
-        const bool vis = kvalid && q < a.L && (!a.causal || kj <= q);
-        p[r] = vis ? exp2f(s[r] * a.scale_log2 - lds_lse[ql]) : 0.0f;
-        ds[r] = p[r] * (dp[r] - lds_dv[ql]);
-      }
-      pb[qt][0] = pack_half(p, 0);
-      pb[qt][1] = pack_half(p, 1);
-      dsb[qt][0] = pack_half(ds, 0);
-      dsb[qt][1] = pack_half(ds, 1);
+  };
+  auto commit = [&](int buf) {
+    tq.store(lds_q[buf], tid);
+    tdo.store(lds_do[buf], tid);
+    if (tid < 64) {
+      lds_lse[buf][tid] = lse_r;
+      lds_dv[buf][tid] = dv_r;
     }
+  };
+  if (nqb > 0) {
+    fetch(q_begin);
+    commit(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nqb; ++it) {
+    const int q0 = q_begin + it * 64, cur = it & 1;
+    const bool more = it + 1 < nqb;
+    if (more) fetch(q0 + 64);
+    if (!(a.causal && q0 + 63 < kw0)) {  // else every query of the block precedes this wave's keys
+      const uint4* qt_ = lds_q[cur];
+      const uint4* dot_ = lds_do[cur];
+      uint4 pb[2][2], dsb[2][2];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int qt = 0; qt < 2; ++qt) {
+        f32x16_t sv, dp;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+        for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.0f;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          dv[dt] = mfma_32x32x16(lds_t_frag(lds_dot, dt * 32 + frow, qt, s2, g), pb[qt][s2], dv[dt]);
-          dk[dt] = mfma_32x32x16(lds_t_frag(lds_qt, dt * 32 + frow, qt, s2, g), dsb[qt][s2], dk[dt]);
+        for (int st = 0; st < KS; ++st) {
+          sv = mfma_32x32x16(lds_row_frag(qt_, qt * 32 + frow, st, g), kf[st], sv);
+          dp = mfma_32x32x16(lds_row_frag(dot_, qt * 32 + frow, st, g), vf[st], dp);
         }
+        float p[16], ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = qt * 32 + mfma_row(r, lane);
+          const int q = q0 + ql;
+          const bool vis = kvalid && q < a.L && (!a.causal || kj <= q);
+          p[r] = vis ? exp2f(sv[r] * a.scale_log2 - lds_lse[cur][ql]) : 0.0f;
+          ds[r] = p[r] * (dp[r] - lds_dv[cur][ql]);
+        }
+        pb[qt][0] = pack_half(p, 0);
+        pb[qt][1] = pack_half(p, 1);
+        dsb[qt][0] = pack_half(ds, 0);
+        dsb[qt][1] = pack_half(ds, 1);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            dv[dt] = mfma_32x32x16(lds_tr_frag(dot_, dt, qt, s2, lane), pb[qt][s2], dv[dt]);
+            dk[dt] = mfma_32x32x16(lds_tr_frag(qt_, dt, qt, s2, lane), dsb[qt][s2], dk[dt]);
+          }
+    }
+    if (more) commit(cur ^ 1);
+    __syncthreads();
   }
   if (!kvalid) return;
   uint16_t* row = a.dqkv + (static_cast<int64_t>(b) * a.L + kj) * S3 + hh * D;

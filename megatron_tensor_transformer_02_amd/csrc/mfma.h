@@ -49,6 +49,20 @@ __device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 8 + (
 // Row m of the MFMA result held by register r of lane `lane`.
 __device__ __forceinline__ int mfma_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// ------------------------------------------------- LDS transpose reads
+// ds_read_b64_tr_b16 (gfx950) works on groups of 16 lanes: source lane q of a
+// group supplies the address of 4 consecutive 16-bit values, and lane i of the
+// group receives value (i % 4) of source lane 4*j + i/4, for j = 0..3.  If
+// source lane q points at row k0 + q/4, columns m0 + 4*(q%4) .. +3 of a
+// row-major [k][m] tile, lane i therefore receives column m0 + i of rows
+// k0 .. k0+3: four consecutive k-values of one column, i.e. a transposed read.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // 8x8 transpose of 16-bit values: in[k] holds 8 values (columns 0..7) of row
 // k; out[c] receives the 8 values of column c (rows 0..7).
 __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
