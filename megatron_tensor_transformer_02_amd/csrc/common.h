@@ -233,6 +233,48 @@ __device__ __forceinline__ float act_grad(float z, int act) {
   return 1.0f;
 }
 
+// Branch-free variants for bf16 outputs, where a few 1e-7 of absolute error
+// is far below the output's resolution.  erf uses Abramowitz & Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7):
+// erf(a) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),
+// t = 1 / (1 + p a), a = |x|, odd in x.  tanh(u) = 1 - 2 / (exp(2u) + 1).
+// exp and the reciprocal are the hardware's exp2 and rcp instructions.
+__device__ __forceinline__ float erf_fast(float x) {
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
+  float q = fmaf(1.061405429f, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
+  return copysignf(fmaf(-q * t, e, 1.0f), x);
+}
+
+__device__ __forceinline__ float tanh_fast(float u) {
+  const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * u);  // exp(2u)
+  return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
+}
+
+__device__ __forceinline__ float act_fwd_fast(float z, int act) {
+  if (act == MP_ACT_GELU_ERF) return 0.5f * z * (1.0f + erf_fast(z * 0.7071067811865476f));
+  if (act == MP_ACT_GELU_TANH) return 0.5f * z * (1.0f + tanh_fast(0.7978845608028654f * (z + 0.044715f * z * z * z)));
+  return z;
+}
+
+__device__ __forceinline__ float act_grad_fast(float z, int act) {
+  if (act == MP_ACT_GELU_ERF) {
+    const float cdf = 0.5f * (1.0f + erf_fast(z * 0.7071067811865476f));
+    const float pdf = 0.3989422804014327f * __builtin_amdgcn_exp2f(-0.7213475204444817f * z * z);
+    return cdf + z * pdf;
+  }
+  if (act == MP_ACT_GELU_TANH) {
+    const float c = 0.7978845608028654f;
+    const float t = tanh_fast(c * (z + 0.044715f * z * z * z));
+    return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * z * z);
+  }
+  return 1.0f;
+}
+
 inline bool act_ok(int act) { return act == MP_ACT_NONE || act == MP_ACT_GELU_ERF || act == MP_ACT_GELU_TANH; }
 
 }  // namespace mp

@@ -2,16 +2,16 @@
 //
 // Each operand is either K-contiguous (row-major [rows][K], the forward "NT"
 // case) or MN-contiguous ([K][rows], as the weight in an input-gradient GEMM
-// or both operands of a weight-gradient GEMM).  MN-contiguous tiles are
-// transposed in registers (8x8 blocks of 16-bit values) on their way into LDS,
-// so the LDS tile format and the MFMA inner loop are the same for every
-// layout and no transposed copy ever goes through HBM.
+// or both operands of a weight-gradient GEMM).  Both are copied into LDS as
+// they lie in memory (16-byte chunks, swizzled); MN-contiguous fragments are
+// then read with the LDS transpose read, so every layout runs the same MFMA
+// loop and no transposed copy goes through HBM or through registers.
 //
-// bf16 kernel: 256 threads = 4 waves in a 2x2 grid; block tile BM x BN x 64;
-// each wave owns (BM/2) x (BN/2) of the output as 32x32 MFMA tiles
-// (v_mfma_f32_32x32x16_bf16).  The k-loop double-buffers the LDS tile and
-// prefetches the next k-tile into registers while the matrix cores work on
-// the current one (one barrier per k-tile).  Workgroups are renumbered so
+// bf16 kernel: 256 threads = 4 waves in a 2x2 grid, one wave per SIMD; block
+// tile BM x BN x 64; each wave owns (BM/2) x (BN/2) of the output as 32x32
+// MFMA tiles (v_mfma_f32_32x32x16_bf16).  The k-loop is software-pipelined
+// by hand (fragment double-buffering, next k-tile prefetched into registers,
+// explicit MFMA/LDS/global-load interleave).  Workgroups are renumbered so
 // each of the 8 XCDs takes a contiguous range of output tiles, walked in
 // groups of tile-rows, for L2 reuse of the operand panels.
 //
@@ -59,17 +59,15 @@ __device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles
   tn = inner / gsz;
 }
 
-template <int BM, int BN, int NW, bool AK, bool BKC, int EPI, int ACT>
-__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
-  // NW = 8: 2 x 4 waves (two waves per SIMD, so one wave's LDS/memory waits
-  // overlap the other's MFMAs); NW = 4: 2 x 2 waves.
-  constexpr int NT = 64 * NW, WCOLS = NW == 8 ? 4 : 2, WROWS = NW / WCOLS;
-  constexpr int WM = BM / WROWS, WN = BN / WCOLS, TM = WM / 32, TN = WN / 32;
+template <int BM, int BN, bool AK, bool BKC, int EPI, int ACT>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
+  // 2 x 2 waves, one per SIMD; each wave owns (BM/2) x (BN/2) of the tile.
+  constexpr int NT = 256, WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;
   __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WCOLS, wn = wave % WCOLS;
+  const int wm = wave >> 1, wn = wave & 1;
   int tmi, tni;
   map_tile(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, g.group_m, tmi, tni);
   const int64_t m0 = static_cast<int64_t>(tmi) * BM, n0 = static_cast<int64_t>(tni) * BN;
@@ -87,54 +85,75 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // One register stage of prefetch: tile kt+1 is loaded from global memory
-  // into registers while tile kt is multiplied out of LDS[kt & 1], then
-  // written to the other LDS buffer; one barrier per k-tile.
   TileLoader<BM, AK, NT> la;
   TileLoader<BN, BKC, NT> lb;
   const BufRes ra = TileLoader<BM, AK, NT>::resource(A, g.lda, m0, g.M, g.K);
   const BufRes rb = TileLoader<BN, BKC, NT>::resource(B, g.ldb, n0, g.N, g.K);
-  // A transposing (MN-contiguous) loader keeps one 8x8 block per thread for
-  // only 256 of the 512 threads of an 8-wave tile; operand B's blocks go to
-  // the other half so both halves share the load and transpose work.
-  const int tid_b = (!BKC && NT == 512) ? (tid + 256) & 511 : tid;
-  if (nk > 0) {
-    la.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
-    lb.load(rb, g.ldb, n0, g.N, kbeg, kend, tid_b);
-    la.store(lds[0], tid);
-    lb.store(lds[0] + A_SLOTS, tid_b);
-  }
+  la.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
+  lb.load(rb, g.ldb, n0, g.N, kbeg, kend, tid);
+  la.store(lds[0], tid);
+  lb.store(lds[0] + A_SLOTS, tid);
   __syncthreads();
 
-  const int frow = lane & 31, fgrp = lane >> 5;
+  // Software pipeline.  Fragments are double-buffered in registers: while
+  // the MFMAs of k-step ks run, the fragments of ks+1 are read from LDS.
+  // The next k-tile is loaded into registers at the start of a k-tile and
+  // written to the other LDS buffer during the last two k-steps (operand A
+  // in step 2, B in step 3); the barrier that publishes it sits inside step
+  // 3, so the first fragments of the next k-tile are read while that step's
+  // remaining MFMAs run.  The loop body has no branches (past the end of K
+  // the loads return zeros and go unused), so each part is one scheduling
+  // region and the interleave patterns below apply as written.
+  constexpr int NRA = AK ? TM : 2 * TM, NRB = BKC ? TN : 2 * TN, NR = NRA + NRB;
+  constexpr int NGA = TileLoader<BM, AK, NT>::NREG, NGB = TileLoader<BN, BKC, NT>::NREG;
+  constexpr int NM = TM * TN, H = TM / 2;
+  const int ar0 = wm * WM, br0 = wn * WN;
+  uint4 fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[0][i] = lds_frag<AK>(lds[0], ar0 + 32 * i, 0, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb[0][j] = lds_frag<BKC>(lds[0] + A_SLOTS, br0 + 32 * j, 0, lane);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(ra, g.lda, m0, g.M, kbeg + (kt + 1) * 64, kend, tid);
-      lb.load(rb, g.ldb, n0, g.N, kbeg + (kt + 1) * 64, kend, tid_b);
-    }
-    const uint4* ta = lds[cur];
-    const uint4* tb = lds[cur] + A_SLOTS;
+    const uint4* ta = lds[kt & 1];
+    const uint4* tb = ta + A_SLOTS;
+    uint4* na = lds[(kt & 1) ^ 1];
+    la.load(ra, g.lda, m0, g.M, kbeg + (kt + 1) * 64, kend, tid);
+    lb.load(rb, g.ldb, n0, g.N, kbeg + (kt + 1) * 64, kend, tid);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = 2 * ks + fgrp;
-      uint4 af[TM], bfr[TN];
+    for (int ks = 0; ks < 3; ++ks) {
+      const int c = ks & 1, n = c ^ 1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = ta[lds_slot(wm * WM + i * 32 + frow, ch)];
+      for (int i = 0; i < TM; ++i) fa[n][i] = lds_frag<AK>(ta, ar0 + 32 * i, ks + 1, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = tb[lds_slot(wn * WN + j * 32 + frow, ch)];
+      for (int j = 0; j < TN; ++j) fb[n][j] = lds_frag<BKC>(tb, br0 + 32 * j, ks + 1, lane);
+      if (ks == 2) la.store(na, tid);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[c][i], fb[c][j], acc[i][j]);
+      if (ks == 0) sched_mfma_interleave<0, NM, 0x100, NR, NGA + NGB>();
+      else if (ks == 1) sched_mfma_interleave<0, NM, 0x100, NR, 0>();
+      else sched_mfma_interleave<0, NM, 0x180, NR + NGA, 0>();
     }
-    if (more) {
-      la.store(lds[cur ^ 1], tid);
-      lb.store(lds[cur ^ 1] + A_SLOTS, tid_b);
-    }
+    lb.store(na + A_SLOTS, tid);
+#pragma unroll
+    for (int i = 0; i < H; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[1][i], fb[1][j], acc[i][j]);
+    sched_mfma_interleave<0, H * TN, 0x200, NGB, 0>();
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = lds_frag<AK>(na, ar0 + 32 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = lds_frag<BKC>(na + A_SLOTS, br0 + 32 * j, 0, lane);
+#pragma unroll
+    for (int i = H; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[1][i], fb[1][j], acc[i][j]);
+    sched_mfma_interleave<0, (TM - H) * TN, 0x100, NR, 0>();
   }
+  __syncthreads();
 
   // Epilogue, staged through LDS one 32-row strip of the wave's tile at a
   // time: the accumulators (register r of lane l = row mfma_row(r, l),
@@ -149,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) strip[mfma_row(r, lane) * SP + j * 32 + frow] = acc[i][j][r];
+      for (int r = 0; r < 16; ++r) strip[mfma_row(r, lane) * SP + j * 32 + (lane & 31)] = acc[i][j][r];
     __syncthreads();
 #pragma unroll 1
     for (int v = lane; v < 32 * VPR; v += 64) {
@@ -173,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
         float z[8];
         unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.zin) + o), z);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) val[e] *= act_grad(z[e], ACT);
+        for (int e = 0; e < 8; ++e) val[e] *= act_grad_fast(z[e], ACT);
       } else {
         if (g.bias != nullptr) {
           float b[8];
@@ -191,7 +210,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
         }
         if constexpr (ACT != MP_ACT_NONE) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) val[e] = act_fwd(val[e], ACT);
+          for (int e = 0; e < 8; ++e) val[e] = act_fwd_fast(val[e], ACT);
         }
       }
       if (g.out_bf16) {
@@ -304,7 +323,7 @@ __global__ __launch_bounds__(256) void dact_kernel(int64_t nvec, const void* __r
   V::load(dy, v * E, a);
   V::load(z, v * E, b);
 #pragma unroll
-  for (int i = 0; i < E; ++i) a[i] *= act_grad(b[i], act);
+  for (int i = 0; i < E; ++i) a[i] *= BF16 ? act_grad_fast(b[i], act) : act_grad(b[i], act);
   V::store(dz, v * E, a);
 }
 
@@ -317,20 +336,23 @@ struct Plan {
 };
 
 // Chooses the tile shape and the K split by estimated time (microseconds):
-// waves of workgroups x k-steps x the measured time of one 64-deep k-step of
-// that tile, plus, for a split, writing and re-reading the fp32 partials.
+// rounds of workgroups x (k-steps x the time of one 64-deep k-step + the
+// fixed prologue/epilogue time of a tile), plus, for a split, writing and
+// re-reading the fp32 partials.  The per-tile constants were measured on
+// MI355X with random bf16 operands (the layouts run within a few percent of
+// each other).  128x128 tiles fit two workgroups per CU; a last round in
+// which no CU holds two of them runs at ~0.6 of a full round.
 // MP_GEMM_PLAN="bm,bn,splits" forces a plan (for tuning sweeps).
 static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split, Layout lay) {
-  // Measured on MI355X: one 64-deep k-step of a tile when every CU holds
-  // `slots / 256` workgroups, for the forward (NT) and weight-gradient (TN)
-  // layouts; the input-gradient layout (NN) runs ~10% slower than NT.
-  struct Cand { int bm, bn, slots; double t_nt_us, t_tn_us; };
-  const Cand cands[] = {{256, 256, 256, 2.1, 3.8}, {256, 128, 256, 1.5, 2.7}, {128, 128, 512, 1.0, 1.9}};
+  (void)lay;
+  struct Cand { int bm, bn, slots; double t_step_us, t_fixed_us; };
+  const Cand cands[] = {{256, 256, 256, 1.64, 17.7}, {256, 192, 256, 1.62, 12.0}, {256, 128, 256, 1.22, 9.0},
+                        {128, 128, 512, 1.08, 6.1}};
   const int64_t kt_total = ceil_div(K > 0 ? K : 1, 64);
   if (const char* env = getenv("MP_GEMM_PLAN")) {
     int bm = 0, bn = 0, sp = 1;
     if (sscanf(env, "%d,%d,%d", &bm, &bn, &sp) == 3 && sp >= 1 && (allow_split || sp == 1) &&
-        ((bm == 256 && bn == 256) || (bm == 256 && bn == 128) || (bm == 128 && bn == 128))) {
+        ((bm == 256 && (bn == 256 || bn == 192 || bn == 128)) || (bm == 128 && bn == 128))) {
       const int64_t kt = ceil_div(kt_total, sp);
       return Plan{bm, bn, static_cast<int>(ceil_div(kt_total, kt)), kt * 64};
     }
@@ -344,10 +366,11 @@ static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split, Layout 
       const int64_t kt = ceil_div(kt_total, s);
       if (s > 1 && kt < 4) break;
       if (ceil_div(kt_total, kt) != s) continue;  // every split non-empty
-      const int64_t waves = ceil_div(tiles * s, c.slots);
-      const double t_step = lay == TN ? c.t_tn_us : (lay == NN ? 1.1 * c.t_nt_us : c.t_nt_us);
-      double cost = static_cast<double>(waves) * kt * t_step;
-      if (s > 1) cost += 2.0 * 4.0 * M * N * s / 5e12 * 1e6 + 3.0;
+      const int64_t blocks = tiles * s;
+      const int64_t full = blocks / c.slots, rem = blocks - full * c.slots;
+      const double part = rem == 0 ? 0.0 : (c.slots > 256 && rem <= 256 ? 0.6 : 1.0);
+      double cost = (static_cast<double>(full) + part) * (kt * c.t_step_us + c.t_fixed_us);
+      if (s > 1) cost += 3.0 + (s + 1) * 4.0 * M * N / 6.5e6;
       if (cost < best_cost) {
         best_cost = cost;
         best = Plan{c.bm, c.bn, s, kt * 64};
@@ -359,14 +382,14 @@ static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split, Layout 
 
 template <int BM, int BN, bool AK, bool BKC, int EPI, int ACT>
 static void launch_bf16_tile(const GemmArgs& g, int splits, hipStream_t s) {
-  constexpr int NW = (BM == 256 && BN == 256) ? 8 : 4;
   const dim3 grid(static_cast<unsigned>(g.tiles_m * g.tiles_n), 1, static_cast<unsigned>(splits));
-  gemm_bf16_kernel<BM, BN, NW, AK, BKC, EPI, ACT><<<grid, 64 * NW, 0, s>>>(g);
+  gemm_bf16_kernel<BM, BN, AK, BKC, EPI, ACT><<<grid, 256, 0, s>>>(g);
 }
 
 template <bool AK, bool BKC, int EPI, int ACT>
 static void launch_bf16_layout(const GemmArgs& g, const Plan& p, hipStream_t s) {
   if (p.bm == 256 && p.bn == 256) launch_bf16_tile<256, 256, AK, BKC, EPI, ACT>(g, p.splits, s);
+  else if (p.bm == 256 && p.bn == 192) launch_bf16_tile<256, 192, AK, BKC, EPI, ACT>(g, p.splits, s);
   else if (p.bm == 256 && p.bn == 128) launch_bf16_tile<256, 128, AK, BKC, EPI, ACT>(g, p.splits, s);
   else launch_bf16_tile<128, 128, AK, BKC, EPI, ACT>(g, p.splits, s);
 }

@@ -1,12 +1,16 @@
 // gfx950 matrix-core helpers: the bf16 MFMA wrappers and the LDS tile format
 // shared by the GEMM, grouped-GEMM and attention kernels.
 //
-// LDS tile format: a tile of R rows x 64 k-values (bf16) is stored as R rows
-// of eight 16-byte chunks (8 k-values each).  Chunk c of row r lives at slot
-// r*8 + (c ^ (r & 7)): the XOR swizzle puts the same chunk of 8 consecutive
-// rows in 8 different bank groups, so both the 16-byte row-wise stores and
-// the 16-byte fragment reads (32 consecutive rows, one chunk) are free of
-// bank conflicts.
+// LDS tile format: 64-deep k-tiles of bf16, stored as rows of eight 16-byte
+// chunks.  For a K-contiguous operand a row is one operand row (8 chunks of 8
+// k-values); for an MN-contiguous operand the tile is split into sub-tiles of
+// 64 operand columns and a row is one k-value of a sub-tile (8 chunks of 8
+// consecutive columns).  Chunk c of row r lives at slot r*8 + (c ^ swz(r)),
+// where swz maps (r/2) % 8 one-to-one onto 0..7 and flips bit 2 between rows
+// r and r+2 when r % 4 < 2.  With 64 four-byte banks (256 bytes per LDS cycle)
+// this keeps three access patterns free of bank conflicts: 16-byte fragment
+// reads (one chunk of 16 consecutive rows), 16-byte row-wise stores (two
+// whole rows), and transpose reads (four consecutive rows x 64 bytes).
 #pragma once
 
 #include "common.h"
@@ -44,7 +48,11 @@ __device__ __forceinline__ uint4 buf_load16(const BufRes& r, uint32_t off) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+__device__ __forceinline__ int lds_swz(int row) {
+  const int t = (row >> 1) & 7;
+  return t ^ ((t & 1) << 2);
+}
+__device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 8 + (chunk ^ lds_swz(row)); }
 
 // Row m of the MFMA result held by register r of lane `lane`.
 __device__ __forceinline__ int mfma_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
@@ -63,37 +71,19 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// 8x8 transpose of 16-bit values: in[k] holds 8 values (columns 0..7) of row
-// k; out[c] receives the 8 values of column c (rows 0..7).
-__device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ void transpose8x8_b16(const uint4* in, uint4* out) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {      // column pair (2p, 2p+1)
-    uint32_t ev[4], od[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {    // row pair (2w, 2w+1)
-      const uint32_t r0 = u4_word(in[2 * w], p);
-      const uint32_t r1 = u4_word(in[2 * w + 1], p);
-      ev[w] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // low halves
-      od[w] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // high halves
-    }
-    out[2 * p] = make_uint4(ev[0], ev[1], ev[2], ev[3]);
-    out[2 * p + 1] = make_uint4(od[0], od[1], od[2], od[3]);
-  }
-}
-
-// Global -> register -> LDS loader of one R x 64 operand tile, NT threads.  Loads go
-// through a buffer resource whose base is the tile's first row (K-contiguous)
-// or first column (MN-contiguous); an element outside the matrix or past the
-// k-range gets an out-of-range offset, which the hardware returns as zeros.
+// Global -> register -> LDS loader of one operand tile of R operand rows x 64
+// k-values, NT threads.  Loads go through a buffer resource whose base is the
+// tile's first row (K-contiguous) or first column (MN-contiguous); an element
+// outside the matrix or past the k-range gets an out-of-range offset, which
+// the hardware returns as zeros.  Eight consecutive threads read 128
+// contiguous bytes: one operand row (K-contiguous) or 64 columns of one
+// k-row (MN-contiguous); the latter are stored as they are, in the
+// sub-tile format, and read back with transpose reads.
 template <int R, bool KC, int NT>
 struct TileLoader {
-  static constexpr int NBLK = KC ? 0 : (R + NT - 1) / NT;  // 8x8 blocks per thread
-  static constexpr int NREG = KC ? R * 8 / NT : 8 * NBLK;
-  static_assert(!KC || (R * 8) % NT == 0, "tile rows must cover the threads");
+  static_assert((R * 8) % NT == 0, "tile chunks must cover the threads");
+  static_assert(KC || R % 64 == 0, "MN-contiguous tiles are whole 64-column sub-tiles");
+  static constexpr int NREG = R * 8 / NT;
   uint4 reg[NREG];
 
   // Resource for rows [row0, rows) of a K-contiguous matrix with row stride
@@ -107,51 +97,67 @@ struct TileLoader {
   // `res_row` = rows between the resource base and row0 (K-contiguous only).
   __device__ __forceinline__ void load(const BufRes& rs, int64_t ld, int64_t row0, int64_t rows, int64_t k0,
                                        int64_t kend, int tid, int64_t res_row = 0) {
-    if constexpr (KC) {
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int idx = tid + NT * i;
+    for (int i = 0; i < NREG; ++i) {
+      const int idx = tid + NT * i;
+      if constexpr (KC) {
         const int64_t r = idx >> 3;
         const int64_t gk = k0 + (idx & 7) * 8;
         const bool ok = row0 + r < rows && gk < kend;
         reg[i] = buf_load16(rs, ok ? static_cast<uint32_t>(((res_row + r) * ld + gk) * 2) : kBufOOB);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NBLK; ++b) {
-        const int idx = tid + NT * b;
-        const int64_t mm = (idx >> 3) * 8;
-        const int64_t gk = k0 + (idx & 7) * 8;
-        const bool ok = idx < R && row0 + mm < rows;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          reg[8 * b + kk] =
-              buf_load16(rs, (ok && gk + kk < kend) ? static_cast<uint32_t>(((gk + kk) * ld + mm) * 2) : kBufOOB);
+      } else {
+        const int64_t mm = (idx >> 9) * 64 + (idx & 7) * 8;
+        const int64_t gk = k0 + ((idx >> 3) & 63);
+        const bool ok = row0 + mm < rows && gk < kend;
+        reg[i] = buf_load16(rs, ok ? static_cast<uint32_t>((gk * ld + mm) * 2) : kBufOOB);
       }
     }
   }
 
   __device__ __forceinline__ void store(uint4* __restrict__ tile, int tid) const {
-    if constexpr (KC) {
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int idx = tid + NT * i;
-        tile[lds_slot(idx >> 3, idx & 7)] = reg[i];
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NBLK; ++b) {
-        const int idx = tid + NT * b;
-        if (idx < R) {
-          uint4 t[8];
-          transpose8x8_b16(reg + 8 * b, t);
-          const int mb = (idx >> 3) * 8, kb = idx & 7;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) tile[lds_slot(mb + i, kb)] = t[i];
-        }
-      }
+    for (int i = 0; i < NREG; ++i) {
+      const int idx = tid + NT * i;
+      if constexpr (KC) tile[lds_slot(idx >> 3, idx & 7)] = reg[i];
+      else tile[(idx >> 9) * 512 + lds_slot((idx >> 3) & 63, idx & 7)] = reg[i];
     }
   }
 };
+
+// MFMA operand fragment of k-step ks (16 k-values) for operand rows
+// r0 .. r0+31 (r0 % 32 == 0) of a tile stored by TileLoader: lane l gets row
+// r0 + l%32, k-values 16*ks + 8*(l/32) .. +7.  An MN-contiguous tile is read
+// with two transpose reads of four k-rows each.
+template <bool KC>
+__device__ __forceinline__ uint4 lds_frag(const uint4* tile, int r0, int ks, int lane) {
+  if constexpr (KC) {
+    return tile[lds_slot(r0 + (lane & 31), 2 * ks + (lane >> 5))];
+  } else {
+    const int i = lane & 15;
+    const int k = 16 * ks + 8 * (lane >> 5) + (i >> 2);
+    const int c = r0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+    const char* sub = reinterpret_cast<const char*>(tile + (c >> 6) * 512) + (c & 7) * 2;
+    const uint2 lo = lds_read_tr16(sub + lds_slot(k, (c & 63) >> 3) * 16);
+    const uint2 hi = lds_read_tr16(sub + lds_slot(k + 4, (c & 63) >> 3) * 16);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+// Instruction-scheduling pattern for a software-pipelined MFMA step: NM
+// MFMAs, each followed by its share of NDS LDS operations (kind DSM: 0x100
+// reads, 0x200 writes) and NVM global loads.
+template <int M, int NM, int DSM, int NDS, int NVM>
+__device__ __forceinline__ void sched_mfma_interleave() {
+  if constexpr (M < NM) {
+    constexpr int dper = (NDS + NM - 1) / NM, d0 = M * dper;
+    constexpr int dn = d0 >= NDS ? 0 : (NDS - d0 < dper ? NDS - d0 : dper);
+    constexpr int vper = (NVM + NM - 1) / NM, v0 = M * vper;
+    constexpr int vn = v0 >= NVM ? 0 : (NVM - v0 < vper ? NVM - v0 : vper);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (dn > 0) __builtin_amdgcn_sched_group_barrier(DSM, dn, 0);
+    if constexpr (vn > 0) __builtin_amdgcn_sched_group_barrier(0x020, vn, 0);
+    sched_mfma_interleave<M + 1, NM, DSM, NDS, NVM>();
+  }
+}
 
 }  // namespace mp
