@@ -85,27 +85,39 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  TileLoader<BM, AK, NT> la;
-  TileLoader<BN, BKC, NT> lb;
-  const BufRes ra = TileLoader<BM, AK, NT>::resource(A, g.lda, m0, g.M, g.K);
-  const BufRes rb = TileLoader<BN, BKC, NT>::resource(B, g.ldb, n0, g.N, g.K);
-  la.load(ra, g.lda, m0, g.M, kbeg, kend, tid);
-  lb.load(rb, g.ldb, n0, g.N, kbeg, kend, tid);
-  la.store(lds[0], tid);
-  lb.store(lds[0] + A_SLOTS, tid);
+  DmaTile<BM, AK, NT> da;
+  DmaTile<BN, BKC, NT> db;
+  da.init(A, g.lda, m0, g.M, g.K, tid);
+  db.init(B, g.ldb, n0, g.N, g.K, tid);
+  constexpr int NI = DmaTile<BM, AK, NT>::NI + DmaTile<BN, BKC, NT>::NI;
+  // k-tile t of this split starts at kbeg + 64 t; only a ragged last k-tile
+  // (K not a multiple of 64) needs the checked issue.
+  const bool ragged = (kend - kbeg) % 64 != 0;
+  auto fill = [&](uint4* buf, int t) {
+    const int64_t k0 = kbeg + 64 * static_cast<int64_t>(t);
+    if (ragged && t == nk - 1) {
+      da.issue_checked(buf, k0, kend, tid);
+      db.issue_checked(buf + A_SLOTS, k0, kend, tid);
+    } else {
+      da.issue(buf, k0, t < nk);
+      db.issue(buf + A_SLOTS, k0, t < nk);
+    }
+  };
+  fill(lds[0], 0);
+  fill(lds[1], 1);
+  wait_vmcnt<NI>();
   __syncthreads();
 
-  // Software pipeline.  Fragments are double-buffered in registers: while
-  // the MFMAs of k-step ks run, the fragments of ks+1 are read from LDS.
-  // The next k-tile is loaded into registers at the start of a k-tile and
-  // written to the other LDS buffer during the last two k-steps (operand A
-  // in step 2, B in step 3); the barrier that publishes it sits inside step
-  // 3, so the first fragments of the next k-tile are read while that step's
-  // remaining MFMAs run.  The loop body has no branches (past the end of K
-  // the loads return zeros and go unused), so each part is one scheduling
-  // region and the interleave patterns below apply as written.
+  // Software pipeline.  k-tiles stream through two LDS buffers by direct
+  // loads: k-tile kt+2 is issued into the buffer of k-tile kt as soon as the
+  // barrier inside kt's last k-step has retired every read of it, so a load
+  // has a whole k-tile of MFMAs to land.  Fragments are double-buffered in
+  // registers: while the MFMAs of k-step ks run, the fragments of ks+1 are
+  // read.  The barrier sits inside the last k-step, so the first fragments
+  // of the next k-tile are read while that step's remaining MFMAs run.  The
+  // loop body has no branches (past the end of K the loads write zeros and
+  // go unused), so the interleave patterns below apply as written.
   constexpr int NRA = AK ? TM : 2 * TM, NRB = BKC ? TN : 2 * TN, NR = NRA + NRB;
-  constexpr int NGA = TileLoader<BM, AK, NT>::NREG, NGB = TileLoader<BN, BKC, NT>::NREG;
   constexpr int NM = TM * TN, H = TM / 2;
   const int ar0 = wm * WM, br0 = wn * WN;
   uint4 fa[2][TM], fb[2][TN];
@@ -115,11 +127,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   for (int j = 0; j < TN; ++j) fb[0][j] = lds_frag<BKC>(lds[0] + A_SLOTS, br0 + 32 * j, 0, lane);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const uint4* ta = lds[kt & 1];
-    const uint4* tb = ta + A_SLOTS;
-    uint4* na = lds[(kt & 1) ^ 1];
-    la.load(ra, g.lda, m0, g.M, kbeg + (kt + 1) * 64, kend, tid);
-    lb.load(rb, g.ldb, n0, g.N, kbeg + (kt + 1) * 64, kend, tid);
+    uint4* cur = lds[kt & 1];
+    const uint4* ta = cur;
+    const uint4* tb = cur + A_SLOTS;
+    const uint4* na = lds[(kt & 1) ^ 1];
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       const int c = ks & 1, n = c ^ 1;
@@ -127,32 +138,29 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
       for (int i = 0; i < TM; ++i) fa[n][i] = lds_frag<AK>(ta, ar0 + 32 * i, ks + 1, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j) fb[n][j] = lds_frag<BKC>(tb, br0 + 32 * j, ks + 1, lane);
-      if (ks == 2) la.store(na, tid);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[c][i], fb[c][j], acc[i][j]);
-      if (ks == 0) sched_mfma_interleave<0, NM, 0x100, NR, NGA + NGB>();
-      else if (ks == 1) sched_mfma_interleave<0, NM, 0x100, NR, 0>();
-      else sched_mfma_interleave<0, NM, 0x180, NR + NGA, 0>();
+      sched_mfma_interleave<0, NM, 0x100, NR, 0>();
     }
-    lb.store(na + A_SLOTS, tid);
 #pragma unroll
     for (int i = 0; i < H; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[1][i], fb[1][j], acc[i][j]);
-    sched_mfma_interleave<0, H * TN, 0x200, NGB, 0>();
+    wait_vm_lds();  // k-tile kt+1 has landed (this wave's share); reads of kt retired
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[0][i] = lds_frag<AK>(na, ar0 + 32 * i, 0, lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[0][j] = lds_frag<BKC>(na + A_SLOTS, br0 + 32 * j, 0, lane);
+    fill(cur, kt + 2);
 #pragma unroll
     for (int i = H; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[1][i], fb[1][j], acc[i][j]);
-    sched_mfma_interleave<0, (TM - H) * TN, 0x100, NR, 0>();
   }
+  wait_vm_lds();  // the trailing (all-zero) loads write LDS the epilogue reuses
   __syncthreads();
 
   // Epilogue, staged through LDS one 32-row strip of the wave's tile at a
@@ -436,6 +444,11 @@ int gemm(mp_dtype dt, Layout lay, int64_t M, int64_t N, int64_t K, const void* A
   g.M = M; g.N = N; g.K = K; g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.bias = bias; g.zsave = zsave; g.zin = zin; g.act = act; g.out_bf16 = out_bf16 ? 1 : 0;
   if (dt == MP_BF16) {
+    // Direct loads address an MN-contiguous operand with 32-bit offsets from
+    // the tile's first column across all of K.
+    const int64_t lim = 0x7fffffffLL;
+    if ((lay == TN && (K + 64) * lda * 2 > lim) || (lay != NT && (K + 64) * ldb * 2 > lim))
+      return fail(MP_ERR_SHAPE, "gemm: an MN-contiguous operand spans more than 2 GiB");
     const Plan p = plan_bf16(M, N, K, allow_split && epi == EPI_STORE && bias == nullptr && act == MP_ACT_NONE &&
                                           zsave == nullptr && lay == TN, lay);
     g.tiles_m = static_cast<int>(ceil_div(M, p.bm));

@@ -124,6 +124,133 @@ struct TileLoader {
   }
 };
 
+// ------------------------------------------------ direct global -> LDS
+// buffer_load_dwordx4 with the LDS flag writes the 16 bytes each lane fetches
+// to LDS at M0 + 16 * lane (64 consecutive 16-byte slots per wave), without
+// passing through registers; a lane whose offset lies outside the resource
+// writes zeros.  It is issued from inline assembly so that the compiler's
+// wait-count tracking, which would otherwise wait for it before every LDS
+// read, leaves it alone: completion is awaited explicitly (wait_vmcnt).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base, stride 0, num_records = bytes, default format.
+__device__ __forceinline__ i32x4_t make_desc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  i32x4_t d;
+  d[0] = static_cast<int>(a & 0xffffffffu);
+  d[1] = static_cast<int>((a >> 32) & 0xffffu);
+  d[2] = static_cast<int>(n);
+  d[3] = 0x00020000;
+  return d;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(const_cast<void*>(p))));
+}
+
+__device__ __forceinline__ void dma16(const i32x4_t& desc, uint32_t voff, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(desc), "s"(base)
+               : "memory", "m0");
+}
+
+// Waits until at most N vector-memory loads of this wave are outstanding.
+// (Inline assembly: the compiler may relax a waitcnt builtin it believes
+// unnecessary, and it does not know about the direct loads.)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Waits until this wave has no vector-memory load and no LDS operation
+// outstanding.  Before a barrier that hands an LDS buffer over to direct
+// loads, this retires the wave's own reads of it: a plain __syncthreads()
+// only waits for LDS writes.
+__device__ __forceinline__ void wait_vm_lds() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+
+// Direct loader of one operand tile (R operand rows x 64 k-values, NT
+// threads) into the LDS tile format.  Wave instruction q of wave w fills
+// slots (q * NT/64 + w) * 64 .. +63; lane l fetches whichever global chunk
+// belongs in slot base + l (the swizzle is undone on the global side, so the
+// 8 lanes of a row still read 128 contiguous bytes).  Only the per-lane part
+// of the address lives in a VGPR: the copy and k-step parts go in the
+// instruction's scalar offset and M0, so issuing costs no vector ALU work.
+// Rows past the end of a K-contiguous operand lie outside the resource and
+// arrive as zeros; columns past the end of an MN-contiguous operand read
+// neighbouring values that only reach discarded outputs.  A k-tile that
+// extends past the k-range must use issue_checked(), which zeroes those
+// elements.  Offsets are 32-bit: the operand panel must stay below 2 GiB.
+template <int R, bool KC, int NT>
+struct DmaTile {
+  static_assert((R * 8) % NT == 0, "tile chunks must cover the threads");
+  static_assert(KC || R % 64 == 0, "MN-contiguous tiles are whole 64-column sub-tiles");
+  static constexpr int NWV = NT / 64, NI = R * 8 / NT;
+  static constexpr uint32_t kOOB = 0x80000000u;
+  i32x4_t desc;
+  uint32_t voff;   // per-lane byte offset of copy 0 at k = 0
+  int wave;        // wave index (uniform)
+  int64_t ld, row0, rows;
+
+  // K-contiguous: rows [row0, rows) of a matrix with row stride ld.
+  // MN-contiguous: columns [row0, rows) of a [kdim][ld] matrix.
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld_, int64_t row0_, int64_t rows_, int64_t kdim,
+                                       int tid) {
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    ld = ld_;
+    row0 = row0_;
+    rows = rows_;
+    if constexpr (KC) desc = make_desc(base + row0 * ld, (rows - row0) * ld * 2);
+    else desc = make_desc(base + row0, (kdim * ld - row0) * 2);
+    // Slot (q * NWV + w) * 64 + l holds row/k-row wave*8 + l/8 (+ a per-copy
+    // step), chunk (l % 8) ^ swz(row): the swizzle term does not depend on q.
+    const int r = wave * 8 + (lane >> 3), c = (lane & 7) ^ lds_swz(r);
+    voff = static_cast<uint32_t>((r * ld + c * 8) * 2);
+  }
+
+  // Scalar offset of copy q at k-tile start k0.
+  __device__ __forceinline__ uint32_t soff(int q, int64_t k0) const {
+    if constexpr (KC) return static_cast<uint32_t>((q * NWV * 8 * ld + k0) * 2);
+    else return static_cast<uint32_t>((((q & 1) * 32 + k0) * ld + (q >> 1) * 64) * 2);
+  }
+
+  // Fills `tile` with the k-tile starting at k0 (all 64 k-values in range),
+  // or with zeros when `live` is false.
+  __device__ __forceinline__ void issue(uint4* tile, int64_t k0, bool live) const {
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(tile)) + wave * 1024;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const uint32_t so = live ? soff(q, k0) : kOOB;
+      const uint32_t m0v = lb + q * NWV * 1024;
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(desc),
+                   "s"(m0v), "s"(so)
+                   : "memory", "m0");
+    }
+  }
+
+  // As issue(), zeroing elements at k >= kend and, for an MN-contiguous
+  // operand, columns past its end.
+  __device__ __forceinline__ void issue_checked(uint4* tile, int64_t k0, int64_t kend, int tid) const {
+    const int lane = tid & 63;
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(tile)) + wave * 1024;
+    const int r = wave * 8 + (lane >> 3), c = (lane & 7) ^ lds_swz(r);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      bool ok;
+      if constexpr (KC) ok = k0 + c * 8 < kend;
+      else ok = k0 + (q & 1) * 32 + r < kend && row0 + (q >> 1) * 64 + c * 8 < rows;
+      const uint32_t v = ok ? voff + soff(q, k0) : kOOB;
+      const uint32_t m0v = lb + q * NWV * 1024;
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(v), "s"(desc),
+                   "s"(m0v)
+                   : "memory", "m0");
+    }
+  }
+};
+
 // MFMA operand fragment of k-step ks (16 k-values) for operand rows
 // r0 .. r0+31 (r0 % 32 == 0) of a tile stored by TileLoader: lane l gets row
 // r0 + l%32, k-values 16*ks + 8*(l/32) .. +7.  An MN-contiguous tile is read

@@ -87,6 +87,29 @@ def test_row_linear_bwd(dtype, T, Fi, K):
     assert rel_frobenius(f64(db), wdb) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("plan", ["256,256,1", "256,192,1", "256,128,1", "128,128,3", "256,192,2"])
+def test_forced_tile_plans_ragged(plan, monkeypatch):
+    """Every tile shape and a split-K whose last split is ragged, on ragged
+    M, N and K in all three layouts (forward NT; backward NN and TN)."""
+    say("forced plan", plan)
+    monkeypatch.setenv("MP_GEMM_PLAN", plan)
+    T, Fi, K = 1000, 200, 264
+    y = randn(13, (T, Fi), "bf16")
+    b = randn(14, (K, Fi), "bf16", 0.05)
+    dout = randn(15, (T, K), "bf16")
+    p = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dy = torch.empty((T, Fi), dtype=torch.bfloat16, device="cuda")
+    db = torch.empty((K, Fi), dtype=torch.float32, device="cuda")
+    yd, bd = cu(y), cu(b)
+    mp.mp_row_linear_partial(yd, bd, p)
+    mp.mp_row_linear_partial_bwd(yd, bd, cu(dout), dy, db)
+    sync()
+    assert rel_frobenius(f64(p), O.row_linear_partial(f64(y), f64(b))) <= TOL["bf16"]
+    wdy, wdb = O.row_linear_partial_bwd(f64(y), f64(b), f64(dout))
+    assert rel_frobenius(f64(dy), wdy) <= TOL["bf16"]
+    assert rel_frobenius(f64(db), wdb) <= TOL["bf16"]
+
+
 @pytest.mark.slow
 def test_full_size_mlp_shard_sampled_rows():
     # One rank's MLP share of the 8.3B-config layer: X [8192, 3072],
