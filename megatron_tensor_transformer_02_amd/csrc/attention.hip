@@ -2,15 +2,17 @@
 // fused QKV GEMM over the rank's heads, then attention per (batch, head)
 // (heads are independent, so a rank's heads need no communication).
 //
-// Forward (flash-style, one pass over the keys): a wave owns 32 queries and
-// computes S^T = K Q^T with 32x32x16 bf16 MFMAs, so each lane holds the
-// scores of ONE query (16 of every 32 keys; its partner lane l^32 holds the
-// other 16).  The online softmax therefore needs only a lane-pair exchange
-// for the running max.  The probabilities' registers 8s..8s+7 are, as they
-// stand, the B operand of O^T += V^T P^T for keys {16s+4g..+3, 16s+8+4g..+3}
-// (g = lane / 32); the V^T fragments come from the plain V row tile through
-// two LDS transpose reads (4 consecutive keys each) in that same key order,
-// so P never leaves registers and no transposed tile is ever stored.
+// Forward (flash-style, one pass over the keys): a wave owns 16 queries and
+// computes S^T = K Q^T with 16x16x32 bf16 MFMAs, so lane l holds scores of
+// query l % 16 only (4 of every 16 keys; the four lanes l % 16 + 16j share
+// the query), and the online softmax needs two lane exchanges for the
+// running max.  The probabilities of keys {32t + 4g .. +3, 32t+16+4g .. +3}
+// (g = lane / 16) are, as they stand, the B operand of O^T += V^T P^T for
+// the 32-key step t; the V^T fragments come from the plain V row tile
+// through two LDS transpose reads (4 consecutive keys each) in that same key
+// order, so P never leaves registers and no transposed tile is stored.
+// Sixteen rows per wave keep the register footprint small enough for two or
+// more waves per SIMD and give short sequences with few heads enough waves.
 //
 // Every kernel streams 64-row tiles through two LDS buffers: the next tile is
 // loaded into registers while the current one is multiplied, then written to
@@ -18,8 +20,8 @@
 //
 // Backward (P recomputed from the saved log-sum-exp, no atomics):
 //  * dQ kernel -- lanes own queries: S^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
-//  * dK/dV kernel -- lanes own keys: S = Q K^T, dV^T += dO^T P, dP = dO V^T,
-//    dS, dK^T += Q^T dS.
+//  * dK/dV kernel -- lanes own keys: S = Q K^T, dP = dO V^T, dS,
+//    dV^T += dO^T P, dK^T += Q^T dS.
 // The QKV GEMM's input and weight gradients then run on the GEMM family.
 #include "gemm.h"
 #include "mfma.h"
@@ -46,13 +48,10 @@ __device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
   return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
 }
 
-// Packs registers 8*s2 .. 8*s2+7 of a 32x32 result into a bf16 B operand.
-__device__ __forceinline__ uint4 pack_half(const float* v, int s2) { return pack8(v + 8 * s2); }
-
 // A 64-row x D-column tile of a [L, ld] bf16 matrix (a head slice), held in
-// KH = D/64 LDS sub-tiles of the GEMM tile format (64 rows x 64 columns,
-// rows of eight swizzled 16-byte chunks).  load() fetches rows r0..r0+63
-// into registers (rows >= L read as zeros), store() writes them to LDS.
+// D/64 LDS sub-tiles of the GEMM tile format (64 rows x 64 columns, rows of
+// eight swizzled 16-byte chunks).  load() fetches rows r0..r0+63 into
+// registers (rows >= L read as zeros), store() writes them to LDS.
 template <int D, int NT>
 struct RowTile {
   TileLoader<64, true, NT> part[D / 64];
@@ -66,10 +65,11 @@ struct RowTile {
   }
 };
 
-// Row fragment (A or B operand) of a row tile: row `row`, k-step `st`
-// (16 columns), lane group g.
-__device__ __forceinline__ uint4 lds_row_frag(const uint4* tile, int row, int st, int g) {
-  return tile[(st >> 2) * 512 + lds_slot(row, 2 * (st & 3) + g)];
+// Row fragment (A or B operand) of a row tile: row r0 + lane%16, columns
+// 32*st + 8*(lane/16) .. +7.
+__device__ __forceinline__ uint4 row_frag(const uint4* tile, int r0, int st, int lane) {
+  const int c = 32 * st + 8 * (lane >> 4);
+  return tile[(c >> 6) * 512 + lds_slot(r0 + (lane & 15), (c & 63) >> 3)];
 }
 
 // Byte address of element (r, d) of a row tile.
@@ -78,47 +78,61 @@ __device__ __forceinline__ const char* tile_elem(const uint4* tile, int r, int d
 }
 
 // Transposed A-operand fragment from a row tile: operand row = tile column
-// d = dt*32 + lane%32; its 8 k-slots are tile rows {kt*32 + 16*s2 + 4g .. +3}
-// and {kt*32 + 16*s2 + 8 + 4g .. +3} (g = lane / 32), the register order of a
-// 32x32 result used as the B operand.  Two transpose reads of 4 rows each.
-__device__ __forceinline__ uint4 lds_tr_frag(const uint4* tile, int dt, int kt, int s2, int lane) {
+// d0 + lane%16; its 8 k-slots are tile rows {32t + 4g .. +3} and
+// {32t + 16 + 4g .. +3} (g = lane / 16): two transpose reads of 4 rows.
+__device__ __forceinline__ uint4 tr_frag(const uint4* tile, int d0, int t, int lane) {
   const int grp = lane >> 4, i = lane & 15;
-  const int r = kt * 32 + 16 * s2 + 4 * (grp >> 1) + (i >> 2);
-  const int d = dt * 32 + 16 * (grp & 1) + 4 * (i & 3);
+  const int r = 32 * t + 4 * grp + (i >> 2);
+  const int d = d0 + 4 * (i & 3);
   const uint2 lo = lds_read_tr16(tile_elem(tile, r, d));
-  const uint2 hi = lds_read_tr16(tile_elem(tile, r + 8, d));
+  const uint2 hi = lds_read_tr16(tile_elem(tile, r + 16, d));
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// B operand for the 32-row step t from two 16-row results (rows 4g + r):
+// rows {32t + 4g + r} from x0 and {32t + 16 + 4g + r} from x1, as bf16.
+__device__ __forceinline__ uint4 pack_pair(const f32x4_t& x0, const f32x4_t& x1) {
+  return make_uint4(pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]),
+                    pack_bf16x2(x1[2], x1[3]));
+}
+
+// Max over the four lanes that share lane % 16.
+__device__ __forceinline__ float max4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float sum4(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
 }
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
-  constexpr int NT = 64 * NW, BQ = 32 * NW, DT = D / 32, KS = D / 16, TS = D / 64 * 512;
+  constexpr int NT = 64 * NW, BQ = 16 * NW, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
   __shared__ uint4 lds_k[2][TS];
   __shared__ uint4 lds_v[2][TS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, frow = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qc = lane & 15, g = lane >> 4;
   const int nbh = a.B * a.h;
   const int bh = blockIdx.x % nbh;
   const int qb = a.nblk - 1 - static_cast<int>(blockIdx.x / nbh);  // heavy (late) query blocks first
   const int b = bh / a.h, hh = bh % a.h;
   const int64_t S3 = 3LL * a.h * D, HD = static_cast<int64_t>(a.h) * D;
   const uint16_t* base = a.qkv + static_cast<int64_t>(b) * a.L * S3;
-  const int q0 = qb * BQ, qw0 = q0 + wave * 32, qi = qw0 + frow;
+  const int q0 = qb * BQ, qw0 = q0 + wave * 16, qi = qw0 + qc;
   const bool qvalid = qi < a.L;
 
-  uint4 qf[KS];
+  uint4 qf[KS];  // Q^T as the B operand: query qi, d = 32 st + 8 g .. +7
 #pragma unroll
-  for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 16 * st + 8 * g, qvalid);
+  for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * g, qvalid);
 
   const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
   const BufRes rk = make_bufres(base + HD + hh * D, batch_bytes - (HD + hh * D) * 2);
   const BufRes rv = make_bufres(base + 2 * HD + hh * D, batch_bytes - (2 * HD + hh * D) * 2);
 
   float m = -INFINITY, l = 0.0f;
-  f32x16_t o[DT];
+  f32x4_t o[DB];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
   const int nkb = (kv_end + 63) / 64;
@@ -135,53 +149,51 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
       tk.load(rk, S3, kv0 + 64, a.L, tid);
       tv.load(rv, S3, kv0 + 64, a.L, tid);
     }
-    if (!(a.causal && kv0 > qw0 + 31)) {  // else every key of the block is in this wave's future
+    if (!(a.causal && kv0 > qw0 + 15)) {  // else every key of the tile is in this wave's future
       const uint4* kt_ = lds_k[cur];
       const uint4* vt_ = lds_v[cur];
-      f32x16_t s[2];
+      f32x4_t s[4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
+        for (int st = 0; st < KS; ++st) s[kb] = mfma_16x16x32(row_frag(kt_, 16 * kb, st, lane), qf[st], s[kb]);
+      }
+      // Keys of this lane: kv0 + 16 kb + 4 g + r.
+      if (kv0 + 63 >= a.L || (a.causal && kv0 + 63 > qw0)) {
 #pragma unroll
-        for (int st = 0; st < KS; ++st) s[kt] = mfma_32x32x16(lds_row_frag(kt_, kt * 32 + frow, st, g), qf[st], s[kt]);
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kv0 + 16 * kb + 4 * g + r;
+            if (key >= a.L || (a.causal && key > qi)) s[kb][r] = -INFINITY;
+          }
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kt * 32 + mfma_row(r, lane);
-          const bool vis = key < a.L && (!a.causal || key <= qi);
-          if (!vis) s[kt][r] = -INFINITY;
-          mx = fmaxf(mx, s[kt][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max4(mx);
       const float mn = fmaxf(m, mx);
       const float ms = mn == -INFINITY ? 0.0f : mn;
       const float alpha = exp2f((m - ms) * a.scale_log2);
+      const float msc = ms * a.scale_log2;
       float ps = 0.0f;
-      uint4 pb[2][2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float p[16];
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = exp2f((s[kt][r] - ms) * a.scale_log2);
-          ps += p[r];
+        for (int r = 0; r < 4; ++r) {
+          s[kb][r] = exp2f(fmaf(s[kb][r], a.scale_log2, -msc));
+          ps += s[kb][r];
         }
-        pb[kt][0] = pack_half(p, 0);
-        pb[kt][1] = pack_half(p, 1);
-      }
       l = l * alpha + ps;
+      const uint4 pb0 = pack_pair(s[0], s[1]), pb1 = pack_pair(s[2], s[3]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma_32x32x16(lds_tr_frag(vt_, dt, kt, s2, lane), pb[kt][s2], o[dt]);
+      for (int db = 0; db < DB; ++db) {
+        o[db] *= alpha;
+        o[db] = mfma_16x16x32(tr_frag(vt_, 16 * db, 0, lane), pb0, o[db]);
+        o[db] = mfma_16x16x32(tr_frag(vt_, 16 * db, 1, lane), pb1, o[db]);
       }
       m = mn;
     }
@@ -191,20 +203,17 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
     }
     __syncthreads();
   }
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = sum4(l);
   if (!qvalid) return;
   const float inv = 1.0f / lt;
   uint16_t* crow = a.ctx + (static_cast<int64_t>(b) * a.L + qi) * HD + hh * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = dt * 32 + 8 * q4 + 4 * g;
-      uint2 v;
-      v.x = pack_bf16x2(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv);
-      v.y = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
-      *reinterpret_cast<uint2*>(crow + d) = v;
-    }
+  for (int db = 0; db < DB; ++db) {
+    uint2 v;
+    v.x = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
+    v.y = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
+    *reinterpret_cast<uint2*>(crow + 16 * db + 4 * g) = v;
+  }
   if (g == 0) a.lse[(static_cast<int64_t>(b) * a.h + hh) * a.L + qi] = m * a.scale + logf(lt);
 }
 
@@ -234,25 +243,25 @@ __global__ __launch_bounds__(256) void attn_dvec_kernel(const AttnArgs a) {
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) {
-  constexpr int NT = 64 * NW, BQ = 32 * NW, DT = D / 32, KS = D / 16, TS = D / 64 * 512;
+  constexpr int NT = 64 * NW, BQ = 16 * NW, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
   __shared__ uint4 lds_k[2][TS];
   __shared__ uint4 lds_v[2][TS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, frow = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qc = lane & 15, g = lane >> 4;
   const int nbh = a.B * a.h;
   const int bh = blockIdx.x % nbh;
   const int qb = a.nblk - 1 - static_cast<int>(blockIdx.x / nbh);
   const int b = bh / a.h, hh = bh % a.h;
   const int64_t S3 = 3LL * a.h * D, HD = static_cast<int64_t>(a.h) * D;
   const uint16_t* base = a.qkv + static_cast<int64_t>(b) * a.L * S3;
-  const int q0 = qb * BQ, qw0 = q0 + wave * 32, qi = qw0 + frow;
+  const int q0 = qb * BQ, qw0 = q0 + wave * 16, qi = qw0 + qc;
   const bool qvalid = qi < a.L;
   const int64_t trow = static_cast<int64_t>(b) * a.L + qi;
 
   uint4 qf[KS], dof[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
-    qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 16 * st + 8 * g, qvalid);
-    dof[st] = ld16_or_zero(a.dctx + trow * HD + hh * D + 16 * st + 8 * g, qvalid);
+    qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * g, qvalid);
+    dof[st] = ld16_or_zero(a.dctx + trow * HD + hh * D + 32 * st + 8 * g, qvalid);
   }
   const int64_t sidx = (static_cast<int64_t>(b) * a.h + hh) * a.L + qi;
   const float lse2 = qvalid ? a.lse[sidx] * kLog2eA : 0.0f;
@@ -262,11 +271,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
   const BufRes rk = make_bufres(base + HD + hh * D, batch_bytes - (HD + hh * D) * 2);
   const BufRes rv = make_bufres(base + 2 * HD + hh * D, batch_bytes - (2 * HD + hh * D) * 2);
 
-  f32x16_t dq[DT];
+  f32x4_t dq[DB];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.0f;
+  for (int db = 0; db < DB; ++db) dq[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
   const int nkb = (kv_end + 63) / 64;
@@ -283,37 +290,33 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
       tk.load(rk, S3, kv0 + 64, a.L, tid);
       tv.load(rv, S3, kv0 + 64, a.L, tid);
     }
-    if (!(a.causal && kv0 > qw0 + 31)) {
+    if (!(a.causal && kv0 > qw0 + 15)) {
       const uint4* kt_ = lds_k[cur];
       const uint4* vt_ = lds_v[cur];
-      uint4 dsb[2][2];
+      const bool edge = kv0 + 63 >= a.L || (a.causal && kv0 + 63 > qw0);
+      f32x4_t ds[4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x16_t sv, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.0f;
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4_t sv = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
-          sv = mfma_32x32x16(lds_row_frag(kt_, kt * 32 + frow, st, g), qf[st], sv);
-          dp = mfma_32x32x16(lds_row_frag(vt_, kt * 32 + frow, st, g), dof[st], dp);
+          sv = mfma_16x16x32(row_frag(kt_, 16 * kb, st, lane), qf[st], sv);
+          dp = mfma_16x16x32(row_frag(vt_, 16 * kb, st, lane), dof[st], dp);
         }
-        float ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kt * 32 + mfma_row(r, lane);
-          const bool vis = qvalid && key < a.L && (!a.causal || key <= qi);
-          const float p = vis ? exp2f(sv[r] * a.scale_log2 - lse2) : 0.0f;
-          ds[r] = p * (dp[r] - dq_d);
+        for (int r = 0; r < 4; ++r) {
+          const int key = kv0 + 16 * kb + 4 * g + r;
+          const bool vis = qvalid && (!edge || (key < a.L && (!a.causal || key <= qi)));
+          const float p = vis ? exp2f(fmaf(sv[r], a.scale_log2, -lse2)) : 0.0f;
+          ds[kb][r] = p * (dp[r] - dq_d);
         }
-        dsb[kt][0] = pack_half(ds, 0);
-        dsb[kt][1] = pack_half(ds, 1);
       }
+      const uint4 d0 = pack_pair(ds[0], ds[1]), d1 = pack_pair(ds[2], ds[3]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) dq[dt] = mfma_32x32x16(lds_tr_frag(kt_, dt, kt, s2, lane), dsb[kt][s2], dq[dt]);
+      for (int db = 0; db < DB; ++db) {
+        dq[db] = mfma_16x16x32(tr_frag(kt_, 16 * db, 0, lane), d0, dq[db]);
+        dq[db] = mfma_16x16x32(tr_frag(kt_, 16 * db, 1, lane), d1, dq[db]);
+      }
     }
     if (more) {
       tk.store(lds_k[cur ^ 1], tid);
@@ -324,38 +327,35 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
   if (!qvalid) return;
   uint16_t* row = a.dqkv + trow * S3 + hh * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = dt * 32 + 8 * q4 + 4 * g;
-      uint2 v;
-      v.x = pack_bf16x2(dq[dt][4 * q4] * a.scale, dq[dt][4 * q4 + 1] * a.scale);
-      v.y = pack_bf16x2(dq[dt][4 * q4 + 2] * a.scale, dq[dt][4 * q4 + 3] * a.scale);
-      *reinterpret_cast<uint2*>(row + d) = v;
-    }
+  for (int db = 0; db < DB; ++db) {
+    uint2 v;
+    v.x = pack_bf16x2(dq[db][0] * a.scale, dq[db][1] * a.scale);
+    v.y = pack_bf16x2(dq[db][2] * a.scale, dq[db][3] * a.scale);
+    *reinterpret_cast<uint2*>(row + 16 * db + 4 * g) = v;
+  }
 }
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a) {
-  constexpr int NT = 64 * NW, BK = 32 * NW, DT = D / 32, KS = D / 16, TS = D / 64 * 512;
+  constexpr int NT = 64 * NW, BK = 16 * NW, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
   __shared__ uint4 lds_q[2][TS];
   __shared__ uint4 lds_do[2][TS];
   __shared__ float lds_lse[2][64], lds_dv[2][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, frow = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kc = lane & 15, g = lane >> 4;
   const int nbh = a.B * a.h;
   const int bh = blockIdx.x % nbh;
   const int kb = static_cast<int>(blockIdx.x / nbh);  // early key blocks see the most queries
   const int b = bh / a.h, hh = bh % a.h;
   const int64_t S3 = 3LL * a.h * D, HD = static_cast<int64_t>(a.h) * D;
   const uint16_t* base = a.qkv + static_cast<int64_t>(b) * a.L * S3;
-  const int k0 = kb * BK, kw0 = k0 + wave * 32, kj = kw0 + frow;
+  const int k0 = kb * BK, kw0 = k0 + wave * 16, kj = kw0 + kc;
   const bool kvalid = kj < a.L;
 
-  uint4 kf[KS], vf[KS];
+  uint4 kf[KS], vf[KS];  // K^T, V^T as B operands: key kj, d = 32 st + 8 g .. +7
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
-    kf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + HD + hh * D + 16 * st + 8 * g, kvalid);
-    vf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + 2 * HD + hh * D + 16 * st + 8 * g, kvalid);
+    kf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + HD + hh * D + 32 * st + 8 * g, kvalid);
+    vf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + 2 * HD + hh * D + 32 * st + 8 * g, kvalid);
   }
   const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
   const BufRes rq = make_bufres(base + hh * D, batch_bytes - hh * D * 2);
@@ -363,11 +363,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a)
   const BufRes rdo = make_bufres(dbase + hh * D, (static_cast<int64_t>(a.L) * HD - hh * D) * 2);
   const int64_t sbase = (static_cast<int64_t>(b) * a.h + hh) * a.L;
 
-  f32x16_t dk[DT], dv[DT];
+  f32x4_t dk[DB], dv[DB];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.0f;
+  for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int q_begin = a.causal ? (k0 / 64) * 64 : 0;
   const int nqb = (a.L - q_begin + 63) / 64;
@@ -399,43 +397,36 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a)
     const int q0 = q_begin + it * 64, cur = it & 1;
     const bool more = it + 1 < nqb;
     if (more) fetch(q0 + 64);
-    if (!(a.causal && q0 + 63 < kw0)) {  // else every query of the block precedes this wave's keys
+    if (!(a.causal && q0 + 63 < kw0)) {  // else every query of the tile precedes this wave's keys
       const uint4* qt_ = lds_q[cur];
       const uint4* dot_ = lds_do[cur];
-      uint4 pb[2][2], dsb[2][2];
+      const bool edge = q0 + 63 >= a.L || (a.causal && q0 < kw0 + 15);
+      f32x4_t p[4], ds[4];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x16_t sv, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.0f;
+      for (int qb4 = 0; qb4 < 4; ++qb4) {
+        f32x4_t sv = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
-          sv = mfma_32x32x16(lds_row_frag(qt_, qt * 32 + frow, st, g), kf[st], sv);
-          dp = mfma_32x32x16(lds_row_frag(dot_, qt * 32 + frow, st, g), vf[st], dp);
+          sv = mfma_16x16x32(row_frag(qt_, 16 * qb4, st, lane), kf[st], sv);
+          dp = mfma_16x16x32(row_frag(dot_, 16 * qb4, st, lane), vf[st], dp);
         }
-        float p[16], ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = qt * 32 + mfma_row(r, lane);
-          const int q = q0 + ql;
-          const bool vis = kvalid && q < a.L && (!a.causal || kj <= q);
-          p[r] = vis ? exp2f(sv[r] * a.scale_log2 - lds_lse[cur][ql]) : 0.0f;
-          ds[r] = p[r] * (dp[r] - lds_dv[cur][ql]);
+        for (int r = 0; r < 4; ++r) {
+          const int ql = 16 * qb4 + 4 * g + r, q = q0 + ql;
+          const bool vis = kvalid && (!edge || (q < a.L && (!a.causal || kj <= q)));
+          p[qb4][r] = vis ? exp2f(fmaf(sv[r], a.scale_log2, -lds_lse[cur][ql])) : 0.0f;
+          ds[qb4][r] = p[qb4][r] * (dp[r] - lds_dv[cur][ql]);
         }
-        pb[qt][0] = pack_half(p, 0);
-        pb[qt][1] = pack_half(p, 1);
-        dsb[qt][0] = pack_half(ds, 0);
-        dsb[qt][1] = pack_half(ds, 1);
       }
+      const uint4 p0 = pack_pair(p[0], p[1]), p1 = pack_pair(p[2], p[3]);
+      const uint4 d0 = pack_pair(ds[0], ds[1]), d1 = pack_pair(ds[2], ds[3]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            dv[dt] = mfma_32x32x16(lds_tr_frag(dot_, dt, qt, s2, lane), pb[qt][s2], dv[dt]);
-            dk[dt] = mfma_32x32x16(lds_tr_frag(qt_, dt, qt, s2, lane), dsb[qt][s2], dk[dt]);
-          }
+      for (int db = 0; db < DB; ++db) {
+        dv[db] = mfma_16x16x32(tr_frag(dot_, 16 * db, 0, lane), p0, dv[db]);
+        dv[db] = mfma_16x16x32(tr_frag(dot_, 16 * db, 1, lane), p1, dv[db]);
+        dk[db] = mfma_16x16x32(tr_frag(qt_, 16 * db, 0, lane), d0, dk[db]);
+        dk[db] = mfma_16x16x32(tr_frag(qt_, 16 * db, 1, lane), d1, dk[db]);
+      }
     }
     if (more) commit(cur ^ 1);
     __syncthreads();
@@ -443,36 +434,33 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a)
   if (!kvalid) return;
   uint16_t* row = a.dqkv + (static_cast<int64_t>(b) * a.L + kj) * S3 + hh * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = dt * 32 + 8 * q4 + 4 * g;
-      uint2 vk, vv;
-      vk.x = pack_bf16x2(dk[dt][4 * q4] * a.scale, dk[dt][4 * q4 + 1] * a.scale);
-      vk.y = pack_bf16x2(dk[dt][4 * q4 + 2] * a.scale, dk[dt][4 * q4 + 3] * a.scale);
-      vv.x = pack_bf16x2(dv[dt][4 * q4], dv[dt][4 * q4 + 1]);
-      vv.y = pack_bf16x2(dv[dt][4 * q4 + 2], dv[dt][4 * q4 + 3]);
-      *reinterpret_cast<uint2*>(row + HD + d) = vk;
-      *reinterpret_cast<uint2*>(row + 2 * HD + d) = vv;
-    }
+  for (int db = 0; db < DB; ++db) {
+    uint2 vk, vv;
+    vk.x = pack_bf16x2(dk[db][0] * a.scale, dk[db][1] * a.scale);
+    vk.y = pack_bf16x2(dk[db][2] * a.scale, dk[db][3] * a.scale);
+    vv.x = pack_bf16x2(dv[db][0], dv[db][1]);
+    vv.y = pack_bf16x2(dv[db][2], dv[db][3]);
+    *reinterpret_cast<uint2*>(row + HD + 16 * db + 4 * g) = vk;
+    *reinterpret_cast<uint2*>(row + 2 * HD + 16 * db + 4 * g) = vv;
+  }
 }
 
-// Waves per block: 4 (128 queries) unless that leaves fewer than two blocks
-// per CU, then 2 (64 queries).
+// Waves per block (16 rows each): 8 (128 rows, half the tile loads per row)
+// when that still gives two blocks per CU, else 4 (64 rows).
 static int attn_waves(int B, int L, int h) {
-  const int64_t blocks4 = static_cast<int64_t>(B) * h * ceil_div(L, 128);
-  return blocks4 >= 512 ? 4 : 2;
+  const int64_t blocks8 = static_cast<int64_t>(B) * h * ceil_div(L, 128);
+  return blocks8 >= 512 ? 8 : 4;
 }
 
 template <int D, int NW>
 static void launch_fwd(AttnArgs a, hipStream_t s) {
-  a.nblk = static_cast<int>(ceil_div(a.L, 32 * NW));
+  a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
   attn_fwd_kernel<D, NW><<<static_cast<unsigned>(a.nblk * a.B * a.h), 64 * NW, 0, s>>>(a);
 }
 
 template <int D, int NW>
 static void launch_bwd(AttnArgs a, hipStream_t s) {
-  a.nblk = static_cast<int>(ceil_div(a.L, 32 * NW));
+  a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
   const unsigned grid = static_cast<unsigned>(a.nblk * a.B * a.h);
   attn_bwd_dq_kernel<D, NW><<<grid, 64 * NW, 0, s>>>(a);
   attn_bwd_dkv_kernel<D, NW><<<grid, 64 * NW, 0, s>>>(a);
@@ -527,8 +515,8 @@ extern "C" int mp_head_attention(mp_dtype dtype, int B, int L, int K, int h, int
   a.ctx = static_cast<uint16_t*>(ctx_i);
   a.lse = lse;
   const int nw = attn_waves(B, L, h);
-  if (d == 64) nw == 4 ? launch_fwd<64, 4>(a, s) : launch_fwd<64, 2>(a, s);
-  else nw == 4 ? launch_fwd<128, 4>(a, s) : launch_fwd<128, 2>(a, s);
+  if (d == 64) nw == 8 ? launch_fwd<64, 8>(a, s) : launch_fwd<64, 4>(a, s);
+  else nw == 8 ? launch_fwd<128, 8>(a, s) : launch_fwd<128, 4>(a, s);
   return check_launch(fn);
 }
 
@@ -587,8 +575,8 @@ extern "C" int mp_head_attention_bwd(mp_dtype dtype, int B, int L, int K, int h,
   if (d == 64) attn_dvec_kernel<64><<<dgrid, 256, 0, s>>>(a);
   else attn_dvec_kernel<128><<<dgrid, 256, 0, s>>>(a);
   const int nw = attn_waves(B, L, h);
-  if (d == 64) nw == 4 ? launch_bwd<64, 4>(a, s) : launch_bwd<64, 2>(a, s);
-  else nw == 4 ? launch_bwd<128, 4>(a, s) : launch_bwd<128, 2>(a, s);
+  if (d == 64) nw == 8 ? launch_bwd<64, 8>(a, s) : launch_bwd<64, 4>(a, s);
+  else nw == 8 ? launch_bwd<128, 8>(a, s) : launch_bwd<128, 4>(a, s);
   if (int rc = check_launch(fn)) return rc;
   // dX_partial[T,K] = dqkv[T,N3] * Wqkv_i[N3,K]
   if (int rc = gemm(MP_BF16, NN, T, K, N3, dqkv, N3, Wqkv_i, K, dX_partial, K, true, nullptr, MP_ACT_NONE, nullptr,

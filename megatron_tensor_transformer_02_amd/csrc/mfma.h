@@ -30,6 +30,15 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(const uint4& a, const uint4& b
                                                  0, 0, 0);
 }
 
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.  Lane l
+// gives row (l % 16) of A and column (l % 16) of B, each with 8 k-values
+// 8*(l/16) .. +7; register r of lane l receives element
+// (row 4*(l/16) + r, column l%16).
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
 // ------------------------------------------------------------ buffer loads
 // A buffer resource covers [base, base + bytes); a load at an offset outside
 // it returns zeros, which the tile loaders use for every out-of-range element.
