@@ -285,6 +285,43 @@ int mp_layernorm_bwd(mp_dtype dtype, int64_t T, int64_t K, const void* x, const 
                      void* dx, float* dgamma, float* dbeta, void* ws, size_t ws_bytes,
                      hipStream_t s);
 
+/* ------------------------------------------- reduce fused with LayerNorm */
+
+/* The all-reduce stand-in followed by the LayerNorm it feeds (MLM-notes,
+ * "Model Parallel Transformers": the all-reduce after the attention block
+ * precedes the next block's LayerNorm), in one pass per row:
+ *   out = residual + Drop(sum_{j=0..N-1} partials[j] + bias)   (as mp_shard_reduce)
+ *   y   = (out - mean) * rstd * gamma + beta                    (as mp_layernorm of out)
+ * Same arguments and rules as mp_shard_reduce plus gamma, beta [cols] dtype,
+ * eps > 0, y [rows,cols] dtype, mean, rstd [rows] fp32 (or NULL).  out and
+ * mask_out equal mp_shard_reduce's bit for bit; the LN statistics are those of
+ * the stored out (rounded to dtype), summed in a fixed order, so y matches
+ * mp_layernorm(out) to rounding.  cols <= 16*64*(16/size). */
+int mp_shard_reduce_layernorm(mp_dtype dtype, int N, int64_t rows, int64_t cols,
+                              const void* const* partials, const void* bias,
+                              const void* residual, float p, uint64_t seed, uint64_t offset,
+                              uint64_t index_base, void* out, uint8_t* mask_out,
+                              const void* gamma, const void* beta, float eps, void* y,
+                              float* mean, float* rstd, hipStream_t s);
+
+/* Workspace bytes of mp_shard_reduce_layernorm_bwd's dgamma/dbeta partials. */
+size_t mp_shard_reduce_layernorm_bwd_workspace(int64_t rows, int64_t cols);
+
+/* The backward all-reduce of the input-gradient partials fused with the
+ * LayerNorm backward it feeds (MLM-notes, "Model Parallel Transformers": one
+ * all-reduce in each block's backward):
+ *   dy = sum_{j=0..N-1} partials[j]   (rounded to dtype, never stored)
+ *   dx, dgamma, dbeta as mp_layernorm_bwd(x, gamma, mean, rstd, dy, dres).
+ * partials as in mp_shard_reduce; x [rows,cols] is the LayerNorm input, mean,
+ * rstd its saved statistics; dres [rows,cols] or NULL (may alias dx); dgamma,
+ * dbeta [cols] fp32 or NULL (then ws may be NULL).  The parameter gradients
+ * are summed in a fixed order (deterministic). */
+int mp_shard_reduce_layernorm_bwd(mp_dtype dtype, int N, int64_t rows, int64_t cols,
+                                  const void* const* partials, const void* x,
+                                  const void* gamma, const float* mean, const float* rstd,
+                                  const void* dres, void* dx, float* dgamma, float* dbeta,
+                                  void* ws, size_t ws_bytes, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -209,6 +209,14 @@ __global__ __launch_bounds__(256) void layernorm_param_final_kernel(const float*
   }
 }
 
+// dgamma[c] = sum_s partial[s, c], dbeta[c] = sum_s partial[s, K + c] in a
+// fixed order (shared with the fused reduce + LayerNorm backward).
+void layernorm_param_final(const float* partial, int64_t slabs, int64_t K, float* dgamma, float* dbeta,
+                           hipStream_t s) {
+  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(2 * K, 64)), 256, 0, s>>>(partial, slabs, K, dgamma,
+                                                                                         dbeta);
+}
+
 static void ln_slabs(int64_t T, int64_t& slab_rows, int64_t& slabs) {
   slab_rows = T / 256;
   if (slab_rows < 64) slab_rows = 64;

@@ -6,7 +6,9 @@ each reduce (the all-reduce of the pages, MLM-notes "Model Parallel
 Transformers": one all-reduce after the attention block and one after the
 MLP in the forward, two in the backward), so N ranks can be emulated on one
 GPU: run every rank's ``*_partial`` stage, then feed all partials to one
-rank's ``*_reduce`` stage, which calls ``mp_shard_reduce``.
+rank's ``*_reduce`` stage, which calls ``mp_shard_reduce`` or, where a
+LayerNorm follows the reduce, the fused ``mp_shard_reduce_layernorm`` /
+``mp_shard_reduce_layernorm_bwd``.
 
 Layer (pre-LN; the placement the GPT-2-style block uses):
 ``H1 = X + Drop(sum_i Attn_i(LN1(X)) W_o,i^T + b_o)``,
@@ -55,8 +57,8 @@ class RankLayer:
         self.mu2, self.rs2 = _empty(T, f32, dev), _empty(T, f32, dev)
         self.y, self.z = e(T, Fi), e(T, Fi)
         # backward buffers
-        self.d_mlp, self.dy, self.dh2p, self.dh2, self.dh1 = e(T, K), e(T, Fi), e(T, K), e(T, K), e(T, K)
-        self.d_attn, self.dctx, self.dhp, self.dh, self.dx = e(T, K), e(T, hd), e(T, K), e(T, K), e(T, K)
+        self.d_mlp, self.dy, self.dh2p, self.dh1 = e(T, K), e(T, Fi), e(T, K), e(T, K)
+        self.d_attn, self.dctx, self.dhp, self.dx = e(T, K), e(T, hd), e(T, K), e(T, K)
         self.g = {
             "w_qkv": _empty(shard["w_qkv"].shape, f32, dev), "b_qkv": _empty(shard["b_qkv"].shape, f32, dev),
             "w_o": _empty(shard["w_o"].shape, f32, dev), "b_o": _empty(K, f32, dev),
@@ -76,12 +78,15 @@ class RankLayer:
         return self.p_attn
 
     def attn_reduce(self, partials, x):
-        mp.mp_shard_reduce(partials, self.h1, self.c["b_o"], x, self.p, self.seed, self.off[0])
+        # The reduce and the LN2 it feeds in one pass: H1 and LN2(H1).
+        c = self.c
+        mp.mp_shard_reduce_layernorm(partials, self.h1, c["ln2_g"], c["ln2_b"], self.h2, self.mu2, self.rs2,
+                                     bias=c["b_o"], residual=x, p=self.p, seed=self.seed, offset=self.off[0],
+                                     eps=self.eps)
         return self.h1
 
     def mlp_partial(self):
-        s, c = self.s, self.c
-        mp.mp_layernorm(self.h1, c["ln2_g"], c["ln2_b"], self.h2, self.mu2, self.rs2, self.eps)
+        s = self.s
         if self.probe is not None:
             self.probe("col_begin")
         mp.mp_column_linear_gelu(self.h2, s["w_a"], s["b_a"], self.act, self.y, self.z)
@@ -104,10 +109,11 @@ class RankLayer:
         return self.dh2p
 
     def mlp_bwd_reduce(self, partials, dout):
+        # Backward all-reduce of the MLP input gradient fused with LN2's
+        # backward; the residual branch adds dOut.
         c, g = self.c, self.g
-        mp.mp_shard_reduce(partials, self.dh2)
-        mp.mp_layernorm_bwd(self.h1, c["ln2_g"], self.mu2, self.rs2, self.dh2, self.dh1, dout, g["ln2_g"],
-                            g["ln2_b"])
+        mp.mp_shard_reduce_layernorm_bwd(partials, self.h1, c["ln2_g"], self.mu2, self.rs2, self.dh1, dout,
+                                         g["ln2_g"], g["ln2_b"])
         return self.dh1
 
     def attn_bwd_partial(self):
@@ -121,8 +127,8 @@ class RankLayer:
 
     def attn_bwd_reduce(self, partials, x):
         c, g = self.c, self.g
-        mp.mp_shard_reduce(partials, self.dh)
-        mp.mp_layernorm_bwd(x, c["ln1_g"], self.mu1, self.rs1, self.dh, self.dx, self.dh1, g["ln1_g"], g["ln1_b"])
+        mp.mp_shard_reduce_layernorm_bwd(partials, x, c["ln1_g"], self.mu1, self.rs1, self.dx, self.dh1, g["ln1_g"],
+                                         g["ln1_b"])
         return self.dx
 
 

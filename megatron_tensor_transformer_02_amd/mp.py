@@ -43,6 +43,11 @@ _SIGS = {
     "mp_shard_reduce": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_f32, c_u64, c_u64, c_u64, c_p, c_p,
                                 c_p]),
     "mp_shared_seed_dropout": (c_i32, [c_i32, c_i64, c_p, c_p, c_p, c_f32, c_u64, c_u64, c_u64, c_p]),
+    "mp_shard_reduce_layernorm": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_f32, c_u64, c_u64, c_u64,
+                                          c_p, c_p, c_p, c_p, c_f32, c_p, c_p, c_p, c_p]),
+    "mp_shard_reduce_layernorm_bwd_workspace": (c_sz, [c_i64, c_i64]),
+    "mp_shard_reduce_layernorm_bwd": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                              c_p, c_p, c_sz, c_p]),
     "mp_bias_grad_workspace": (c_sz, [c_i64, c_i64]),
     "mp_bias_grad": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_p, c_sz, c_p]),
     "mp_head_attention": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_p,
@@ -194,6 +199,26 @@ def mp_shard_reduce(partials, out, bias=None, residual=None, p=0.0, seed=0, offs
     arr = _ptr_array(partials)
     _call("mp_shard_reduce", _dt(partials[0]), len(partials), rows, cols, arr, _p(bias), _p(residual), p, seed,
           offset, index_base, _p(out), _p(mask_out), _s(stream))
+
+
+def mp_shard_reduce_layernorm(partials, out, gamma, beta, y, mean=None, rstd=None, bias=None, residual=None, p=0.0,
+                              seed=0, offset=0, index_base=0, mask_out=None, eps=1e-5, stream=None):
+    rows, cols = partials[0].shape
+    arr = _ptr_array(partials)
+    _call("mp_shard_reduce_layernorm", _dt(partials[0]), len(partials), rows, cols, arr, _p(bias), _p(residual), p,
+          seed, offset, index_base, _p(out), _p(mask_out), _p(gamma), _p(beta), eps, _p(y), _p(mean), _p(rstd),
+          _s(stream))
+
+
+def mp_shard_reduce_layernorm_bwd(partials, x, gamma, mean, rstd, dx, dres=None, dgamma=None, dbeta=None, ws=None,
+                                  stream=None):
+    rows, cols = x.shape
+    arr = _ptr_array(partials)
+    need = lib().mp_shard_reduce_layernorm_bwd_workspace(rows, cols) if (dgamma is not None or dbeta is not None) \
+        else 0
+    ws = ws if ws is not None else workspace(need, x.device)
+    _call("mp_shard_reduce_layernorm_bwd", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
+          _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), _p(ws), need if ws is not None else 0, _s(stream))
 
 
 def mp_shared_seed_dropout(x, y, p, seed, offset, index_base=0, mask_out=None, stream=None):

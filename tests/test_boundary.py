@@ -52,6 +52,21 @@ def call(lib, name, *args):
     return rc, lib.mp_last_error().decode()
 
 
+def test_fused_reduce_layernorm_validation(lib):
+    arr = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED)
+    rc, msg = call(lib, "mp_shard_reduce_layernorm", mp.MP_BF16, 2, 4, 8, arr, None, None, 0.0, 0, 0, 0, ALIGNED,
+                   None, ALIGNED, ALIGNED, ctypes.c_float(0.0), ALIGNED, None, None, None)
+    assert rc == -8 and "eps" in msg
+    rc, msg = call(lib, "mp_shard_reduce_layernorm", mp.MP_BF16, 2, 4, 8 * 64 * 17, arr, None, None, 0.0, 0, 0, 0,
+                   ALIGNED, None, ALIGNED, ALIGNED, ctypes.c_float(1e-5), ALIGNED, None, None, None)
+    assert rc == -4
+    rc, msg = call(lib, "mp_shard_reduce_layernorm_bwd", mp.MP_BF16, 2, 4, 8, arr, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                   None, ALIGNED, ALIGNED, None, None, 0, None)
+    assert rc == -6 and "workspace" in msg
+    need = lib.mp_shard_reduce_layernorm_bwd_workspace(8192, 3072)
+    assert need >= 2 * 3072 * 4 and need % 256 == 0
+
+
 def test_shard_reduce_validation(lib):
     arr = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED)
     rc, msg = call(lib, "mp_shard_reduce", mp.MP_BF16, 0, 4, 8, arr, None, None, 0.0, 0, 0, 0, ALIGNED, None, None)
