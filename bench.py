@@ -7,9 +7,10 @@ resident in HBM:
 * layer -- one rank's share (3 of 24 heads of 128, FFN 12288/8) of the
   8.3B-config layer at N=8, forward + backward: LayerNorm, fused-QKV
   attention, out-projection partial, 8-way shard reduce (+bias, shared-seed
-  dropout, residual), LayerNorm, column GEMM + GeLU, row GEMM partial, 8-way
-  reduce, then the backward of all of it including the two 8-way reduces of
-  the input-gradient partials.  The other 7 ranks' partials are computed
+  dropout, residual) fused with the LayerNorm that follows, column GEMM +
+  GeLU, row GEMM partial, 8-way reduce, then the backward of all of it
+  including the two 8-way reduces of the input-gradient partials (each fused
+  with the LayerNorm backward it feeds).  The other 7 ranks' partials are computed
   once in setup by emulating those ranks (untimed);
 * vocab -- one vocab shard of N=8 (6400 of 51200 rows, K=3072, 8x1024
   tokens): embedding lookup + 8-way reduce, logits GEMM (fp32 out), per-shard
@@ -38,6 +39,39 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
+# HBM traffic of the roofline kernel, measured with rocprofv3 counters and
+# recorded (with the hash of the sources it was measured on) in this file.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "col_gemm_gelu_hbm_traffic.md")
+TRAFFIC_SOURCES = ["megatron_tensor_transformer_02_amd/csrc/gemm.hip", "megatron_tensor_transformer_02_amd/csrc/mfma.h",
+                   "megatron_tensor_transformer_02_amd/csrc/common.h"]
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != sources_sha256():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -60,6 +94,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parts", default="layer,vocab,moe")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 256 MiB device copy (the reference kernel for HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -228,7 +264,7 @@ def main():
         ach = col_fl / (col_ms * 1e-3) / 1e12
         roofs.append({"kernel": "column-parallel GEMM + GeLU (gemm_bf16_kernel, act=erf) [8192x3072]x[1536x3072]^T",
                       "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                      "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                      "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
                       "avg_launch_us": round(col_ms * 1e3, 2), "algorithmic_per_launch": col_fl})
     if "vocab" in parts:
         xs = [r["xent"][0].elapsed_time(r["xent"][1]) for r in recs]
@@ -267,6 +303,13 @@ def main():
         out["roofline"] = roofs[0]
         out["rooflines"] = roofs
 
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline and "layer" in parts:
         out["cpu_baseline"] = cpu_baseline(wl, hi, Fi)
     print(json.dumps(out), flush=True)
