@@ -7,9 +7,9 @@
 // then read with the LDS transpose read, so every layout runs the same MFMA
 // loop and no transposed copy goes through HBM or through registers.
 //
-// bf16 kernel: 256 threads = 4 waves in a 2x2 grid, one wave per SIMD; block
-// tile BM x BN x 64; each wave owns (BM/2) x (BN/2) of the output as 32x32
-// MFMA tiles (v_mfma_f32_32x32x16_bf16).  The k-loop is software-pipelined
+// bf16 kernel: 256-row tiles run 8 waves (two per SIMD), 128x128 tiles 4;
+// block tile BM x BN x 64; each wave owns a (BM/WR) x (BN/(NW/WR)) piece of
+// the output as 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16).  The k-loop is software-pipelined
 // by hand (fragment double-buffering, next k-tile prefetched into registers,
 // explicit MFMA/LDS/global-load interleave).  Workgroups are renumbered so
 // each of the 8 XCDs takes a contiguous range of output tiles, walked in
@@ -59,15 +59,18 @@ __device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles
   tn = inner / gsz;
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int ACT>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
-  // 2 x 2 waves, one per SIMD; each wave owns (BM/2) x (BN/2) of the tile.
-  constexpr int NT = 256, WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+template <int BM, int BN, int NW, int WR, bool AK, bool BKC, int EPI, int ACT>
+__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
+  // WR x (NW / WR) waves; each wave owns (BM / WR) x (BN / (NW / WR)) of the
+  // tile.  Eight waves put two on each SIMD, so one wave's MFMAs run while
+  // the other waits at the barrier or on its fragment reads.
+  constexpr int NT = 64 * NW, WC = NW / WR, WM = BM / WR, WN = BN / WC, TM = WM / 32, TN = WN / 32;
+  static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
   constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;
   __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WC, wn = wave % WC;
   int tmi, tni;
   map_tile(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, g.group_m, tmi, tni);
   const int64_t m0 = static_cast<int64_t>(tmi) * BM, n0 = static_cast<int64_t>(tni) * BN;
@@ -103,6 +106,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
       db.issue(buf + A_SLOTS, k0, t < nk);
     }
   };
+  constexpr int VPR = WN / 8;          // 8-wide vectors per epilogue strip row
+  constexpr int NV = 32 * VPR / 64;    // vectors per lane per strip
+  static_assert((32 * VPR) % 64 == 0, "strip vectors must cover the wave evenly");
   fill(lds[0], 0);
   fill(lds[1], 1);
   wait_vmcnt<NI>();
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   // loop body has no branches (past the end of K the loads write zeros and
   // go unused), so the interleave patterns below apply as written.
   constexpr int NRA = AK ? TM : 2 * TM, NRB = BKC ? TN : 2 * TN, NR = NRA + NRB;
-  constexpr int NM = TM * TN, H = TM / 2;
+  constexpr int NM = TM * TN, H = TM > 1 ? TM / 2 : 1;
   const int ar0 = wm * WM, br0 = wn * WN;
   uint4 fa[2][TM], fb[2][TN];
 #pragma unroll
@@ -163,32 +169,74 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   wait_vm_lds();  // the trailing (all-zero) loads write LDS the epilogue reuses
   __syncthreads();
 
+  // Bias: lane l holds column (l % 32) of every 32x32 accumulator tile, so
+  // the bias is added in registers before the epilogue (one value per tile
+  // column), keeping the unrolled store loop below free of it.
+  if constexpr (EPI == EPI_STORE) {
+    if (g.bias != nullptr) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + wn * WN + j * 32 + (lane & 31);
+        const float b =
+            n < g.N ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(g.bias)[n]) << 16) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += b;
+      }
+    }
+  }
+
   // Epilogue, staged through LDS one 32-row strip of the wave's tile at a
   // time: the accumulators (register r of lane l = row mfma_row(r, l),
   // column l % 32) are written to a wave-private LDS strip, then read back
   // row-major so each lane finishes 8 consecutive outputs of one row with
-  // 16-byte loads (bias, saved pre-activation) and 16/32-byte stores.
+  // 16-byte loads (saved pre-activation) and 16/32-byte stores.  The
+  // strip is private to the wave and a wave's LDS operations complete in
+  // order, so no barrier is needed between writing and reading it (the one
+  // above retires every wave's reads of the operand tiles); the loop over a
+  // lane's NV vectors is unrolled so their global loads issue together.
   constexpr int SP = WN + 4;  // padded strip row (floats)
   float* strip = reinterpret_cast<float*>(&lds[0][0]) + wave * 32 * SP;
-  constexpr int VPR = WN / 8;  // 8-wide vectors per strip row
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) strip[mfma_row(r, lane) * SP + j * 32 + (lane & 31)] = acc[i][j][r];
-    __syncthreads();
-#pragma unroll 1
-    for (int v = lane; v < 32 * VPR; v += 64) {
+    __builtin_amdgcn_wave_barrier();
+    // The saved pre-activation of the activation-gradient epilogue, likewise
+    // loaded for the whole strip before any of it is used.
+    uint4 zraw[NV];
+    if constexpr (EPI == EPI_DACT) {
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int v = lane + 64 * it;
+        const int row = v / VPR, c8 = (v - row * VPR) * 8;
+        const int64_t m = m0 + wm * WM + i * 32 + row, n = n0 + wn * WN + c8;
+        const int64_t o = (m < g.M && n < g.N) ? m * g.ldc + n : 0;
+        zraw[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.zin) + o);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int v = lane + 64 * it;
       const int row = v / VPR, c8 = (v - row * VPR) * 8;
       const int64_t m = m0 + wm * WM + i * 32 + row;
       const int64_t n = n0 + wn * WN + c8;
-      if (m >= g.M || n >= g.N) continue;
       float val[8];
       const float4 lo = *reinterpret_cast<const float4*>(strip + row * SP + c8);
       const float4 hi = *reinterpret_cast<const float4*>(strip + row * SP + c8 + 4);
       val[0] = lo.x; val[1] = lo.y; val[2] = lo.z; val[3] = lo.w;
       val[4] = hi.x; val[5] = hi.y; val[6] = hi.z; val[7] = hi.w;
+      if constexpr (EPI == EPI_DACT) {
+        float z[8];
+        unpack8(zraw[it], z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) val[e] *= act_grad_fast(z[e], ACT);
+      }
+      if (m >= g.M || n >= g.N) continue;
       if constexpr (EPI == EPI_SPLITK) {
         float* dst = g.partial + (static_cast<int64_t>(blockIdx.z) * g.M + m) * g.N + n;
         reinterpret_cast<float4*>(dst)[0] = lo;
@@ -196,18 +244,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
         continue;
       }
       const int64_t o = m * g.ldc + n;
-      if constexpr (EPI == EPI_DACT) {
-        float z[8];
-        unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.zin) + o), z);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) val[e] *= act_grad_fast(z[e], ACT);
-      } else {
-        if (g.bias != nullptr) {
-          float b[8];
-          unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.bias) + n), b);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) val[e] += b[e];
-        }
+      if constexpr (EPI == EPI_STORE) {
         if (g.zsave != nullptr) {
           if (g.out_bf16) {
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.zsave) + o) = pack8(val);
@@ -228,7 +265,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
         reinterpret_cast<float4*>(static_cast<float*>(g.C) + o)[1] = make_float4(val[4], val[5], val[6], val[7]);
       }
     }
-    __syncthreads();
   }
 }
 
@@ -354,8 +390,8 @@ struct Plan {
 static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split, Layout lay) {
   (void)lay;
   struct Cand { int bm, bn, slots; double t_step_us, t_fixed_us; };
-  const Cand cands[] = {{256, 256, 256, 1.64, 17.7}, {256, 192, 256, 1.62, 12.0}, {256, 128, 256, 1.22, 9.0},
-                        {128, 128, 512, 1.08, 6.1}};
+  const Cand cands[] = {{256, 256, 256, 1.57, 13.0}, {256, 192, 256, 1.41, 11.2}, {256, 128, 256, 1.14, 7.3},
+                        {128, 128, 512, 0.98, 8.3}};
   const int64_t kt_total = ceil_div(K > 0 ? K : 1, 64);
   if (const char* env = getenv("MP_GEMM_PLAN")) {
     int bm = 0, bn = 0, sp = 1;
@@ -388,10 +424,14 @@ static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split, Layout 
   return best;
 }
 
+// 256-row tiles run 8 waves (two per SIMD); 128x128 tiles 4 waves (two
+// workgroups per CU).
 template <int BM, int BN, bool AK, bool BKC, int EPI, int ACT>
 static void launch_bf16_tile(const GemmArgs& g, int splits, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(g.tiles_m * g.tiles_n), 1, static_cast<unsigned>(splits));
-  gemm_bf16_kernel<BM, BN, AK, BKC, EPI, ACT><<<grid, 256, 0, s>>>(g);
+  if constexpr (BM == 128) gemm_bf16_kernel<BM, BN, 4, 2, AK, BKC, EPI, ACT><<<grid, 256, 0, s>>>(g);
+  else if constexpr (BN == 256) gemm_bf16_kernel<BM, BN, 8, 2, AK, BKC, EPI, ACT><<<grid, 512, 0, s>>>(g);
+  else gemm_bf16_kernel<BM, BN, 8, 4, AK, BKC, EPI, ACT><<<grid, 512, 0, s>>>(g);
 }
 
 template <bool AK, bool BKC, int EPI, int ACT>

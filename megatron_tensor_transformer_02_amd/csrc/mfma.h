@@ -197,6 +197,7 @@ struct DmaTile {
   static_assert((R * 8) % NT == 0, "tile chunks must cover the threads");
   static_assert(KC || R % 64 == 0, "MN-contiguous tiles are whole 64-column sub-tiles");
   static constexpr int NWV = NT / 64, NI = R * 8 / NT;
+  static_assert(NWV == 4 || NWV == 8, "4 or 8 waves");
   static constexpr uint32_t kOOB = 0x80000000u;
   i32x4_t desc;
   uint32_t voff;   // per-lane byte offset of copy 0 at k = 0
@@ -220,10 +221,16 @@ struct DmaTile {
     voff = static_cast<uint32_t>((r * ld + c * 8) * 2);
   }
 
+  // Copy q covers slots (q * NWV + w) * 64 + l: K-contiguous rows
+  // q * NWV * 8 + (w * 8 + l / 8); MN-contiguous sub-tile (q * NWV) / 8 and
+  // k-rows ((q * NWV) % 8) * 8 + (w * 8 + l / 8) (NWV divides 8).
+  static constexpr int kq(int q) { return ((q * NWV) & 7) * 8; }
+  static constexpr int subq(int q) { return (q * NWV) >> 3; }
+
   // Scalar offset of copy q at k-tile start k0.
   __device__ __forceinline__ uint32_t soff(int q, int64_t k0) const {
     if constexpr (KC) return static_cast<uint32_t>((q * NWV * 8 * ld + k0) * 2);
-    else return static_cast<uint32_t>((((q & 1) * 32 + k0) * ld + (q >> 1) * 64) * 2);
+    else return static_cast<uint32_t>(((kq(q) + k0) * ld + subq(q) * 64) * 2);
   }
 
   // Fills `tile` with the k-tile starting at k0 (all 64 k-values in range),
@@ -250,7 +257,7 @@ struct DmaTile {
     for (int q = 0; q < NI; ++q) {
       bool ok;
       if constexpr (KC) ok = k0 + c * 8 < kend;
-      else ok = k0 + (q & 1) * 32 + r < kend && row0 + (q >> 1) * 64 + c * 8 < rows;
+      else ok = k0 + kq(q) + r < kend && row0 + subq(q) * 64 + c * 8 < rows;
       const uint32_t v = ok ? voff + soff(q, k0) : kOOB;
       const uint32_t m0v = lb + q * NWV * 1024;
       asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(v), "s"(desc),
