@@ -187,6 +187,10 @@ __device__ __forceinline__ void wait_vm_lds() { asm volatile("s_waitcnt vmcnt(0)
 // 8 lanes of a row still read 128 contiguous bytes).  Only the per-lane part
 // of the address lives in a VGPR: the copy and k-step parts go in the
 // instruction's scalar offset and M0, so issuing costs no vector ALU work.
+// The range check covers the sum of the vector and scalar offsets (measured
+// on gfx950: a lane whose in-range vector offset plus the scalar offset ends
+// past the resource receives zeros), so a copy or k-step moved past the end
+// by the scalar offset alone is fetched as zeros without touching memory.
 // Rows past the end of a K-contiguous operand lie outside the resource and
 // arrive as zeros; columns past the end of an MN-contiguous operand read
 // neighbouring values that only reach discarded outputs.  A k-tile that

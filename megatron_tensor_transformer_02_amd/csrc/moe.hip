@@ -115,16 +115,71 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const MoeArgs a) {
   }
 }
 
+// Direct global -> LDS loader for a 256-row x 64-k operand tile whose rows
+// are gathered: the byte offset of every row this lane fetches (one per copy)
+// is computed once per tile, so a row may come from anywhere in the operand
+// (a token of X picked by the routing, or a gate/up row of W_gu).  The slot
+// layout is that of DmaTile: copy q of wave w fills slots (q*NWV + w)*64 + l
+// with tile row q*NWV*8 + w*8 + l/8, chunk (l%8) ^ swz(row).  An absent row,
+// a dead copy and a chunk past the k-range get an offset beyond the resource
+// in the per-lane (vector) offset, so they are fetched as zeros without
+// touching memory; every live address lies inside the operand.
+template <int R, int NT>
+struct GatherDma {
+  static constexpr int NWV = NT / 64, NI = R * 8 / NT;
+  static_assert(NWV == 8 && (R * 8) % NT == 0, "8 waves, whole copies");
+  static constexpr uint32_t kOOB = 0x80000000u;
+  i32x4_t desc;
+  uint32_t voff[NI];
+  int wave, kc;  // kc: first k-value of this lane's chunk
+
+  // row_off(r) returns the element offset of tile row r from `base`, or -1
+  // for a row that must read as zeros.
+  template <typename F>
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t elems, int tid, F row_off) {
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    desc = make_desc(base, elems * 2);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int r = q * NWV * 8 + wave * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ lds_swz(r);
+      kc = c * 8;
+      const int64_t o = row_off(r);
+      voff[q] = o < 0 ? kOOB : static_cast<uint32_t>((o + c * 8) * 2);
+    }
+  }
+
+  // Fills `tile` with k-values [k0, k0+64); `live` false fills zeros, and
+  // chunks at k >= kend read as zeros (kend % 8 == 0).
+  __device__ __forceinline__ void issue(uint4* tile, int64_t k0, int64_t kend, bool live) const {
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(tile)) + wave * 1024;
+    const bool ok = live && k0 + kc < kend;
+    const uint32_t so = live ? static_cast<uint32_t>(k0 * 2) : 0u;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const uint32_t v = ok ? voff[q] : kOOB;
+      const uint32_t m0v = lb + q * NWV * 1024;
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(v), "s"(desc),
+                   "s"(m0v), "s"(so)
+                   : "memory", "m0");
+    }
+  }
+};
+
 // Grouped GEMM.  MODE 0: act[rows of e, :] = SwiGLU(X[tokens] W_gu[e]^T);
-// MODE 1: yperm[rows of e, :] = act[rows of e] W_d[e]^T.  256x256x64 tiles,
-// 4 waves in a 2x2 grid, LDS double buffering as in the dense GEMM.
+// MODE 1: yperm[rows of e, :] = act[rows of e] W_d[e]^T.  256x256x64 tiles on
+// 8 waves in a 2x4 grid (two per SIMD), each wave owning 128x64 of the tile;
+// the same software pipeline as the dense GEMM: both operands stream into two
+// LDS buffers by direct loads issued two k-tiles ahead, fragments are
+// double-buffered in registers, and the barrier sits inside the last k-step.
 template <int MODE>
-__global__ __launch_bounds__(256) void moe_gemm_kernel(const MoeArgs a) {
-  constexpr int BM = MOE_BM, BN = MOE_BN, WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-  constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8, NR = BM * 8 / 256;
+__global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
+  constexpr int BM = MOE_BM, BN = MOE_BN, NT = 512, WC = 4, WM = BM / 2, WN = BN / WC;
+  constexpr int TM = WM / 32, TN = WN / 32, A_SLOTS = BM * 8, B_SLOTS = BN * 8;
+  static_assert(TN == 2, "the SwiGLU epilogue pairs the gate and up 32-column tiles of a wave");
   __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int frow = lane & 31, fgrp = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / WC, wn = wave % WC;
 
   // Device-side schedule: real tiles = tile_start[E_loc] * tiles_n.
   const int n_real = a.tile_start[a.E_loc] * a.tiles_n;
@@ -139,50 +194,34 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const MoeArgs a) {
   const int64_t row_end = a.offsets[e + 1];
   const int64_t K = MODE == 0 ? a.Hd : a.Fe;
 
-  // Per-thread row offsets (elements) of the A and B rows this thread loads.
-  int64_t aoff[NR], boff[NR];
-  bool aok[NR], bok[NR];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int r = (tid + 256 * i) >> 3;
-    const int64_t grow = row0 + r;
-    aok[i] = grow < row_end;
-    if constexpr (MODE == 0) {
-      aoff[i] = aok[i] ? static_cast<int64_t>(a.perm[grow] / a.topk) * a.Hd : 0;
-      // Wave column block wn holds WN/2 gate rows then the WN/2 up rows of the
-      // same output columns.
+  GatherDma<BM, NT> da;
+  GatherDma<BN, NT> db;
+  if constexpr (MODE == 0) {
+    da.init(a.X, a.T * a.Hd, tid, [&](int r) -> int64_t {
+      const int64_t grow = row0 + r;
+      return grow < row_end ? static_cast<int64_t>(a.perm[grow] / a.topk) * a.Hd : -1;
+    });
+    // Wave column block c holds WN/2 gate rows, then the WN/2 up rows of the
+    // same output columns.
+    db.init(a.W_gu + static_cast<int64_t>(e) * 2 * a.Fe * a.Hd, 2 * a.Fe * a.Hd, tid, [&](int r) -> int64_t {
       const int wcol = r / WN, within = r % WN;
       const int64_t j = static_cast<int64_t>(nt) * (BN / 2) + wcol * (WN / 2) + (within % (WN / 2));
-      bok[i] = j < a.Fe;
-      boff[i] = ((within < WN / 2) ? j : a.Fe + j) * a.Hd;
-    } else {
-      aoff[i] = grow * a.Fe;
-      const int64_t n = static_cast<int64_t>(nt) * BN + r;
-      bok[i] = n < a.Hd;
-      boff[i] = n * a.Fe;
-    }
+      if (j >= a.Fe) return -1;
+      return ((within < WN / 2) ? j : a.Fe + j) * a.Hd;
+    });
+  } else {
+    da.init(a.act + row0 * a.Fe, (row_end - row0) * a.Fe, tid,
+            [&](int r) -> int64_t { return row0 + r < row_end ? static_cast<int64_t>(r) * a.Fe : -1; });
+    const int64_t n0 = static_cast<int64_t>(nt) * BN;
+    db.init(a.W_d + static_cast<int64_t>(e) * a.Hd * a.Fe + n0 * a.Fe, (a.Hd - n0) * a.Fe, tid,
+            [&](int r) -> int64_t { return n0 + r < a.Hd ? static_cast<int64_t>(r) * a.Fe : -1; });
   }
-  const BufRes ra = MODE == 0 ? make_bufres(a.X, a.T * a.Hd * 2) : make_bufres(a.act, a.r_cap * a.Fe * 2);
-  const BufRes rb = MODE == 0 ? make_bufres(a.W_gu + static_cast<int64_t>(e) * 2 * a.Fe * a.Hd, 2 * a.Fe * a.Hd * 2)
-                              : make_bufres(a.W_d + static_cast<int64_t>(e) * a.Hd * a.Fe, a.Hd * a.Fe * 2);
-
-  uint4 ra_reg[NR], rb_reg[NR];
-  auto load = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int64_t gk = k0 + ((tid + 256 * i) & 7) * 8;
-      const bool kin = gk < K;
-      ra_reg[i] = buf_load16(ra, (aok[i] && kin) ? static_cast<uint32_t>((aoff[i] + gk) * 2) : kBufOOB);
-      rb_reg[i] = buf_load16(rb, (bok[i] && kin) ? static_cast<uint32_t>((boff[i] + gk) * 2) : kBufOOB);
-    }
-  };
-  auto store = [&](uint4* tile) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int id2 = tid + 256 * i;
-      tile[lds_slot(id2 >> 3, id2 & 7)] = ra_reg[i];
-      tile[A_SLOTS + lds_slot(id2 >> 3, id2 & 7)] = rb_reg[i];
-    }
+  constexpr int NI = GatherDma<BM, NT>::NI + GatherDma<BN, NT>::NI;
+  const int nk = static_cast<int>((K + 63) / 64);
+  auto fill = [&](uint4* buf, int t) {
+    const int64_t k0 = 64 * static_cast<int64_t>(t);
+    da.issue(buf, k0, K, t < nk);
+    db.issue(buf + A_SLOTS, k0, K, t < nk);
   };
 
   f32x16_t acc[TM][TN];
@@ -193,60 +232,92 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const MoeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = static_cast<int>((K + 63) / 64);
-  load(0);
-  store(lds[0]);
+  fill(lds[0], 0);
+  fill(lds[1], 1);
+  wait_vmcnt<NI>();
   __syncthreads();
+
+  constexpr int NR = TM + TN, NM = TM * TN, H = TM / 2;
+  const int ar0 = wm * WM, br0 = wn * WN;
+  uint4 fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[0][i] = lds_frag<true>(lds[0], ar0 + 32 * i, 0, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb[0][j] = lds_frag<true>(lds[0] + A_SLOTS, br0 + 32 * j, 0, lane);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load(static_cast<int64_t>(kt + 1) * 64);
-    const uint4* ta = lds[cur];
-    const uint4* tb = lds[cur] + A_SLOTS;
+    uint4* cur = lds[kt & 1];
+    const uint4* ta = cur;
+    const uint4* tb = cur + A_SLOTS;
+    const uint4* na = lds[(kt & 1) ^ 1];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = 2 * ks + fgrp;
-      uint4 af[TM], bfr[TN];
+    for (int ks = 0; ks < 3; ++ks) {
+      const int c = ks & 1, n = c ^ 1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = ta[lds_slot(wm * WM + i * 32 + frow, ch)];
+      for (int i = 0; i < TM; ++i) fa[n][i] = lds_frag<true>(ta, ar0 + 32 * i, ks + 1, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = tb[lds_slot(wn * WN + j * 32 + frow, ch)];
+      for (int j = 0; j < TN; ++j) fb[n][j] = lds_frag<true>(tb, br0 + 32 * j, ks + 1, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[c][i], fb[c][j], acc[i][j]);
+      sched_mfma_interleave<0, NM, 0x100, NR, 0>();
     }
-    if (more) store(lds[cur ^ 1]);
+#pragma unroll
+    for (int i = 0; i < H; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[1][i], fb[1][j], acc[i][j]);
+    wait_vm_lds();  // k-tile kt+1 has landed (this wave's share); reads of kt retired
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = lds_frag<true>(na, ar0 + 32 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = lds_frag<true>(na + A_SLOTS, br0 + 32 * j, 0, lane);
+    fill(cur, kt + 2);
+#pragma unroll
+    for (int i = H; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[1][i], fb[1][j], acc[i][j]);
   }
+  wait_vm_lds();  // the trailing (all-zero) loads write LDS the epilogue reuses
+  __syncthreads();
 
-  // LDS-staged epilogue (see the dense GEMM): one 32-row strip at a time.
-  constexpr int SP = WN + 4;
+  // Epilogue through a wave-private LDS strip, one 32-row strip at a time (as
+  // in the dense GEMM; no barrier needed).  MODE 0: lane l holds the gate and
+  // the up value of the same output column (l % 32) in its two accumulator
+  // tiles, so SwiGLU is applied in registers and the strip is 32 columns wide.
+  constexpr int SC = MODE == 0 ? WN / 2 : WN;  // strip columns
+  constexpr int SP = SC + 4;                   // padded strip row (floats)
+  constexpr int VPR = SC / 8, NV = 32 * VPR / 64;
+  static_assert((32 * VPR) % 64 == 0, "strip vectors must cover the wave evenly");
   float* strip = reinterpret_cast<float*>(&lds[0][0]) + wave * 32 * SP;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int r = 0; r < 16; ++r) {
+      const int srow = mfma_row(r, lane) * SP + (lane & 31);
+      if constexpr (MODE == 0) {
+        const float g = acc[i][0][r];
+        strip[srow] = g / (1.0f + expf(-g)) * acc[i][1][r];
+      } else {
+        strip[srow] = acc[i][0][r];
+        strip[srow + 32] = acc[i][1][r];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) strip[mfma_row(r, lane) * SP + j * 32 + frow] = acc[i][j][r];
-    __syncthreads();
-    constexpr int VPR = MODE == 0 ? WN / 16 : WN / 8;  // output vectors of 8 per strip row
-#pragma unroll 1
-    for (int v = lane; v < 32 * VPR; v += 64) {
+    for (int it = 0; it < NV; ++it) {
+      const int v = lane + 64 * it;
       const int row = v / VPR, c8 = (v - row * VPR) * 8;
       const int64_t grow = row0 + wm * WM + i * 32 + row;
+      const float4 lo = *reinterpret_cast<const float4*>(strip + row * SP + c8);
+      const float4 hi = *reinterpret_cast<const float4*>(strip + row * SP + c8 + 4);
+      const float val[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       if (grow >= row_end) continue;
-      const float4 g0 = *reinterpret_cast<const float4*>(strip + row * SP + c8);
-      const float4 g1 = *reinterpret_cast<const float4*>(strip + row * SP + c8 + 4);
-      float val[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       if constexpr (MODE == 0) {
         const int64_t jcol = static_cast<int64_t>(nt) * (BN / 2) + wn * (WN / 2) + c8;
         if (jcol >= a.Fe) continue;
-        const float4 u0 = *reinterpret_cast<const float4*>(strip + row * SP + WN / 2 + c8);
-        const float4 u1 = *reinterpret_cast<const float4*>(strip + row * SP + WN / 2 + c8 + 4);
-        const float up[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) val[q] = val[q] / (1.0f + expf(-val[q])) * up[q];
         *reinterpret_cast<uint4*>(a.act + grow * a.Fe + jcol) = pack8(val);
       } else {
         const int64_t n = static_cast<int64_t>(nt) * BN + wn * WN + c8;
@@ -254,7 +325,6 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const MoeArgs a) {
         *reinterpret_cast<uint4*>(a.yperm + grow * a.Hd + n) = pack8(val);
       }
     }
-    __syncthreads();
   }
 }
 
@@ -364,9 +434,9 @@ extern "C" int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int top
   moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
   const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc;
   a.tiles_n = static_cast<int>(ceil_div(Fe, MOE_BN / 2));
-  moe_gemm_kernel<0><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 256, 0, s>>>(a);
+  moe_gemm_kernel<0><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
-  moe_gemm_kernel<1><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 256, 0, s>>>(a);
+  moe_gemm_kernel<1><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a);
   return check_launch(fn);
 }

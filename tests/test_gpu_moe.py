@@ -38,6 +38,8 @@ def run(x, ids, w, wgu, wd, e_start):
     (77, 128, 64, 8, 1, 5, 2),      # a single local expert
     (40, 64, 64, 16, 16, 0, 3),     # every expert local
     (33, 64, 64, 16, 4, 12, 1),     # top-1
+    (700, 200, 264, 4, 2, 1, 2),    # >256 rows per expert, ragged k-tiles in both GEMMs
+    (513, 72, 520, 8, 3, 2, 4),     # K = 72 (one full and one 8-wide k-tile), 5 act tiles
 ])
 def test_grouped_expert_gemm(T, Hd, Fe, experts, e_local, e_start, topk):
     say("moe", T, Hd, Fe, experts, e_local, e_start, topk)
