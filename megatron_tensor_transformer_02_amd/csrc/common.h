@@ -80,11 +80,33 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 }
 
 // Loads/stores of one 16-byte vector as floats: 8 bf16 or 4 fp32.
+// Streaming (non-temporal) 16-byte loads/stores for data read or written
+// once, such as the shard partials of a reduce: they do not displace what the
+// next kernel reads (its GEMM operands) from the last-level cache.
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void store_stream16(void* p, const uint4& v) {
+  const nt_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x4*>(p));
+}
+
 template <bool BF16>
 struct Vec16 {
   static constexpr int N = BF16 ? 8 : 4;
   __device__ __forceinline__ static void load(const void* base, int64_t elem, float* f) {
-    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem * (BF16 ? 2 : 4));
+    unpack(*reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem * (BF16 ? 2 : 4)), f);
+  }
+  // As load(), for data read exactly once (streaming).
+  __device__ __forceinline__ static void load_stream(const void* base, int64_t elem, float* f) {
+    unpack(load_stream16(static_cast<const char*>(base) + elem * (BF16 ? 2 : 4)), f);
+  }
+  __device__ __forceinline__ static void unpack(const uint4& v, float* f) {
     if constexpr (BF16) {
       unpack8(v, f);
     } else {
@@ -173,9 +195,6 @@ __device__ __forceinline__ void apply_dropout(const DropoutParams& d, uint64_t j
   }
 }
 
-// Streaming (non-temporal) 16-byte fp32 loads/stores for data read or written
-// once.
-typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 load_nt4(const float* p) {
   const nt_f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));

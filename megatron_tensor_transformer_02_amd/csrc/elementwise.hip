@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void shard_reduce_kernel(PtrArray parts, int n
   float part[NMAX][E];
 #pragma unroll
   for (int j = 0; j < NMAX; ++j)
-    if (j < n_parts) V::load(parts.p[j], e0, part[j]);
+    if (j < n_parts) V::load_stream(parts.p[j], e0, part[j]);
   float acc[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) acc[i] = part[0][i];

@@ -36,6 +36,12 @@ template <bool BF16>
 __device__ __forceinline__ uint4 ld_raw(const void* base, int64_t elem) {
   return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem * (BF16 ? 2 : 4));
 }
+// Shard partials are read exactly once: streaming loads keep them from
+// displacing the operands of the GEMM that runs next.
+template <bool BF16>
+__device__ __forceinline__ uint4 ld_part(const void* base, int64_t elem) {
+  return load_stream16(static_cast<const char*>(base) + elem * (BF16 ? 2 : 4));
+}
 template <bool BF16>
 __device__ __forceinline__ void raw_to_f(const uint4& v, float* f) {
   if constexpr (BF16) {
@@ -60,7 +66,7 @@ __device__ __forceinline__ void load_row(RowIn<NMAX>& in, const PartPtrs& parts,
                                          const void* b) {
 #pragma unroll
   for (int j = 0; j < NMAX; ++j)
-    if (j < n) in.p[j] = ld_raw<BF16>(parts.p[j], e0);
+    if (j < n) in.p[j] = ld_part<BF16>(parts.p[j], e0);
   if (a != nullptr) in.a = ld_raw<BF16>(a, e0);
   if (b != nullptr) in.b = ld_raw<BF16>(b, e0);
 }

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
         const int row = v / VPR, c8 = (v - row * VPR) * 8;
         const int64_t m = m0 + wm * WM + i * 32 + row, n = n0 + wn * WN + c8;
         const int64_t o = (m < g.M && n < g.N) ? m * g.ldc + n : 0;
-        zraw[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g.zin) + o);
+        zraw[it] = load_stream16(static_cast<const uint16_t*>(g.zin) + o);
       }
     }
 #pragma unroll
@@ -246,8 +246,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
       const int64_t o = m * g.ldc + n;
       if constexpr (EPI == EPI_STORE) {
         if (g.zsave != nullptr) {
+          // The pre-activation is read back only by the backward pass.
           if (g.out_bf16) {
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.zsave) + o) = pack8(val);
+            store_stream16(static_cast<uint16_t*>(g.zsave) + o, pack8(val));
           } else {
             reinterpret_cast<float4*>(static_cast<float*>(g.zsave) + o)[0] = make_float4(val[0], val[1], val[2], val[3]);
             reinterpret_cast<float4*>(static_cast<float*>(g.zsave) + o)[1] = make_float4(val[4], val[5], val[6], val[7]);
@@ -275,9 +276,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t nq = N >> 2;
   if (q >= M * nq) return;
   const int64_t m = q / nq, n = (q - m * nq) * 4;
-  float4 s = reinterpret_cast<const float4*>(partial + m * N + n)[0];
+  float4 s = load_nt4(partial + m * N + n);
   for (int z = 1; z < splits; ++z) {
-    const float4 v = reinterpret_cast<const float4*>(partial + (static_cast<int64_t>(z) * M + m) * N + n)[0];
+    const float4 v = load_nt4(partial + (static_cast<int64_t>(z) * M + m) * N + n);
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
   if (out_bf16) {
@@ -396,7 +397,7 @@ static Plan plan_bf16(int64_t M, int64_t N, int64_t K, bool allow_split, Layout 
   if (const char* env = getenv("MP_GEMM_PLAN")) {
     int bm = 0, bn = 0, sp = 1;
     if (sscanf(env, "%d,%d,%d", &bm, &bn, &sp) == 3 && sp >= 1 && (allow_split || sp == 1) &&
-        ((bm == 256 && (bn == 256 || bn == 192 || bn == 128)) || (bm == 128 && bn == 128))) {
+        ((bm == 256 && (bn == 256 || bn == 192 || bn == 128)) || (bm == 128 && (bn == 128 || bn == 192)))) {
       const int64_t kt = ceil_div(kt_total, sp);
       return Plan{bm, bn, static_cast<int>(ceil_div(kt_total, kt)), kt * 64};
     }
@@ -439,6 +440,7 @@ static void launch_bf16_layout(const GemmArgs& g, const Plan& p, hipStream_t s) 
   if (p.bm == 256 && p.bn == 256) launch_bf16_tile<256, 256, AK, BKC, EPI, ACT>(g, p.splits, s);
   else if (p.bm == 256 && p.bn == 192) launch_bf16_tile<256, 192, AK, BKC, EPI, ACT>(g, p.splits, s);
   else if (p.bm == 256 && p.bn == 128) launch_bf16_tile<256, 128, AK, BKC, EPI, ACT>(g, p.splits, s);
+  else if (p.bn == 192) launch_bf16_tile<128, 192, AK, BKC, EPI, ACT>(g, p.splits, s);
   else launch_bf16_tile<128, 128, AK, BKC, EPI, ACT>(g, p.splits, s);
 }
 
