@@ -59,6 +59,12 @@ __device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles
   tn = inner / gsz;
 }
 
+// Distance, in k-tiles beyond the direct loads, of the grid-wide warm-up of
+// the operands into the last-level cache (0 turns it off).
+#ifndef MP_GEMM_WARM
+#define MP_GEMM_WARM 2
+#endif
+
 template <int BM, int BN, int NW, int WR, bool AK, bool BKC, int EPI, int ACT>
 __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
   // WR x (NW / WR) waves; each wave owns (BM / WR) x (BN / (NW / WR)) of the
@@ -68,6 +74,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
   static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
   constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;
   __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
+  __shared__ uint32_t warm_sink[64];
+  constexpr int WD = MP_GEMM_WARM;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WC, wn = wave % WC;
@@ -109,9 +117,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
   constexpr int VPR = WN / 8;          // 8-wide vectors per epilogue strip row
   constexpr int NV = 32 * VPR / 64;    // vectors per lane per strip
   static_assert((32 * VPR) % 64 == 0, "strip vectors must cover the wave evenly");
+  // Each wave warms its share of k-tile t + WD while the direct loads of
+  // k-tile t are in flight.  The prologue warms k-tiles 2 .. 1+WD, ordered so
+  // that exactly one warm-up load follows the last direct load, as in every
+  // iteration below (whose waits leave that one in flight).
+  GridWarm gw;
+  if constexpr (WD > 0)
+    gw.init(A, g.lda, g.M, g.K, AK, B, g.ldb, g.N, BKC,
+            static_cast<int>(blockIdx.x) * NW + __builtin_amdgcn_readfirstlane(wave), static_cast<int>(gridDim.x) * NW,
+            lane);
+  auto warm = [&](int t) { gw.issue(warm_sink, kbeg + 64 * static_cast<int64_t>(t), t < nk); };
+  constexpr int NWU = WD > 0 ? 1 : 0;
+  if constexpr (WD > 1) {
+#pragma unroll
+    for (int t = 2; t < 1 + WD; ++t) warm(t);
+  }
   fill(lds[0], 0);
   fill(lds[1], 1);
-  wait_vmcnt<NI>();
+  if constexpr (WD > 0) warm(1 + WD);
+  wait_vmcnt<NI + NWU>();
   __syncthreads();
 
   // Software pipeline.  k-tiles stream through two LDS buffers by direct
@@ -154,13 +178,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
     for (int i = 0; i < H; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[1][i], fb[1][j], acc[i][j]);
-    wait_vm_lds();  // k-tile kt+1 has landed (this wave's share); reads of kt retired
+    wait_vm_lds_n<NWU>();  // k-tile kt+1 has landed (this wave's share); reads of kt retired
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[0][i] = lds_frag<AK>(na, ar0 + 32 * i, 0, lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[0][j] = lds_frag<BKC>(na + A_SLOTS, br0 + 32 * j, 0, lane);
     fill(cur, kt + 2);
+    if constexpr (WD > 0) warm(kt + 2 + WD);
 #pragma unroll
     for (int i = H; i < TM; ++i)
 #pragma unroll

@@ -271,6 +271,67 @@ struct DmaTile {
   }
 };
 
+// As wait_vm_lds(), leaving the N most recent vector-memory loads in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// Grid-wide warm-up of a future k-tile: the 128-byte lines that k-tile
+// covers in both operands (all rows, not just this workgroup's) are split
+// over every wave of the grid, each wave requesting its few lines with one
+// 4-byte direct load into a dummy LDS word.  Each line is thus requested once
+// for the whole grid, so by the time the workgroups' own loads reach it the
+// line sits in the last-level cache instead of HBM.  The waves of the first
+// operand's share of the grid request its lines, the others the second's.
+// A K-contiguous operand has one line per row and k-tile (row r, k0..k0+63);
+// an MN-contiguous one ceil(cols/64) lines per k-row.  Lanes without a line,
+// and k-tiles past the end, request nothing.
+struct GridWarm {
+  i32x4_t desc;
+  uint32_t voff;     // per-lane byte offset at k = 0, or out of range
+  uint32_t kstride;  // bytes per k-value (2, or 2*ld for an MN-contiguous operand)
+
+  // lines_a / lines_b: lines of one k-tile of each operand; slot = this wave's
+  // index in the grid, nslots = waves in the grid.
+  __device__ __forceinline__ void init(const uint16_t* a, int64_t lda, int64_t rows_a, int64_t kdim, bool a_kc,
+                                       const uint16_t* b, int64_t ldb, int64_t rows_b, bool b_kc, int slot,
+                                       int nslots, int lane) {
+    const int64_t la = a_kc ? rows_a : 64 * ((rows_a + 63) / 64);
+    const int64_t lb = b_kc ? rows_b : 64 * ((rows_b + 63) / 64);
+    // Waves [0, sa) warm A, the rest B, in proportion to their line counts.
+    int64_t sa = (nslots * la + (la + lb) / 2) / (la + lb);
+    sa = sa < 1 ? 1 : (sa > nslots - 1 ? nslots - 1 : sa);
+    const bool is_a = slot < sa;
+    const int64_t ns = is_a ? sa : nslots - sa;
+    const int64_t line = (is_a ? slot : slot - sa) + static_cast<int64_t>(lane) * ns;
+    const uint16_t* base = is_a ? a : b;
+    const int64_t ld = is_a ? lda : ldb, rows = is_a ? rows_a : rows_b, nl = is_a ? la : lb;
+    const bool kc = is_a ? a_kc : b_kc;
+    desc = make_desc(base, kc ? rows * ld * 2 : kdim * ld * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) desc[i] = __builtin_amdgcn_readfirstlane(desc[i]);  // uniform per wave
+    if (line >= nl) {
+      voff = 0x80000000u;
+    } else if (kc) {
+      voff = static_cast<uint32_t>(line * ld * 2);
+    } else {
+      const int64_t cpr = (rows + 63) / 64;
+      voff = static_cast<uint32_t>(((line / cpr) * ld + (line % cpr) * 64) * 2);
+    }
+    kstride = kc ? 2u : static_cast<uint32_t>(ld * 2);
+  }
+
+  __device__ __forceinline__ void issue(const void* sink, int64_t k0, bool live) const {
+    const uint32_t so = live ? static_cast<uint32_t>(k0) * kstride : 0x80000000u;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(sink));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %3 offen lds" ::"v"(voff), "s"(desc),
+                 "s"(m0v), "s"(so)
+                 : "memory", "m0");
+  }
+};
+
 // MFMA operand fragment of k-step ks (16 k-values) for operand rows
 // r0 .. r0+31 (r0 % 32 == 0) of a tile stored by TileLoader: lane l gets row
 // r0 + l%32, k-values 16*ks + 8*(l/32) .. +7.  An MN-contiguous tile is read
