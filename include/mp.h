@@ -132,6 +132,20 @@ int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K,
                               const void* Y_i, const void* B_i, const void* dOut, void* dY_i,
                               float* dB_i, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* mp_row_linear_partial_bwd for the second GEMM of the MLP block, whose input
+ * Y_i = act(Z_save) came from mp_column_linear_gelu (MLM-notes, "Model
+ * Parallel Transformers": the GeLU sits between the column- and the
+ * row-parallel GEMM of one rank).  The input gradient leaves the GEMM already
+ * passed through the activation gradient:
+ *   dZ_i = (dOut * B_i) .* act'(Z_save)   [T,Fi] (dtype, one rounding)
+ * so mp_column_linear_gelu_bwd then runs with act = MP_ACT_NONE on dZ_i.
+ * dB_i, workspace (mp_row_linear_partial_bwd_workspace) and errors as
+ * mp_row_linear_partial_bwd; act must be a GeLU and Z_save [T,Fi] non-NULL. */
+int mp_row_linear_partial_bwd_dact(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K,
+                                   const void* Y_i, const void* B_i, const void* dOut,
+                                   const void* Z_save, int act, void* dZ_i, float* dB_i,
+                                   void* ws, size_t ws_bytes, hipStream_t s);
+
 /* ------------------------------------------------------ reduce and dropout */
 
 /* Local N-way shard reduce standing in for the all-reduce after each
@@ -141,8 +155,9 @@ int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K,
  *   out = residual + Drop(sum_{j=0..N-1} partials[j] + bias)
  * partials: host array of N device pointers, each [rows,cols] in dtype,
  * summed in fp32 in order j = 0..N-1.  bias [cols] or NULL, residual
- * [rows,cols] or NULL, out [rows,cols] (may alias residual), mask_out
- * [rows*cols] uint8 (1 = kept) or NULL.  Dropout as mp_shared_seed_dropout with
+ * [rows,cols] or NULL, out [rows,cols] (may alias residual), mask_out: the
+ * keep flags as bits (format as in mp_shared_seed_dropout) or NULL; for the
+ * backward, see mp_dropout_mask_bwd.  Dropout as mp_shared_seed_dropout with
  * element (r,c) at flat index index_base + r*cols + c.  1 <= N <= MP_MAX_SHARDS;
  * 0 <= p < 1 (p = 0: no dropout). */
 int mp_shard_reduce(mp_dtype dtype, int N, int64_t rows, int64_t cols,
@@ -157,10 +172,28 @@ int mp_shard_reduce(mp_dtype dtype, int N, int64_t rows, int64_t cols,
  * float32 p; kept values are scaled by 1/(1-p), the rest set to 0.  The mask
  * depends on (seed, offset, j) only, never on the rank, so every shard draws
  * it identically; applied to an upstream gradient with the same arguments it
- * is the backward.  x, y [n] in dtype (y may alias x), mask_out [n] or NULL. */
+ * is the backward.  x, y [n] in dtype (y may alias x).  mask_out: NULL, or
+ * ceil(n/8) bytes receiving the keep flags as bits, bit (i & 7) of byte i >> 3
+ * for x[i] (1 = kept), so a backward can apply the mask without drawing it
+ * again (mp_dropout_mask_bwd). */
 int mp_shared_seed_dropout(mp_dtype dtype, int64_t n, const void* x, void* y,
                            uint8_t* mask_out, float p, uint64_t seed, uint64_t offset,
                            uint64_t index_base, hipStream_t s);
+
+/* Backward of a dropout whose forward saved its keep flags as bits (mask_out
+ * of mp_shared_seed_dropout, mp_shard_reduce or mp_shard_reduce_layernorm;
+ * MLM-review, "key terms": the mask is the one all ranks drew from the shared
+ * seed, and its backward reuses it):
+ *   dx = dy .* keep / (1 - p)        [rows,cols] dtype (dx may alias dy)
+ *   dbias = column sums of dx        [cols] fp32 or NULL: the gradient of the
+ *                                    bias added before the dropout.
+ * keep_bits: ceil(rows*cols/8) bytes, element (r,c) at bit index r*cols + c.
+ * ws: mp_dropout_mask_bwd_workspace bytes when dbias is non-NULL.  The column
+ * sums are of dx as stored, in a fixed order (deterministic). */
+size_t mp_dropout_mask_bwd_workspace(int64_t rows, int64_t cols);
+int mp_dropout_mask_bwd(mp_dtype dtype, int64_t rows, int64_t cols, const void* dy,
+                        const uint8_t* keep_bits, float p, void* dx, float* dbias, void* ws,
+                        size_t ws_bytes, hipStream_t s);
 
 /* Column sums of dy [rows,cols] (dtype) into db [cols] fp32: the gradient of
  * a bias added to every row (deterministic, fixed summation order). */
@@ -296,7 +329,8 @@ int mp_layernorm_bwd(mp_dtype dtype, int64_t T, int64_t K, const void* x, const 
  * eps > 0, y [rows,cols] dtype, mean, rstd [rows] fp32 (or NULL).  out and
  * mask_out equal mp_shard_reduce's bit for bit; the LN statistics are those of
  * the stored out (rounded to dtype), summed in a fixed order, so y matches
- * mp_layernorm(out) to rounding.  cols <= 16*64*(16/size). */
+ * mp_layernorm(out) to rounding.  cols <= 16*64*(16/size); with mask_out,
+ * cols % 8 == 0. */
 int mp_shard_reduce_layernorm(mp_dtype dtype, int N, int64_t rows, int64_t cols,
                               const void* const* partials, const void* bias,
                               const void* residual, float p, uint64_t seed, uint64_t offset,
@@ -304,7 +338,8 @@ int mp_shard_reduce_layernorm(mp_dtype dtype, int N, int64_t rows, int64_t cols,
                               const void* gamma, const void* beta, float eps, void* y,
                               float* mean, float* rstd, hipStream_t s);
 
-/* Workspace bytes of mp_shard_reduce_layernorm_bwd's dgamma/dbeta partials. */
+/* Workspace bytes of the dgamma/dbeta (and dbias) partials of
+ * mp_shard_reduce_layernorm_bwd and mp_shard_reduce_layernorm_bwd_dropout. */
 size_t mp_shard_reduce_layernorm_bwd_workspace(int64_t rows, int64_t cols);
 
 /* The backward all-reduce of the input-gradient partials fused with the
@@ -321,6 +356,24 @@ int mp_shard_reduce_layernorm_bwd(mp_dtype dtype, int N, int64_t rows, int64_t c
                                   const void* gamma, const float* mean, const float* rstd,
                                   const void* dres, void* dx, float* dgamma, float* dbeta,
                                   void* ws, size_t ws_bytes, hipStream_t s);
+
+/* mp_shard_reduce_layernorm_bwd followed, in the same pass, by the start of
+ * the backward of the branch that feeds this residual join (MLM-notes,
+ * "Model Parallel Transformers": each block ends in bias, dropout and the
+ * residual add), with the keep bits that branch's forward dropout saved:
+ *   ddrop = Drop(dx)       as mp_dropout_mask_bwd(dx, keep_bits, p) on dx as
+ *                          stored, [rows,cols] dtype;
+ *   dbias = column sums of ddrop  [cols] fp32 or NULL (the branch's bias
+ *                          gradient).
+ * dx, dgamma, dbeta, workspace and errors as mp_shard_reduce_layernorm_bwd;
+ * keep_bits and ddrop must be non-NULL, ddrop 16-byte aligned; ws is needed
+ * when any of dgamma, dbeta, dbias is non-NULL.  0 <= p < 1. */
+int mp_shard_reduce_layernorm_bwd_dropout(mp_dtype dtype, int N, int64_t rows, int64_t cols,
+                                          const void* const* partials, const void* x,
+                                          const void* gamma, const float* mean, const float* rstd,
+                                          const void* dres, void* dx, float* dgamma, float* dbeta,
+                                          float p, const uint8_t* keep_bits, void* ddrop,
+                                          float* dbias, void* ws, size_t ws_bytes, hipStream_t s);
 
 #ifdef __cplusplus
 }

@@ -195,6 +195,31 @@ __device__ __forceinline__ void apply_dropout(const DropoutParams& d, uint64_t j
   }
 }
 
+// Saved dropout keep flags, one bit per element: bit (e & 7) of byte e >> 3
+// is the flag of flat element e (1 = kept).  A thread holds E (8 or 4)
+// consecutive elements starting at e0, a multiple of E.  With E = 4 the two
+// halves of a byte sit in neighbouring lanes (lane ^ 1): the lane holding
+// the even half writes the byte, so every lane of the wave must make this
+// call together (non-live lanes pass live = false and all-zero flags).
+template <int E>
+__device__ __forceinline__ void store_keep_bits(uint8_t* bits, int64_t e0, const uint8_t* keep, bool live) {
+  uint32_t b = 0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) b |= static_cast<uint32_t>(keep[i] & 1u) << i;
+  if constexpr (E == 8) {
+    if (live) bits[e0 >> 3] = static_cast<uint8_t>(b);
+  } else {
+    const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(b), 1, 64));
+    if (live && (e0 & 7) == 0) bits[e0 >> 3] = static_cast<uint8_t>(b | (other << 4));
+  }
+}
+
+// The E flags of elements e0 .. e0+E-1 from saved bits.
+template <int E>
+__device__ __forceinline__ uint32_t load_keep_bits(const uint8_t* bits, int64_t e0) {
+  const uint32_t byte = bits[e0 >> 3];
+  return E == 8 ? byte : (byte >> (e0 & 7)) & 0xFu;
+}
 
 __device__ __forceinline__ float4 load_nt4(const float* p) {
   const nt_f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));

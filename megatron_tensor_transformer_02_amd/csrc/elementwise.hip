@@ -24,44 +24,91 @@ __global__ __launch_bounds__(256) void shard_reduce_kernel(PtrArray parts, int n
   using V = Vec16<BF16>;
   constexpr int E = V::N;
   const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (v >= nvec) return;
+  const bool live = v < nvec;
+  if (!live && (E == 8 || mask == nullptr)) return;  // fp32 lanes stay for the mask-bit exchange
   const int64_t e0 = v * E;
-  float part[NMAX][E];
+  uint8_t keep[E];
 #pragma unroll
-  for (int j = 0; j < NMAX; ++j)
-    if (j < n_parts) V::load_stream(parts.p[j], e0, part[j]);
+  for (int i = 0; i < E; ++i) keep[i] = 0;
+  if (live) {
+    float part[NMAX][E];
+#pragma unroll
+    for (int j = 0; j < NMAX; ++j)
+      if (j < n_parts) V::load_stream(parts.p[j], e0, part[j]);
+    float acc[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] = part[0][i];
+#pragma unroll
+    for (int j = 1; j < NMAX; ++j)
+      if (j < n_parts) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] += part[j][i];
+      }
+    float tmp[E];
+    if (bias != nullptr) {
+      V::load(bias, e0 % cols, tmp);
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[i] += tmp[i];
+    }
+    apply_dropout<E>(dp, dp.index_base + static_cast<uint64_t>(e0), acc, keep);
+    if (residual != nullptr) {
+      V::load(residual, e0, tmp);
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[i] += tmp[i];
+    }
+    V::store(out, e0, acc);
+  }
+  if (mask != nullptr) store_keep_bits<E>(mask, e0, keep, live);
+}
+
+// Dropout backward from saved keep bits over a slab of rows, one column vector
+// per thread (block: 32 column vectors x 8 row lanes, as the column sums):
+// dx = dy * keep * scale, and with SUM the slab's column sums of dx as stored
+// go to partial[slab, :] (the bias gradient's first stage).
+template <bool BF16, bool SUM>
+__global__ __launch_bounds__(256) void dropout_mask_bwd_kernel(const void* __restrict__ dy,
+                                                               const uint8_t* __restrict__ bits, float scale,
+                                                               int64_t rows, int64_t cols, int64_t slab_rows,
+                                                               void* __restrict__ dx, float* __restrict__ partial) {
+  using V = Vec16<BF16>;
+  constexpr int E = V::N;
+  __shared__ float red[SUM ? 8 : 1][SUM ? 32 * E : 1];
+  const int cv = threadIdx.x & 31;
+  const int rl = threadIdx.x >> 5;
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 32 + cv) * E;
+  const int64_t r_begin = static_cast<int64_t>(blockIdx.y) * slab_rows;
+  const int64_t r_end = r_begin + slab_rows < rows ? r_begin + slab_rows : rows;
   float acc[E];
 #pragma unroll
-  for (int i = 0; i < E; ++i) acc[i] = part[0][i];
+  for (int i = 0; i < E; ++i) acc[i] = 0.0f;
+  if (c0 < cols) {
+    for (int64_t r = r_begin + rl; r < r_end; r += 8) {
+      const int64_t e0 = r * cols + c0;
+      float v[E];
+      V::load_stream(dy, e0, v);
+      const uint32_t k = load_keep_bits<E>(bits, e0);
 #pragma unroll
-  for (int j = 1; j < NMAX; ++j)
-    if (j < n_parts) {
+      for (int i = 0; i < E; ++i) v[i] = ((k >> i) & 1u) ? v[i] * scale : 0.0f;
+      V::store(dx, e0, v);
+      if constexpr (SUM) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) acc[i] += part[j][i];
+        for (int i = 0; i < E; ++i) acc[i] += BF16 ? __uint_as_float(static_cast<uint32_t>(f32_to_bf16(v[i])) << 16)
+                                                   : v[i];
+      }
     }
-  float tmp[E];
-  if (bias != nullptr) {
-    V::load(bias, e0 % cols, tmp);
-#pragma unroll
-    for (int i = 0; i < E; ++i) acc[i] += tmp[i];
   }
-  uint8_t keep[E];
-  apply_dropout<E>(dp, dp.index_base + static_cast<uint64_t>(e0), acc, keep);
-  if (residual != nullptr) {
-    V::load(residual, e0, tmp);
+  if constexpr (SUM) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) acc[i] += tmp[i];
-  }
-  V::store(out, e0, acc);
-  if (mask != nullptr) {
-    if constexpr (E == 8) {
-      uint2 m;
-      m.x = keep[0] | (keep[1] << 8) | (keep[2] << 16) | (static_cast<uint32_t>(keep[3]) << 24);
-      m.y = keep[4] | (keep[5] << 8) | (keep[6] << 16) | (static_cast<uint32_t>(keep[7]) << 24);
-      *reinterpret_cast<uint2*>(mask + e0) = m;
-    } else {
-      *reinterpret_cast<uint32_t*>(mask + e0) =
-          keep[0] | (keep[1] << 8) | (keep[2] << 16) | (static_cast<uint32_t>(keep[3]) << 24);
+    for (int i = 0; i < E; ++i) red[rl][cv * E + i] = acc[i];
+    __syncthreads();
+    if (rl == 0 && c0 < cols) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        float t = red[0][cv * E + i];
+#pragma unroll
+        for (int l = 1; l < 8; ++l) t += red[l][cv * E + i];
+        partial[static_cast<int64_t>(blockIdx.y) * cols + c0 + i] = t;
+      }
     }
   }
 }
@@ -217,7 +264,6 @@ extern "C" int mp_shard_reduce(mp_dtype dtype, int N, int64_t rows, int64_t cols
   MP_REQUIRE_ALIGN(out);
   MP_REQUIRE_OPT_ALIGN(bias);
   MP_REQUIRE_OPT_ALIGN(residual);
-  MP_REQUIRE((reinterpret_cast<uintptr_t>(mask_out) & 7u) == 0, MP_ERR_ALIGN, "mp_shard_reduce: mask_out not 8-byte aligned");
   if (int rc = validate_dropout(p, index_base, "mp_shard_reduce")) return rc;
   PtrArray arr{};
   for (int j = 0; j < N; ++j) {
@@ -243,8 +289,6 @@ extern "C" int mp_shared_seed_dropout(mp_dtype dtype, int64_t n, const void* x, 
   MP_REQUIRE_PTR(y);
   MP_REQUIRE_ALIGN(x);
   MP_REQUIRE_ALIGN(y);
-  MP_REQUIRE((reinterpret_cast<uintptr_t>(mask_out) & 7u) == 0, MP_ERR_ALIGN,
-             "mp_shared_seed_dropout: mask_out not 8-byte aligned");
   if (int rc = validate_dropout(p, index_base, "mp_shared_seed_dropout")) return rc;
   if (n == 0) return MP_OK;
   PtrArray arr{};
@@ -253,6 +297,46 @@ extern "C" int mp_shared_seed_dropout(mp_dtype dtype, int64_t n, const void* x, 
   const int64_t nvec = n / vec_elems(dtype);
   return dtype == MP_BF16 ? launch_reduce<true>(1, arr, nvec, n, nullptr, nullptr, dp, y, mask_out, s)
                           : launch_reduce<false>(1, arr, nvec, n, nullptr, nullptr, dp, y, mask_out, s);
+}
+
+extern "C" size_t mp_dropout_mask_bwd_workspace(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0) return 0;
+  return colsum_workspace(rows, cols);
+}
+
+extern "C" int mp_dropout_mask_bwd(mp_dtype dtype, int64_t rows, int64_t cols, const void* dy,
+                                   const uint8_t* keep_bits, float p, void* dx, float* dbias, void* ws,
+                                   size_t ws_bytes, hipStream_t s) {
+  static const char* fn = "mp_dropout_mask_bwd";
+  MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype %d", fn, static_cast<int>(dtype));
+  MP_REQUIRE(rows >= 0 && cols > 0 && cols % vec_elems(dtype) == 0, MP_ERR_SHAPE, "%s: bad shape %lld x %lld", fn,
+             (long long)rows, (long long)cols);
+  MP_REQUIRE(p >= 0.0f && p < 1.0f, MP_ERR_ARG, "%s: dropout probability %g not in [0, 1)", fn, p);
+  MP_REQUIRE(rows == 0 || (dy != nullptr && dx != nullptr && keep_bits != nullptr), MP_ERR_NULL,
+             "%s: dy, dx and keep_bits must be non-NULL", fn);
+  MP_REQUIRE_OPT_ALIGN(dy);
+  MP_REQUIRE_OPT_ALIGN(dx);
+  const size_t need = dbias != nullptr ? colsum_workspace(rows, cols) : 0;
+  MP_REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn,
+             need);
+  MP_REQUIRE_OPT_ALIGN(ws);
+  int64_t slab_rows, slabs;
+  colsum_plan(rows, slab_rows, slabs);
+  const float scale = 1.0f / (1.0f - p);
+  float* partial = static_cast<float*>(ws);
+  if (slabs > 0) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(cols / vec_elems(dtype), 32)), static_cast<unsigned>(slabs));
+    if (dtype == MP_BF16) {
+      if (dbias) dropout_mask_bwd_kernel<true, true><<<grid, 256, 0, s>>>(dy, keep_bits, scale, rows, cols, slab_rows, dx, partial);
+      else dropout_mask_bwd_kernel<true, false><<<grid, 256, 0, s>>>(dy, keep_bits, scale, rows, cols, slab_rows, dx, partial);
+    } else {
+      if (dbias) dropout_mask_bwd_kernel<false, true><<<grid, 256, 0, s>>>(dy, keep_bits, scale, rows, cols, slab_rows, dx, partial);
+      else dropout_mask_bwd_kernel<false, false><<<grid, 256, 0, s>>>(dy, keep_bits, scale, rows, cols, slab_rows, dx, partial);
+    }
+  }
+  if (dbias != nullptr)
+    colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, 64)), 256, 0, s>>>(partial, slabs, cols, dbias);
+  return check_launch(fn);
 }
 
 extern "C" size_t mp_bias_grad_workspace(int64_t rows, int64_t cols) {

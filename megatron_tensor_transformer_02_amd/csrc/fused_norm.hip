@@ -21,7 +21,7 @@
 namespace mp {
 
 void layernorm_param_final(const float* partial, int64_t slabs, int64_t K, float* dgamma, float* dbeta,
-                           hipStream_t s);
+                           hipStream_t s, float* dthird = nullptr);
 
 struct PartPtrs {
   const void* p[MP_MAX_SHARDS];
@@ -140,11 +140,13 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_fwd_kernel(PartPtrs parts, 
     if (act && row + 1 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, e0 + K, residual, nullptr);
     float h[E];
     float sum = 0.0f;
+    uint8_t keep[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) keep[i] = 0;
     if (act) {
       sum_row<BF16, NMAX>(cur, n_parts, h);
 #pragma unroll
       for (int i = 0; i < E; ++i) h[i] += bv[i];
-      uint8_t keep[E];
       apply_dropout<E>(dp, dp.index_base + static_cast<uint64_t>(e0), h, keep);
       if (residual != nullptr) {
         float tmp[E];
@@ -157,20 +159,10 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_fwd_kernel(PartPtrs parts, 
         for (int i = 0; i < E; ++i) h[i] = round_to_bf16(h[i]);
       }
       V::store(out, e0, h);
-      if (mask != nullptr) {
-        if constexpr (E == 8) {
-          uint2 m;
-          m.x = keep[0] | (keep[1] << 8) | (keep[2] << 16) | (static_cast<uint32_t>(keep[3]) << 24);
-          m.y = keep[4] | (keep[5] << 8) | (keep[6] << 16) | (static_cast<uint32_t>(keep[7]) << 24);
-          *reinterpret_cast<uint2*>(mask + e0) = m;
-        } else {
-          *reinterpret_cast<uint32_t*>(mask + e0) =
-              keep[0] | (keep[1] << 8) | (keep[2] << 16) | (static_cast<uint32_t>(keep[3]) << 24);
-        }
-      }
 #pragma unroll
       for (int i = 0; i < E; ++i) sum += h[i];
     }
+    if (mask != nullptr) store_keep_bits<E>(mask, e0, keep, act);
     // red[slot], red[slot + 1] alternate with the next row's pair, so one
     // barrier per reduction suffices.
     const float mean = block_sum<NW>(sum, red[slot]) * inv_k;
@@ -198,7 +190,11 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_fwd_kernel(PartPtrs parts, 
 
 // dy = sum_j parts[j]; dx = dres + rstd * (g - mean(g) - xhat * mean(g * xhat)),
 // g = dy * gamma.  Same block layout as the forward; the block's column sums
-// of dy * xhat and dy go to partial[blockIdx.x, 0:K] and [.., K:2K].
+// of dy * xhat and dy go to partial[blockIdx.x, 0:K] and [.., K:2K].  With
+// `ddrop`, the dropout of the branch below this residual join is applied to
+// dx as stored, from the keep bits its forward saved (ddrop = Drop(dx), the
+// input gradient of that branch's bias + dropout), and its column sums go to
+// [.., 2K:3K] (partial rows 3K wide).
 template <bool BF16, int NMAX, int NW>
 __global__ __launch_bounds__(64 * NW) void reduce_ln_bwd_kernel(PartPtrs parts, int n_parts, int64_t T, int64_t K,
                                                                 int64_t rpb, const void* __restrict__ x,
@@ -206,7 +202,9 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_bwd_kernel(PartPtrs parts, 
                                                                 const float* __restrict__ mean_in,
                                                                 const float* __restrict__ rstd_in,
                                                                 const void* __restrict__ dres, void* __restrict__ dx,
-                                                                float* __restrict__ partial) {
+                                                                float* __restrict__ partial,
+                                                                const uint8_t* __restrict__ keep_bits, float dscale,
+                                                                void* __restrict__ ddrop) {
   using V = Vec16<BF16>;
   constexpr int E = V::N;
   __shared__ float red[4][NW];
@@ -214,9 +212,9 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_bwd_kernel(PartPtrs parts, 
   const bool act = vi < K / E;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
   const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
-  float gm[E], pg[E], pb[E];
+  float gm[E], pg[E], pb[E], pd[E];
 #pragma unroll
-  for (int i = 0; i < E; ++i) pg[i] = pb[i] = 0.0f;
+  for (int i = 0; i < E; ++i) pg[i] = pb[i] = pd[i] = 0.0f;
   if (act) V::load(gamma, vi * E, gm);
   const float inv_k = 1.0f / static_cast<float>(K);
   RowIn<NMAX> nxt;
@@ -257,14 +255,30 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_bwd_kernel(PartPtrs parts, 
 #pragma unroll
       for (int i = 0; i < E; ++i) o[i] = r[i] + rstd * (g[i] - m1 - xh[i] * m2);
       V::store(dx, e0, o);
+      if (ddrop != nullptr) {
+        // Dropout (saved keep bits) of dx as stored (bf16-rounded), rounded
+        // again on store: the values a separate pass over dx produces.
+        const uint32_t k = load_keep_bits<E>(keep_bits, e0);
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          if constexpr (BF16) o[i] = round_to_bf16(o[i]);
+          o[i] = ((k >> i) & 1u) ? o[i] * dscale : 0.0f;
+        }
+        V::store(ddrop, e0, o);
+#pragma unroll
+        for (int i = 0; i < E; ++i) pd[i] += BF16 ? round_to_bf16(o[i]) : o[i];
+      }
     }
   }
   if (partial == nullptr || !act) return;
-  float* pw = partial + static_cast<int64_t>(blockIdx.x) * 2 * K + vi * E;
+  const int64_t w = (ddrop != nullptr ? 3 : 2) * K;
+  float* pw = partial + static_cast<int64_t>(blockIdx.x) * w + vi * E;
 #pragma unroll
   for (int i = 0; i < E; i += 4) {
     *reinterpret_cast<float4*>(pw + i) = make_float4(pg[i], pg[i + 1], pg[i + 2], pg[i + 3]);
     *reinterpret_cast<float4*>(pw + K + i) = make_float4(pb[i], pb[i + 1], pb[i + 2], pb[i + 3]);
+    if (ddrop != nullptr)
+      *reinterpret_cast<float4*>(pw + 2 * K + i) = make_float4(pd[i], pd[i + 1], pd[i + 2], pd[i + 3]);
   }
 }
 
@@ -288,10 +302,10 @@ static void launch_fwd_n(const PartPtrs& parts, int n, int64_t T, int64_t K, con
 template <bool BF16, int NMAX, int NW>
 static void launch_bwd_n(const PartPtrs& parts, int n, int64_t T, int64_t K, const void* x, const void* gamma,
                          const float* mean, const float* rstd, const void* dres, void* dx, float* partial,
-                         hipStream_t s) {
+                         const uint8_t* keep_bits, float dscale, void* ddrop, hipStream_t s) {
   const int64_t rpb = bwd_rows_per_block(T);
   reduce_ln_bwd_kernel<BF16, NMAX, NW><<<static_cast<unsigned>(ceil_div(T, rpb)), 64 * NW, 0, s>>>(
-      parts, n, T, K, rpb, x, gamma, mean, rstd, dres, dx, partial);
+      parts, n, T, K, rpb, x, gamma, mean, rstd, dres, dx, partial, keep_bits, dscale, ddrop);
 }
 
 // Dispatch on the partial count (NMAX) and the waves per block (one thread
@@ -366,7 +380,7 @@ extern "C" int mp_shard_reduce_layernorm(mp_dtype dtype, int N, int64_t rows, in
   MP_REQUIRE_ALIGN(y);
   MP_REQUIRE_OPT_ALIGN(bias);
   MP_REQUIRE_OPT_ALIGN(residual);
-  MP_REQUIRE((reinterpret_cast<uintptr_t>(mask_out) & 7u) == 0, MP_ERR_ALIGN, "%s: mask_out not 8-byte aligned", fn);
+  MP_REQUIRE(mask_out == nullptr || cols % 8 == 0, MP_ERR_SHAPE, "%s: mask_out needs cols %% 8 == 0", fn);
   if (rows == 0) return MP_OK;
   const DropoutParams dp = make_dropout(p, seed, offset, index_base);
   const int64_t nw = ceil_div(cols / vec_elems(dtype), 64);
@@ -381,14 +395,14 @@ extern "C" int mp_shard_reduce_layernorm(mp_dtype dtype, int N, int64_t rows, in
 extern "C" size_t mp_shard_reduce_layernorm_bwd_workspace(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0) return 0;
   const int64_t blocks = ceil_div(rows, bwd_rows_per_block(rows));
-  return align_up(static_cast<size_t>(blocks * 2 * cols) * sizeof(float), 256);
+  return align_up(static_cast<size_t>(blocks * 3 * cols) * sizeof(float), 256);
 }
 
-extern "C" int mp_shard_reduce_layernorm_bwd(mp_dtype dtype, int N, int64_t rows, int64_t cols,
-                                             const void* const* partials, const void* x, const void* gamma,
-                                             const float* mean, const float* rstd, const void* dres, void* dx,
-                                             float* dgamma, float* dbeta, void* ws, size_t ws_bytes, hipStream_t s) {
-  static const char* fn = "mp_shard_reduce_layernorm_bwd";
+static int reduce_ln_bwd(const char* fn, mp_dtype dtype, int N, int64_t rows, int64_t cols,
+                         const void* const* partials, const void* x, const void* gamma, const float* mean,
+                         const float* rstd, const void* dres, void* dx, float* dgamma, float* dbeta,
+                         const uint8_t* keep_bits, float dscale, void* ddrop, float* dbias, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
   MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype %d", fn, static_cast<int>(dtype));
   MP_REQUIRE(rows >= 0 && cols > 0 && cols % vec_elems(dtype) == 0, MP_ERR_SHAPE, "%s: bad shape %lld x %lld", fn,
              (long long)rows, (long long)cols);
@@ -404,7 +418,9 @@ extern "C" int mp_shard_reduce_layernorm_bwd(mp_dtype dtype, int N, int64_t rows
   MP_REQUIRE_ALIGN(gamma);
   MP_REQUIRE_ALIGN(dx);
   MP_REQUIRE_OPT_ALIGN(dres);
-  const bool params = dgamma != nullptr || dbeta != nullptr;
+  MP_REQUIRE_OPT_ALIGN(ddrop);
+  MP_REQUIRE(dbias == nullptr || ddrop != nullptr, MP_ERR_NULL, "%s: dbias needs ddrop", fn);
+  const bool params = dgamma != nullptr || dbeta != nullptr || dbias != nullptr;
   const size_t need = params ? mp_shard_reduce_layernorm_bwd_workspace(rows, cols) : 0;
   MP_REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes",
              fn, need);
@@ -414,12 +430,36 @@ extern "C" int mp_shard_reduce_layernorm_bwd(mp_dtype dtype, int N, int64_t rows
   float* partial = params ? static_cast<float*>(ws) : nullptr;
   const int64_t nw = ceil_div(cols / vec_elems(dtype), 64);
   if (dtype == MP_BF16)
-    by_n<true, false>(N, nw, arr, N, rows, cols, x, gamma, mean, rstd, dres, dx, partial, s);
+    by_n<true, false>(N, nw, arr, N, rows, cols, x, gamma, mean, rstd, dres, dx, partial, keep_bits, dscale, ddrop,
+                      s);
   else
-    by_n<false, false>(N, nw, arr, N, rows, cols, x, gamma, mean, rstd, dres, dx, partial, s);
+    by_n<false, false>(N, nw, arr, N, rows, cols, x, gamma, mean, rstd, dres, dx, partial, keep_bits, dscale, ddrop,
+                       s);
   if (params) {
     const int64_t blocks = ceil_div(rows, bwd_rows_per_block(rows));
-    layernorm_param_final(partial, blocks, cols, dgamma, dbeta, s);
+    layernorm_param_final(partial, blocks, cols, dgamma, dbeta, s, ddrop != nullptr ? dbias : nullptr);
   }
   return check_launch(fn);
+}
+
+extern "C" int mp_shard_reduce_layernorm_bwd(mp_dtype dtype, int N, int64_t rows, int64_t cols,
+                                             const void* const* partials, const void* x, const void* gamma,
+                                             const float* mean, const float* rstd, const void* dres, void* dx,
+                                             float* dgamma, float* dbeta, void* ws, size_t ws_bytes, hipStream_t s) {
+  return reduce_ln_bwd("mp_shard_reduce_layernorm_bwd", dtype, N, rows, cols, partials, x, gamma, mean, rstd, dres,
+                       dx, dgamma, dbeta, nullptr, 1.0f, nullptr, nullptr, ws, ws_bytes, s);
+}
+
+extern "C" int mp_shard_reduce_layernorm_bwd_dropout(mp_dtype dtype, int N, int64_t rows, int64_t cols,
+                                                     const void* const* partials, const void* x, const void* gamma,
+                                                     const float* mean, const float* rstd, const void* dres,
+                                                     void* dx, float* dgamma, float* dbeta, float p,
+                                                     const uint8_t* keep_bits, void* ddrop, float* dbias, void* ws,
+                                                     size_t ws_bytes, hipStream_t s) {
+  static const char* fn = "mp_shard_reduce_layernorm_bwd_dropout";
+  MP_REQUIRE(p >= 0.0f && p < 1.0f, MP_ERR_ARG, "%s: dropout probability %g not in [0, 1)", fn, p);
+  MP_REQUIRE_PTR(keep_bits);
+  MP_REQUIRE_PTR(ddrop);
+  return reduce_ln_bwd(fn, dtype, N, rows, cols, partials, x, gamma, mean, rstd, dres, dx, dgamma, dbeta, keep_bits,
+                       1.0f / (1.0f - p), ddrop, dbias, ws, ws_bytes, s);
 }

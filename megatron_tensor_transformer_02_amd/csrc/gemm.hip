@@ -477,7 +477,10 @@ static void launch_bf16(Layout lay, int epi, int act, const GemmArgs& g, const P
     else if (act == MP_ACT_GELU_TANH) launch_bf16_layout<true, true, EPI_STORE, MP_ACT_GELU_TANH>(g, p, s);
     else launch_bf16_layout<true, true, EPI_STORE, MP_ACT_NONE>(g, p, s);
   } else if (lay == NN) {
-    launch_bf16_layout<true, false, EPI_STORE, MP_ACT_NONE>(g, p, s);
+    if (epi == EPI_DACT && act == MP_ACT_GELU_ERF) launch_bf16_layout<true, false, EPI_DACT, MP_ACT_GELU_ERF>(g, p, s);
+    else if (epi == EPI_DACT && act == MP_ACT_GELU_TANH)
+      launch_bf16_layout<true, false, EPI_DACT, MP_ACT_GELU_TANH>(g, p, s);
+    else launch_bf16_layout<true, false, EPI_STORE, MP_ACT_NONE>(g, p, s);
   } else if (epi == EPI_SPLITK) {
     launch_bf16_layout<false, false, EPI_SPLITK, MP_ACT_NONE>(g, p, s);
   } else {
@@ -533,9 +536,10 @@ int gemm(mp_dtype dt, Layout lay, int64_t M, int64_t N, int64_t K, const void* A
       splitk_reduce_kernel<<<static_cast<unsigned>(ceil_div(nq, 256)), 256, 0, s>>>(g.partial, p.splits, M, N, ldc,
                                                                                      g.out_bf16, C);
     } else {
-      if (epi != EPI_STORE || (lay != NT && act != MP_ACT_NONE))
+      const bool dact_nn = epi == EPI_DACT && lay == NN && act != MP_ACT_NONE && zin != nullptr;
+      if (!dact_nn && (epi != EPI_STORE || (lay != NT && act != MP_ACT_NONE)))
         return fail(MP_ERR_UNSUPPORTED, "gemm: epilogue not built for this layout");
-      launch_bf16(lay, EPI_STORE, act, g, p, s);
+      launch_bf16(lay, epi, act, g, p, s);
     }
   } else {
     g.k_split = K > 0 ? K : 16;
@@ -659,10 +663,11 @@ extern "C" size_t mp_row_linear_partial_bwd_workspace(mp_dtype dtype, int64_t T,
   return gemm_splitk_workspace(dtype, K, Fi, T);
 }
 
-extern "C" int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K, const void* Y_i,
-                                         const void* B_i, const void* dOut, void* dY_i, float* dB_i, void* ws,
-                                         size_t ws_bytes, hipStream_t s) {
-  static const char* fn = "mp_row_linear_partial_bwd";
+// Backward of the row-parallel partial; with act != NONE the input gradient
+// leaves the GEMM already multiplied by the activation gradient at Z_save.
+static int row_linear_bwd(const char* fn, mp_dtype dtype, int64_t T, int64_t Fi, int64_t K, const void* Y_i,
+                          const void* B_i, const void* dOut, const void* Z_save, int act, void* dY_i, float* dB_i,
+                          void* ws, size_t ws_bytes, hipStream_t s) {
   MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype", fn);
   MP_REQUIRE(T >= 0 && K > 0 && Fi > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
   if (int rc = validate_mat(dtype, K, fn, "K")) return rc;
@@ -681,11 +686,28 @@ extern "C" int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, 
   MP_REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn,
              need);
   MP_REQUIRE_OPT_ALIGN(ws);
-  // dY_i[T,Fi] = dOut[T,K] * B_i[K,Fi]
-  if (int rc = gemm(dtype, NN, T, Fi, K, dOut, K, B_i, Fi, dY_i, Fi, dtype == MP_BF16, nullptr, MP_ACT_NONE, nullptr,
-                    false, nullptr, 0, s))
+  // dY_i[T,Fi] = dOut[T,K] * B_i[K,Fi]  (times act'(Z_save) in the epilogue)
+  if (int rc = gemm(dtype, NN, T, Fi, K, dOut, K, B_i, Fi, dY_i, Fi, dtype == MP_BF16, nullptr, act, nullptr, false,
+                    nullptr, 0, s, act != MP_ACT_NONE ? EPI_DACT : EPI_STORE, Z_save))
     return rc;
   // dB_i[K,Fi] = dOut^T * Y_i (reduction over T), fp32
   return gemm(dtype, TN, K, Fi, T, dOut, K, Y_i, Fi, dB_i, Fi, false, nullptr, MP_ACT_NONE, nullptr, true, ws, ws_bytes,
               s);
+}
+
+extern "C" int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K, const void* Y_i,
+                                         const void* B_i, const void* dOut, void* dY_i, float* dB_i, void* ws,
+                                         size_t ws_bytes, hipStream_t s) {
+  return row_linear_bwd("mp_row_linear_partial_bwd", dtype, T, Fi, K, Y_i, B_i, dOut, nullptr, MP_ACT_NONE, dY_i,
+                        dB_i, ws, ws_bytes, s);
+}
+
+extern "C" int mp_row_linear_partial_bwd_dact(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K, const void* Y_i,
+                                              const void* B_i, const void* dOut, const void* Z_save, int act,
+                                              void* dZ_i, float* dB_i, void* ws, size_t ws_bytes, hipStream_t s) {
+  static const char* fn = "mp_row_linear_partial_bwd_dact";
+  MP_REQUIRE(act_ok(act) && act != MP_ACT_NONE, MP_ERR_ARG, "%s: bad activation %d", fn, act);
+  MP_REQUIRE_PTR(Z_save);
+  MP_REQUIRE_ALIGN(Z_save);
+  return row_linear_bwd(fn, dtype, T, Fi, K, Y_i, B_i, dOut, Z_save, act, dZ_i, dB_i, ws, ws_bytes, s);
 }

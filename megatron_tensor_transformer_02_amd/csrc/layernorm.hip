@@ -179,12 +179,12 @@ __global__ __launch_bounds__(256) void layernorm_bwd_param_kernel(int64_t T, int
 // Sums the slab partials of dgamma (columns [0, K)) and dbeta ([K, 2K)):
 // the same deterministic 4-group scheme as the column-sum final pass.
 __global__ __launch_bounds__(256) void layernorm_param_final_kernel(const float* __restrict__ partial, int64_t slabs,
-                                                                    int64_t K, float* __restrict__ dgamma,
-                                                                    float* __restrict__ dbeta) {
+                                                                    int64_t K, int64_t w, float* __restrict__ dgamma,
+                                                                    float* __restrict__ dbeta,
+                                                                    float* __restrict__ dthird) {
   __shared__ float red[4][64];
   const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
-  const int64_t w = 2 * K;
   float t = 0.0f;
   if (c < w) {
     int64_t s = q;
@@ -204,17 +204,21 @@ __global__ __launch_bounds__(256) void layernorm_param_final_kernel(const float*
   const float v = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
   if (c < K) {
     if (dgamma) dgamma[c] = v;
-  } else if (dbeta) {
-    dbeta[c - K] = v;
+  } else if (c < 2 * K) {
+    if (dbeta) dbeta[c - K] = v;
+  } else if (dthird) {
+    dthird[c - 2 * K] = v;
   }
 }
 
 // dgamma[c] = sum_s partial[s, c], dbeta[c] = sum_s partial[s, K + c] in a
-// fixed order (shared with the fused reduce + LayerNorm backward).
+// fixed order (shared with the fused reduce + LayerNorm backward); with
+// `dthird`, partial rows are 3K wide and dthird[c] = sum_s partial[s, 2K + c].
 void layernorm_param_final(const float* partial, int64_t slabs, int64_t K, float* dgamma, float* dbeta,
-                           hipStream_t s) {
-  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(2 * K, 64)), 256, 0, s>>>(partial, slabs, K, dgamma,
-                                                                                         dbeta);
+                           hipStream_t s, float* dthird = nullptr) {
+  const int64_t w = (dthird != nullptr ? 3 : 2) * K;
+  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(w, 64)), 256, 0, s>>>(partial, slabs, K, w, dgamma,
+                                                                                     dbeta, dthird);
 }
 
 static void ln_slabs(int64_t T, int64_t& slab_rows, int64_t& slabs) {
@@ -323,7 +327,6 @@ extern "C" int mp_layernorm_bwd(mp_dtype dtype, int64_t T, int64_t K, const void
     else
       layernorm_bwd_param_kernel<false><<<grid, 256, 0, s>>>(T, K, x, mean, rstd, dy, slab_rows, static_cast<float*>(ws));
   }
-  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(2 * K, 64)), 256, 0, s>>>(
-      static_cast<const float*>(ws), slabs, K, dgamma, dbeta);
+  layernorm_param_final(static_cast<const float*>(ws), slabs, K, dgamma, dbeta, s);
   return check_launch("mp_layernorm_bwd");
 }

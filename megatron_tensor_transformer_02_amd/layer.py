@@ -56,6 +56,9 @@ class RankLayer:
         self.p_attn, self.h1, self.h2, self.p_mlp, self.out = e(T, K), e(T, K), e(T, K), e(T, K), e(T, K)
         self.mu2, self.rs2 = _empty(T, f32, dev), _empty(T, f32, dev)
         self.y, self.z = e(T, Fi), e(T, Fi)
+        # keep flags of the two dropouts, one bit per element, for the backward
+        self.keep_attn = _empty(((T * K + 7) // 8,), torch.uint8, dev)
+        self.keep_mlp = _empty(((T * K + 7) // 8,), torch.uint8, dev)
         # backward buffers
         self.d_mlp, self.dy, self.dh2p, self.dh1 = e(T, K), e(T, Fi), e(T, K), e(T, K)
         self.d_attn, self.dctx, self.dhp, self.dx = e(T, K), e(T, hd), e(T, K), e(T, K)
@@ -82,7 +85,7 @@ class RankLayer:
         c = self.c
         mp.mp_shard_reduce_layernorm(partials, self.h1, c["ln2_g"], c["ln2_b"], self.h2, self.mu2, self.rs2,
                                      bias=c["b_o"], residual=x, p=self.p, seed=self.seed, offset=self.off[0],
-                                     eps=self.eps)
+                                     mask_out=self.keep_attn, eps=self.eps)
         return self.h1
 
     def mlp_partial(self):
@@ -96,30 +99,35 @@ class RankLayer:
         return self.p_mlp
 
     def mlp_reduce(self, partials):
-        mp.mp_shard_reduce(partials, self.out, self.c["b_b"], self.h1, self.p, self.seed, self.off[1])
+        mp.mp_shard_reduce(partials, self.out, self.c["b_b"], self.h1, self.p, self.seed, self.off[1], 0,
+                           self.keep_mlp)
         return self.out
 
     # ----------------------------------------------------------- backward
     def mlp_bwd_partial(self, dout):
         s, g = self.s, self.g
-        mp.mp_shared_seed_dropout(dout, self.d_mlp, self.p, self.seed, self.off[1])
-        mp.mp_bias_grad(self.d_mlp, g["b_b"])
-        mp.mp_row_linear_partial_bwd(self.y, s["w_b"], self.d_mlp, self.dy, g["w_b"])
-        mp.mp_column_linear_gelu_bwd(self.h2, s["w_a"], self.z, self.dy, self.act, self.dh2p, g["w_a"], g["b_a"])
+        # Dropout backward from the saved keep bits, with the bias gradient.
+        mp.mp_dropout_mask_bwd(dout, self.keep_mlp, self.p, self.d_mlp, g["b_b"])
+        # The GeLU gradient is applied in the epilogue of the row-parallel
+        # input-gradient GEMM, so the column backward gets dZ directly.
+        mp.mp_row_linear_partial_bwd_dact(self.y, s["w_b"], self.d_mlp, self.z, self.act, self.dy, g["w_b"])
+        mp.mp_column_linear_gelu_bwd(self.h2, s["w_a"], None, self.dy, "none", self.dh2p, g["w_a"], g["b_a"])
         return self.dh2p
 
     def mlp_bwd_reduce(self, partials, dout):
         # Backward all-reduce of the MLP input gradient fused with LN2's
-        # backward; the residual branch adds dOut.
+        # backward; the residual branch adds dOut.  The same pass starts the
+        # attention block's backward: its output dropout (the keep bits saved
+        # by the forward) applied to dH1 and the column sums of the result
+        # (the out-projection bias gradient).
         c, g = self.c, self.g
-        mp.mp_shard_reduce_layernorm_bwd(partials, self.h1, c["ln2_g"], self.mu2, self.rs2, self.dh1, dout,
-                                         g["ln2_g"], g["ln2_b"])
+        mp.mp_shard_reduce_layernorm_bwd_dropout(partials, self.h1, c["ln2_g"], self.mu2, self.rs2, self.dh1, self.p,
+                                                 self.keep_attn, self.d_attn, dres=dout, dgamma=g["ln2_g"],
+                                                 dbeta=g["ln2_b"], dbias=g["b_o"])
         return self.dh1
 
     def attn_bwd_partial(self):
         s, g = self.s, self.g
-        mp.mp_shared_seed_dropout(self.dh1, self.d_attn, self.p, self.seed, self.off[0])
-        mp.mp_bias_grad(self.d_attn, g["b_o"])
         mp.mp_row_linear_partial_bwd(self.ctx, s["w_o"], self.d_attn, self.dctx, g["w_o"])
         mp.mp_head_attention_bwd(self.h, s["w_qkv"], self.qkv, self.ctx, self.lse, self.dctx, self.B, self.L,
                                  self.nh, self.d, self.dhp, g["w_qkv"], g["b_qkv"], self.causal)

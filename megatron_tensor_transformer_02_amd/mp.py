@@ -40,6 +40,8 @@ _SIGS = {
     "mp_row_linear_partial": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p]),
     "mp_row_linear_partial_bwd_workspace": (c_sz, [c_i32, c_i64, c_i64, c_i64]),
     "mp_row_linear_partial_bwd": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "mp_row_linear_partial_bwd_dact": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_p,
+                                               c_sz, c_p]),
     "mp_shard_reduce": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_f32, c_u64, c_u64, c_u64, c_p, c_p,
                                 c_p]),
     "mp_shared_seed_dropout": (c_i32, [c_i32, c_i64, c_p, c_p, c_p, c_f32, c_u64, c_u64, c_u64, c_p]),
@@ -48,6 +50,10 @@ _SIGS = {
     "mp_shard_reduce_layernorm_bwd_workspace": (c_sz, [c_i64, c_i64]),
     "mp_shard_reduce_layernorm_bwd": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                               c_p, c_p, c_sz, c_p]),
+    "mp_shard_reduce_layernorm_bwd_dropout": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                                      c_p, c_p, c_f32, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "mp_dropout_mask_bwd_workspace": (c_sz, [c_i64, c_i64]),
+    "mp_dropout_mask_bwd": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_f32, c_p, c_p, c_p, c_sz, c_p]),
     "mp_bias_grad_workspace": (c_sz, [c_i64, c_i64]),
     "mp_bias_grad": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_p, c_sz, c_p]),
     "mp_head_attention": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_p,
@@ -191,6 +197,16 @@ def mp_row_linear_partial_bwd(Y_i, B_i, dOut, dY_i, dB_i, ws=None, stream=None):
           need if ws is not None else 0, _s(stream))
 
 
+def mp_row_linear_partial_bwd_dact(Y_i, B_i, dOut, Z_save, act, dZ_i, dB_i, ws=None, stream=None):
+    T, Fi = Y_i.shape
+    K = B_i.shape[0]
+    dt = _dt(Y_i)
+    need = lib().mp_row_linear_partial_bwd_workspace(dt, T, Fi, K)
+    ws = ws if ws is not None else workspace(need, Y_i.device)
+    _call("mp_row_linear_partial_bwd_dact", dt, T, Fi, K, _p(Y_i), _p(B_i), _p(dOut), _p(Z_save), _act(act),
+          _p(dZ_i), _p(dB_i), _p(ws), need if ws is not None else 0, _s(stream))
+
+
 # ------------------------------------------------------- reduce and dropout
 
 def mp_shard_reduce(partials, out, bias=None, residual=None, p=0.0, seed=0, offset=0, index_base=0,
@@ -219,6 +235,26 @@ def mp_shard_reduce_layernorm_bwd(partials, x, gamma, mean, rstd, dx, dres=None,
     ws = ws if ws is not None else workspace(need, x.device)
     _call("mp_shard_reduce_layernorm_bwd", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
           _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), _p(ws), need if ws is not None else 0, _s(stream))
+
+
+def mp_shard_reduce_layernorm_bwd_dropout(partials, x, gamma, mean, rstd, dx, p, keep_bits, ddrop, dres=None,
+                                          dgamma=None, dbeta=None, dbias=None, ws=None, stream=None):
+    rows, cols = x.shape
+    arr = _ptr_array(partials)
+    params = dgamma is not None or dbeta is not None or dbias is not None
+    need = lib().mp_shard_reduce_layernorm_bwd_workspace(rows, cols) if params else 0
+    ws = ws if ws is not None else workspace(need, x.device)
+    _call("mp_shard_reduce_layernorm_bwd_dropout", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
+          _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), p, _p(keep_bits), _p(ddrop), _p(dbias), _p(ws),
+          need if ws is not None else 0, _s(stream))
+
+
+def mp_dropout_mask_bwd(dy, keep_bits, p, dx, dbias=None, ws=None, stream=None):
+    rows, cols = dy.shape
+    need = lib().mp_dropout_mask_bwd_workspace(rows, cols) if dbias is not None else 0
+    ws = ws if ws is not None else workspace(need, dy.device)
+    _call("mp_dropout_mask_bwd", _dt(dy), rows, cols, _p(dy), _p(keep_bits), p, _p(dx), _p(dbias), _p(ws),
+          need if ws is not None else 0, _s(stream))
 
 
 def mp_shared_seed_dropout(x, y, p, seed, offset, index_base=0, mask_out=None, stream=None):

@@ -44,3 +44,13 @@ def randn(gen_seed, shape, dtype, std=1.0):
     rng = np.random.default_rng(gen_seed)
     a = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
     return torch.from_numpy(a).to(tdtype(dtype))
+
+
+def mask_bits(n):
+    """Device buffer for n dropout keep flags saved as bits."""
+    return torch.empty((n + 7) // 8, dtype=torch.uint8, device="cuda")
+
+
+def unpack_bits(t, n):
+    """Keep flags (bool [n]) from a bit buffer: bit i & 7 of byte i >> 3."""
+    return np.unpackbits(t.cpu().numpy(), bitorder="little")[:n].astype(bool)

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import TOL, cu, f64, randn, rel_frobenius, say, sync, tdtype
+from gpu_util import TOL, cu, f64, mask_bits, randn, rel_frobenius, say, sync, tdtype, unpack_bits
 from megatron_tensor_transformer_02_amd import mp
 
 pytestmark = pytest.mark.gpu
@@ -26,13 +26,13 @@ def test_shard_reduce(dtype, n, rows, cols, p, index_base):
     res = randn(51, (rows, cols), dtype)
     seed, off = 0x1234ABCD5678, 7
     out = torch.empty((rows, cols), dtype=tdtype(dtype), device="cuda")
-    mask = torch.empty(rows * cols, dtype=torch.uint8, device="cuda")
+    mask = mask_bits(rows * cols)
     mp.mp_shard_reduce([cu(t) for t in parts], out, cu(bias), cu(res), p, seed, off, index_base, mask)
     sync()
     acc = sum(f64(t) for t in parts) + f64(bias)
     want_pre, keep = O.dropout(acc, p, seed, off, start=index_base)
     want = want_pre + f64(res)
-    assert np.array_equal(mask.cpu().numpy().astype(bool).reshape(rows, cols), keep)
+    assert np.array_equal(unpack_bits(mask, rows * cols).reshape(rows, cols), keep)
     assert rel_frobenius(f64(out), want) <= TOL[dtype]
 
 
@@ -55,19 +55,57 @@ def test_shared_seed_dropout(dtype, n, p):
     say("dropout", dtype, n, p)
     x = randn(5, (n,), dtype)
     y = torch.empty_like(x, device="cuda")
-    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    mask = mask_bits(n)
     mp.mp_shared_seed_dropout(cu(x), y, p, 99, 3, 0, mask)
     sync()
     want, keep = O.dropout(f64(x), p, 99, 3)
-    assert np.array_equal(mask.cpu().numpy().astype(bool), keep)
+    assert np.array_equal(unpack_bits(mask, n), keep)
     assert rel_frobenius(f64(y), want) <= TOL[dtype]
-    # Backward = the same call on the gradient: identical mask, any rank.
+    # The backward redrawn from the shared seed: identical mask, any rank.
     g = randn(6, (n,), dtype)
     dg = torch.empty_like(g, device="cuda")
-    mask2 = torch.empty(n, dtype=torch.uint8, device="cuda")
+    mask2 = mask_bits(n)
     mp.mp_shared_seed_dropout(cu(g), dg, p, 99, 3, 0, mask2)
+    # ... and the backward from the saved bits gives the same values.
+    dg2 = torch.empty_like(dg)
+    mp.mp_dropout_mask_bwd(cu(g).reshape(1, n), mask, p, dg2.reshape(1, n))
     sync()
     assert torch.equal(mask, mask2)
+    assert torch.equal(dg, dg2)
+
+
+@pytest.mark.parametrize("dtype,rows,cols,p", [
+    ("f32", 9, 12, 0.5),        # rows start mid-byte (cols % 8 == 4)
+    ("bf16", 77, 3072, 0.1),    # the 8.3B-config hidden size, ragged rows
+    ("bf16", 300, 136, 0.9),
+    ("bf16", 2048, 3072, 0.1),  # a quarter of the full token count
+])
+def test_dropout_mask_bwd(dtype, rows, cols, p):
+    """Backward of a dropout from the keep bits its forward saved: dx equals
+    the redrawn shared-seed dropout of dy bit for bit; the bias gradient (column
+    sums of dx) matches mp_bias_grad and the oracle."""
+    say("dropout bwd from bits", dtype, rows, cols, p)
+    n = rows * cols
+    x = randn(80, (rows, cols), dtype)
+    mask = mask_bits(n)
+    mp.mp_shared_seed_dropout(cu(x), torch.empty_like(cu(x)), p, 1234, 9, 0, mask)
+    dy = cu(randn(81, (rows, cols), dtype))
+    dx = torch.empty_like(dy)
+    db = torch.empty(cols, device="cuda")
+    mp.mp_dropout_mask_bwd(dy, mask, p, dx, db)
+    dx2 = torch.empty_like(dy)
+    mp.mp_shared_seed_dropout(dy, dx2, p, 1234, 9, 0)
+    db2 = torch.empty(cols, device="cuda")
+    mp.mp_bias_grad(dx2, db2)
+    dx3 = torch.empty_like(dy)
+    mp.mp_dropout_mask_bwd(dy, mask, p, dx3)  # without the bias gradient
+    sync()
+    assert torch.equal(dx, dx2) and torch.equal(dx, dx3)
+    assert rel_frobenius(f64(db), f64(db2)) <= 1e-5
+    want, keep = O.dropout(f64(dy), p, 1234, 9)
+    assert np.array_equal(unpack_bits(mask, n).reshape(rows, cols), keep)
+    assert rel_frobenius(f64(dx), want) <= TOL[dtype]
+    assert rel_frobenius(f64(db), O.bias_grad(f64(dx))) <= 1e-5
 
 
 @pytest.mark.slow
@@ -76,11 +114,11 @@ def test_dropout_mask_full_layer_size():
     say("dropout full size")
     n = 8192 * 3072
     x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
-    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    mask = mask_bits(n)
     mp.mp_shared_seed_dropout(x, torch.empty_like(x), 0.1, 303, 1, 0, mask)
     sync()
     keep = O.dropout_keep_mask(n, 0.1, 303, 1)
-    assert np.array_equal(mask.cpu().numpy().astype(bool), keep)
+    assert np.array_equal(unpack_bits(mask, n), keep)
 
 
 @pytest.mark.parametrize("T,V,K,n,dtype", [(40, 64, 8, 2, "f32"), (257, 1000, 64, 8, "bf16"),

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import TOL, cu, f64, randn, rel_frobenius, say, sync, tdtype
+from gpu_util import TOL, cu, f64, mask_bits, randn, rel_frobenius, say, sync, tdtype, unpack_bits
 from megatron_tensor_transformer_02_amd import mp
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,7 @@ def test_reduce_layernorm_fwd(dtype, n, rows, cols, p):
     t = tdtype(dtype)
     out, y = torch.empty((rows, cols), dtype=t, device="cuda"), torch.empty((rows, cols), dtype=t, device="cuda")
     mean, rstd = torch.empty(rows, device="cuda"), torch.empty(rows, device="cuda")
-    mask = torch.empty(rows * cols, dtype=torch.uint8, device="cuda")
+    mask = mask_bits(rows * cols)
     mp.mp_shard_reduce_layernorm(parts, out, gamma, beta, y, mean, rstd, bias=bias, residual=res, p=p, seed=seed,
                                  offset=off, index_base=ib, mask_out=mask)
     # unfused GPU path
@@ -51,7 +51,7 @@ def test_reduce_layernorm_fwd(dtype, n, rows, cols, p):
     # oracle: the reduce from the inputs, LayerNorm of the stored (rounded) sum
     acc = sum(f64(t_) for t_ in parts) + f64(bias)
     want_pre, keep = O.dropout(acc, p, seed, off, start=ib)
-    assert np.array_equal(mask.cpu().numpy().astype(bool).reshape(rows, cols), keep)
+    assert np.array_equal(unpack_bits(mask, rows * cols).reshape(rows, cols), keep)
     assert rel_frobenius(f64(out), want_pre + f64(res)) <= TOL[dtype]
     wy, wm, wr = O.layernorm(f64(out), f64(gamma), f64(beta))
     assert rel_frobenius(f64(y), wy) <= TOL[dtype]
@@ -117,3 +117,48 @@ def test_reduce_layernorm_bwd_aliasing_and_no_params():
     mp.mp_layernorm_bwd(x, gamma, mean, rstd, dy, want, ref)
     sync()
     assert rel_frobenius(f64(d), f64(want)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,n,rows,cols,p", CASES)
+def test_reduce_layernorm_bwd_dropout(dtype, n, rows, cols, p):
+    """The fused backward that also applies the next branch's dropout (from
+    the keep bits its forward saved) to dx and sums its columns: dx and the
+    parameter gradients are those of the plain fused backward bit for bit,
+    ddrop is a separate dropout-backward pass over dx bit for bit, dbias
+    matches that pass's column sums and the oracle."""
+    say("reduce+LN bwd + dropout", dtype, n, rows, cols, p)
+    parts = [cu(randn(90 + j, (rows, cols), dtype)) for j in range(n)]
+    x = cu(randn(74, (rows, cols), dtype))
+    gamma, beta = cu(randn(75, (cols,), dtype, 0.2) + 1), cu(randn(76, (cols,), dtype, 0.1))
+    dres = cu(randn(77, (rows, cols), dtype))
+    t = tdtype(dtype)
+    y = torch.empty((rows, cols), dtype=t, device="cuda")
+    mean, rstd = torch.empty(rows, device="cuda"), torch.empty(rows, device="cuda")
+    mp.mp_layernorm(x, gamma, beta, y, mean, rstd)
+    seed, off = 0xFEEDFACE12, 5
+    bits = mask_bits(rows * cols)  # the branch's forward dropout, saved as bits
+    mp.mp_shared_seed_dropout(x, torch.empty_like(x), p, seed, off, 0, bits)
+    dx, dd = torch.empty((rows, cols), dtype=t, device="cuda"), torch.empty((rows, cols), dtype=t, device="cuda")
+    dg, db, dbias = (torch.empty(cols, device="cuda") for _ in range(3))
+    mp.mp_shard_reduce_layernorm_bwd_dropout(parts, x, gamma, mean, rstd, dx, p, bits, dd, dres=dres, dgamma=dg,
+                                             dbeta=db, dbias=dbias)
+    # unfused GPU path: plain fused backward, then dropout backward + bias gradient
+    dx2 = torch.empty_like(dx)
+    dg2, db2, dbias2 = (torch.empty(cols, device="cuda") for _ in range(3))
+    mp.mp_shard_reduce_layernorm_bwd(parts, x, gamma, mean, rstd, dx2, dres, dg2, db2)
+    dd2 = torch.empty_like(dd)
+    mp.mp_shared_seed_dropout(dx2, dd2, p, seed, off, 0)
+    mp.mp_bias_grad(dd2, dbias2)
+    sync()
+    assert torch.equal(dx, dx2) and torch.equal(dg, dg2) and torch.equal(db, db2)
+    assert torch.equal(dd, dd2)
+    assert rel_frobenius(f64(dbias), f64(dbias2)) <= 1e-5
+    # oracle: dropout of the stored dx (mask from the shared-seed generator) and its column sums
+    want_dd, _ = O.dropout(f64(dx), p, seed, off)
+    assert rel_frobenius(f64(dd), want_dd) <= TOL[dtype]
+    assert rel_frobenius(f64(dbias), O.bias_grad(f64(dd))) <= 1e-5
+    # without dbias (no workspace needed for it) the outputs are unchanged
+    dd3 = torch.empty_like(dd)
+    mp.mp_shard_reduce_layernorm_bwd_dropout(parts, x, gamma, mean, rstd, dx2, p, bits, dd3, dres=dres)
+    sync()
+    assert torch.equal(dd3, dd) and torch.equal(dx2, dx)

@@ -87,7 +87,34 @@ def test_row_linear_bwd(dtype, T, Fi, K):
     assert rel_frobenius(f64(db), wdb) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("plan", ["256,256,1", "256,192,1", "256,128,1", "128,128,3", "256,192,2"])
+@pytest.mark.parametrize("dtype,T,Fi,K,act", [("f32", 32, 128, 64, "erf"), ("bf16", 300, 136, 264, "erf"),
+                                              ("bf16", 1000, 200, 392, "tanh"), ("bf16", 2048, 1536, 3072, "erf")])
+def test_row_linear_bwd_dact(dtype, T, Fi, K, act):
+    """The row-parallel input gradient with the GeLU gradient of the
+    preceding column-parallel GEMM applied in its epilogue, and the column
+    backward fed that dZ with act = none, against the oracle's MLP backward."""
+    say("row bwd dact", dtype, T, Fi, K, act)
+    zpre = randn(16, (T, Fi), dtype)
+    b = randn(17, (K, Fi), dtype, 0.02)
+    dout = randn(18, (T, K), dtype)
+    y = cu(torch.from_numpy(O.gelu(f64(zpre), act)).to(tdtype(dtype)))
+    zd = cu(zpre)
+    dz = torch.empty((T, Fi), dtype=tdtype(dtype), device="cuda")
+    db = torch.empty((K, Fi), dtype=torch.float32, device="cuda")
+    mp.mp_row_linear_partial_bwd_dact(y, cu(b), cu(dout), zd, act, dz, db)
+    sync()
+    wdy, wdb = O.row_linear_partial_bwd(f64(y), f64(b), f64(dout))
+    assert rel_frobenius(f64(dz), wdy * O.gelu_grad(f64(zpre), act)) <= TOL[dtype]
+    assert rel_frobenius(f64(db), wdb) <= TOL[dtype]
+    # The weight gradient is the same GEMM as in the unfused call: bit-identical.
+    dy2 = torch.empty_like(dz)
+    db2 = torch.empty_like(db)
+    mp.mp_row_linear_partial_bwd(y, cu(b), cu(dout), dy2, db2)
+    sync()
+    assert torch.equal(db, db2)
+
+
+@pytest.mark.parametrize("plan", ["256,256,1", "256,192,1", "256,128,1", "128,128,3", "128,192,1", "256,192,2"])
 def test_forced_tile_plans_ragged(plan, monkeypatch):
     """Every tile shape and a split-K whose last split is ragged, on ragged
     M, N and K in all three layouts (forward NT; backward NN and TN)."""
@@ -103,11 +130,14 @@ def test_forced_tile_plans_ragged(plan, monkeypatch):
     yd, bd = cu(y), cu(b)
     mp.mp_row_linear_partial(yd, bd, p)
     mp.mp_row_linear_partial_bwd(yd, bd, cu(dout), dy, db)
+    dz = torch.empty_like(dy)
+    mp.mp_row_linear_partial_bwd_dact(yd, bd, cu(dout), yd, "erf", dz, db)  # y doubles as the pre-activation
     sync()
     assert rel_frobenius(f64(p), O.row_linear_partial(f64(y), f64(b))) <= TOL["bf16"]
     wdy, wdb = O.row_linear_partial_bwd(f64(y), f64(b), f64(dout))
     assert rel_frobenius(f64(dy), wdy) <= TOL["bf16"]
     assert rel_frobenius(f64(db), wdb) <= TOL["bf16"]
+    assert rel_frobenius(f64(dz), wdy * O.gelu_grad(f64(y), "erf")) <= TOL["bf16"]
 
 
 @pytest.mark.slow
