@@ -217,6 +217,152 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
   if (g == 0) a.lse[(static_cast<int64_t>(b) * a.h + hh) * a.L + qi] = m * a.scale + logf(lt);
 }
 
+// Forward with the keys of each query tile split between two waves: a block
+// holds 4 query tiles of 16 rows x 2 key halves (8 waves, two per SIMD).
+// Wave (qt, hf) multiplies keys 32*hf .. 32*hf+31 of every 64-key tile, so
+// each wave's dependent chain per tile (S^T, softmax, O^T) is half as long and
+// a second wave per SIMD covers its latency.  At the end the two halves'
+// (running max, exp-sum, O) are merged through LDS, rescaled to the common
+// max as the online softmax does between tiles.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_split_kernel(
+    const AttnArgs a) {  // <= 128 VGPRs: two blocks per CU
+  constexpr int NT = 512, BQ = 64, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
+  __shared__ uint4 lds[4][TS];  // K tiles in [0], [1]; V tiles in [2], [3]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qt = wave & 3, hf = wave >> 2;
+  const int qc = lane & 15, g = lane >> 4;
+  const int nbh = a.B * a.h;
+  const int bh = blockIdx.x % nbh;
+  const int qb = a.nblk - 1 - static_cast<int>(blockIdx.x / nbh);  // heavy (late) query blocks first
+  const int b = bh / a.h, hh = bh % a.h;
+  const int64_t S3 = 3LL * a.h * D, HD = static_cast<int64_t>(a.h) * D;
+  const uint16_t* base = a.qkv + static_cast<int64_t>(b) * a.L * S3;
+  const int q0 = qb * BQ, qw0 = q0 + qt * 16, qi = qw0 + qc;
+  const bool qvalid = qi < a.L;
+
+  uint4 qf[KS];  // Q^T as the B operand: query qi, d = 32 st + 8 g .. +7
+#pragma unroll
+  for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * g, qvalid);
+
+  const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
+  const BufRes rk = make_bufres(base + HD + hh * D, batch_bytes - (HD + hh * D) * 2);
+  const BufRes rv = make_bufres(base + 2 * HD + hh * D, batch_bytes - (2 * HD + hh * D) * 2);
+
+  float m = -INFINITY, l = 0.0f;
+  f32x4_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
+  const int nkb = (kv_end + 63) / 64;
+  RowTile<D, NT> tk, tv;
+  tk.load(rk, S3, 0, a.L, tid);
+  tv.load(rv, S3, 0, a.L, tid);
+  tk.store(lds[0], tid);
+  tv.store(lds[2], tid);
+  __syncthreads();
+  for (int it = 0; it < nkb; ++it) {
+    const int kv0 = it * 64, cur = it & 1;
+    const bool more = it + 1 < nkb;
+    if (more) {
+      tk.load(rk, S3, kv0 + 64, a.L, tid);
+      tv.load(rv, S3, kv0 + 64, a.L, tid);
+    }
+    const int k0h = kv0 + 32 * hf;  // this wave's 32 keys
+    if (k0h < a.L && !(a.causal && k0h > qw0 + 15)) {
+      const uint4* kt_ = lds[cur];
+      const uint4* vt_ = lds[2 + cur];
+      f32x4_t s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) s[kb] = mfma_16x16x32(row_frag(kt_, 32 * hf + 16 * kb, st, lane), qf[st], s[kb]);
+      }
+      // Keys of this lane: k0h + 16 kb + 4 g + r.
+      if (k0h + 31 >= a.L || (a.causal && k0h + 31 > qw0)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0h + 16 * kb + 4 * g + r;
+            if (key >= a.L || (a.causal && key > qi)) s[kb][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max4(mx);
+      const float mn = fmaxf(m, mx);
+      const float ms = mn == -INFINITY ? 0.0f : mn;
+      const float alpha = exp2f((m - ms) * a.scale_log2);
+      const float msc = ms * a.scale_log2;
+      float ps = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[kb][r] = exp2f(fmaf(s[kb][r], a.scale_log2, -msc));
+          ps += s[kb][r];
+        }
+      l = l * alpha + ps;
+      const uint4 pb = pack_pair(s[0], s[1]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        o[db] *= alpha;
+        o[db] = mfma_16x16x32(tr_frag(vt_, 16 * db, hf, lane), pb, o[db]);
+      }
+      m = mn;
+    }
+    if (more) {
+      tk.store(lds[cur ^ 1], tid);
+      tv.store(lds[2 + (cur ^ 1)], tid);
+    }
+    __syncthreads();
+  }
+  // Merge the key halves: the second half's wave leaves (m, l, O) in LDS,
+  // laid out [tile][value][lane] (conflict-free), the first half's wave
+  // rescales both to the common max and finishes.
+  constexpr int MS = 4 * DB + 2;
+  float* mrg = reinterpret_cast<float*>(&lds[0][0]) + qt * MS * 64 + lane;
+  if (hf == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mrg[(4 * db + r) * 64] = o[db][r];
+    mrg[(4 * DB) * 64] = m;
+    mrg[(4 * DB + 1) * 64] = l;
+  }
+  __syncthreads();
+  if (hf == 1) return;
+  {
+    const float m1 = mrg[(4 * DB) * 64], l1 = mrg[(4 * DB + 1) * 64];
+    const float mn = fmaxf(m, m1);
+    const float ms = mn == -INFINITY ? 0.0f : mn;
+    const float a0 = exp2f((m - ms) * a.scale_log2), a1 = exp2f((m1 - ms) * a.scale_log2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * a0 + mrg[(4 * db + r) * 64] * a1;
+    l = l * a0 + l1 * a1;
+    m = mn;
+  }
+  const float lt = sum4(l);
+  if (!qvalid) return;
+  const float inv = 1.0f / lt;
+  uint16_t* crow = a.ctx + (static_cast<int64_t>(b) * a.L + qi) * HD + hh * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    uint2 v;
+    v.x = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
+    v.y = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
+    *reinterpret_cast<uint2*>(crow + 16 * db + 4 * g) = v;
+  }
+  if (g == 0) a.lse[(static_cast<int64_t>(b) * a.h + hh) * a.L + qi] = m * a.scale + logf(lt);
+}
+
 // dvec[b, h, l] = sum_d dctx[t, h*D + d] * ctx[t, h*D + d]; one thread per (t, head).
 template <int D>
 __global__ __launch_bounds__(256) void attn_dvec_kernel(const AttnArgs a) {
@@ -452,10 +598,13 @@ static int attn_waves(int B, int L, int h) {
   return blocks8 >= 512 ? 8 : 4;
 }
 
+// With 4-wave blocks (few (batch, head) pairs) the forward runs the split-key
+// kernel instead: the same 64-query blocks on 8 waves.
 template <int D, int NW>
 static void launch_fwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
-  attn_fwd_kernel<D, NW><<<static_cast<unsigned>(a.nblk * a.B * a.h), 64 * NW, 0, s>>>(a);
+  if constexpr (NW == 4) attn_fwd_split_kernel<D><<<static_cast<unsigned>(a.nblk * a.B * a.h), 512, 0, s>>>(a);
+  else attn_fwd_kernel<D, NW><<<static_cast<unsigned>(a.nblk * a.B * a.h), 64 * NW, 0, s>>>(a);
 }
 
 template <int D, int NW>

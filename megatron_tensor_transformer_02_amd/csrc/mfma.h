@@ -324,7 +324,9 @@ struct GridWarm {
   }
 
   __device__ __forceinline__ void issue(const void* sink, int64_t k0, bool live) const {
-    const uint32_t so = live ? static_cast<uint32_t>(k0) * kstride : 0x80000000u;
+    // Uniform per wave; readfirstlane keeps it in a scalar register even where
+    // the compiler cannot prove that.
+    const uint32_t so = __builtin_amdgcn_readfirstlane(live ? static_cast<uint32_t>(k0) * kstride : 0x80000000u);
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(sink));
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %3 offen lds" ::"v"(voff), "s"(desc),
                  "s"(m0v), "s"(so)

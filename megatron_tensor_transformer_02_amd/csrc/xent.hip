@@ -2,7 +2,7 @@
 // fp32 logits shard), the cross-shard combine and the logits gradient.
 //
 // The statistics pass is HBM-bound: one wave owns one row, streams it with
-// 16-byte loads (four in flight per lane per step) and keeps an online
+// 16-byte loads (a round of them in flight per lane) and keeps an online
 // (max, scaled exp-sum) pair per lane, folded across the wave with shuffles.
 #include "common.h"
 
@@ -19,7 +19,10 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mn;
 }
 
-// One wave per row; `UNROLL` float4 loads in flight per lane.
+// One wave per row.  A lane owns float4s lane, lane+64, ... of its row and
+// loads them in rounds of UNROLL, all issued before any is used (lanes past
+// the row's end read -inf, which leaves the pair unchanged), so a row takes
+// ceil(Vi/4/64/UNROLL) dependent memory round trips.
 template <int UNROLL>
 __global__ __launch_bounds__(256) void xent_triples_kernel(int64_t T, int64_t Vi, int64_t v_start,
                                                            const float* __restrict__ Z,
@@ -31,12 +34,13 @@ __global__ __launch_bounds__(256) void xent_triples_kernel(int64_t T, int64_t Vi
   const float* zr = Z + row * Vi;
   float m = -INFINITY, s = 0.0f;
   const int64_t nv = Vi >> 2;  // Vi is a multiple of 4
-  const float4* z4 = reinterpret_cast<const float4*>(zr);
-  int64_t i = lane;
-  for (; i + 64 * (UNROLL - 1) < nv; i += 64 * UNROLL) {
+  for (int64_t i0 = lane; i0 < nv; i0 += 64 * UNROLL) {
     float4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = load_nt4(zr + 4 * (i + 64 * u));
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t i = i0 + 64 * u;
+      v[u] = i < nv ? load_nt4(zr + 4 * i) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
     float lm = m;
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) lm = fmaxf(lm, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
@@ -49,16 +53,6 @@ __global__ __launch_bounds__(256) void xent_triples_kernel(int64_t T, int64_t Vi
       acc += exp2f(fmaf(v[u].z, kLog2e, -ml));
       acc += exp2f(fmaf(v[u].w, kLog2e, -ml));
     }
-    m = lm;
-    s = acc;
-  }
-  for (; i < nv; i += 64) {
-    const float4 v = z4[i];
-    const float lm = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-    const float ml = lm * kLog2e;
-    float acc = (m == -INFINITY) ? 0.0f : s * exp2f(m * kLog2e - ml);
-    acc += exp2f(fmaf(v.x, kLog2e, -ml)) + exp2f(fmaf(v.y, kLog2e, -ml)) + exp2f(fmaf(v.z, kLog2e, -ml)) +
-           exp2f(fmaf(v.w, kLog2e, -ml));
     m = lm;
     s = acc;
   }
@@ -160,7 +154,11 @@ extern "C" int mp_vocab_parallel_xent(int64_t T, int64_t Vi, int64_t v_start, co
   MP_REQUIRE_PTR(triples);
   MP_REQUIRE_ALIGN(Z_i);
   if (T == 0) return MP_OK;
-  xent_triples_kernel<4><<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(T, Vi, v_start, Z_i, labels, triples);
+#ifndef MP_XENT_UNROLL
+#define MP_XENT_UNROLL 25
+#endif
+  xent_triples_kernel<MP_XENT_UNROLL><<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(T, Vi, v_start, Z_i,
+                                                                                           labels, triples);
   return check_launch("mp_vocab_parallel_xent");
 }
 
