@@ -21,7 +21,11 @@ resident in HBM:
 
 ``value`` is the layer's model TFLOP/s (forward + backward = 3x the forward
 FLOPs, attention counted on the causal half); the vocab cross-entropy's GB/s
-is reported beside it.  Prints one JSON line.
+is reported beside it.  After the timed steps, the sequence-parallel form of
+the same layer share (each 8-way reduce on the rank's 1024 tokens only, an
+all-gather before each column-parallel GEMM) is timed on its own and reported
+as ``sp_layer_ms`` / ``sp_layer_TFLOPS`` (``--no-sp`` skips it).  Prints one
+JSON line.
 """
 
 import argparse
@@ -94,6 +98,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parts", default="layer,vocab,moe")
+    ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel layer timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 256 MiB device copy (the reference kernel for HBM counter calibration)")
     args = ap.parse_args()
@@ -104,7 +109,7 @@ def main():
 
     import torch
     from megatron_tensor_transformer_02_amd import mp, synthetic as S
-    from megatron_tensor_transformer_02_amd.layer import VocabShard, make_ranks, run_ranks
+    from megatron_tensor_transformer_02_amd.layer import VocabShard, make_ranks, make_sp_ranks, run_ranks, run_ranks_sp
 
     torch.cuda.set_device(0)
     rc = mp.mp_device_supported(0)
@@ -302,6 +307,47 @@ def main():
     if roofs:
         out["roofline"] = roofs[0]
         out["rooflines"] = roofs
+
+    if "layer" in parts and not args.no_sp:
+        # The sequence-parallel form of the same rank share (reduce-scatter on
+        # the rank's 1024 tokens, all-gather before the column-parallel GEMMs),
+        # timed on its own after the main steps: rank 0's work, the other 7
+        # ranks' partials and token slices prepared in untimed setup.
+        sp = make_sp_ranks(shards, shared, B, L, hi, d, p=wl.p, seed=wl.seed, offsets=(1, 2))
+        sib_sp = run_ranks_sp(sp, xd, dd)
+        s0 = sp[0]
+
+        def gather0(name):
+            mp.mp_all_gather_rows([r._rows(getattr(r, name)) for r in sp], getattr(s0, name))
+
+        def sp_step():
+            s0.ln1_slice(s0._rows(xd))
+            gather0("h")
+            pa = s0.attn_core()
+            s0.attn_reduce([pa] + sib_sp["attn"][1:], s0._rows(xd))
+            gather0("h2")
+            pm = s0.mlp_partial()
+            s0.mlp_reduce([pm] + sib_sp["mlp"][1:])
+            s0.mlp_bwd_slice(s0._rows(dd))
+            gather0("d_mlp")
+            pb = s0.mlp_bwd_core()
+            s0.mlp_bwd_reduce([pb] + sib_sp["mlp_bwd"][1:], s0._rows(dd))
+            gather0("d_attn")
+            pq = s0.attn_bwd_partial()
+            s0.attn_bwd_reduce([pq] + sib_sp["attn_bwd"][1:], s0._rows(xd))
+
+        for _ in range(args.warmup):
+            sp_step()
+        torch.cuda.synchronize()
+        sev = [(EV(), EV()) for _ in range(args.steps)]
+        for b_, e_ in sev:
+            b_.record(stream)
+            sp_step()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        sp_ms = float(np.mean([b_.elapsed_time(e_) for b_, e_ in sev]))
+        out["sp_layer_ms"] = round(sp_ms, 4)
+        out["sp_layer_TFLOPS"] = round(3 * layer_flops(B, L, K, hi, d, Fi) / (sp_ms * 1e-3) / 1e12, 2)
 
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")

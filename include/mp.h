@@ -195,6 +195,20 @@ int mp_dropout_mask_bwd(mp_dtype dtype, int64_t rows, int64_t cols, const void* 
                         const uint8_t* keep_bits, float p, void* dx, float* dbias, void* ws,
                         size_t ws_bytes, hipStream_t s);
 
+/* All-gather stand-in for the sequence-parallel layer (MLM-notes, "Model
+ * Parallel Transformers": the per-block all-reduce splits into a
+ * reduce-scatter, after which LayerNorm, dropout and the residual work on the
+ * rank's token slice, and an all-gather that restores the full sequence
+ * before the next column-parallel GEMM).  out [N*rows, cols] receives slice j
+ * (a host array of N device pointers, each [rows, cols] dtype) in rows
+ * [j*rows, (j+1)*rows); slices[j] may be those very rows of out.  The
+ * reduce-scatter side needs no call of its own: it is mp_shard_reduce,
+ * mp_shard_reduce_layernorm or their backward on the rank's rows of each
+ * partial, with index_base = first row * cols so the dropout mask is the one
+ * the whole sequence would draw.  1 <= N <= MP_MAX_SHARDS. */
+int mp_all_gather_rows(mp_dtype dtype, int N, int64_t rows, int64_t cols,
+                       const void* const* slices, void* out, hipStream_t s);
+
 /* Column sums of dy [rows,cols] (dtype) into db [cols] fp32: the gradient of
  * a bias added to every row (deterministic, fixed summation order). */
 size_t mp_bias_grad_workspace(int64_t rows, int64_t cols);

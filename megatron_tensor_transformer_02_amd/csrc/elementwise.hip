@@ -232,6 +232,16 @@ int colsum(mp_dtype dt, int64_t rows, int64_t cols, const void* dy, float* out, 
   return check_launch("colsum");
 }
 
+// All-gather stand-in: out rows [j*rows, (j+1)*rows) = slices[j], one 16-byte
+// vector per thread (a slice may be out's own rows: then it copies onto itself).
+__global__ __launch_bounds__(256) void gather_rows_kernel(PtrArray slices, int n, int64_t vec_per_slice,
+                                                          uint4* __restrict__ out) {
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (v >= n * vec_per_slice) return;
+  const int64_t j = v / vec_per_slice;
+  out[v] = static_cast<const uint4*>(slices.p[j])[v - j * vec_per_slice];
+}
+
 // Vocab-parallel embedding: one 16-byte vector of one token's row per thread.
 __global__ __launch_bounds__(256) void embedding_kernel(int64_t nvec, int64_t vec_per_row, int64_t Vi, int64_t v_start,
                                                         const int32_t* __restrict__ ids, const uint4* __restrict__ emb,
@@ -356,6 +366,30 @@ extern "C" int mp_bias_grad(mp_dtype dtype, int64_t rows, int64_t cols, const vo
              "mp_bias_grad: workspace needs %zu bytes", need);
   MP_REQUIRE_OPT_ALIGN(ws);
   return colsum(dtype, rows, cols, dy, db, ws, s);
+}
+
+extern "C" int mp_all_gather_rows(mp_dtype dtype, int N, int64_t rows, int64_t cols, const void* const* slices,
+                                  void* out, hipStream_t s) {
+  static const char* fn = "mp_all_gather_rows";
+  MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype %d", fn, static_cast<int>(dtype));
+  MP_REQUIRE(N >= 1 && N <= MP_MAX_SHARDS, MP_ERR_SHAPE, "%s: N=%d not in [1, %d]", fn, N, MP_MAX_SHARDS);
+  MP_REQUIRE(rows >= 0 && cols > 0 && cols % vec_elems(dtype) == 0, MP_ERR_SHAPE, "%s: bad shape %lld x %lld", fn,
+             (long long)rows, (long long)cols);
+  MP_REQUIRE_PTR(slices);
+  MP_REQUIRE_PTR(out);
+  MP_REQUIRE_ALIGN(out);
+  PtrArray arr{};
+  for (int j = 0; j < N; ++j) {
+    MP_REQUIRE(slices[j] != nullptr, MP_ERR_NULL, "%s: slices[%d] is NULL", fn, j);
+    MP_REQUIRE((reinterpret_cast<uintptr_t>(slices[j]) & 15u) == 0, MP_ERR_ALIGN,
+               "%s: slices[%d] is not 16-byte aligned", fn, j);
+    arr.p[j] = slices[j];
+  }
+  if (rows == 0) return MP_OK;
+  const int64_t vps = rows * cols / vec_elems(dtype);
+  gather_rows_kernel<<<static_cast<unsigned>(ceil_div(N * vps, 256)), 256, 0, s>>>(arr, N, vps,
+                                                                                  static_cast<uint4*>(out));
+  return check_launch(fn);
 }
 
 extern "C" int mp_vocab_parallel_embedding(mp_dtype dtype, int64_t T, int64_t Vi, int64_t v_start, int64_t K,

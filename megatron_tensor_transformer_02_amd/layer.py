@@ -8,7 +8,9 @@ MLP in the forward, two in the backward), so N ranks can be emulated on one
 GPU: run every rank's ``*_partial`` stage, then feed all partials to one
 rank's ``*_reduce`` stage, which calls ``mp_shard_reduce`` or, where a
 LayerNorm follows the reduce, the fused ``mp_shard_reduce_layernorm`` /
-``mp_shard_reduce_layernorm_bwd``.
+``mp_shard_reduce_layernorm_bwd``.  :class:`SPRankLayer` is the
+sequence-parallel form (reduce-scatter and all-gather in place of each
+all-reduce).
 
 Layer (pre-LN; the placement the GPT-2-style block uses):
 ``H1 = X + Drop(sum_i Attn_i(LN1(X)) W_o,i^T + b_o)``,
@@ -73,8 +75,14 @@ class RankLayer:
 
     # ------------------------------------------------------------ forward
     def attn_partial(self, x):
-        s, c = self.s, self.c
+        c = self.c
         mp.mp_layernorm(x, c["ln1_g"], c["ln1_b"], self.h, self.mu1, self.rs1, self.eps)
+        return self.attn_core()
+
+    def attn_core(self):
+        # Attention over this rank's heads of LN1(X) (in self.h), then the
+        # out-projection's partial sum.
+        s = self.s
         mp.mp_head_attention(self.h, s["w_qkv"], s["b_qkv"], self.B, self.L, self.nh, self.d, self.ctx,
                              self.qkv, self.lse, self.causal)
         mp.mp_row_linear_partial(self.ctx, s["w_o"], self.p_attn)
@@ -105,9 +113,12 @@ class RankLayer:
 
     # ----------------------------------------------------------- backward
     def mlp_bwd_partial(self, dout):
-        s, g = self.s, self.g
         # Dropout backward from the saved keep bits, with the bias gradient.
-        mp.mp_dropout_mask_bwd(dout, self.keep_mlp, self.p, self.d_mlp, g["b_b"])
+        mp.mp_dropout_mask_bwd(dout, self.keep_mlp, self.p, self.d_mlp, self.g["b_b"])
+        return self.mlp_bwd_core()
+
+    def mlp_bwd_core(self):
+        s, g = self.s, self.g
         # The GeLU gradient is applied in the epilogue of the row-parallel
         # input-gradient GEMM, so the column backward gets dZ directly.
         mp.mp_row_linear_partial_bwd_dact(self.y, s["w_b"], self.d_mlp, self.z, self.act, self.dy, g["w_b"])
@@ -138,6 +149,116 @@ class RankLayer:
         mp.mp_shard_reduce_layernorm_bwd(partials, x, c["ln1_g"], self.mu1, self.rs1, self.dx, self.dh1, g["ln1_g"],
                                          g["ln1_b"])
         return self.dx
+
+
+class SPRankLayer(RankLayer):
+    """Rank ``r`` of ``n`` in the sequence-parallel form of the same layer
+    (MLM-notes, "Model Parallel Transformers": each all-reduce becomes a
+    reduce-scatter followed, before the next column-parallel GEMM, by an
+    all-gather).  The rank owns tokens ``[r*T/n, (r+1)*T/n)`` for LayerNorm,
+    dropout and the residual; its attention and MLP work on the gathered
+    full sequence exactly as in :class:`RankLayer`.  The reduce-scatter is a
+    shard reduce over the rank's rows of every partial, with the dropout
+    drawn at the global element index; ``mp_all_gather_rows`` stands in for
+    the all-gather.  The replicated parameters' gradients (LayerNorm, the two
+    reduced biases) cover the rank's tokens only: the ranks' values sum to the
+    full gradient (the all-reduce a real run would do)."""
+
+    def __init__(self, shard, shared, B, L, heads, d, rank, n, **kw):
+        super().__init__(shard, shared, B, L, heads, d, **kw)
+        assert (B * L) % n == 0, "tokens must split evenly over the ranks"
+        self.rank, self.n = rank, n
+        self.ts = B * L // n
+        self.r0, self.r1 = rank * self.ts, (rank + 1) * self.ts
+
+    def _rows(self, t):
+        return t[self.r0:self.r1]
+
+    def _bits(self, keep):
+        k = self.K
+        return keep[self.r0 * k // 8:self.r1 * k // 8]
+
+    # ------------------------------------------------------------ forward
+    def ln1_slice(self, x_slice):
+        c = self.c
+        mp.mp_layernorm(x_slice, c["ln1_g"], c["ln1_b"], self._rows(self.h), self._rows(self.mu1),
+                        self._rows(self.rs1), self.eps)
+
+    def attn_reduce(self, partials, x_slice):
+        # Reduce-scatter + bias + dropout + residual on the rank's tokens,
+        # fused with LN2 of those tokens.
+        c = self.c
+        mp.mp_shard_reduce_layernorm([self._rows(p) for p in partials], self._rows(self.h1), c["ln2_g"], c["ln2_b"],
+                                     self._rows(self.h2), self._rows(self.mu2), self._rows(self.rs2), bias=c["b_o"],
+                                     residual=x_slice, p=self.p, seed=self.seed, offset=self.off[0],
+                                     index_base=self.r0 * self.K, mask_out=self._bits(self.keep_attn), eps=self.eps)
+        return self._rows(self.h1)
+
+    def mlp_reduce(self, partials):
+        mp.mp_shard_reduce([self._rows(p) for p in partials], self._rows(self.out), self.c["b_b"],
+                           self._rows(self.h1), self.p, self.seed, self.off[1], self.r0 * self.K,
+                           self._bits(self.keep_mlp))
+        return self._rows(self.out)
+
+    # ----------------------------------------------------------- backward
+    def mlp_bwd_slice(self, dout_slice):
+        mp.mp_dropout_mask_bwd(dout_slice, self._bits(self.keep_mlp), self.p, self._rows(self.d_mlp), self.g["b_b"])
+
+    def mlp_bwd_reduce(self, partials, dout_slice):
+        c, g = self.c, self.g
+        mp.mp_shard_reduce_layernorm_bwd_dropout([self._rows(p) for p in partials], self._rows(self.h1), c["ln2_g"],
+                                                 self._rows(self.mu2), self._rows(self.rs2), self._rows(self.dh1),
+                                                 self.p, self._bits(self.keep_attn), self._rows(self.d_attn),
+                                                 dres=dout_slice, dgamma=g["ln2_g"], dbeta=g["ln2_b"],
+                                                 dbias=g["b_o"])
+        return self._rows(self.dh1)
+
+    def attn_bwd_reduce(self, partials, x_slice):
+        c, g = self.c, self.g
+        mp.mp_shard_reduce_layernorm_bwd([self._rows(p) for p in partials], x_slice, c["ln1_g"], self._rows(self.mu1),
+                                         self._rows(self.rs1), self._rows(self.dx), self._rows(self.dh1),
+                                         g["ln1_g"], g["ln1_b"])
+        return self._rows(self.dx)
+
+
+def gather(ranks, name):
+    """The all-gather of every rank's slice of buffer ``name`` into each rank's
+    full buffer (one ``mp_all_gather_rows`` per rank)."""
+    slices = [r._rows(getattr(r, name)) for r in ranks]
+    for r in ranks:
+        mp.mp_all_gather_rows(slices, getattr(r, name))
+
+
+def run_ranks_sp(ranks, x, dout):
+    """Emulates the n sequence-parallel ranks on one GPU; ``x``, ``dout`` are
+    the full [T, K] input and upstream gradient, of which rank r reads only
+    its token slice.  Returns every stage's partials, as :func:`run_ranks`."""
+    for r in ranks:
+        r.ln1_slice(r._rows(x))
+    gather(ranks, "h")
+    pa = [r.attn_core() for r in ranks]
+    for r in ranks:
+        r.attn_reduce(pa, r._rows(x))
+    gather(ranks, "h2")
+    pm = [r.mlp_partial() for r in ranks]
+    for r in ranks:
+        r.mlp_reduce(pm)
+    for r in ranks:
+        r.mlp_bwd_slice(r._rows(dout))
+    gather(ranks, "d_mlp")
+    pb = [r.mlp_bwd_core() for r in ranks]
+    for r in ranks:
+        r.mlp_bwd_reduce(pb, r._rows(dout))
+    gather(ranks, "d_attn")
+    pq = [r.attn_bwd_partial() for r in ranks]
+    for r in ranks:
+        r.attn_bwd_reduce(pq, r._rows(x))
+    return {"attn": pa, "mlp": pm, "mlp_bwd": pb, "attn_bwd": pq}
+
+
+def make_sp_ranks(shards, shared, B, L, heads_per_rank, d, **kw):
+    n = len(shards)
+    return [SPRankLayer(sh, shared, B, L, heads_per_rank, d, i, n, **kw) for i, sh in enumerate(shards)]
 
 
 def make_ranks(shards, shared, B, L, heads_per_rank, d, **kw):

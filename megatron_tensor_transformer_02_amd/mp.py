@@ -52,6 +52,7 @@ _SIGS = {
                                               c_p, c_p, c_sz, c_p]),
     "mp_shard_reduce_layernorm_bwd_dropout": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                                       c_p, c_p, c_f32, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "mp_all_gather_rows": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p]),
     "mp_dropout_mask_bwd_workspace": (c_sz, [c_i64, c_i64]),
     "mp_dropout_mask_bwd": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_f32, c_p, c_p, c_p, c_sz, c_p]),
     "mp_bias_grad_workspace": (c_sz, [c_i64, c_i64]),
@@ -247,6 +248,11 @@ def mp_shard_reduce_layernorm_bwd_dropout(partials, x, gamma, mean, rstd, dx, p,
     _call("mp_shard_reduce_layernorm_bwd_dropout", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
           _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), p, _p(keep_bits), _p(ddrop), _p(dbias), _p(ws),
           need if ws is not None else 0, _s(stream))
+
+
+def mp_all_gather_rows(slices, out, stream=None):
+    rows, cols = slices[0].shape
+    _call("mp_all_gather_rows", _dt(out), len(slices), rows, cols, _ptr_array(slices), _p(out), _s(stream))
 
 
 def mp_dropout_mask_bwd(dy, keep_bits, p, dx, dbias=None, ws=None, stream=None):

@@ -93,6 +93,37 @@ def test_shard_reduce_validation(lib):
     assert rc == 0
 
 
+def test_gather_and_dropout_bwd_validation(lib):
+    arr = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED)
+    rc, msg = call(lib, "mp_all_gather_rows", mp.MP_BF16, 0, 4, 8, arr, ALIGNED, None)
+    assert rc == -2 and "N=0" in msg
+    rc, _ = call(lib, "mp_all_gather_rows", mp.MP_BF16, 2, 4, 12, arr, ALIGNED, None)
+    assert rc == -2  # cols not a multiple of 8
+    bad = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED + 4)
+    rc, msg = call(lib, "mp_all_gather_rows", mp.MP_BF16, 2, 4, 8, bad, ALIGNED, None)
+    assert rc == -5 and "slices[1]" in msg
+    rc, _ = call(lib, "mp_all_gather_rows", mp.MP_BF16, 2, 0, 8, arr, ALIGNED, None)
+    assert rc == 0  # zero rows: nothing to do
+    rc, msg = call(lib, "mp_dropout_mask_bwd", mp.MP_BF16, 4, 8, ALIGNED, None, ctypes.c_float(0.1), ALIGNED, None,
+                   None, 0, None)
+    assert rc == -1 and "keep_bits" in msg
+    rc, _ = call(lib, "mp_dropout_mask_bwd", mp.MP_BF16, 4, 8, ALIGNED, ALIGNED, ctypes.c_float(1.0), ALIGNED, None,
+                 None, 0, None)
+    assert rc == -8  # p must be < 1
+    rc, msg = call(lib, "mp_dropout_mask_bwd", mp.MP_BF16, 4, 8, ALIGNED, ALIGNED, ctypes.c_float(0.1), ALIGNED,
+                   ALIGNED, None, 0, None)
+    assert rc == -6 and "workspace" in msg  # dbias needs the column-sum workspace
+    rc, msg = call(lib, "mp_shard_reduce_layernorm_bwd_dropout", mp.MP_BF16, 2, 4, 8, arr, ALIGNED, ALIGNED, ALIGNED,
+                   ALIGNED, None, ALIGNED, None, None, ctypes.c_float(0.1), None, ALIGNED, None, None, 0, None)
+    assert rc == -1 and "keep_bits" in msg
+    rc, msg = call(lib, "mp_row_linear_partial_bwd_dact", mp.MP_BF16, 16, 16, 16, ALIGNED, ALIGNED, ALIGNED, None,
+                   1, ALIGNED, ALIGNED, None, 0, None)
+    assert rc == -1 and "Z_save" in msg
+    rc, _ = call(lib, "mp_row_linear_partial_bwd_dact", mp.MP_BF16, 16, 16, 16, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                 0, ALIGNED, ALIGNED, None, 0, None)
+    assert rc == -8  # act must be a GeLU
+
+
 def test_linear_validation(lib):
     rc, _ = call(lib, "mp_column_linear_gelu", mp.MP_BF16, mp.MP_BF16, 16, 12, 16, ALIGNED, ALIGNED, None, 1,
                  ALIGNED, None, None)

@@ -152,3 +152,22 @@ def test_bias_grad(dtype, rows, cols):
     sync()
     want = O.bias_grad(f64(dy)) if rows else np.zeros(cols)
     assert rel_frobenius(f64(db), want) <= 1e-5 or np.allclose(f64(db), want, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype,n,rows,cols", [("bf16", 8, 1024, 3072), ("f32", 3, 5, 12), ("bf16", 1, 7, 8)])
+def test_all_gather_rows_exact(dtype, n, rows, cols):
+    """The all-gather stand-in: slice j lands in rows [j*rows, (j+1)*rows),
+    bit for bit, also when a slice is already the output's own rows."""
+    say("all-gather", dtype, n, rows, cols)
+    slices = [cu(randn(300 + j, (rows, cols), dtype)) for j in range(n)]
+    out = torch.empty((n * rows, cols), dtype=tdtype(dtype), device="cuda")
+    mp.mp_all_gather_rows(slices, out)
+    sync()
+    assert torch.equal(out, torch.cat(slices))
+    # in place: the last slice is out's own rows
+    out2 = torch.zeros_like(out)
+    own = out2[(n - 1) * rows:]
+    own.copy_(slices[-1])
+    mp.mp_all_gather_rows(slices[:-1] + [own], out2)
+    sync()
+    assert torch.equal(out2, out)
