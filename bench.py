@@ -25,7 +25,9 @@ is reported beside it.  After the timed steps, the sequence-parallel form of
 the same layer share (each 8-way reduce on the rank's 1024 tokens only, an
 all-gather before each column-parallel GEMM) is timed on its own and reported
 as ``sp_layer_ms`` / ``sp_layer_TFLOPS`` (``--no-sp`` skips it).  Prints one
-JSON line.
+JSON line.  ``logits_xent_fused_us`` / ``logits_xent_unfused_us`` time the
+vocab shard's logits GEMM + statistics with the statistics fused into the
+GEMM's epilogue (no logits stored) and as two passes.
 """
 
 import argparse
@@ -294,6 +296,20 @@ def main():
         del flush
         cold_ms = float(np.median(cold))
         out["xent_cold_GBps"] = round(xbytes / (cold_ms * 1e-3) / 1e9, 1)
+        # The logits GEMM with the statistics fused into its epilogue, against
+        # the unfused pair (logits GEMM writing the fp32 logits + the triples
+        # pass reading them back), each timed on its own.
+        def timed_us(fn, reps=10):
+            evs = [(EV(), EV()) for _ in range(reps)]
+            for b_, e_ in evs:
+                b_.record(stream)
+                fn()
+                e_.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([b_.elapsed_time(e_) for b_, e_ in evs])) * 1e3
+        v0.logits_triples(hidden, labels)
+        out["logits_xent_fused_us"] = round(timed_us(lambda: v0.logits_triples(hidden, labels)), 1)
+        out["logits_xent_unfused_us"] = round(timed_us(lambda: (v0.logits(hidden), v0.triples(labels))), 1)
         roofs.append({"kernel": "vocab xent triples (xent_triples_kernel) [8192x6400] fp32", "bound": "hbm",
                       "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                       "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "avg_launch_us": round(x_ms * 1e3, 2),

@@ -265,6 +265,23 @@ int mp_vocab_parallel_embedding(mp_dtype dtype, int64_t T, int64_t Vi, int64_t v
 int mp_vocab_parallel_xent(int64_t T, int64_t Vi, int64_t v_start, const float* Z_i,
                            const int32_t* labels, float* triples, hipStream_t s);
 
+/* The logits GEMM and the per-shard statistics in one pass (a11 + a12 fused;
+ * MLM-notes, output paragraph: each shard reduces its own logits so only
+ * (max, sum, target) triples cross GPUs, never the [T, V_i] logits).  The
+ * fp32 logits Z_i = H * E_i^T live only in the GEMM's accumulators: its
+ * epilogue folds every row over each wave's columns into (max, exp-sum,
+ * target logit) partials in the workspace, and a second pass folds those in a
+ * fixed order into triples [T, 3] fp32 exactly as mp_vocab_parallel_xent
+ * defines them (up to summation order), so the 4*T*V_i-byte logits round
+ * trip disappears.  H [T, K] bf16, E_i [V_i, K] bf16 (K % 8 == 0), labels
+ * [T] int32 (global ids), v_start as in mp_vocab_parallel_xent.  bf16 only.
+ * ws: mp_vocab_parallel_logits_xent_workspace bytes.  (The backward still
+ * needs the logits: recompute them, or use the unfused calls.) */
+size_t mp_vocab_parallel_logits_xent_workspace(int64_t T, int64_t K, int64_t Vi);
+int mp_vocab_parallel_logits_xent(mp_dtype dtype, int64_t T, int64_t K, int64_t Vi, int64_t v_start,
+                                  const void* H, const void* E_i, const int32_t* labels,
+                                  float* triples, void* ws, size_t ws_bytes, hipStream_t s);
+
 /* Combine N shards' triples into the loss: M = max_j m_j,
  * S = sum_j s_j exp(m_j - M), loss[t] = ln S + M - sum_j tgt_j.  triples: host
  * array of N device pointers to [T,3] fp32; loss [T] fp32; stats [T,2] fp32

@@ -42,6 +42,10 @@ struct GemmArgs {
   int act;
   int out_bf16;
   int tiles_m, tiles_n, group_m;
+  const int32_t* labels;  // [M] (EPI_LSE)
+  int64_t v_start;        // first vocabulary row of the shard (EPI_LSE)
+  float* lse_part;        // [M, lse_slots, 3] (EPI_LSE)
+  int lse_slots;
 };
 
 // Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs;
@@ -193,6 +197,60 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
   }
   wait_vm_lds();  // the trailing (all-zero) loads write LDS the epilogue reuses
   __syncthreads();
+
+  // Row statistics of the fp32 logits instead of a store.  Each 32-row strip
+  // of the wave's tile goes through the wave-private LDS strip (as in the
+  // store epilogue below); there, lanes 2q and 2q+1 own strip row q and fold
+  // half of its WN columns each, then combine with one exchange.
+  if constexpr (EPI == EPI_LSE) {
+    constexpr float kL2e = 1.4426950408889634f;
+    constexpr int SP = WN + 4, HC = WN / 2;
+    static_assert(HC % 4 == 0, "half a wave column must be whole float4s");
+    float* strip = reinterpret_cast<float*>(&lds[0][0]) + wave * 32 * SP;
+    const int rr = lane >> 1, hh = lane & 1;
+    const int64_t c0 = n0 + wn * WN + hh * HC;  // first column of this lane's half
+    const int slot = tni * WC + wn;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) strip[mfma_row(r, lane) * SP + j * 32 + (lane & 31)] = acc[i][j][r];
+      __builtin_amdgcn_wave_barrier();
+      const int64_t row = m0 + wm * WM + i * 32 + rr;
+      const int64_t lab = row < g.M ? static_cast<int64_t>(g.labels[row]) - g.v_start : -1;
+      float v[HC];
+#pragma unroll
+      for (int q = 0; q < HC / 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(strip + rr * SP + hh * HC + 4 * q);
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < HC; ++c)
+        if (c0 + c < g.N) mx = fmaxf(mx, v[c]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      float se = 0.0f, tg = 0.0f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int c = 0; c < HC; ++c)
+          if (c0 + c < g.N) {
+            se += exp2f((v[c] - mx) * kL2e);
+            if (c0 + c == lab) tg = v[c];
+          }
+      }
+      se += __shfl_xor(se, 1, 64);
+      tg += __shfl_xor(tg, 1, 64);
+      if (hh == 0 && row < g.M) {
+        float* pp = g.lse_part + (row * g.lse_slots + slot) * 3;
+        pp[0] = mx;
+        pp[1] = se;
+        pp[2] = tg;
+      }
+    }
+    return;
+  }
 
   // Bias: lane l holds column (l % 32) of every 32x32 accumulator tile, so
   // the bias is added in registers before the epilogue (one value per tile
@@ -472,7 +530,9 @@ static void launch_bf16_layout(const GemmArgs& g, const Plan& p, hipStream_t s) 
 // Instantiated combinations: the forward (NT) with each activation, the
 // input-gradient (NN) and weight-gradient (TN, plain or split-K) GEMMs.
 static void launch_bf16(Layout lay, int epi, int act, const GemmArgs& g, const Plan& p, hipStream_t s) {
-  if (lay == NT) {
+  if (lay == NT && epi == EPI_LSE) {
+    launch_bf16_layout<true, true, EPI_LSE, MP_ACT_NONE>(g, p, s);
+  } else if (lay == NT) {
     if (act == MP_ACT_GELU_ERF) launch_bf16_layout<true, true, EPI_STORE, MP_ACT_GELU_ERF>(g, p, s);
     else if (act == MP_ACT_GELU_TANH) launch_bf16_layout<true, true, EPI_STORE, MP_ACT_GELU_TANH>(g, p, s);
     else launch_bf16_layout<true, true, EPI_STORE, MP_ACT_NONE>(g, p, s);
@@ -550,6 +610,31 @@ int gemm(mp_dtype dt, Layout lay, int64_t M, int64_t N, int64_t K, const void* A
 }
 
 size_t gemm_splitk_workspace(mp_dtype dt, int64_t M, int64_t N, int64_t K) { return splitk_bytes(dt, M, N, K); }
+
+// Wave columns per tile of each tile shape (see launch_bf16_tile).
+static int wave_cols(const Plan& p) { return p.bm == 128 ? 2 : (p.bn == 256 ? 4 : 2); }
+
+int gemm_lse_slots(int64_t T, int64_t V, int64_t K) {
+  const Plan p = plan_bf16(T, V, K, false, NT);
+  return static_cast<int>(ceil_div(V, p.bn)) * wave_cols(p);
+}
+
+int gemm_logits_lse(int64_t T, int64_t V, int64_t K, const void* H, const void* E, const int32_t* labels,
+                    int64_t v_start, float* part, hipStream_t s) {
+  if (T == 0) return MP_OK;
+  GemmArgs g{};
+  g.M = T; g.N = V; g.K = K; g.A = H; g.lda = K; g.B = E; g.ldb = K; g.ldc = V;
+  g.out_bf16 = 1;
+  g.labels = labels; g.v_start = v_start; g.lse_part = part;
+  const Plan p = plan_bf16(T, V, K, false, NT);
+  g.tiles_m = static_cast<int>(ceil_div(T, p.bm));
+  g.tiles_n = static_cast<int>(ceil_div(V, p.bn));
+  g.group_m = 8;
+  g.k_split = p.k_split;
+  g.lse_slots = g.tiles_n * wave_cols(p);
+  launch_bf16(NT, EPI_LSE, MP_ACT_NONE, g, p, s);
+  return check_launch("gemm_logits_lse");
+}
 
 static int validate_mat(mp_dtype dt, int64_t contiguous, const char* fn, const char* what) {
   MP_REQUIRE(contiguous % vec_elems(dt) == 0, MP_ERR_SHAPE, "%s: %s=%lld must be a multiple of %lld", fn, what,

@@ -5,6 +5,7 @@
 // 16-byte loads (a round of them in flight per lane) and keeps an online
 // (max, scaled exp-sum) pair per lane, folded across the wave with shuffles.
 #include "common.h"
+#include "gemm.h"
 
 namespace mp {
 
@@ -68,6 +69,34 @@ __global__ __launch_bounds__(256) void xent_triples_kernel(int64_t T, int64_t Vi
     triples[row * 3 + 0] = m;
     triples[row * 3 + 1] = s;
     triples[row * 3 + 2] = tgt;
+  }
+}
+
+// The fused logits GEMM's per-slot row statistics folded into the shard's
+// triple (max, exp-sum, target logit): one wave per row, lane l merges slots
+// l, l+64, ... in order, then a fixed butterfly merges the lanes.
+__global__ __launch_bounds__(256) void lse_fold_kernel(int64_t T, int P, const float* __restrict__ part,
+                                                       float* __restrict__ triples) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* pp = part + t * P * 3;
+  float m = -INFINITY, s = 0.0f, tg = 0.0f;
+  for (int k = lane; k < P; k += 64) {
+    lse_merge(m, s, pp[3 * k], pp[3 * k + 1]);
+    tg += pp[3 * k + 2];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const float s2 = __shfl_xor(s, o, 64);
+    lse_merge(m, s, m2, s2);
+    tg += __shfl_xor(tg, o, 64);
+  }
+  if (lane == 0) {
+    triples[t * 3 + 0] = m;
+    triples[t * 3 + 1] = s;
+    triples[t * 3 + 2] = tg;
   }
 }
 
@@ -160,6 +189,35 @@ extern "C" int mp_vocab_parallel_xent(int64_t T, int64_t Vi, int64_t v_start, co
   xent_triples_kernel<MP_XENT_UNROLL><<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(T, Vi, v_start, Z_i,
                                                                                            labels, triples);
   return check_launch("mp_vocab_parallel_xent");
+}
+
+extern "C" size_t mp_vocab_parallel_logits_xent_workspace(int64_t T, int64_t K, int64_t Vi) {
+  if (T <= 0 || K <= 0 || Vi <= 0) return 0;
+  return align_up(static_cast<size_t>(T) * gemm_lse_slots(T, Vi, K) * 3 * sizeof(float), 256);
+}
+
+extern "C" int mp_vocab_parallel_logits_xent(mp_dtype dtype, int64_t T, int64_t K, int64_t Vi, int64_t v_start,
+                                             const void* H, const void* E_i, const int32_t* labels, float* triples,
+                                             void* ws, size_t ws_bytes, hipStream_t s) {
+  static const char* fn = "mp_vocab_parallel_logits_xent";
+  MP_REQUIRE(dtype == MP_BF16, MP_ERR_DTYPE, "%s: the fused logits GEMM runs in bf16 only", fn);
+  MP_REQUIRE(T >= 0 && K > 0 && Vi > 0 && v_start >= 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  MP_REQUIRE(K % 8 == 0, MP_ERR_SHAPE, "%s: K=%lld must be a multiple of 8", fn, (long long)K);
+  MP_REQUIRE_PTR(H);
+  MP_REQUIRE_PTR(E_i);
+  MP_REQUIRE_PTR(labels);
+  MP_REQUIRE_PTR(triples);
+  MP_REQUIRE_ALIGN(H);
+  MP_REQUIRE_ALIGN(E_i);
+  const size_t need = mp_vocab_parallel_logits_xent_workspace(T, K, Vi);
+  MP_REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn,
+             need);
+  MP_REQUIRE_OPT_ALIGN(ws);
+  if (T == 0) return MP_OK;
+  float* part = static_cast<float*>(ws);
+  if (int rc = gemm_logits_lse(T, Vi, K, H, E_i, labels, v_start, part, s)) return rc;
+  lse_fold_kernel<<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(T, gemm_lse_slots(T, Vi, K), part, triples);
+  return check_launch(fn);
 }
 
 extern "C" int mp_vocab_xent_combine(int N, int64_t T, const float* const* triples, float* loss, float* stats,

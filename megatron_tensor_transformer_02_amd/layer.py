@@ -319,6 +319,12 @@ class VocabShard:
         mp.mp_vocab_parallel_xent(self.z, labels, self.v0, self.tr)
         return self.tr
 
+    def logits_triples(self, hidden, labels):
+        # The logits GEMM and the shard's statistics in one pass (no logits
+        # stored): for a forward that needs the loss but not dZ.
+        mp.mp_vocab_parallel_logits_xent(hidden, self.E, labels, self.v0, self.tr)
+        return self.tr
+
     def combine(self, triples):
         mp.mp_vocab_xent_combine(triples, self.loss, self.stats, self.mean)
         return self.loss

@@ -53,6 +53,8 @@ _SIGS = {
     "mp_shard_reduce_layernorm_bwd_dropout": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                                       c_p, c_p, c_f32, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "mp_all_gather_rows": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p]),
+    "mp_vocab_parallel_logits_xent_workspace": (c_sz, [c_i64, c_i64, c_i64]),
+    "mp_vocab_parallel_logits_xent": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "mp_dropout_mask_bwd_workspace": (c_sz, [c_i64, c_i64]),
     "mp_dropout_mask_bwd": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_f32, c_p, c_p, c_p, c_sz, c_p]),
     "mp_bias_grad_workspace": (c_sz, [c_i64, c_i64]),
@@ -304,6 +306,15 @@ def mp_vocab_parallel_embedding(ids, E_i, v_start, out_partial, stream=None):
 def mp_vocab_parallel_xent(Z_i, labels, v_start, triples, stream=None):
     T, Vi = Z_i.shape
     _call("mp_vocab_parallel_xent", T, Vi, v_start, _p(Z_i), _p(labels), _p(triples), _s(stream))
+
+
+def mp_vocab_parallel_logits_xent(H, E_i, labels, v_start, triples, ws=None, stream=None):
+    T, K = H.shape
+    Vi = E_i.shape[0]
+    need = lib().mp_vocab_parallel_logits_xent_workspace(T, K, Vi)
+    ws = ws if ws is not None else workspace(need, H.device)
+    _call("mp_vocab_parallel_logits_xent", _dt(H), T, K, Vi, v_start, _p(H), _p(E_i), _p(labels), _p(triples), _p(ws),
+          need if ws is not None else 0, _s(stream))
 
 
 def mp_vocab_xent_combine(triples, loss, stats=None, mean_loss=None, stream=None):

@@ -84,3 +84,37 @@ def test_xent_zero_logits_is_log_v():
     mp.mp_vocab_xent_combine(trip, loss)
     sync()
     assert np.max(np.abs(f64(loss) - np.log(V))) <= 1e-5
+
+
+@pytest.mark.parametrize("T,K,V,n", [(300, 264, 4000, 4), (77, 64, 968, 8), (513, 1024, 6400, 1), (8192, 3072, 51200, 8)])
+def test_fused_logits_xent(T, K, V, n):
+    """The logits GEMM with the per-shard statistics in its epilogue (no
+    logits stored): each shard's triples against the oracle's triples of the
+    fp64 logits of the same bf16 inputs (max and target to fp32 rounding of
+    the dot product, exp-sum to fp32), and the combined per-token loss within
+    the cross-entropy bound.  Ragged T, V (not multiples of the tile) and K."""
+    say("fused logits+xent", T, K, V, n)
+    rng = np.random.default_rng(T + V)
+    h = torch.from_numpy(rng.standard_normal((T, K), dtype=np.float32)).to(torch.bfloat16)
+    emb = torch.from_numpy((rng.standard_normal((V, K), dtype=np.float32) * 0.05)).to(torch.bfloat16)
+    labels = torch.from_numpy(rng.integers(0, V, size=T).astype(np.int32))
+    vi = V // n
+    hd, ed, ld = cu(h), cu(emb), cu(labels)
+    trip = [torch.empty((T, 3), dtype=torch.float32, device="cuda") for _ in range(n)]
+    for i in range(n):
+        mp.mp_vocab_parallel_logits_xent(hd, ed[i * vi:(i + 1) * vi], ld, i * vi, trip[i])
+    loss = torch.empty(T, dtype=torch.float32, device="cuda")
+    mp.mp_vocab_xent_combine(trip, loss)
+    sync()
+    rows = np.arange(T) if T <= 1024 else np.random.default_rng(0).choice(T, 96, replace=False)
+    z64 = f64(h)[rows] @ f64(emb).T
+    lab = labels.numpy()[rows]
+    for i in (0, n - 1):
+        want = O.vocab_parallel_xent_triples(z64[:, i * vi:(i + 1) * vi], lab, i * vi)
+        got = f64(trip[i])[rows]
+        scale = np.abs(z64).max()
+        assert np.max(np.abs(got[:, 0] - want[:, 0])) <= 1e-5 * scale
+        assert np.max(np.abs(got[:, 2] - want[:, 2])) <= 1e-5 * scale
+        assert rel_frobenius(got[:, 1], want[:, 1]) <= 1e-4
+    want_loss = O.full_cross_entropy(z64, lab)
+    assert np.max(np.abs(f64(loss)[rows] - want_loss)) <= XENT_ABS
