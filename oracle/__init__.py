@@ -40,7 +40,7 @@ from .layer import (
     head_attention_bwd, layer_forward, layer_backward, bias_grad,
 )
 from .vocab import (
-    embedding, vocab_parallel_embedding, full_cross_entropy, full_cross_entropy_grad,
+    embedding, vocab_parallel_embedding, vocab_parallel_embedding_bwd, full_cross_entropy, full_cross_entropy_grad,
     vocab_parallel_xent_triples, vocab_xent_combine, vocab_parallel_xent_bwd,
 )
 from .moe import moe_permutation, expert_swiglu_ffn, moe_forward, moe_forward_rows

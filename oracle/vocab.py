@@ -36,6 +36,22 @@ def vocab_parallel_embedding(ids, emb_shard, v_start):
     return out
 
 
+def vocab_parallel_embedding_bwd(ids, d_out, vi, v_start):
+    """Gradient of one rank's partial lookup with respect to its shard: the
+    lookup copies row ``id - v_start`` into token t's output, so row v of the
+    gradient is the sum of ``d_out[t]`` over the tokens t whose id is
+    ``v_start + v`` (zero for rows no token picked).  Summed token by token in
+    ascending order."""
+    ids = np.asarray(ids, dtype=np.int64)
+    d_out = _f64(d_out)
+    grad = np.zeros((vi, d_out.shape[1]))
+    for t in range(ids.size):
+        v = ids[t] - v_start
+        if 0 <= v < vi:
+            grad[v] += d_out[t]
+    return grad
+
+
 def full_cross_entropy(logits, labels):
     """Per-token softmax cross-entropy over the full vocabulary:
     ``log(sum_v exp(z_v)) - z_label``, the max subtracted inside the log."""

@@ -42,6 +42,31 @@ def test_embedding_split_sums_exactly(n):
     assert np.array_equal(O.embedding(ids, emb), emb[ids])
 
 
+@pytest.mark.parametrize("n", [1, 4])
+def test_embedding_backward_is_the_lookup_adjoint(n):
+    # <lookup(E), G> = <E, lookup_bwd(G)> for every shard (the adjoint of a
+    # linear map is its gradient), the shards' gradients stacked equal
+    # torch's embedding gradient, and a hand case sums repeated ids.
+    rng = np.random.default_rng(11)
+    T, V, K = 37, 24, 5
+    ids = rng.integers(0, V, size=T)
+    emb = rng.standard_normal((V, K))
+    g = rng.standard_normal((T, K))
+    vi = V // n
+    grads = []
+    for i in range(n):
+        sh = emb[i * vi:(i + 1) * vi]
+        lhs = np.sum(O.vocab_parallel_embedding(ids, sh, i * vi) * g)
+        gi = O.vocab_parallel_embedding_bwd(ids, g, vi, i * vi)
+        assert abs(lhs - np.sum(sh * gi)) <= 1e-12 * (1 + abs(lhs))
+        grads.append(gi)
+    e = torch.tensor(emb, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.embedding(torch.tensor(ids), e).backward(torch.tensor(g))
+    assert np.allclose(np.concatenate(grads), e.grad.numpy(), rtol=0, atol=1e-12)
+    hand = O.vocab_parallel_embedding_bwd([2, 0, 2, 5], np.array([[1.0], [10.0], [100.0], [7.0]]), 4, 0)
+    assert np.array_equal(hand[:, 0], [10.0, 0.0, 101.0, 0.0])
+
+
 def test_cross_entropy_matches_torch_and_closed_forms():
     z = rnd(17, 50) * 3
     y = RNG.integers(0, 50, size=17)
