@@ -27,7 +27,9 @@ all-gather before each column-parallel GEMM) is timed on its own and reported
 as ``sp_layer_ms`` / ``sp_layer_TFLOPS`` (``--no-sp`` skips it).  Prints one
 JSON line.  ``logits_xent_fused_us`` / ``logits_xent_unfused_us`` time the
 vocab shard's logits GEMM + statistics with the statistics fused into the
-GEMM's epilogue (no logits stored) and as two passes.
+GEMM's epilogue (no logits stored) and as two passes; ``embedding_bwd_us``
+the vocab shard's embedding backward (token-order scatter-add, accumulating
+into its fp32 gradient).
 """
 
 import argparse
@@ -310,6 +312,12 @@ def main():
         v0.logits_triples(hidden, labels)
         out["logits_xent_fused_us"] = round(timed_us(lambda: v0.logits_triples(hidden, labels)), 1)
         out["logits_xent_unfused_us"] = round(timed_us(lambda: (v0.logits(hidden), v0.triples(labels))), 1)
+        # The embedding's backward into the shard's fp32 gradient (accumulating,
+        # as onto the tied logits weight's gradient).
+        de = torch.zeros((Vi, Kv), dtype=torch.float32, device="cuda")
+        out["embedding_bwd_us"] = round(timed_us(lambda: mp.mp_vocab_parallel_embedding_bwd(
+            ids, hidden, v0.v0, de, accumulate=True)), 1)
+        del de
         roofs.append({"kernel": "vocab xent triples (xent_triples_kernel) [8192x6400] fp32", "bound": "hbm",
                       "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                       "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "avg_launch_us": round(x_ms * 1e3, 2),

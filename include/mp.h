@@ -255,6 +255,19 @@ int mp_vocab_parallel_embedding(mp_dtype dtype, int64_t T, int64_t Vi, int64_t v
                                 int64_t K, const int32_t* ids, const void* E_i,
                                 void* out_partial, hipStream_t s);
 
+/* Backward of mp_vocab_parallel_embedding with respect to the rank's shard
+ * (MLM-notes, "Model Parallel Transformers", embedding paragraph; with the
+ * output layer's tied weight, the embedding's and the logits GEMM's
+ * gradients of E_i add up):
+ *   dE_i[v] (+)= sum of dOut[t] over tokens t with ids[t] = v_start + v,
+ *                in ascending t (deterministic; rows no token picked get 0,
+ *                or keep their value when accumulate != 0).
+ * ids [T] int32, dOut [T, K] dtype (the gradient of the reduced embedding,
+ * replicated on every rank), dE_i [Vi, K] fp32, K % 8 == 0. */
+int mp_vocab_parallel_embedding_bwd(mp_dtype dtype, int64_t T, int64_t Vi, int64_t v_start,
+                                    int64_t K, const int32_t* ids, const void* dOut, float* dE_i,
+                                    int accumulate, hipStream_t s);
+
 /* Per-shard cross-entropy statistics (MLM-notes, "Model Parallel
  * Transformers", output paragraph: each GPU computes its exponentials, then
  * the row sums are combined).  One pass over the rank's fp32 logits

@@ -232,6 +232,88 @@ int colsum(mp_dtype dt, int64_t rows, int64_t cols, const void* dy, float* out, 
   return check_launch("colsum");
 }
 
+// Embedding backward (the lookup's adjoint, a deterministic scatter-add):
+// block b owns shard rows [16b, 16b+16).  Tokens are taken in chunks of
+// 8192; a chunk's tokens whose row falls in the block's range are compacted
+// into LDS in token order (per-thread counts and an exclusive scan), then each
+// of the block's rows adds its tokens' gradient rows in that order, one
+// 16-byte vector of columns per thread.  No atomics: the sums are fixed-order.
+template <bool BF16>
+__global__ __launch_bounds__(256) void embedding_bwd_kernel(int64_t T, int64_t Vi, int64_t v_start, int64_t K,
+                                                            const int32_t* __restrict__ ids,
+                                                            const void* __restrict__ dout, float* __restrict__ dE,
+                                                            int accumulate) {
+  using V = Vec16<BF16>;
+  constexpr int E = V::N, R = 16, CH = 8192, TPT = CH / 256;
+  __shared__ int list[CH];  // (token within the chunk) * R + (row within the block)
+  __shared__ int offs[257];
+  const int tid = threadIdx.x;
+  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * R;
+  const int rows = static_cast<int>(Vi - v0 < R ? Vi - v0 : R);
+  const int64_t nvec = K / E;
+  for (int64_t c0 = 0; c0 < T || c0 == 0; c0 += CH) {  // T = 0 still writes the zero rows
+    int n = 0;
+#pragma unroll 4
+    for (int u = 0; u < TPT; ++u) {
+      const int64_t t = c0 + tid * TPT + u;
+      if (t < T) {
+        const int64_t v = static_cast<int64_t>(ids[t]) - v_start - v0;
+        n += (v >= 0 && v < rows) ? 1 : 0;
+      }
+    }
+    offs[tid] = n;
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int i = 0; i < 256; ++i) {
+        const int x = offs[i];
+        offs[i] = acc;
+        acc += x;
+      }
+      offs[256] = acc;
+    }
+    __syncthreads();
+    int pos = offs[tid];
+    for (int u = 0; u < TPT; ++u) {
+      const int64_t t = c0 + tid * TPT + u;
+      if (t < T) {
+        const int64_t v = static_cast<int64_t>(ids[t]) - v_start - v0;
+        if (v >= 0 && v < rows) list[pos++] = (tid * TPT + u) * R + static_cast<int>(v);
+      }
+    }
+    __syncthreads();
+    const int L = offs[256];
+    for (int r = 0; r < rows; ++r) {
+      float* drow = dE + (v0 + r) * K;
+      for (int64_t cv = tid; cv < nvec; cv += 256) {
+        float acc[E];
+        if (c0 == 0 && !accumulate) {
+#pragma unroll
+          for (int i = 0; i < E; ++i) acc[i] = 0.0f;
+        } else {
+#pragma unroll
+          for (int i = 0; i < E; i += 4) {
+            const float4 f = *reinterpret_cast<const float4*>(drow + cv * E + i);
+            acc[i] = f.x; acc[i + 1] = f.y; acc[i + 2] = f.z; acc[i + 3] = f.w;
+          }
+        }
+        for (int e = 0; e < L; ++e) {
+          const int x = list[e];
+          if ((x & (R - 1)) != r) continue;
+          float g[E];
+          V::load(dout, (c0 + (x >> 4)) * K + cv * E, g);
+#pragma unroll
+          for (int i = 0; i < E; ++i) acc[i] += g[i];
+        }
+#pragma unroll
+        for (int i = 0; i < E; i += 4)
+          *reinterpret_cast<float4*>(drow + cv * E + i) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+      }
+    }
+    __syncthreads();  // the next chunk reuses list and offs
+  }
+}
+
 // All-gather stand-in: out rows [j*rows, (j+1)*rows) = slices[j], one 16-byte
 // vector per thread (a slice may be out's own rows: then it copies onto itself).
 __global__ __launch_bounds__(256) void gather_rows_kernel(PtrArray slices, int n, int64_t vec_per_slice,
@@ -366,6 +448,25 @@ extern "C" int mp_bias_grad(mp_dtype dtype, int64_t rows, int64_t cols, const vo
              "mp_bias_grad: workspace needs %zu bytes", need);
   MP_REQUIRE_OPT_ALIGN(ws);
   return colsum(dtype, rows, cols, dy, db, ws, s);
+}
+
+extern "C" int mp_vocab_parallel_embedding_bwd(mp_dtype dtype, int64_t T, int64_t Vi, int64_t v_start, int64_t K,
+                                               const int32_t* ids, const void* dOut, float* dE_i, int accumulate,
+                                               hipStream_t s) {
+  static const char* fn = "mp_vocab_parallel_embedding_bwd";
+  MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype %d", fn, static_cast<int>(dtype));
+  MP_REQUIRE(T >= 0 && Vi > 0 && v_start >= 0 && K > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  MP_REQUIRE(K % 8 == 0, MP_ERR_SHAPE, "%s: K=%lld must be a multiple of 8", fn, (long long)K);
+  MP_REQUIRE(T == 0 || (ids != nullptr && dOut != nullptr), MP_ERR_NULL, "%s: ids and dOut must be non-NULL", fn);
+  MP_REQUIRE_PTR(dE_i);
+  MP_REQUIRE_OPT_ALIGN(dOut);
+  MP_REQUIRE_ALIGN(dE_i);
+  const unsigned grid = static_cast<unsigned>(ceil_div(Vi, 16));
+  if (dtype == MP_BF16)
+    embedding_bwd_kernel<true><<<grid, 256, 0, s>>>(T, Vi, v_start, K, ids, dOut, dE_i, accumulate);
+  else
+    embedding_bwd_kernel<false><<<grid, 256, 0, s>>>(T, Vi, v_start, K, ids, dOut, dE_i, accumulate);
+  return check_launch(fn);
 }
 
 extern "C" int mp_all_gather_rows(mp_dtype dtype, int N, int64_t rows, int64_t cols, const void* const* slices,

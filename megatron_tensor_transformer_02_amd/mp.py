@@ -53,6 +53,7 @@ _SIGS = {
     "mp_shard_reduce_layernorm_bwd_dropout": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                                       c_p, c_p, c_f32, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "mp_all_gather_rows": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p]),
+    "mp_vocab_parallel_embedding_bwd": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_i32, c_p]),
     "mp_vocab_parallel_logits_xent_workspace": (c_sz, [c_i64, c_i64, c_i64]),
     "mp_vocab_parallel_logits_xent": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "mp_dropout_mask_bwd_workspace": (c_sz, [c_i64, c_i64]),
@@ -250,6 +251,13 @@ def mp_shard_reduce_layernorm_bwd_dropout(partials, x, gamma, mean, rstd, dx, p,
     _call("mp_shard_reduce_layernorm_bwd_dropout", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
           _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), p, _p(keep_bits), _p(ddrop), _p(dbias), _p(ws),
           need if ws is not None else 0, _s(stream))
+
+
+def mp_vocab_parallel_embedding_bwd(ids, dOut, v_start, dE_i, accumulate=False, stream=None):
+    T, K = dOut.shape
+    Vi = dE_i.shape[0]
+    _call("mp_vocab_parallel_embedding_bwd", _dt(dOut), T, Vi, v_start, K, _p(ids), _p(dOut), _p(dE_i),
+          int(bool(accumulate)), _s(stream))
 
 
 def mp_all_gather_rows(slices, out, stream=None):

@@ -171,3 +171,37 @@ def test_all_gather_rows_exact(dtype, n, rows, cols):
     mp.mp_all_gather_rows(slices[:-1] + [own], out2)
     sync()
     assert torch.equal(out2, out)
+
+
+@pytest.mark.parametrize("T,V,K,n,dtype", [(40, 64, 8, 2, "f32"), (257, 1000, 64, 8, "bf16"),
+                                           (9000, 512, 24, 4, "bf16"), (8192, 51200, 3072, 8, "bf16")])
+def test_vocab_parallel_embedding_bwd(T, V, K, n, dtype):
+    """The embedding's backward on every shard against the oracle's
+    token-order scatter-add (ids repeat; T = 9000 spans two token chunks),
+    accumulation onto an existing gradient, bit-identical repeats, T = 0."""
+    say("embedding bwd", T, V, K, n)
+    vi = V // n
+    rng = np.random.default_rng(T + V)
+    ids = torch.from_numpy(rng.integers(0, V if V > 64 else V, size=T).astype(np.int32))
+    if T > 1000:
+        ids[: T // 4] = ids[0]  # a hot id: many tokens on one row
+    dout = randn(9, (T, K), dtype)
+    ids_d, dout_d = cu(ids), cu(dout)
+    for i in (0, n - 1):
+        de = torch.empty((vi, K), dtype=torch.float32, device="cuda")
+        mp.mp_vocab_parallel_embedding_bwd(ids_d, dout_d, i * vi, de)
+        de2 = torch.full((vi, K), 0.5, dtype=torch.float32, device="cuda")
+        mp.mp_vocab_parallel_embedding_bwd(ids_d, dout_d, i * vi, de2, accumulate=True)
+        de3 = torch.empty_like(de)
+        mp.mp_vocab_parallel_embedding_bwd(ids_d, dout_d, i * vi, de3)
+        sync()
+        want = O.vocab_parallel_embedding_bwd(ids.numpy(), f64(dout), vi, i * vi)
+        assert rel_frobenius(f64(de), want) <= TOL["f32"]
+        assert rel_frobenius(f64(de2), want + 0.5) <= TOL["f32"]
+        assert torch.equal(de, de3)
+        untouched = np.setdiff1d(np.arange(vi), ids.numpy() - i * vi)
+        assert np.all(f64(de)[untouched] == 0)
+    empty = torch.full((vi, K), 3.0, dtype=torch.float32, device="cuda")
+    mp.mp_vocab_parallel_embedding_bwd(ids_d[:0], dout_d[:0], 0, empty)
+    sync()
+    assert torch.all(empty == 0)
