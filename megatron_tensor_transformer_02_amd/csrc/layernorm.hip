@@ -176,32 +176,37 @@ __global__ __launch_bounds__(256) void layernorm_bwd_param_kernel(int64_t T, int
   }
 }
 
-// Sums the slab partials of dgamma (columns [0, K)) and dbeta ([K, 2K)):
-// the same deterministic 4-group scheme as the column-sum final pass.
-__global__ __launch_bounds__(256) void layernorm_param_final_kernel(const float* __restrict__ partial, int64_t slabs,
-                                                                    int64_t K, int64_t w, float* __restrict__ dgamma,
-                                                                    float* __restrict__ dbeta,
-                                                                    float* __restrict__ dthird) {
-  __shared__ float red[4][64];
+// Sums the slab partials of dgamma (columns [0, K)) and dbeta ([K, 2K)).
+// 64 columns x 16 slab lanes per block: lane q sums slabs q, q+16, ... in
+// ascending order (4 loads in flight), then the 16 lane sums are added in
+// lane order (deterministic).
+__global__ __launch_bounds__(1024) void layernorm_param_final_kernel(const float* __restrict__ partial, int64_t slabs,
+                                                                     int64_t K, int64_t w, float* __restrict__ dgamma,
+                                                                     float* __restrict__ dbeta,
+                                                                     float* __restrict__ dthird) {
+  constexpr int Q = 16;
+  __shared__ float red[Q][64];
   const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
   float t = 0.0f;
   if (c < w) {
     int64_t s = q;
-    for (; s + 12 < slabs; s += 16) {
-      const float a0 = partial[s * w + c], a1 = partial[(s + 4) * w + c];
-      const float a2 = partial[(s + 8) * w + c], a3 = partial[(s + 12) * w + c];
+    for (; s + 3 * Q < slabs; s += 4 * Q) {
+      const float a0 = partial[s * w + c], a1 = partial[(s + Q) * w + c];
+      const float a2 = partial[(s + 2 * Q) * w + c], a3 = partial[(s + 3 * Q) * w + c];
       t += a0;
       t += a1;
       t += a2;
       t += a3;
     }
-    for (; s < slabs; s += 4) t += partial[s * w + c];
+    for (; s < slabs; s += Q) t += partial[s * w + c];
   }
   red[q][cl] = t;
   __syncthreads();
   if (q != 0 || c >= w) return;
-  const float v = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
+  float v = red[0][cl];
+#pragma unroll
+  for (int i = 1; i < Q; ++i) v += red[i][cl];
   if (c < K) {
     if (dgamma) dgamma[c] = v;
   } else if (c < 2 * K) {
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(256) void layernorm_param_final_kernel(const float*
 void layernorm_param_final(const float* partial, int64_t slabs, int64_t K, float* dgamma, float* dbeta,
                            hipStream_t s, float* dthird = nullptr) {
   const int64_t w = (dthird != nullptr ? 3 : 2) * K;
-  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(w, 64)), 256, 0, s>>>(partial, slabs, K, w, dgamma,
+  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(w, 64)), 1024, 0, s>>>(partial, slabs, K, w, dgamma,
                                                                                      dbeta, dthird);
 }
 
