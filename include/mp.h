@@ -236,7 +236,8 @@ size_t mp_head_attention_bwd_workspace(mp_dtype dtype, int B, int L, int K, int 
 /* Backward of mp_head_attention (P recomputed from lse).  Inputs as saved by
  * the forward plus dctx_i [T, h*d]; outputs dX_partial [T,K] (this rank's
  * share of the input gradient), dWqkv_i [3*h*d, K] fp32, dbqkv_i [3*h*d] fp32
- * or NULL. */
+ * or NULL.  On return the first T*3*h*d bf16 of ws hold dQKV [T, 3*h*d], the
+ * gradient of qkv in its column order (the attention core's dQ, dK, dV). */
 int mp_head_attention_bwd(mp_dtype dtype, int B, int L, int K, int h, int d, int causal,
                           const void* X, const void* Wqkv_i, const void* qkv,
                           const void* ctx_i, const float* lse, const void* dctx_i,

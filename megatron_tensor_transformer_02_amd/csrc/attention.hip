@@ -387,19 +387,49 @@ __global__ __launch_bounds__(256) void attn_dvec_kernel(const AttnArgs a) {
   const_cast<float*>(a.dvec)[(b * a.h + hh) * a.L + l] = acc;
 }
 
-template <int D, int NW>
+// Backward kernels.  NH = 1: each wave owns 16 rows (queries for dQ, keys
+// for dK/dV) and walks every visible 64-row tile of the other side.  NH = 2
+// (few (batch, head) pairs): two waves share each 16-row group and take one
+// 32-row half of every tile each, which halves the dependent chain per wave
+// and puts two waves on each SIMD; the halves' fp32 sums are added through
+// LDS at the end (half 0 + half 1, a fixed order).
+
+// Adds the NV fp32 vectors of the half-1 wave of each group to those of the
+// half-0 wave through `buf` (NG * NV * 64 vectors); every thread of the block
+// must call it.
+template <int NV, int NG>
+__device__ __forceinline__ void merge_halves(f32x4_t* x, f32x4_t* buf, int grp, int half, int lane) {
+  if (half == 1) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) buf[(grp * NV + v) * 64 + lane] = x[v];
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const f32x4_t y = buf[(grp * NV + v) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[v][r] += y[r];
+    }
+  }
+}
+
+template <int D, int NW, int NH>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) {
-  constexpr int NT = 64 * NW, BQ = 16 * NW, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
+  constexpr int NT = 64 * NW, NG = NW / NH, BQ = 16 * NG, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
+  constexpr int SUB = 4 / NH;  // 16-key sub-blocks per wave per tile
+  static_assert(NH == 1 || NH == 2, "one or two waves per row group");
   __shared__ uint4 lds_k[2][TS];
   __shared__ uint4 lds_v[2][TS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qc = lane & 15, g = lane >> 4;
+  const int grp = wave % NG, half = wave / NG;
   const int nbh = a.B * a.h;
   const int bh = blockIdx.x % nbh;
   const int qb = a.nblk - 1 - static_cast<int>(blockIdx.x / nbh);
   const int b = bh / a.h, hh = bh % a.h;
   const int64_t S3 = 3LL * a.h * D, HD = static_cast<int64_t>(a.h) * D;
   const uint16_t* base = a.qkv + static_cast<int64_t>(b) * a.L * S3;
-  const int q0 = qb * BQ, qw0 = q0 + wave * 16, qi = qw0 + qc;
+  const int q0 = qb * BQ, qw0 = q0 + grp * 16, qi = qw0 + qc;
   const bool qvalid = qi < a.L;
   const int64_t trow = static_cast<int64_t>(b) * a.L + qi;
 
@@ -431,18 +461,20 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
   __syncthreads();
   for (int it = 0; it < nkb; ++it) {
     const int kv0 = it * 64, cur = it & 1;
+    const int ks0 = kv0 + 16 * SUB * half;  // first key of this wave's part of the tile
     const bool more = it + 1 < nkb;
     if (more) {
       tk.load(rk, S3, kv0 + 64, a.L, tid);
       tv.load(rv, S3, kv0 + 64, a.L, tid);
     }
-    if (!(a.causal && kv0 > qw0 + 15)) {
+    if (!(a.causal && ks0 > qw0 + 15)) {
       const uint4* kt_ = lds_k[cur];
       const uint4* vt_ = lds_v[cur];
-      const bool edge = kv0 + 63 >= a.L || (a.causal && kv0 + 63 > qw0);
-      f32x4_t ds[4];
+      const bool edge = ks0 + 16 * SUB - 1 >= a.L || (a.causal && ks0 + 16 * SUB - 1 > qw0);
+      f32x4_t ds[SUB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int j = 0; j < SUB; ++j) {
+        const int kb = SUB * half + j;
         f32x4_t sv = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
@@ -454,14 +486,15 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
           const int key = kv0 + 16 * kb + 4 * g + r;
           const bool vis = qvalid && (!edge || (key < a.L && (!a.causal || key <= qi)));
           const float p = vis ? exp2f(fmaf(sv[r], a.scale_log2, -lse2)) : 0.0f;
-          ds[kb][r] = p * (dp[r] - dq_d);
+          ds[j][r] = p * (dp[r] - dq_d);
         }
       }
-      const uint4 d0 = pack_pair(ds[0], ds[1]), d1 = pack_pair(ds[2], ds[3]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dq[db] = mfma_16x16x32(tr_frag(kt_, 16 * db, 0, lane), d0, dq[db]);
-        dq[db] = mfma_16x16x32(tr_frag(kt_, 16 * db, 1, lane), d1, dq[db]);
+      for (int t2 = 0; t2 < SUB / 2; ++t2) {
+        const uint4 d = pack_pair(ds[2 * t2], ds[2 * t2 + 1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dq[db] = mfma_16x16x32(tr_frag(kt_, 16 * db, (SUB / 2) * half + t2, lane), d, dq[db]);
       }
     }
     if (more) {
@@ -469,6 +502,11 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
       tv.store(lds_v[cur ^ 1], tid);
     }
     __syncthreads();
+  }
+  if constexpr (NH == 2) {
+    static_assert(NG * DB * 64 * 16 <= sizeof(lds_k), "merge buffer exceeds the tile buffers");
+    merge_halves<DB, NG>(dq, reinterpret_cast<f32x4_t*>(&lds_k[0][0]), grp, half, lane);
+    if (half != 0) return;
   }
   if (!qvalid) return;
   uint16_t* row = a.dqkv + trow * S3 + hh * D;
@@ -481,20 +519,26 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
   }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a) {
-  constexpr int NT = 64 * NW, BK = 16 * NW, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
+// At most 256 registers: two waves per SIMD also with 4-wave blocks, whose
+// launch bound alone would let the compiler take more and run one.
+template <int D, int NW, int NH>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_dkv_kernel(
+    const AttnArgs a) {
+  constexpr int NT = 64 * NW, NG = NW / NH, BK = 16 * NG, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
+  constexpr int SUB = 4 / NH;  // 16-query sub-blocks per wave per tile
+  static_assert(NH == 1 || NH == 2, "one or two waves per row group");
   __shared__ uint4 lds_q[2][TS];
   __shared__ uint4 lds_do[2][TS];
   __shared__ float lds_lse[2][64], lds_dv[2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kc = lane & 15, g = lane >> 4;
+  const int grp = wave % NG, half = wave / NG;
   const int nbh = a.B * a.h;
   const int bh = blockIdx.x % nbh;
   const int kb = static_cast<int>(blockIdx.x / nbh);  // early key blocks see the most queries
   const int b = bh / a.h, hh = bh % a.h;
   const int64_t S3 = 3LL * a.h * D, HD = static_cast<int64_t>(a.h) * D;
   const uint16_t* base = a.qkv + static_cast<int64_t>(b) * a.L * S3;
-  const int k0 = kb * BK, kw0 = k0 + wave * 16, kj = kw0 + kc;
+  const int k0 = kb * BK, kw0 = k0 + grp * 16, kj = kw0 + kc;
   const bool kvalid = kj < a.L;
 
   uint4 kf[KS], vf[KS];  // K^T, V^T as B operands: key kj, d = 32 st + 8 g .. +7
@@ -509,9 +553,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a)
   const BufRes rdo = make_bufres(dbase + hh * D, (static_cast<int64_t>(a.L) * HD - hh * D) * 2);
   const int64_t sbase = (static_cast<int64_t>(b) * a.h + hh) * a.L;
 
-  f32x4_t dk[DB], dv[DB];
+  f32x4_t dkv[2 * DB];  // dK in [0, DB), dV in [DB, 2 DB)
 #pragma unroll
-  for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int v = 0; v < 2 * DB; ++v) dkv[v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int q_begin = a.causal ? (k0 / 64) * 64 : 0;
   const int nqb = (a.L - q_begin + 63) / 64;
@@ -541,15 +585,17 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a)
   __syncthreads();
   for (int it = 0; it < nqb; ++it) {
     const int q0 = q_begin + it * 64, cur = it & 1;
+    const int qs0 = q0 + 16 * SUB * half;  // first query of this wave's part of the tile
     const bool more = it + 1 < nqb;
     if (more) fetch(q0 + 64);
-    if (!(a.causal && q0 + 63 < kw0)) {  // else every query of the tile precedes this wave's keys
+    if (!(a.causal && qs0 + 16 * SUB - 1 < kw0)) {  // else every such query precedes this wave's keys
       const uint4* qt_ = lds_q[cur];
       const uint4* dot_ = lds_do[cur];
-      const bool edge = q0 + 63 >= a.L || (a.causal && q0 < kw0 + 15);
-      f32x4_t p[4], ds[4];
+      const bool edge = qs0 + 16 * SUB - 1 >= a.L || (a.causal && qs0 < kw0 + 15);
+      f32x4_t p[SUB], ds[SUB];
 #pragma unroll
-      for (int qb4 = 0; qb4 < 4; ++qb4) {
+      for (int j = 0; j < SUB; ++j) {
+        const int qb4 = SUB * half + j;
         f32x4_t sv = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
@@ -560,32 +606,40 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_kernel(const AttnArgs a)
         for (int r = 0; r < 4; ++r) {
           const int ql = 16 * qb4 + 4 * g + r, q = q0 + ql;
           const bool vis = kvalid && (!edge || (q < a.L && (!a.causal || kj <= q)));
-          p[qb4][r] = vis ? exp2f(fmaf(sv[r], a.scale_log2, -lds_lse[cur][ql])) : 0.0f;
-          ds[qb4][r] = p[qb4][r] * (dp[r] - lds_dv[cur][ql]);
+          p[j][r] = vis ? exp2f(fmaf(sv[r], a.scale_log2, -lds_lse[cur][ql])) : 0.0f;
+          ds[j][r] = p[j][r] * (dp[r] - lds_dv[cur][ql]);
         }
       }
-      const uint4 p0 = pack_pair(p[0], p[1]), p1 = pack_pair(p[2], p[3]);
-      const uint4 d0 = pack_pair(ds[0], ds[1]), d1 = pack_pair(ds[2], ds[3]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dv[db] = mfma_16x16x32(tr_frag(dot_, 16 * db, 0, lane), p0, dv[db]);
-        dv[db] = mfma_16x16x32(tr_frag(dot_, 16 * db, 1, lane), p1, dv[db]);
-        dk[db] = mfma_16x16x32(tr_frag(qt_, 16 * db, 0, lane), d0, dk[db]);
-        dk[db] = mfma_16x16x32(tr_frag(qt_, 16 * db, 1, lane), d1, dk[db]);
+      for (int t2 = 0; t2 < SUB / 2; ++t2) {
+        const int t = (SUB / 2) * half + t2;
+        const uint4 pp = pack_pair(p[2 * t2], p[2 * t2 + 1]), dd = pack_pair(ds[2 * t2], ds[2 * t2 + 1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dkv[DB + db] = mfma_16x16x32(tr_frag(dot_, 16 * db, t, lane), pp, dkv[DB + db]);
+          dkv[db] = mfma_16x16x32(tr_frag(qt_, 16 * db, t, lane), dd, dkv[db]);
+        }
       }
     }
     if (more) commit(cur ^ 1);
     __syncthreads();
+  }
+  if constexpr (NH == 2) {
+    // dK through the Q tile buffers, then dV through the dO tile buffers.
+    static_assert(NG * DB * 64 * 16 <= sizeof(lds_q), "merge buffer exceeds the tile buffers");
+    merge_halves<DB, NG>(dkv, reinterpret_cast<f32x4_t*>(&lds_q[0][0]), grp, half, lane);
+    merge_halves<DB, NG>(dkv + DB, reinterpret_cast<f32x4_t*>(&lds_do[0][0]), grp, half, lane);
+    if (half != 0) return;
   }
   if (!kvalid) return;
   uint16_t* row = a.dqkv + (static_cast<int64_t>(b) * a.L + kj) * S3 + hh * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     uint2 vk, vv;
-    vk.x = pack_bf16x2(dk[db][0] * a.scale, dk[db][1] * a.scale);
-    vk.y = pack_bf16x2(dk[db][2] * a.scale, dk[db][3] * a.scale);
-    vv.x = pack_bf16x2(dv[db][0], dv[db][1]);
-    vv.y = pack_bf16x2(dv[db][2], dv[db][3]);
+    vk.x = pack_bf16x2(dkv[db][0] * a.scale, dkv[db][1] * a.scale);
+    vk.y = pack_bf16x2(dkv[db][2] * a.scale, dkv[db][3] * a.scale);
+    vv.x = pack_bf16x2(dkv[DB + db][0], dkv[DB + db][1]);
+    vv.y = pack_bf16x2(dkv[DB + db][2], dkv[DB + db][3]);
     *reinterpret_cast<uint2*>(row + HD + 16 * db + 4 * g) = vk;
     *reinterpret_cast<uint2*>(row + 2 * HD + 16 * db + 4 * g) = vv;
   }
@@ -607,12 +661,19 @@ static void launch_fwd(AttnArgs a, hipStream_t s) {
   else attn_fwd_kernel<D, NW><<<static_cast<unsigned>(a.nblk * a.B * a.h), 64 * NW, 0, s>>>(a);
 }
 
+// With 4-wave blocks (few pairs) both backward kernels run the same 64-row
+// blocks on 8 waves, two per 16-row group.
 template <int D, int NW>
 static void launch_bwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
   const unsigned grid = static_cast<unsigned>(a.nblk * a.B * a.h);
-  attn_bwd_dq_kernel<D, NW><<<grid, 64 * NW, 0, s>>>(a);
-  attn_bwd_dkv_kernel<D, NW><<<grid, 64 * NW, 0, s>>>(a);
+  if constexpr (NW == 4) {
+    attn_bwd_dq_kernel<D, 8, 2><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dkv_kernel<D, 8, 2><<<grid, 512, 0, s>>>(a);
+  } else {
+    attn_bwd_dq_kernel<D, NW, 1><<<grid, 64 * NW, 0, s>>>(a);
+    attn_bwd_dkv_kernel<D, NW, 1><<<grid, 64 * NW, 0, s>>>(a);
+  }
 }
 
 static int validate_attn(const char* fn, mp_dtype dtype, int B, int L, int K, int h, int d) {

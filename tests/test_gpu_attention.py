@@ -27,6 +27,22 @@ def run_fwd(B, L, K, h, d, causal, seed):
     return x, w, bq, xd, wd, ctx, qkv, lse
 
 
+def check_core_grads(ws, qkv, dctx, B, L, h, d, causal, seqs=None):
+    """dQ, dK and dV (left in the workspace's first T*3hd bf16) against the
+    oracle's attention-core backward on the GPU's own projection, each on its
+    own so an error in one is not diluted by the others."""
+    T, hd = B * L, h * d
+    dqkv = f64(ws[:T * 3 * hd * 2].view(torch.bfloat16).reshape(T, 3 * hd))
+    q, k, v = O.split_qkv_heads(f64(qkv), B, L, h, d)
+    do = f64(dctx).reshape(B, L, h, d).transpose(0, 2, 1, 3)
+    sel = list(range(B)) if seqs is None else seqs
+    want = O.attention_core_bwd(q[sel], k[sel], v[sel], do[sel], causal)
+    got = dqkv.reshape(B, L, 3, h, d)[sel]
+    for i, name in enumerate("qkv"):
+        err = rel_frobenius(got[:, :, i].transpose(0, 2, 1, 3), want[i])
+        assert err <= TOL["bf16"], (name, err)
+
+
 @pytest.mark.parametrize("B,L,K,h,d,causal", [
     (2, 100, 64, 2, 64, True), (1, 257, 128, 3, 128, True), (2, 70, 96, 1, 64, False),
     (3, 1, 64, 2, 128, True), (1, 200, 256, 2, 128, False)])
@@ -45,8 +61,10 @@ def test_head_attention_fwd_bwd(B, L, K, h, d, causal):
     dx = torch.empty((B * L, K), dtype=torch.bfloat16, device="cuda")
     dw = torch.empty((3 * h * d, K), dtype=torch.float32, device="cuda")
     db = torch.empty(3 * h * d, dtype=torch.float32, device="cuda")
-    mp.mp_head_attention_bwd(xd, wd, qkv, ctx, lse, cu(dctx), B, L, h, d, dx, dw, db, causal)
+    ws = torch.empty(mp.lib().mp_head_attention_bwd_workspace(mp.MP_BF16, B, L, K, h, d), dtype=torch.uint8, device="cuda")
+    mp.mp_head_attention_bwd(xd, wd, qkv, ctx, lse, cu(dctx), B, L, h, d, dx, dw, db, causal, ws=ws)
     sync()
+    check_core_grads(ws, qkv, dctx, B, L, h, d, causal)
     wdx, wdw, wdb = O.head_attention_bwd(f64(x), f64(w), f64(qkv), f64(dctx), B, L, h, d, causal)
     assert rel_frobenius(f64(dx), wdx) <= TOL["bf16"]
     assert rel_frobenius(f64(dw), wdw) <= TOL["bf16"]
@@ -69,8 +87,10 @@ def test_head_attention_full_size(B, L, K, h, d):
     dctx = randn(40, (B * L, h * d), "bf16")
     dx = torch.empty((B * L, K), dtype=torch.bfloat16, device="cuda")
     dw = torch.empty((3 * h * d, K), dtype=torch.float32, device="cuda")
-    mp.mp_head_attention_bwd(xd, wd, qkv, ctx, lse, cu(dctx), B, L, h, d, dx, dw, None, True)
+    ws = torch.empty(mp.lib().mp_head_attention_bwd_workspace(mp.MP_BF16, B, L, K, h, d), dtype=torch.uint8, device="cuda")
+    mp.mp_head_attention_bwd(xd, wd, qkv, ctx, lse, cu(dctx), B, L, h, d, dx, dw, None, True, ws=ws)
     sync()
+    check_core_grads(ws, qkv, dctx, B, L, h, d, True, seqs=sel)
     wdx, wdw, _ = O.head_attention_bwd(f64(x), f64(w), f64(qkv), f64(dctx), B, L, h, d, True)
     assert rel_frobenius(f64(dx), wdx) <= TOL["bf16"]
     assert rel_frobenius(f64(dw), wdw) <= TOL["bf16"]
