@@ -177,14 +177,14 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
       mx = max4(mx);
       const float mn = fmaxf(m, mx);
       const float ms = mn == -INFINITY ? 0.0f : mn;
-      const float alpha = exp2f((m - ms) * a.scale_log2);
+      const float alpha = exp2_fast((m - ms) * a.scale_log2);
       const float msc = ms * a.scale_log2;
       float ps = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          s[kb][r] = exp2f(fmaf(s[kb][r], a.scale_log2, -msc));
+          s[kb][r] = exp2_fast(fmaf(s[kb][r], a.scale_log2, -msc));
           ps += s[kb][r];
         }
       l = l * alpha + ps;
@@ -297,14 +297,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
       mx = max4(mx);
       const float mn = fmaxf(m, mx);
       const float ms = mn == -INFINITY ? 0.0f : mn;
-      const float alpha = exp2f((m - ms) * a.scale_log2);
+      const float alpha = exp2_fast((m - ms) * a.scale_log2);
       const float msc = ms * a.scale_log2;
       float ps = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          s[kb][r] = exp2f(fmaf(s[kb][r], a.scale_log2, -msc));
+          s[kb][r] = exp2_fast(fmaf(s[kb][r], a.scale_log2, -msc));
           ps += s[kb][r];
         }
       l = l * alpha + ps;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
     const float m1 = mrg[(4 * DB) * 64], l1 = mrg[(4 * DB + 1) * 64];
     const float mn = fmaxf(m, m1);
     const float ms = mn == -INFINITY ? 0.0f : mn;
-    const float a0 = exp2f((m - ms) * a.scale_log2), a1 = exp2f((m1 - ms) * a.scale_log2);
+    const float a0 = exp2_fast((m - ms) * a.scale_log2), a1 = exp2_fast((m1 - ms) * a.scale_log2);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
         for (int r = 0; r < 4; ++r) {
           const int key = kv0 + 16 * kb + 4 * g + r;
           const bool vis = qvalid && (!edge || (key < a.L && (!a.causal || key <= qi)));
-          const float p = vis ? exp2f(fmaf(sv[r], a.scale_log2, -lse2)) : 0.0f;
+          const float p = vis ? exp2_fast(fmaf(sv[r], a.scale_log2, -lse2)) : 0.0f;
           ds[j][r] = p * (dp[r] - dq_d);
         }
       }
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int r = 0; r < 4; ++r) {
           const int ql = 16 * qb4 + 4 * g + r, q = q0 + ql;
           const bool vis = kvalid && (!edge || (q < a.L && (!a.causal || kj <= q)));
-          p[j][r] = vis ? exp2f(fmaf(sv[r], a.scale_log2, -lds_lse[cur][ql])) : 0.0f;
+          p[j][r] = vis ? exp2_fast(fmaf(sv[r], a.scale_log2, -lds_lse[cur][ql])) : 0.0f;
           ds[j][r] = p[j][r] * (dp[r] - lds_dv[cur][ql]);
         }
       }

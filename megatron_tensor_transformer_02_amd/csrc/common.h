@@ -61,6 +61,13 @@ typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
+// 2^x by the hardware instruction (v_exp_f32, about 1 ulp).  Results below
+// 2^-126 flush to zero instead of going through the library's denormal
+// rescaling: every use is a softmax weight (the exponential of a value at or
+// below the running maximum, whose own weight is 1), where a term that small
+// is negligible.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, bf16x2v_t));
 }

@@ -236,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
         for (int c = 0; c < HC; ++c)
           if (c0 + c < g.N) {
-            se += exp2f((v[c] - mx) * kL2e);
+            se += exp2_fast((v[c] - mx) * kL2e);
             if (c0 + c == lab) tg = v[c];
           }
       }

@@ -298,8 +298,12 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int srow = mfma_row(r, lane) * SP + (lane & 31);
       if constexpr (MODE == 0) {
+        // silu(g) = g / (1 + e^-g): e^-g by the hardware exp2, the division
+        // by v_rcp_f32 (about 1 ulp each, far below the bf16 output's
+        // resolution); large |g| still gives g or -0.
         const float g = acc[i][0][r];
-        strip[srow] = g / (1.0f + expf(-g)) * acc[i][1][r];
+        const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+        strip[srow] = g * __builtin_amdgcn_rcpf(1.0f + e) * acc[i][1][r];
       } else {
         strip[srow] = acc[i][0][r];
         strip[srow + 32] = acc[i][1][r];

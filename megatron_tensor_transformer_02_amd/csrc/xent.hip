@@ -16,7 +16,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
   if (mn == -INFINITY) return;  // both empty
-  s = s * exp2f((m - mn) * kLog2e) + s2 * exp2f((m2 - mn) * kLog2e);
+  s = s * exp2_fast((m - mn) * kLog2e) + s2 * exp2_fast((m2 - mn) * kLog2e);
   m = mn;
 }
 
@@ -46,13 +46,13 @@ __global__ __launch_bounds__(256) void xent_triples_kernel(int64_t T, int64_t Vi
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) lm = fmaxf(lm, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
     const float ml = lm * kLog2e;
-    float acc = (m == -INFINITY) ? 0.0f : s * exp2f(m * kLog2e - ml);
+    float acc = (m == -INFINITY) ? 0.0f : s * exp2_fast(m * kLog2e - ml);
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      acc += exp2f(fmaf(v[u].x, kLog2e, -ml));
-      acc += exp2f(fmaf(v[u].y, kLog2e, -ml));
-      acc += exp2f(fmaf(v[u].z, kLog2e, -ml));
-      acc += exp2f(fmaf(v[u].w, kLog2e, -ml));
+      acc += exp2_fast(fmaf(v[u].x, kLog2e, -ml));
+      acc += exp2_fast(fmaf(v[u].y, kLog2e, -ml));
+      acc += exp2_fast(fmaf(v[u].z, kLog2e, -ml));
+      acc += exp2_fast(fmaf(v[u].w, kLog2e, -ml));
     }
     m = lm;
     s = acc;
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void xent_bwd_kernel(int64_t T, int64_t Vi, in
   float r[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r[i] = gs * exp2f((r[i] - big_m) * kLog2e);
+    r[i] = gs * exp2_fast((r[i] - big_m) * kLog2e);
     if (lc == i) r[i] -= g;
   }
   if constexpr (OUT_BF16) {
