@@ -10,9 +10,12 @@ top-k expert ids and their weights are given.
 Readings: an expert is a SwiGLU FFN, ``silu(x W_g^T) * (x W_u^T)`` followed by
 ``W_d``, with the gate rows first and the up rows second in ``W_gu``; the
 routing weight is applied when the expert outputs are summed back per token
-(the "unpermute with routing weights" form; the memory-efficient variant that
-applies it earlier gives the same result by linearity); the permutation lists
-the local picks expert-major, then by token, then by slot.
+(the "unpermute with routing weights" form), or, in the memory-efficient
+variant of section 2.2, to the expert's activation before its down projection
+(so the unpermute is a plain sum and the backward needs no saved expert
+output); the two agree in exact arithmetic because the down projection is
+linear.  The permutation lists the local picks expert-major, then by token,
+then by slot.
 """
 
 import numpy as np
@@ -100,4 +103,34 @@ def moe_forward(x, topk_ids, topk_w, w_gu, w_d, e_start):
             r = row_of.get(t * topk + k)
             if r is not None:
                 out[t] += w[t, k] * y_perm[r]
+    return out, counts, offsets, picks, y_perm
+
+
+def moe_forward_weighted_act(x, topk_ids, topk_w, w_gu, w_d, e_start):
+    """Memory-efficient permutation form of :func:`moe_forward` (MOE-core,
+    technical summary 2.2: the routing weight is applied before the expert's
+    activation leaves it, here to the SwiGLU activation ahead of the down
+    projection).  Row ``r`` of the permuted activation is
+    ``w[pick_r] * silu(g_r) * u_r``; ``y_perm = act W_d^T``; the unpermute
+    sums ``y_perm`` rows per token without weights.  Returns
+    ``(out [T, Hd], counts, offsets, picks, y_perm [R, Hd])``."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    tokens, topk = ids.shape
+    w = _f64(topk_w).reshape(-1)
+    x = _f64(x)
+    e_local = np.shape(w_gu)[0]
+    counts, offsets, picks = moe_permutation(ids, e_start, e_local)
+    y_perm = np.zeros((picks.size, x.shape[1]))
+    for e in range(e_local):
+        sel = picks[offsets[e]:offsets[e + 1]]
+        if sel.size:
+            wgu, wd = _f64(w_gu[e]), _f64(w_d[e])
+            fe = wd.shape[1]
+            xe = x[sel // topk]
+            act = _silu(xe @ wgu[:fe].T) * (xe @ wgu[fe:].T)
+            act = act * w[sel][:, None]
+            y_perm[offsets[e]:offsets[e + 1]] = act @ wd.T
+    out = np.zeros_like(x)
+    for r, pk in enumerate(picks):
+        out[int(pk) // topk] += y_perm[r]
     return out, counts, offsets, picks, y_perm

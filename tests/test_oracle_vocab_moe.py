@@ -9,7 +9,8 @@ float64 cross-entropy and autograd as independent library routines.
 MoE (MOE-core, technical summary 2.2 and 2.4): the permutation is pinned
 against numpy's stable argsort; the expert FFN against a hand-computed scalar
 case and a brute-force loop; the permuted forward against the per-token
-definition.
+definition; the memory-efficient form (weight on the activation) against the
+weighted-unpermute form, which linearity of the down projection makes equal.
 """
 
 import math
@@ -168,3 +169,29 @@ def test_moe_forward_matches_per_token_definition():
     # Linearity in the routing weights: doubling every weight doubles the output.
     out2 = O.moe_forward(x, ids, 2 * w, wgu, wd, e_start)[0]
     assert np.allclose(out2, 2 * out, rtol=1e-14, atol=1e-14)
+
+
+def test_weighted_activation_form_equals_weighted_unpermute():
+    """The memory-efficient form (weight on the activation, MOE-core 2.2)
+    against the weighted-unpermute form and the per-token definition: equal in
+    exact arithmetic because the down projection is linear; row by row its
+    permuted output is the weight times the plain expert output."""
+    t, hd, fe, experts, topk, e_start, e_local = 40, 7, 6, 10, 3, 2, 5
+    ids, w = routing(t, experts, topk)
+    x = rnd(t, hd)
+    wgu, wd = rnd(e_local, 2 * fe, hd, scale=0.5), rnd(e_local, hd, fe, scale=0.5)
+    out, counts, offsets, picks, y_perm = O.moe_forward_weighted_act(x, ids, w, wgu, wd, e_start)
+    out_std, counts_std, offsets_std, picks_std, y_std = O.moe_forward(x, ids, w, wgu, wd, e_start)
+    assert np.array_equal(picks, picks_std) and np.array_equal(offsets, offsets_std)
+    assert np.allclose(out, out_std, rtol=1e-12, atol=1e-13)
+    ref = O.moe_forward_rows(x, ids, w, wgu, wd, e_start, list(range(t)))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)
+    wflat = np.asarray(w, dtype=np.float64).reshape(-1)
+    assert np.allclose(y_perm, wflat[picks][:, None] * y_std, rtol=1e-12, atol=1e-13)
+    # Unit weights: both forms are the same computation.
+    ones = np.ones_like(np.asarray(w, dtype=np.float64))
+    assert np.allclose(O.moe_forward_weighted_act(x, ids, ones, wgu, wd, e_start)[4],
+                       O.moe_forward(x, ids, ones, wgu, wd, e_start)[4], rtol=1e-13, atol=1e-14)
+    # A token whose picks all land elsewhere gets zeros.
+    none_local = ~np.any((ids >= e_start) & (ids < e_start + e_local), axis=1)
+    assert np.all(out[none_local] == 0)
