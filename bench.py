@@ -29,7 +29,8 @@ JSON line.  ``logits_xent_fused_us`` / ``logits_xent_unfused_us`` time the
 vocab shard's logits GEMM + statistics with the statistics fused into the
 GEMM's epilogue (no logits stored) and as two passes; ``embedding_bwd_us``
 the vocab shard's embedding backward (token-order scatter-add, accumulating
-into its fp32 gradient).
+into its fp32 gradient); ``moe_weighted_act_ms`` the MoE shard in its
+memory-efficient permutation form (routing weight on the activation).
 """
 
 import argparse
@@ -328,6 +329,18 @@ def main():
         out["moe_ms"] = round(moe_ms, 4)
         out["moe_TFLOPS"] = round(moe_fl / (moe_ms * 1e-3) / 1e12, 2)
         out["moe_rows"] = R_hot
+        # The memory-efficient permutation form (routing weight on the
+        # activation, unweighted unpermute) on the same shard, timed on its own.
+        for _ in range(max(1, args.warmup)):
+            mp.mp_grouped_expert_gemm_weighted_act(mx, mids, mw, mwgu, mwd, 0, mout, mperm, moffs, mws)
+        torch.cuda.synchronize()
+        mev = [(EV(), EV()) for _ in range(args.steps)]
+        for b_, e_ in mev:
+            b_.record(stream)
+            mp.mp_grouped_expert_gemm_weighted_act(mx, mids, mw, mwgu, mwd, 0, mout, mperm, moffs, mws)
+            e_.record(stream)
+        torch.cuda.synchronize()
+        out["moe_weighted_act_ms"] = round(float(np.mean([b_.elapsed_time(e_) for b_, e_ in mev])), 4)
     if roofs:
         out["roofline"] = roofs[0]
         out["rooflines"] = roofs

@@ -343,6 +343,20 @@ int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_lo
                            int32_t* perm_picks, int32_t* expert_offsets, void* ws,
                            size_t ws_bytes, hipStream_t s);
 
+/* Memory-efficient permutation form of mp_grouped_expert_gemm (MOE-core,
+ * technical summary 2.2: the routing weight is applied before the expert's
+ * activation leaves it, so the backward needs no saved expert output).  Steps
+ * 1 and 3 as above; in step 2 the activation row of pick (t,k) is
+ * topk_w[t,k] * silu(x W_g,e^T) * (x W_u,e^T), scaled in fp32 before its bf16
+ * rounding; step 4 sums the down-projection rows per token without weights.
+ * Equal to mp_grouped_expert_gemm in exact arithmetic (the down projection is
+ * linear); arguments, layouts, workspace and errors are the same. */
+int mp_grouped_expert_gemm_weighted_act(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                                        int e_start, const void* X, const int32_t* topk_ids,
+                                        const float* topk_w, const void* W_gu, const void* W_d,
+                                        void* out, int32_t* perm_picks, int32_t* expert_offsets,
+                                        void* ws, size_t ws_bytes, hipStream_t s);
+
 /* --------------------------------------------------------------- LayerNorm */
 
 /* LayerNorm over the last dim (MLM-review, "approach": LayerNorm placement

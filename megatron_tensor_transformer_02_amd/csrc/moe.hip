@@ -42,6 +42,7 @@ struct MoeArgs {
   uint16_t* act;           // [r_cap, Fe]
   uint16_t* yperm;         // [r_cap, Hd]
   int tiles_n;
+  int w_on_act;            // routing weight applied to the activation (memory-efficient form)
 };
 
 __global__ __launch_bounds__(256) void moe_count_kernel(const MoeArgs a) {
@@ -317,11 +318,16 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
       const int64_t grow = row0 + wm * WM + i * 32 + row;
       const float4 lo = *reinterpret_cast<const float4*>(strip + row * SP + c8);
       const float4 hi = *reinterpret_cast<const float4*>(strip + row * SP + c8 + 4);
-      const float val[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float val[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       if (grow >= row_end) continue;
       if constexpr (MODE == 0) {
         const int64_t jcol = static_cast<int64_t>(nt) * (BN / 2) + wn * (WN / 2) + c8;
         if (jcol >= a.Fe) continue;
+        if (a.w_on_act) {  // the row's routing weight, before the bf16 rounding
+          const float wr = a.w[a.perm[grow]];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) val[q] *= wr;
+        }
         *reinterpret_cast<uint4*>(a.act + grow * a.Fe + jcol) = pack8(val);
       } else {
         const int64_t n = static_cast<int64_t>(nt) * BN + wn * WN + c8;
@@ -332,7 +338,8 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   }
 }
 
-// out[t, 8c..8c+7] = sum_k w[t,k] * yperm[row(t,k), 8c..8c+7] (k ascending).
+// out[t, 8c..8c+7] = sum_k w[t,k] * yperm[row(t,k), 8c..8c+7] (k ascending;
+// w = 1 when the weights were applied to the activation).
 __global__ __launch_bounds__(256) void moe_unpermute_kernel(const MoeArgs a) {
   const int64_t vpr = a.Hd / 8;
   const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(256) void moe_unpermute_kernel(const MoeArgs a) {
   for (int k = 0; k < a.topk; ++k) {
     const int32_t row = a.pick_row[t * a.topk + k];
     if (row < 0) continue;
-    const float wk = a.w[t * a.topk + k];
+    const float wk = a.w_on_act ? 1.0f : a.w[t * a.topk + k];
     float y[8];
     unpack8(*reinterpret_cast<const uint4*>(a.yperm + static_cast<int64_t>(row) * a.Hd + c), y);
 #pragma unroll
@@ -385,11 +392,10 @@ extern "C" size_t mp_grouped_expert_gemm_workspace(int64_t T, int64_t Hd, int64_
   return moe_layout(T, Hd, Fe, topk, E_loc).total;
 }
 
-extern "C" int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, int e_start,
-                                      const void* X, const int32_t* topk_ids, const float* topk_w, const void* W_gu,
-                                      const void* W_d, void* out, int32_t* perm_picks, int32_t* expert_offsets,
-                                      void* ws, size_t ws_bytes, hipStream_t s) {
-  static const char* fn = "mp_grouped_expert_gemm";
+static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t Hd, int64_t Fe, int topk,
+                               int E_loc, int e_start, const void* X, const int32_t* topk_ids, const float* topk_w,
+                               const void* W_gu, const void* W_d, void* out, int32_t* perm_picks,
+                               int32_t* expert_offsets, void* ws, size_t ws_bytes, hipStream_t s) {
   MP_REQUIRE(T >= 0 && Hd > 0 && Fe > 0 && topk > 0 && E_loc > 0 && e_start >= 0, MP_ERR_SHAPE, "%s: bad shape", fn);
   MP_REQUIRE(Hd % 8 == 0 && Fe % 8 == 0, MP_ERR_SHAPE, "%s: Hd and Fe must be multiples of 8", fn);
   MP_REQUIRE(T * Hd * 2 < 0x7fffffffLL && 2 * Fe * Hd * 2 < 0x7fffffffLL && T * topk * Fe * 2 < 0x7fffffffLL,
@@ -431,6 +437,7 @@ extern "C" int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int top
   a.counts = reinterpret_cast<int32_t*>(w + L.counts);
   a.act = reinterpret_cast<uint16_t*>(w + L.act);
   a.yperm = reinterpret_cast<uint16_t*>(w + L.yperm);
+  a.w_on_act = w_on_act ? 1 : 0;
   const unsigned tgrid = static_cast<unsigned>(ceil_div(T, 256));
   moe_count_kernel<<<tgrid, 256, 0, s>>>(a);
   moe_scan_kernel<<<static_cast<unsigned>(E_loc), 1024, 0, s>>>(a);
@@ -443,4 +450,21 @@ extern "C" int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int top
   moe_gemm_kernel<1><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a);
   return check_launch(fn);
+}
+
+extern "C" int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, int e_start,
+                                      const void* X, const int32_t* topk_ids, const float* topk_w, const void* W_gu,
+                                      const void* W_d, void* out, int32_t* perm_picks, int32_t* expert_offsets,
+                                      void* ws, size_t ws_bytes, hipStream_t s) {
+  return grouped_expert_gemm("mp_grouped_expert_gemm", false, T, Hd, Fe, topk, E_loc, e_start, X, topk_ids, topk_w,
+                             W_gu, W_d, out, perm_picks, expert_offsets, ws, ws_bytes, s);
+}
+
+extern "C" int mp_grouped_expert_gemm_weighted_act(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                                                   int e_start, const void* X, const int32_t* topk_ids,
+                                                   const float* topk_w, const void* W_gu, const void* W_d, void* out,
+                                                   int32_t* perm_picks, int32_t* expert_offsets, void* ws,
+                                                   size_t ws_bytes, hipStream_t s) {
+  return grouped_expert_gemm("mp_grouped_expert_gemm_weighted_act", true, T, Hd, Fe, topk, E_loc, e_start, X,
+                             topk_ids, topk_w, W_gu, W_d, out, perm_picks, expert_offsets, ws, ws_bytes, s);
 }

@@ -72,6 +72,8 @@ _SIGS = {
     "mp_grouped_expert_gemm_workspace": (c_sz, [c_i64, c_i64, c_i64, c_i32, c_i32]),
     "mp_grouped_expert_gemm": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                        c_p, c_p, c_sz, c_p]),
+    "mp_grouped_expert_gemm_weighted_act": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p,
+                                                    c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "mp_layernorm": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_p, c_f32, c_p, c_p, c_p, c_p]),
     "mp_layernorm_bwd_workspace": (c_sz, [c_i64, c_i64]),
     "mp_layernorm_bwd": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
@@ -339,16 +341,28 @@ def mp_vocab_parallel_xent_bwd(Z_i, labels, v_start, stats, g, dZ_i, stream=None
 
 # ---------------------------------------------------------------------- MoE
 
-def mp_grouped_expert_gemm(X, topk_ids, topk_w, W_gu, W_d, e_start, out, perm_picks=None, expert_offsets=None,
-                           ws=None, stream=None):
+def _grouped_expert_gemm(name, X, topk_ids, topk_w, W_gu, W_d, e_start, out, perm_picks, expert_offsets, ws,
+                         stream):
     T, Hd = X.shape
     topk = topk_ids.shape[1]
     E_loc, two_fe, _ = W_gu.shape
     Fe = two_fe // 2
     need = lib().mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E_loc)
     ws = ws if ws is not None else workspace(need, X.device)
-    _call("mp_grouped_expert_gemm", T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w), _p(W_gu),
+    _call(name, T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w), _p(W_gu),
           _p(W_d), _p(out), _p(perm_picks), _p(expert_offsets), _p(ws), need if ws is not None else 0, _s(stream))
+
+
+def mp_grouped_expert_gemm(X, topk_ids, topk_w, W_gu, W_d, e_start, out, perm_picks=None, expert_offsets=None,
+                           ws=None, stream=None):
+    _grouped_expert_gemm("mp_grouped_expert_gemm", X, topk_ids, topk_w, W_gu, W_d, e_start, out, perm_picks,
+                         expert_offsets, ws, stream)
+
+
+def mp_grouped_expert_gemm_weighted_act(X, topk_ids, topk_w, W_gu, W_d, e_start, out, perm_picks=None,
+                                        expert_offsets=None, ws=None, stream=None):
+    _grouped_expert_gemm("mp_grouped_expert_gemm_weighted_act", X, topk_ids, topk_w, W_gu, W_d, e_start, out,
+                         perm_picks, expert_offsets, ws, stream)
 
 
 # ---------------------------------------------------------------- LayerNorm

@@ -1,6 +1,8 @@
 """GPU parity: the MoE expert shard (permutation, grouped gate/up GEMM with
-SwiGLU, grouped down GEMM, weighted unpermute) against the oracle.  The
-permutation and expert offsets are compared bit for bit."""
+SwiGLU, grouped down GEMM, weighted unpermute) against the oracle, in both
+the weighted-unpermute form and the memory-efficient form (routing weight on
+the activation).  The permutation and expert offsets are compared bit for
+bit."""
 
 import numpy as np
 import pytest
@@ -20,19 +22,20 @@ def routing(seed, T, experts, topk):
     return torch.from_numpy(ids), torch.from_numpy(w / w.sum(axis=1, keepdims=True))
 
 
-def run(x, ids, w, wgu, wd, e_start):
+def run(x, ids, w, wgu, wd, e_start, fn=None):
+    fn = fn or mp.mp_grouped_expert_gemm
     T, Hd = x.shape
     topk = ids.shape[1]
     e_local = wgu.shape[0]
     out = torch.empty((T, Hd), dtype=torch.bfloat16, device="cuda")
     perm = torch.full((T * topk,), -7, dtype=torch.int32, device="cuda")
     offs = torch.empty(e_local + 1, dtype=torch.int32, device="cuda")
-    mp.mp_grouped_expert_gemm(cu(x), cu(ids), cu(w), cu(wgu), cu(wd), e_start, out, perm, offs)
+    fn(cu(x), cu(ids), cu(w), cu(wgu), cu(wd), e_start, out, perm, offs)
     sync()
     return out, perm.cpu().numpy(), offs.cpu().numpy()
 
 
-@pytest.mark.parametrize("T,Hd,Fe,experts,e_local,e_start,topk", [
+CASES = [
     (50, 64, 40, 16, 4, 4, 4),      # ragged Fe against the 128-column act tile
     (300, 256, 136, 32, 8, 0, 8),
     (77, 128, 64, 8, 1, 5, 2),      # a single local expert
@@ -40,16 +43,23 @@ def run(x, ids, w, wgu, wd, e_start):
     (33, 64, 64, 16, 4, 12, 1),     # top-1
     (700, 200, 264, 4, 2, 1, 2),    # >256 rows per expert, ragged k-tiles in both GEMMs
     (513, 72, 520, 8, 3, 2, 4),     # K = 72 (one full and one 8-wide k-tile), 5 act tiles
-])
-def test_grouped_expert_gemm(T, Hd, Fe, experts, e_local, e_start, topk):
-    say("moe", T, Hd, Fe, experts, e_local, e_start, topk)
+]
+FORMS = {"weighted_unpermute": (lambda: mp.mp_grouped_expert_gemm, O.moe_forward),
+         "weighted_act": (lambda: mp.mp_grouped_expert_gemm_weighted_act, O.moe_forward_weighted_act)}
+
+
+@pytest.mark.parametrize("form", list(FORMS))
+@pytest.mark.parametrize("T,Hd,Fe,experts,e_local,e_start,topk", CASES)
+def test_grouped_expert_gemm(T, Hd, Fe, experts, e_local, e_start, topk, form):
+    say("moe", form, T, Hd, Fe, experts, e_local, e_start, topk)
+    fn, oracle_fn = FORMS[form]
     ids, w = routing(T + Hd, T, experts, topk)
     rng = np.random.default_rng(5)
     x = torch.from_numpy(rng.standard_normal((T, Hd), dtype=np.float32)).to(torch.bfloat16)
     wgu = torch.from_numpy((rng.standard_normal((e_local, 2 * Fe, Hd), dtype=np.float32) * 0.1)).to(torch.bfloat16)
     wd = torch.from_numpy((rng.standard_normal((e_local, Hd, Fe), dtype=np.float32) * 0.1)).to(torch.bfloat16)
-    out, perm, offs = run(x, ids, w, wgu, wd, e_start)
-    want, counts, woffs, picks, _ = O.moe_forward(f64(x), ids.numpy(), w.numpy(), f64(wgu), f64(wd), e_start)
+    out, perm, offs = run(x, ids, w, wgu, wd, e_start, fn())
+    want, counts, woffs, picks, _ = oracle_fn(f64(x), ids.numpy(), w.numpy(), f64(wgu), f64(wd), e_start)
     r = picks.size
     assert np.array_equal(offs, woffs)
     assert np.array_equal(perm[:r], picks)
@@ -57,30 +67,33 @@ def test_grouped_expert_gemm(T, Hd, Fe, experts, e_local, e_start, topk):
     assert rel_frobenius(f64(out), want) <= TOL["bf16"]
 
 
-def test_no_local_picks_gives_zeros():
-    say("moe empty shard")
+@pytest.mark.parametrize("form", list(FORMS))
+def test_no_local_picks_gives_zeros(form):
+    say("moe empty shard", form)
     T, Hd, Fe = 20, 64, 64
     ids, w = routing(1, T, 8, 2)
     x = torch.ones((T, Hd), dtype=torch.bfloat16)
     wgu = torch.ones((2, 2 * Fe, Hd), dtype=torch.bfloat16)
     wd = torch.ones((2, Hd, Fe), dtype=torch.bfloat16)
-    out, perm, offs = run(x, ids, w, wgu, wd, 100)  # experts 100, 101 are never picked
+    out, perm, offs = run(x, ids, w, wgu, wd, 100, FORMS[form][0]())  # experts 100, 101 are never picked
     assert np.all(offs == 0)
     assert np.all(f64(out) == 0)
 
 
 @pytest.mark.slow
-def test_moe_shard_full_size():
+@pytest.mark.parametrize("form", list(FORMS))
+def test_moe_shard_full_size(form):
     # The hot expert-parallel shard (experts 0-7 of 256, Zipf(1.1) routing):
     # permutation in full, outputs for 48 sampled tokens through the oracle.
-    say("moe full size")
+    say("moe full size", form)
+    fn, oracle_fn = FORMS[form]
     wl = S.WORKLOADS["moe"]
     inp = S.moe_inputs(wl)
-    out, perm, offs = run(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_gu"], inp["w_d"], 0)
+    out, perm, offs = run(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_gu"], inp["w_d"], 0, fn())
     counts, woffs, picks = O.moe_permutation(inp["topk_ids"].numpy(), 0, wl.e_local)
     assert np.array_equal(offs, woffs)
     assert np.array_equal(perm[:picks.size], picks)
     toks = np.random.default_rng(3).choice(wl.T, 48, replace=False)
-    sub_out = O.moe_forward(f64(inp["x"])[toks], inp["topk_ids"].numpy()[toks], inp["topk_w"].numpy()[toks],
-                            f64(inp["w_gu"]), f64(inp["w_d"]), 0)[0]
+    sub_out = oracle_fn(f64(inp["x"])[toks], inp["topk_ids"].numpy()[toks], inp["topk_w"].numpy()[toks],
+                        f64(inp["w_gu"]), f64(inp["w_d"]), 0)[0]
     assert rel_frobenius(f64(out)[toks], sub_out) <= TOL["bf16"]
