@@ -30,7 +30,9 @@ vocab shard's logits GEMM + statistics with the statistics fused into the
 GEMM's epilogue (no logits stored) and as two passes; ``embedding_bwd_us``
 the vocab shard's embedding backward (token-order scatter-add, accumulating
 into its fp32 gradient); ``moe_weighted_act_ms`` the MoE shard in its
-memory-efficient permutation form (routing weight on the activation).
+memory-efficient permutation form (routing weight on the activation);
+``moe_mxfp8_ms`` / ``moe_mxfp8_TFLOPS`` the shard with MXFP8 expert GEMMs
+(block-scaled E4M3 operands, fp32 accumulation; the same model FLOPs).
 """
 
 import argparse
@@ -341,6 +343,34 @@ def main():
             e_.record(stream)
         torch.cuda.synchronize()
         out["moe_weighted_act_ms"] = round(float(np.mean([b_.elapsed_time(e_) for b_, e_ in mev])), 4)
+        # The same shard with MXFP8 expert GEMMs (weights quantised once in
+        # untimed setup; token rows and activations quantised inside the call).
+        sw_h, sw_f = mp.mxfp8_scale_width(wm.K), mp.mxfp8_scale_width(wm.Fe)
+        gq = torch.empty((wm.e_local, 2 * wm.Fe, wm.K), dtype=torch.uint8, device="cuda")
+        gs = torch.empty((wm.e_local, 2 * wm.Fe, sw_h), dtype=torch.uint8, device="cuda")
+        dq = torch.empty((wm.e_local, wm.K, wm.Fe), dtype=torch.uint8, device="cuda")
+        ds = torch.empty((wm.e_local, wm.K, sw_f), dtype=torch.uint8, device="cuda")
+        for e in range(wm.e_local):
+            mp.mp_mxfp8_quantize(mwgu[e], gq[e], gs[e])
+            mp.mp_mxfp8_quantize(mwd[e], dq[e], ds[e])
+        mxws = torch.empty(mp.lib().mp_grouped_expert_gemm_mxfp8_workspace(wm.T, wm.K, wm.Fe, wm.topk, wm.e_local),
+                           dtype=torch.uint8, device="cuda")
+
+        def moe_mx():
+            mp.mp_grouped_expert_gemm_mxfp8(mx, mids, mw, gq, gs, dq, ds, 0, mout, mperm, moffs, mxws)
+
+        for _ in range(max(1, args.warmup)):
+            moe_mx()
+        torch.cuda.synchronize()
+        for b_, e_ in mev:
+            b_.record(stream)
+            moe_mx()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        mx_ms = float(np.mean([b_.elapsed_time(e_) for b_, e_ in mev]))
+        out["moe_mxfp8_ms"] = round(mx_ms, 4)
+        out["moe_mxfp8_TFLOPS"] = round(moe_fl / (mx_ms * 1e-3) / 1e12, 2)
+        del gq, gs, dq, ds, mxws
     if roofs:
         out["roofline"] = roofs[0]
         out["rooflines"] = roofs

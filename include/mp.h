@@ -357,6 +357,45 @@ int mp_grouped_expert_gemm_weighted_act(int64_t T, int64_t Hd, int64_t Fe, int t
                                         void* out, int32_t* perm_picks, int32_t* expert_offsets,
                                         void* ws, size_t ws_bytes, hipStream_t s);
 
+/* ------------------------------------------------------------------ MXFP8 */
+
+/* MXFP8 block quantisation (MOE-core, technical summary 2.5: expert GEMMs and
+ * their activations in a low-precision format, MXFP8 among the recipes; the
+ * format itself is read as OCP Microscaling).  Each row of x [rows, K] bf16
+ * (row stride ld elements, ld >= K, ld % 8 == 0; K % 32 == 0) is split into
+ * 32-value blocks along K; a block with largest magnitude X gets the E8M0
+ * exponent se = floor(log2 X) - 8, clamped to [-127, 127] (-127 when
+ * X < 2^-126), stored as se + 127; each value becomes the E4M3 code of
+ * x / 2^se (nearest, ties to the even code, saturating at 448, sign kept).
+ * q [rows, K] uint8 (8-byte aligned); scales [rows, 4*ceil(K/128)] uint8,
+ * block b of a row at byte b, the bytes past the last block set to 127.
+ * Inputs must be finite. */
+int mp_mxfp8_quantize(int64_t rows, int64_t K, const void* x, int64_t ld, uint8_t* q,
+                      uint8_t* scales, hipStream_t s);
+
+size_t mp_grouped_expert_gemm_mxfp8_workspace(int64_t T, int64_t Hd, int64_t Fe, int topk,
+                                              int E_loc);
+
+/* The MoE shard of mp_grouped_expert_gemm with both expert GEMMs in MXFP8
+ * (selective precision, MOE-core 2.5: the routing, the unpermute's fp32 sum
+ * and the output stay high precision).  The token rows are quantised along Hd
+ * inside the call (mp_mxfp8_quantize's rules); the weights arrive quantised:
+ * W_gu_q [E_loc, 2*Fe, Hd] with W_gu_s [E_loc, 2*Fe, 4*ceil(Hd/128)], W_d_q
+ * [E_loc, Hd, Fe] with W_d_s [E_loc, Hd, 4*ceil(Fe/128)] (scale arrays 4-byte
+ * aligned).  Each expert's gate/up products accumulate in fp32 on gfx950's
+ * block-scaled MFMA; the SwiGLU activation is stored as bf16, quantised along
+ * Fe, and projected down the same way; the unpermute is the weighted fp32
+ * sum of mp_grouped_expert_gemm.  Hd % 32 == 0, Fe % 32 == 0; other arguments,
+ * outputs and errors as mp_grouped_expert_gemm, with the workspace from
+ * mp_grouped_expert_gemm_mxfp8_workspace(). */
+int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                                 int e_start, const void* X, const int32_t* topk_ids,
+                                 const float* topk_w, const uint8_t* W_gu_q,
+                                 const uint8_t* W_gu_s, const uint8_t* W_d_q,
+                                 const uint8_t* W_d_s, void* out, int32_t* perm_picks,
+                                 int32_t* expert_offsets, void* ws, size_t ws_bytes,
+                                 hipStream_t s);
+
 /* --------------------------------------------------------------- LayerNorm */
 
 /* LayerNorm over the last dim (MLM-review, "approach": LayerNorm placement

@@ -30,6 +30,26 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(const uint4& a, const uint4& b
                                                  0, 0, 0);
 }
 
+// C += (A x 2^(sa-127)) (B x 2^(sb-127))^T on 32x32 with 64 k-values of FP8
+// E4M3 (OCP MX), fp32 accumulators in the same layout as mfma_32x32x16.
+// Operand lane l (row l%32) holds, in a0, k-values 16*(l/32) .. +15 of the
+// step and, in a1, k-values 32 + 16*(l/32) .. +15 (both 16-byte chunks of a
+// K-contiguous LDS row).  The scale of the step's 32-value block 0 (k 0..31)
+// of row r comes from lane r, that of block 1 (k 32..63) from lane r+32, as
+// byte OS of the lane's scale register (measured on gfx950 against random
+// operands and scales).
+template <int OS>
+__device__ __forceinline__ f32x16_t mfma_mx_32x32x64(const uint4& a0, const uint4& a1, const uint4& b0,
+                                                     const uint4& b1, uint32_t sa, uint32_t sb, const f32x16_t& c) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x8_t a = {static_cast<int>(a0.x), static_cast<int>(a0.y), static_cast<int>(a0.z), static_cast<int>(a0.w),
+                     static_cast<int>(a1.x), static_cast<int>(a1.y), static_cast<int>(a1.z), static_cast<int>(a1.w)};
+  const i32x8_t b = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z), static_cast<int>(b0.w),
+                     static_cast<int>(b1.x), static_cast<int>(b1.y), static_cast<int>(b1.z), static_cast<int>(b1.w)};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OS, static_cast<int>(sa), OS,
+                                                         static_cast<int>(sb));
+}
+
 // D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.  Lane l
 // gives row (l % 16) of A and column (l % 16) of B, each with 8 k-values
 // 8*(l/16) .. +7; register r of lane l receives element

@@ -43,6 +43,16 @@ struct MoeArgs {
   uint16_t* yperm;         // [r_cap, Hd]
   int tiles_n;
   int w_on_act;            // routing weight applied to the activation (memory-efficient form)
+  // MXFP8 operands: E4M3 codes and E8M0 scales (4 * ceil(K / 128) bytes per row).
+  const uint8_t* xq;       // [T, Hd]
+  const uint8_t* xs;       // [T, swh]
+  const uint8_t* gq;       // [E_loc, 2*Fe, Hd]
+  const uint8_t* gs;       // [E_loc, 2*Fe, swh]
+  const uint8_t* dq;       // [E_loc, Hd, Fe]
+  const uint8_t* ds;       // [E_loc, Hd, swf]
+  const uint8_t* aq;       // [r_cap, Fe]
+  const uint8_t* as;       // [r_cap, swf]
+  int64_t swh, swf;
 };
 
 __global__ __launch_bounds__(256) void moe_count_kernel(const MoeArgs a) {
@@ -168,13 +178,71 @@ struct GatherDma {
   }
 };
 
+// ------------------------------------------------------------------ MXFP8
+// OCP MX: 32-value blocks share an E8M0 exponent floor(log2 max|x|) - 8 (8 is
+// E4M3's largest exponent), clamped to [-127, 127], -127 for blocks below
+// 2^-126; values become E4M3 codes of x / 2^exponent.
+
+// E4M3 code of v (|v| < 2^9): nearest, ties to the even code, saturating at
+// 448 (0x7E); the sign bit is kept, so a value rounding to zero gives +-0.
+// Below 2^-6 the grid is the multiples of 2^-9 (codes 0..8, 8 = 2^-6).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t sign = (bits >> 24) & 0x80u, b = bits & 0x7fffffffu;
+  const float m = __uint_as_float(b);
+  uint32_t code;
+  if (m >= 448.0f) code = 0x7eu;
+  else if (m < 0.015625f) code = static_cast<uint32_t>(__builtin_rintf(m * 512.0f));
+  else code = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);  // keep 3 mantissa bits, rebias 127 -> 7
+  return code | sign;
+}
+
+// Rows of x (bf16, row stride ld) to codes q [rows, K] and scales sc
+// [rows, sw] (bytes past the last block set to 127); four lanes per block,
+// eight values each.  With rows_dev the row count is read from the device
+// (rows is then its upper bound).
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __restrict__ x, int64_t ld, int64_t rows,
+                                                          const int32_t* rows_dev, int64_t K,
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
+                                                          int64_t sw) {
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t gpr = K / 8;  // a multiple of 4: the four lanes of a block share a row
+  const int64_t r = v / gpr;
+  const int64_t nrows = rows_dev != nullptr ? min(rows, static_cast<int64_t>(*rows_dev)) : rows;
+  if (r >= nrows) return;
+  const int64_t c = (v - r * gpr) * 8;
+  float f[8];
+  unpack8(*reinterpret_cast<const uint4*>(x + r * ld + c), f);
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(f[i]));
+  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+  const int e8 = static_cast<int>(__float_as_uint(mx) >> 23);
+  const int se = e8 == 0 ? -127 : max(e8 - 135, -127);
+  const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);  // 2^-se, exact scaling
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= e4m3_code(f[i] * inv) << (8 * i);
+    hi |= e4m3_code(f[4 + i] * inv) << (8 * i);
+  }
+  *reinterpret_cast<uint2*>(q + r * K + c) = make_uint2(lo, hi);
+  if ((c & 31) == 0) sc[r * sw + c / 32] = static_cast<uint8_t>(se + 127);
+  if (c == 0)
+    for (int64_t bk = K / 32; bk < sw; ++bk) sc[r * sw + bk] = 127;
+}
+
 // Grouped GEMM.  MODE 0: act[rows of e, :] = SwiGLU(X[tokens] W_gu[e]^T);
 // MODE 1: yperm[rows of e, :] = act[rows of e] W_d[e]^T.  256x256x64 tiles on
 // 8 waves in a 2x4 grid (two per SIMD), each wave owning 128x64 of the tile;
 // the same software pipeline as the dense GEMM: both operands stream into two
 // LDS buffers by direct loads issued two k-tiles ahead, fragments are
 // double-buffered in registers, and the barrier sits inside the last k-step.
-template <int MODE>
+// MX: both operands are MXFP8 (E4M3 codes, k-tiles of 128 codes = the same
+// 128-byte LDS rows), two scaled 32x32x64 MFMA steps per k-tile, each row's
+// four block exponents of a k-tile read as one dword per fragment row.
+template <int MODE, bool MX>
 __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   constexpr int BM = MOE_BM, BN = MOE_BN, NT = 512, WC = 4, WM = BM / 2, WN = BN / WC;
   constexpr int TM = WM / 32, TN = WN / 32, A_SLOTS = BM * 8, B_SLOTS = BN * 8;
@@ -194,35 +262,46 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   const int64_t row0 = a.offsets[e] + static_cast<int64_t>(mtg - a.tile_start[e]) * BM;
   const int64_t row_end = a.offsets[e + 1];
   const int64_t K = MODE == 0 ? a.Hd : a.Fe;
+  // The loaders count 2-byte units: bf16 values, or pairs of E4M3 codes.
+  const int64_t KU = MX ? K / 2 : K;
+  auto base16 = [](const uint8_t* q, const uint16_t* h, int64_t off) -> const uint16_t* {
+    return MX ? reinterpret_cast<const uint16_t*>(q + off) : h + off;
+  };
 
+  // Gate/up weight row (within expert e) of B tile row r, or -1: wave column
+  // block c holds WN/2 gate rows, then the WN/2 up rows of the same output
+  // columns.
+  auto gu_row = [&](int r) -> int64_t {
+    const int wcol = r / WN, within = r % WN;
+    const int64_t j = static_cast<int64_t>(nt) * (BN / 2) + wcol * (WN / 2) + (within % (WN / 2));
+    if (j >= a.Fe) return -1;
+    return (within < WN / 2) ? j : a.Fe + j;
+  };
+  const int64_t n0 = static_cast<int64_t>(nt) * BN;
   GatherDma<BM, NT> da;
   GatherDma<BN, NT> db;
   if constexpr (MODE == 0) {
-    da.init(a.X, a.T * a.Hd, tid, [&](int r) -> int64_t {
+    da.init(base16(a.xq, a.X, 0), a.T * KU, tid, [&](int r) -> int64_t {
       const int64_t grow = row0 + r;
-      return grow < row_end ? static_cast<int64_t>(a.perm[grow] / a.topk) * a.Hd : -1;
+      return grow < row_end ? static_cast<int64_t>(a.perm[grow] / a.topk) * KU : -1;
     });
-    // Wave column block c holds WN/2 gate rows, then the WN/2 up rows of the
-    // same output columns.
-    db.init(a.W_gu + static_cast<int64_t>(e) * 2 * a.Fe * a.Hd, 2 * a.Fe * a.Hd, tid, [&](int r) -> int64_t {
-      const int wcol = r / WN, within = r % WN;
-      const int64_t j = static_cast<int64_t>(nt) * (BN / 2) + wcol * (WN / 2) + (within % (WN / 2));
-      if (j >= a.Fe) return -1;
-      return ((within < WN / 2) ? j : a.Fe + j) * a.Hd;
-    });
+    db.init(base16(a.gq, a.W_gu, static_cast<int64_t>(e) * 2 * a.Fe * a.Hd), 2 * a.Fe * KU, tid,
+            [&](int r) -> int64_t {
+              const int64_t w = gu_row(r);
+              return w < 0 ? -1 : w * KU;
+            });
   } else {
-    da.init(a.act + row0 * a.Fe, (row_end - row0) * a.Fe, tid,
-            [&](int r) -> int64_t { return row0 + r < row_end ? static_cast<int64_t>(r) * a.Fe : -1; });
-    const int64_t n0 = static_cast<int64_t>(nt) * BN;
-    db.init(a.W_d + static_cast<int64_t>(e) * a.Hd * a.Fe + n0 * a.Fe, (a.Hd - n0) * a.Fe, tid,
-            [&](int r) -> int64_t { return n0 + r < a.Hd ? static_cast<int64_t>(r) * a.Fe : -1; });
+    da.init(base16(a.aq, a.act, row0 * a.Fe), (row_end - row0) * KU, tid,
+            [&](int r) -> int64_t { return row0 + r < row_end ? static_cast<int64_t>(r) * KU : -1; });
+    db.init(base16(a.dq, a.W_d, static_cast<int64_t>(e) * a.Hd * a.Fe + n0 * a.Fe), (a.Hd - n0) * KU, tid,
+            [&](int r) -> int64_t { return n0 + r < a.Hd ? static_cast<int64_t>(r) * KU : -1; });
   }
   constexpr int NI = GatherDma<BM, NT>::NI + GatherDma<BN, NT>::NI;
-  const int nk = static_cast<int>((K + 63) / 64);
+  const int nk = static_cast<int>((KU + 63) / 64);
   auto fill = [&](uint4* buf, int t) {
     const int64_t k0 = 64 * static_cast<int64_t>(t);
-    da.issue(buf, k0, K, t < nk);
-    db.issue(buf + A_SLOTS, k0, K, t < nk);
+    da.issue(buf, k0, KU, t < nk);
+    db.issue(buf + A_SLOTS, k0, KU, t < nk);
   };
 
   f32x16_t acc[TM][TN];
@@ -233,13 +312,107 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  const int ar0 = wm * WM, br0 = wn * WN;
+  if constexpr (MX) {
+    // Scale rows of this lane's fragment rows (nullptr: a padding row, whose
+    // codes are zeros).
+    const uint32_t* sra[TM];
+    const uint32_t* srb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t grow = row0 + ar0 + 32 * i + (lane & 31);
+      const uint8_t* p = nullptr;
+      if (grow < row_end)
+        p = MODE == 0 ? a.xs + static_cast<int64_t>(a.perm[grow] / a.topk) * a.swh : a.as + grow * a.swf;
+      sra[i] = reinterpret_cast<const uint32_t*>(p);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = br0 + 32 * j + (lane & 31);
+      const uint8_t* p = nullptr;
+      if constexpr (MODE == 0) {
+        const int64_t w = gu_row(r);
+        if (w >= 0) p = a.gs + (static_cast<int64_t>(e) * 2 * a.Fe + w) * a.swh;
+      } else {
+        if (n0 + r < a.Hd) p = a.ds + (static_cast<int64_t>(e) * a.Hd + n0 + r) * a.swf;
+      }
+      srb[j] = reinterpret_cast<const uint32_t*>(p);
+    }
+    // Lane l < 32 supplies block 0 of each 64-code step, lane l + 32 block 1:
+    // shifting the k-tile's dword by a byte for the upper lanes makes byte 0
+    // (step 0) and byte 2 (step 1) the right exponents for every lane.
+    const int shift = 8 * (lane >> 5);
+    auto scale = [&](const uint32_t* p, int t) -> uint32_t { return p != nullptr ? p[t] >> shift : 0x7f7f7f7fu; };
+    uint32_t sa[TM], sb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = scale(sra[i], 0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = scale(srb[j], 0);
+    fill(lds[0], 0);
+    fill(lds[1], 1);
+    wait_vm_lds();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      uint4* cur = lds[kt & 1];
+      const uint4* ta = cur;
+      const uint4* tb = cur + A_SLOTS;
+      uint32_t na[TM], nb[TN];
+      const int tn = kt + 1 < nk ? kt + 1 : kt;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) na[i] = scale(sra[i], tn);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) nb[j] = scale(srb[j], tn);
+      {
+        uint4 fa0[TM], fa1[TM], fb0[TN], fb1[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          fa0[i] = lds_frag<true>(ta, ar0 + 32 * i, 0, lane);
+          fa1[i] = lds_frag<true>(ta, ar0 + 32 * i, 1, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          fb0[j] = lds_frag<true>(tb, br0 + 32 * j, 0, lane);
+          fb1[j] = lds_frag<true>(tb, br0 + 32 * j, 1, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = mfma_mx_32x32x64<0>(fa0[i], fa1[i], fb0[j], fb1[j], sa[i], sb[j], acc[i][j]);
+      }
+      {
+        uint4 fa0[TM], fa1[TM], fb0[TN], fb1[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          fa0[i] = lds_frag<true>(ta, ar0 + 32 * i, 2, lane);
+          fa1[i] = lds_frag<true>(ta, ar0 + 32 * i, 3, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          fb0[j] = lds_frag<true>(tb, br0 + 32 * j, 2, lane);
+          fb1[j] = lds_frag<true>(tb, br0 + 32 * j, 3, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = mfma_mx_32x32x64<2>(fa0[i], fa1[i], fb0[j], fb1[j], sa[i], sb[j], acc[i][j]);
+      }
+      wait_vm_lds();  // k-tile kt+1 and its exponents have landed; reads of kt retired
+      __syncthreads();
+      fill(cur, kt + 2);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb[j] = nb[j];
+    }
+  } else {
   fill(lds[0], 0);
   fill(lds[1], 1);
   wait_vmcnt<NI>();
   __syncthreads();
 
   constexpr int NR = TM + TN, NM = TM * TN, H = TM / 2;
-  const int ar0 = wm * WM, br0 = wn * WN;
   uint4 fa[2][TM], fb[2][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) fa[0][i] = lds_frag<true>(lds[0], ar0 + 32 * i, 0, lane);
@@ -279,6 +452,7 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
     for (int i = H; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_32x32x16(fa[1][i], fb[1][j], acc[i][j]);
+  }
   }
   wait_vm_lds();  // the trailing (all-zero) loads write LDS the epilogue reuses
   __syncthreads();
@@ -359,10 +533,13 @@ __global__ __launch_bounds__(256) void moe_unpermute_kernel(const MoeArgs a) {
 }
 
 struct MoeLayout {
-  size_t cnt, pick_row, perm, offsets, tile_start, counts, act, yperm, total;
+  size_t cnt, pick_row, perm, offsets, tile_start, counts, act, yperm, xq, xs, aq, as, total;
 };
 
-static MoeLayout moe_layout(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc) {
+static int64_t mx_scale_width(int64_t K) { return 4 * ceil_div(K, 128); }
+
+// With mx, the quantised token rows and activations follow the bf16 buffers.
+static MoeLayout moe_layout(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, bool mx = false) {
   MoeLayout L{};
   const int64_t r_cap = T * topk;
   size_t off = 0;
@@ -379,6 +556,12 @@ static MoeLayout moe_layout(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_l
   L.counts = take(static_cast<size_t>(E_loc) * 4);
   L.act = take(static_cast<size_t>(r_cap * Fe) * 2);
   L.yperm = take(static_cast<size_t>(r_cap * Hd) * 2);
+  if (mx) {
+    L.xq = take(static_cast<size_t>(T * Hd));
+    L.xs = take(static_cast<size_t>(T * mx_scale_width(Hd)));
+    L.aq = take(static_cast<size_t>(r_cap * Fe));
+    L.as = take(static_cast<size_t>(r_cap * mx_scale_width(Fe)));
+  }
   L.total = off;
   return L;
 }
@@ -445,9 +628,9 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
   const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc;
   a.tiles_n = static_cast<int>(ceil_div(Fe, MOE_BN / 2));
-  moe_gemm_kernel<0><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
+  moe_gemm_kernel<0, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
-  moe_gemm_kernel<1><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
+  moe_gemm_kernel<1, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a);
   return check_launch(fn);
 }
@@ -467,4 +650,113 @@ extern "C" int mp_grouped_expert_gemm_weighted_act(int64_t T, int64_t Hd, int64_
                                                    size_t ws_bytes, hipStream_t s) {
   return grouped_expert_gemm("mp_grouped_expert_gemm_weighted_act", true, T, Hd, Fe, topk, E_loc, e_start, X,
                              topk_ids, topk_w, W_gu, W_d, out, perm_picks, expert_offsets, ws, ws_bytes, s);
+}
+
+// ------------------------------------------------------------------ MXFP8
+
+extern "C" int mp_mxfp8_quantize(int64_t rows, int64_t K, const void* x, int64_t ld, uint8_t* q, uint8_t* scales,
+                                 hipStream_t s) {
+  static const char* fn = "mp_mxfp8_quantize";
+  MP_REQUIRE(rows >= 0 && K > 0 && K % 32 == 0, MP_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 32", fn,
+             (long long)K);
+  MP_REQUIRE(ld >= K && ld % 8 == 0, MP_ERR_SHAPE, "%s: ld=%lld must be >= K and a multiple of 8", fn, (long long)ld);
+  if (rows == 0) return MP_OK;
+  MP_REQUIRE_PTR(x);
+  MP_REQUIRE_PTR(q);
+  MP_REQUIRE_PTR(scales);
+  MP_REQUIRE_ALIGN(x);
+  MP_REQUIRE(reinterpret_cast<uintptr_t>(q) % 8 == 0, MP_ERR_ALIGN, "%s: q must be 8-byte aligned", fn);
+  const int64_t groups = rows * (K / 8);
+  mx_quantize_kernel<<<static_cast<unsigned>(ceil_div(groups, 256)), 256, 0, s>>>(
+      static_cast<const uint16_t*>(x), ld, rows, nullptr, K, q, scales, mx_scale_width(K));
+  return check_launch(fn);
+}
+
+extern "C" size_t mp_grouped_expert_gemm_mxfp8_workspace(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc) {
+  if (T < 0 || Hd <= 0 || Fe <= 0 || topk <= 0 || E_loc <= 0) return 0;
+  return moe_layout(T, Hd, Fe, topk, E_loc, true).total;
+}
+
+extern "C" int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, int e_start,
+                                            const void* X, const int32_t* topk_ids, const float* topk_w,
+                                            const uint8_t* W_gu_q, const uint8_t* W_gu_s, const uint8_t* W_d_q,
+                                            const uint8_t* W_d_s, void* out, int32_t* perm_picks,
+                                            int32_t* expert_offsets, void* ws, size_t ws_bytes, hipStream_t s) {
+  static const char* fn = "mp_grouped_expert_gemm_mxfp8";
+  MP_REQUIRE(T >= 0 && Hd > 0 && Fe > 0 && topk > 0 && E_loc > 0 && e_start >= 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  MP_REQUIRE(Hd % 32 == 0 && Fe % 32 == 0, MP_ERR_SHAPE, "%s: Hd and Fe must be multiples of 32 (MX blocks)", fn);
+  MP_REQUIRE(T * Hd * 2 < 0x7fffffffLL && 2 * Fe * Hd < 0x7fffffffLL && T * topk * Fe * 2 < 0x7fffffffLL,
+             MP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+  MP_REQUIRE_PTR(X);
+  MP_REQUIRE_PTR(topk_ids);
+  MP_REQUIRE_PTR(topk_w);
+  MP_REQUIRE_PTR(W_gu_q);
+  MP_REQUIRE_PTR(W_gu_s);
+  MP_REQUIRE_PTR(W_d_q);
+  MP_REQUIRE_PTR(W_d_s);
+  MP_REQUIRE_PTR(out);
+  MP_REQUIRE_ALIGN(X);
+  MP_REQUIRE_ALIGN(W_gu_q);
+  MP_REQUIRE_ALIGN(W_d_q);
+  MP_REQUIRE_ALIGN(out);
+  MP_REQUIRE(reinterpret_cast<uintptr_t>(W_gu_s) % 4 == 0 && reinterpret_cast<uintptr_t>(W_d_s) % 4 == 0,
+             MP_ERR_ALIGN, "%s: scale arrays must be 4-byte aligned", fn);
+  const MoeLayout L = moe_layout(T, Hd, Fe, topk, E_loc, true);
+  MP_REQUIRE(ws != nullptr && ws_bytes >= L.total, MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, L.total);
+  MP_REQUIRE_ALIGN(ws);
+  if (T == 0) return MP_OK;
+  char* w = static_cast<char*>(ws);
+  MoeArgs a{};
+  a.T = T;
+  a.Hd = Hd;
+  a.Fe = Fe;
+  a.topk = topk;
+  a.E_loc = E_loc;
+  a.e_start = e_start;
+  a.r_cap = T * topk;
+  a.X = static_cast<const uint16_t*>(X);
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.out = static_cast<uint16_t*>(out);
+  a.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
+  a.pick_row = reinterpret_cast<int32_t*>(w + L.pick_row);
+  a.perm = perm_picks != nullptr ? perm_picks : reinterpret_cast<int32_t*>(w + L.perm);
+  a.offsets = expert_offsets != nullptr ? expert_offsets : reinterpret_cast<int32_t*>(w + L.offsets);
+  a.tile_start = reinterpret_cast<int32_t*>(w + L.tile_start);
+  a.counts = reinterpret_cast<int32_t*>(w + L.counts);
+  a.act = reinterpret_cast<uint16_t*>(w + L.act);
+  a.yperm = reinterpret_cast<uint16_t*>(w + L.yperm);
+  a.swh = mx_scale_width(Hd);
+  a.swf = mx_scale_width(Fe);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(w + L.xq);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(w + L.xs);
+  uint8_t* aq = reinterpret_cast<uint8_t*>(w + L.aq);
+  uint8_t* as = reinterpret_cast<uint8_t*>(w + L.as);
+  a.xq = xq;
+  a.xs = xs;
+  a.gq = W_gu_q;
+  a.gs = W_gu_s;
+  a.dq = W_d_q;
+  a.ds = W_d_s;
+  a.aq = aq;
+  a.as = as;
+  const unsigned tgrid = static_cast<unsigned>(ceil_div(T, 256));
+  moe_count_kernel<<<tgrid, 256, 0, s>>>(a);
+  moe_scan_kernel<<<static_cast<unsigned>(E_loc), 1024, 0, s>>>(a);
+  moe_offsets_kernel<<<1, 64, 0, s>>>(a);
+  moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
+  // Token rows quantised once along the hidden dimension (the expert GEMMs'
+  // reduction dimension); the weights arrive quantised.
+  mx_quantize_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a.X, Hd, T, nullptr, Hd, xq,
+                                                                                          xs, a.swh);
+  const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc;
+  a.tiles_n = static_cast<int>(ceil_div(Fe, MOE_BN / 2));
+  moe_gemm_kernel<0, true><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
+  // The bf16 activation rows (R of them, known on the device) quantised along Fe.
+  mx_quantize_kernel<<<static_cast<unsigned>(ceil_div(a.r_cap * (Fe / 8), 256)), 256, 0, s>>>(
+      a.act, Fe, a.r_cap, a.offsets + E_loc, Fe, aq, as, a.swf);
+  a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
+  moe_gemm_kernel<1, true><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
+  moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a);
+  return check_launch(fn);
 }

@@ -74,6 +74,10 @@ _SIGS = {
                                        c_p, c_p, c_sz, c_p]),
     "mp_grouped_expert_gemm_weighted_act": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p,
                                                     c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "mp_mxfp8_quantize": (c_i32, [c_i64, c_i64, c_p, c_i64, c_p, c_p, c_p]),
+    "mp_grouped_expert_gemm_mxfp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_i32, c_i32]),
+    "mp_grouped_expert_gemm_mxfp8": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_p,
+                                             c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "mp_layernorm": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_p, c_f32, c_p, c_p, c_p, c_p]),
     "mp_layernorm_bwd_workspace": (c_sz, [c_i64, c_i64]),
     "mp_layernorm_bwd": (c_i32, [c_i32, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
@@ -363,6 +367,30 @@ def mp_grouped_expert_gemm_weighted_act(X, topk_ids, topk_w, W_gu, W_d, e_start,
                                         expert_offsets=None, ws=None, stream=None):
     _grouped_expert_gemm("mp_grouped_expert_gemm_weighted_act", X, topk_ids, topk_w, W_gu, W_d, e_start, out,
                          perm_picks, expert_offsets, ws, stream)
+
+
+# ------------------------------------------------------------------ MXFP8
+
+def mxfp8_scale_width(K):
+    return 4 * ((K + 127) // 128)
+
+
+def mp_mxfp8_quantize(x, q, scales, stream=None):
+    rows, K = x.shape
+    _call("mp_mxfp8_quantize", rows, K, _p(x), x.stride(0), _p(q), _p(scales), _s(stream))
+
+
+def mp_grouped_expert_gemm_mxfp8(X, topk_ids, topk_w, W_gu_q, W_gu_s, W_d_q, W_d_s, e_start, out, perm_picks=None,
+                                 expert_offsets=None, ws=None, stream=None):
+    T, Hd = X.shape
+    topk = topk_ids.shape[1]
+    E_loc, two_fe, _ = W_gu_q.shape
+    Fe = two_fe // 2
+    need = lib().mp_grouped_expert_gemm_mxfp8_workspace(T, Hd, Fe, topk, E_loc)
+    ws = ws if ws is not None else workspace(need, X.device)
+    _call("mp_grouped_expert_gemm_mxfp8", T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w),
+          _p(W_gu_q), _p(W_gu_s), _p(W_d_q), _p(W_d_s), _p(out), _p(perm_picks), _p(expert_offsets), _p(ws),
+          need if ws is not None else 0, _s(stream))
 
 
 # ---------------------------------------------------------------- LayerNorm
