@@ -49,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the MXFP8 expert GEMMs)
 
 # HBM traffic of the roofline kernel, measured with rocprofv3 counters and
 # recorded (with the hash of the sources it was measured on) in this file.
@@ -371,6 +372,16 @@ def main():
         out["moe_mxfp8_ms"] = round(mx_ms, 4)
         out["moe_mxfp8_TFLOPS"] = round(moe_fl / (mx_ms * 1e-3) / 1e12, 2)
         del gq, gs, dq, ds, mxws
+        # Whole-call rates of the two MoE shard forms against their MFMA peaks
+        # (permutation, quantisation and unpermute included in the time).
+        roofs.append({"kernel": "MoE hot shard, bf16 grouped expert GEMMs (whole call)", "bound": "mfma",
+                      "achieved": out["moe_TFLOPS"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(out["moe_TFLOPS"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                      "avg_launch_us": round(moe_ms * 1e3, 1), "algorithmic_per_launch": moe_fl})
+        roofs.append({"kernel": "MoE hot shard, MXFP8 grouped expert GEMMs (whole call)", "bound": "mfma",
+                      "achieved": out["moe_mxfp8_TFLOPS"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(out["moe_mxfp8_TFLOPS"] / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                      "avg_launch_us": round(mx_ms * 1e3, 1), "algorithmic_per_launch": moe_fl})
     if roofs:
         out["roofline"] = roofs[0]
         out["rooflines"] = roofs

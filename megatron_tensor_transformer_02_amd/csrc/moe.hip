@@ -314,97 +314,110 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
 
   const int ar0 = wm * WM, br0 = wn * WN;
   if constexpr (MX) {
-    // Scale rows of this lane's fragment rows (nullptr: a padding row, whose
-    // codes are zeros).
+    // Scale rows of this lane's fragment rows.  A padding row (codes read as
+    // zeros) borrows a real row's exponents, which are finite (never 0xFF),
+    // so every load is unconditional and nothing waits for it before use.
     const uint32_t* sra[TM];
     const uint32_t* srb[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int64_t grow = row0 + ar0 + 32 * i + (lane & 31);
-      const uint8_t* p = nullptr;
-      if (grow < row_end)
-        p = MODE == 0 ? a.xs + static_cast<int64_t>(a.perm[grow] / a.topk) * a.swh : a.as + grow * a.swf;
+      int64_t grow = row0 + ar0 + 32 * i + (lane & 31);
+      if (grow >= row_end) grow = row0;
+      const uint8_t* p =
+          MODE == 0 ? a.xs + static_cast<int64_t>(a.perm[grow] / a.topk) * a.swh : a.as + grow * a.swf;
       sra[i] = reinterpret_cast<const uint32_t*>(p);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = br0 + 32 * j + (lane & 31);
-      const uint8_t* p = nullptr;
+      const uint8_t* p;
       if constexpr (MODE == 0) {
-        const int64_t w = gu_row(r);
-        if (w >= 0) p = a.gs + (static_cast<int64_t>(e) * 2 * a.Fe + w) * a.swh;
+        int64_t w = gu_row(r);
+        if (w < 0) w = 0;
+        p = a.gs + (static_cast<int64_t>(e) * 2 * a.Fe + w) * a.swh;
       } else {
-        if (n0 + r < a.Hd) p = a.ds + (static_cast<int64_t>(e) * a.Hd + n0 + r) * a.swf;
+        const int64_t n = n0 + r < a.Hd ? n0 + r : 0;
+        p = a.ds + (static_cast<int64_t>(e) * a.Hd + n) * a.swf;
       }
       srb[j] = reinterpret_cast<const uint32_t*>(p);
     }
     // Lane l < 32 supplies block 0 of each 64-code step, lane l + 32 block 1:
     // shifting the k-tile's dword by a byte for the upper lanes makes byte 0
-    // (step 0) and byte 2 (step 1) the right exponents for every lane.
+    // (step 0) and byte 2 (step 1) the right exponents for every lane.  The
+    // shift is applied after the barrier that waits for the load.
     const int shift = 8 * (lane >> 5);
-    auto scale = [&](const uint32_t* p, int t) -> uint32_t { return p != nullptr ? p[t] >> shift : 0x7f7f7f7fu; };
     uint32_t sa[TM], sb[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = scale(sra[i], 0);
+    for (int i = 0; i < TM; ++i) sa[i] = sra[i][0];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sb[j] = scale(srb[j], 0);
+    for (int j = 0; j < TN; ++j) sb[j] = srb[j][0];
     fill(lds[0], 0);
     fill(lds[1], 1);
     wait_vm_lds();
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] >>= shift;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] >>= shift;
+    // Software pipeline in registers: a fragment is reloaded as soon as its
+    // last MFMA of the step is issued (step 0's A fragments become step 1's,
+    // step 1's become the next k-tile's step 0), and the barrier sits after
+    // the first half of step 1, when every read of the k-tile has returned.
+    constexpr int H = TM / 2;
+    uint4 fa0[TM], fa1[TM], fb0[TN], fb1[TN];
+    auto load_a = [&](const uint4* t, int i, int step) {
+      fa0[i] = lds_frag<true>(t, ar0 + 32 * i, 2 * step, lane);
+      fa1[i] = lds_frag<true>(t, ar0 + 32 * i, 2 * step + 1, lane);
+    };
+    auto load_b = [&](const uint4* t, int j, int step) {
+      fb0[j] = lds_frag<true>(t + A_SLOTS, br0 + 32 * j, 2 * step, lane);
+      fb1[j] = lds_frag<true>(t + A_SLOTS, br0 + 32 * j, 2 * step + 1, lane);
+    };
+#pragma unroll
+    for (int i = 0; i < TM; ++i) load_a(lds[0], i, 0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) load_b(lds[0], j, 0);
     for (int kt = 0; kt < nk; ++kt) {
       uint4* cur = lds[kt & 1];
-      const uint4* ta = cur;
-      const uint4* tb = cur + A_SLOTS;
+      const uint4* nxt = lds[(kt & 1) ^ 1];
       uint32_t na[TM], nb[TN];
       const int tn = kt + 1 < nk ? kt + 1 : kt;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) na[i] = scale(sra[i], tn);
+      for (int i = 0; i < TM; ++i) na[i] = sra[i][tn];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) nb[j] = scale(srb[j], tn);
-      {
-        uint4 fa0[TM], fa1[TM], fb0[TN], fb1[TN];
+      for (int j = 0; j < TN; ++j) nb[j] = srb[j][tn];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          fa0[i] = lds_frag<true>(ta, ar0 + 32 * i, 0, lane);
-          fa1[i] = lds_frag<true>(ta, ar0 + 32 * i, 1, lane);
-        }
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          fb0[j] = lds_frag<true>(tb, br0 + 32 * j, 0, lane);
-          fb1[j] = lds_frag<true>(tb, br0 + 32 * j, 1, lane);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = mfma_mx_32x32x64<0>(fa0[i], fa1[i], fb0[j], fb1[j], sa[i], sb[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma_mx_32x32x64<0>(fa0[i], fa1[i], fb0[j], fb1[j], sa[i], sb[j], acc[i][j]);
+        load_a(cur, i, 1);
       }
-      {
-        uint4 fa0[TM], fa1[TM], fb0[TN], fb1[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          fa0[i] = lds_frag<true>(ta, ar0 + 32 * i, 2, lane);
-          fa1[i] = lds_frag<true>(ta, ar0 + 32 * i, 3, lane);
-        }
+      for (int j = 0; j < TN; ++j) load_b(cur, j, 1);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          fb0[j] = lds_frag<true>(tb, br0 + 32 * j, 2, lane);
-          fb1[j] = lds_frag<true>(tb, br0 + 32 * j, 3, lane);
-        }
+      for (int i = 0; i < H; ++i)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = mfma_mx_32x32x64<2>(fa0[i], fa1[i], fb0[j], fb1[j], sa[i], sb[j], acc[i][j]);
-      }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma_mx_32x32x64<2>(fa0[i], fa1[i], fb0[j], fb1[j], sa[i], sb[j], acc[i][j]);
       wait_vm_lds();  // k-tile kt+1 and its exponents have landed; reads of kt retired
       __syncthreads();
       fill(cur, kt + 2);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) sa[i] = na[i];
+      for (int i = 0; i < H; ++i) load_a(nxt, i, 0);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sb[j] = nb[j];
+      for (int i = H; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma_mx_32x32x64<2>(fa0[i], fa1[i], fb0[j], fb1[j], sa[i], sb[j], acc[i][j]);
+        load_a(nxt, i, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) load_b(nxt, j, 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa[i] = na[i] >> shift;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb[j] = nb[j] >> shift;
     }
   } else {
   fill(lds[0], 0);
