@@ -168,3 +168,49 @@ def test_workspace_queries_are_pure(lib):
     assert a >= 8192 * 1536 * 2
     assert lib.mp_bias_grad_workspace(8192, 3072) >= 3072 * 4
     assert lib.mp_layernorm_bwd_workspace(8192, 1024) >= 2 * 1024 * 4
+
+
+def test_moe_forms_and_mxfp8_validation(lib):
+    # mp_mxfp8_quantize: K a multiple of 32, ld >= K and a multiple of 8, q 8-byte aligned.
+    rc, msg = call(lib, "mp_mxfp8_quantize", 4, 48, ALIGNED, 48, ALIGNED, ALIGNED, None)
+    assert rc == -2 and "K=48" in msg
+    rc, _ = call(lib, "mp_mxfp8_quantize", 4, 64, ALIGNED, 32, ALIGNED, ALIGNED, None)
+    assert rc == -2  # ld < K
+    rc, _ = call(lib, "mp_mxfp8_quantize", 4, 64, None, 64, ALIGNED, ALIGNED, None)
+    assert rc == -1
+    rc, _ = call(lib, "mp_mxfp8_quantize", 4, 64, ALIGNED, 64, ALIGNED + 4, ALIGNED, None)
+    assert rc == -5
+    rc, _ = call(lib, "mp_mxfp8_quantize", 0, 64, None, 64, None, None, None)
+    assert rc == 0  # no rows: nothing to do
+    # mp_grouped_expert_gemm_mxfp8: MX blocks need Hd, Fe multiples of 32; scales 4-byte aligned.
+    T, Hd, Fe, topk, E = 16, 64, 64, 2, 2
+    need = lib.mp_grouped_expert_gemm_mxfp8_workspace(T, Hd, Fe, topk, E)
+    args = [ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED,
+            ctypes.c_size_t(need), None]
+    rc, msg = call(lib, "mp_grouped_expert_gemm_mxfp8", T, 48, Fe, topk, E, 0, *args)
+    assert rc == -2 and "32" in msg
+    bad = list(args)
+    bad[4] = None  # W_gu_s
+    rc, _ = call(lib, "mp_grouped_expert_gemm_mxfp8", T, Hd, Fe, topk, E, 0, *bad)
+    assert rc == -1
+    bad = list(args)
+    bad[6] = ALIGNED + 2  # W_d_s
+    rc, msg = call(lib, "mp_grouped_expert_gemm_mxfp8", T, Hd, Fe, topk, E, 0, *bad)
+    assert rc == -5 and "scale" in msg
+    bad = list(args)
+    bad[11] = ctypes.c_size_t(need - 1)
+    rc, _ = call(lib, "mp_grouped_expert_gemm_mxfp8", T, Hd, Fe, topk, E, 0, *bad)
+    assert rc == -6
+    rc, _ = call(lib, "mp_grouped_expert_gemm_mxfp8", 0, Hd, Fe, topk, E, 0, *args)
+    assert rc == 0  # no tokens: nothing to do
+    # The weighted-activation form validates like the weighted-unpermute form.
+    need = lib.mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E)
+    rc, _ = call(lib, "mp_grouped_expert_gemm_weighted_act", T, Hd, Fe, topk, E, 0, None, ALIGNED, ALIGNED, ALIGNED,
+                 ALIGNED, ALIGNED, None, None, ALIGNED, ctypes.c_size_t(need), None)
+    assert rc == -1
+    rc, _ = call(lib, "mp_grouped_expert_gemm_weighted_act", T, 12, Fe, topk, E, 0, ALIGNED, ALIGNED, ALIGNED,
+                 ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, ctypes.c_size_t(need), None)
+    assert rc == -2
+    # The MXFP8 workspace holds the bf16 one plus the quantised rows.
+    assert lib.mp_grouped_expert_gemm_mxfp8_workspace(4096, 7168, 2048, 8, 8) >= (
+        lib.mp_grouped_expert_gemm_workspace(4096, 7168, 2048, 8, 8) + 4096 * 7168 + 4096 * 8 * 2048)
