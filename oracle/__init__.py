@@ -43,5 +43,7 @@ from .vocab import (
     embedding, vocab_parallel_embedding, vocab_parallel_embedding_bwd, full_cross_entropy, full_cross_entropy_grad,
     vocab_parallel_xent_triples, vocab_xent_combine, vocab_parallel_xent_bwd,
 )
-from .moe import moe_permutation, expert_swiglu_ffn, moe_forward, moe_forward_rows, moe_forward_weighted_act
+from .moe import (
+    moe_permutation, expert_swiglu_ffn, moe_forward, moe_forward_rows, moe_forward_weighted_act, moe_backward,
+)
 from .mxfp8 import e4m3_value, e4m3_round, shared_exponent, scale_width, mx_quantize, mx_dequantize, moe_forward_mxfp8

@@ -134,3 +134,63 @@ def moe_forward_weighted_act(x, topk_ids, topk_w, w_gu, w_d, e_start):
     for r, pk in enumerate(picks):
         out[int(pk) // topk] += y_perm[r]
     return out, counts, offsets, picks, y_perm
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def moe_backward(x, topk_ids, topk_w, w_gu, w_d, e_start, dout):
+    """Backward of :func:`moe_forward` (the weighted-unpermute form) for the
+    upstream gradient ``dout [T, Hd]`` of the shard's output.
+
+    MOE-core, technical summary 2.4: the backward runs the same grouped
+    structure, per local expert over its permuted rows.  For a local pick
+    ``(t, k)`` of expert ``e`` with ``g = x_t W_g^T``, ``u = x_t W_u^T``,
+    ``a = silu(g) * u`` and ``y = a W_d^T``:
+
+    * ``dy = w[t,k] * dout_t`` and ``d w[t,k] = dout_t . y``;
+    * ``da = dy W_d`` and ``dW_d += dy^T a``;
+    * ``dg = da * u * silu'(g)`` with ``silu'(g) = s (1 + g (1 - s))``,
+      ``s = sigmoid(g)``, and ``du = da * silu(g)``;
+    * ``dW_g += dg^T x_t``, ``dW_u += du^T x_t``, ``dx_t += dg W_g + du W_u``.
+
+    Picks on other shards get ``d w = 0`` and add nothing to ``dx``.  Returns
+    a dict with ``x [T, Hd]``, ``w_gu [E, 2Fe, Hd]``, ``w_d [E, Hd, Fe]`` and
+    ``topk_w [T, topk]``.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    tokens, topk = ids.shape
+    w = _f64(topk_w).reshape(-1)
+    x, dout = _f64(x), _f64(dout)
+    w_gu, w_d = _f64(w_gu), _f64(w_d)
+    e_local, _, fe = w_d.shape
+    counts, offsets, picks = moe_permutation(ids, e_start, e_local)
+    dx = np.zeros_like(x)
+    dw_gu = np.zeros_like(w_gu)
+    dw_d = np.zeros_like(w_d)
+    dw = np.zeros(tokens * topk)
+    for e in range(e_local):
+        sel = picks[offsets[e]:offsets[e + 1]]
+        if sel.size == 0:
+            continue
+        tok = sel // topk
+        xe = x[tok]
+        wg, wu, wd = w_gu[e, :fe], w_gu[e, fe:], w_d[e]
+        g = xe @ wg.T
+        u = xe @ wu.T
+        s = _sigmoid(g)
+        a = g * s * u
+        y = a @ wd.T
+        dy = w[sel][:, None] * dout[tok]
+        dw[sel] = np.sum(dout[tok] * y, axis=1)
+        da = dy @ wd
+        dw_d[e] = dy.T @ a
+        dg = da * u * s * (1.0 + g * (1.0 - s))
+        du = da * g * s
+        dw_gu[e, :fe] = dg.T @ xe
+        dw_gu[e, fe:] = du.T @ xe
+        dxe = dg @ wg + du @ wu
+        for i, t in enumerate(tok):
+            dx[t] += dxe[i]
+    return {"x": dx, "w_gu": dw_gu, "w_d": dw_d, "topk_w": dw.reshape(tokens, topk)}

@@ -10,7 +10,9 @@ MoE (MOE-core, technical summary 2.2 and 2.4): the permutation is pinned
 against numpy's stable argsort; the expert FFN against a hand-computed scalar
 case and a brute-force loop; the permuted forward against the per-token
 definition; the memory-efficient form (weight on the activation) against the
-weighted-unpermute form, which linearity of the down projection makes equal.
+weighted-unpermute form, which linearity of the down projection makes equal;
+the backward against central finite differences of the per-token forward and
+against torch's float64 autograd of a per-token forward written in torch ops.
 """
 
 import math
@@ -195,3 +197,72 @@ def test_weighted_activation_form_equals_weighted_unpermute():
     # A token whose picks all land elsewhere gets zeros.
     none_local = ~np.any((ids >= e_start) & (ids < e_start + e_local), axis=1)
     assert np.all(out[none_local] == 0)
+
+
+def _moe_loss(x, ids, w, wgu, wd, e_start, dout):
+    """sum(dout * out) with out from the per-token definition (not the
+    permuted code the backward mirrors)."""
+    out = O.moe_forward_rows(x, ids, w, wgu, wd, e_start, list(range(x.shape[0])))
+    return float(np.sum(dout * out))
+
+
+def test_moe_backward_central_differences():
+    """Every gradient of the MoE shard (input, gate/up and down weights,
+    routing weights) against central finite differences of the per-token
+    forward definition, at a tiny shape that includes a token with no local
+    pick and a local expert nobody picks."""
+    t, hd, fe, experts, topk, e_start, e_local = 7, 5, 4, 8, 2, 2, 4
+    ids, w = routing(t, experts, topk)
+    ids[0] = [0, 7]          # no local pick
+    ids[ids == 5] = 6        # expert 5 (local index 3) is never picked...
+    ids[1] = [6, 1]          # ...and ids stay distinct per token
+    ids[2] = [2, 6]
+    assert not np.any(ids == 5) and all(len(set(r)) == topk for r in ids)
+    x = rnd(t, hd)
+    wgu, wd = rnd(e_local, 2 * fe, hd, scale=0.5), rnd(e_local, hd, fe, scale=0.5)
+    dout = rnd(t, hd)
+    g = O.moe_backward(x, ids, w, wgu, wd, e_start, dout)
+    args = {"x": x, "w_gu": wgu, "w_d": wd, "topk_w": w}
+    h = 1e-6
+    for name, arr in args.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + h
+            lp = _moe_loss(args["x"], ids, args["topk_w"], args["w_gu"], args["w_d"], e_start, dout)
+            arr[idx] = keep - h
+            lm = _moe_loss(args["x"], ids, args["topk_w"], args["w_gu"], args["w_d"], e_start, dout)
+            arr[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.linalg.norm(g[name] - fd) / max(np.linalg.norm(fd), 1e-30)
+        assert err <= 1e-6, (name, err)
+    assert np.all(g["x"][0] == 0) and np.all(g["topk_w"][0] == 0)
+    assert np.all(g["w_gu"][3] == 0) and np.all(g["w_d"][3] == 0)
+    local = (ids >= e_start) & (ids < e_start + e_local)
+    assert np.all(g["topk_w"][~local] == 0)
+
+
+def test_moe_backward_matches_torch_autograd():
+    """The same gradients from torch's float64 autograd through a per-token
+    forward written with torch ops (an independent library routine)."""
+    t, hd, fe, experts, topk, e_start, e_local = 40, 12, 10, 16, 4, 4, 6
+    ids, w = routing(t, experts, topk)
+    x = rnd(t, hd)
+    wgu, wd = rnd(e_local, 2 * fe, hd, scale=0.3), rnd(e_local, hd, fe, scale=0.3)
+    dout = rnd(t, hd)
+    g = O.moe_backward(x, ids, w, wgu, wd, e_start, dout)
+    tx, tw = torch.tensor(x, requires_grad=True), torch.tensor(w, requires_grad=True)
+    tgu, td = torch.tensor(wgu, requires_grad=True), torch.tensor(wd, requires_grad=True)
+    rows = []
+    for i in range(t):
+        acc = torch.zeros(hd, dtype=torch.float64)
+        for k in range(topk):
+            e = int(ids[i, k]) - e_start
+            if 0 <= e < e_local:
+                act = tF.silu(tgu[e, :fe] @ tx[i]) * (tgu[e, fe:] @ tx[i])
+                acc = acc + tw[i, k] * (td[e] @ act)
+        rows.append(acc)
+    (torch.stack(rows) * torch.tensor(dout)).sum().backward()
+    for name, ref in (("x", tx), ("topk_w", tw), ("w_gu", tgu), ("w_d", td)):
+        r = ref.grad.numpy()
+        assert np.allclose(g[name], r, rtol=1e-11, atol=1e-12), name
