@@ -357,6 +357,50 @@ int mp_grouped_expert_gemm_weighted_act(int64_t T, int64_t Hd, int64_t Fe, int t
                                         void* out, int32_t* perm_picks, int32_t* expert_offsets,
                                         void* ws, size_t ws_bytes, hipStream_t s);
 
+/* Training forward of mp_grouped_expert_gemm (same arguments, layouts and
+ * errors; no perm_picks / expert_offsets: they stay in ws).  It also writes
+ * gu_save [T*topk, 2*Fe] bf16: row r of the permuted order holds that pick's
+ * gate pre-activation x W_g,e^T in columns [0, Fe) and its up pre-activation
+ * x W_u,e^T in [Fe, 2*Fe) (rows >= R untouched).  ws then holds the
+ * permutation, the expert schedule, the activation and the expert outputs
+ * that mp_grouped_expert_gemm_bwd reads: keep it, and gu_save, unchanged
+ * until that call. */
+int mp_grouped_expert_gemm_fwd_train(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                                     int e_start, const void* X, const int32_t* topk_ids,
+                                     const float* topk_w, const void* W_gu, const void* W_d,
+                                     void* out, void* gu_save, void* ws, size_t ws_bytes,
+                                     hipStream_t s);
+
+/* Worst-case workspace bytes of mp_grouped_expert_gemm_bwd (sizes alone). */
+size_t mp_grouped_expert_gemm_bwd_workspace(int64_t T, int64_t Hd, int64_t Fe, int topk,
+                                            int E_loc);
+
+/* Backward of the MoE shard (MOE-core, technical summary 2.4: the expert
+ * GEMMs of the backward are grouped like the forward's, with the shapes on
+ * the device).  Given dOut [T,Hd] bf16, the gradient of the shard's output,
+ * and the state left by mp_grouped_expert_gemm_fwd_train with the same
+ * sizes (gu_save; fwd_ws of fwd_ws_bytes), for every local pick (t,k) of
+ * expert e (row r of the permutation):
+ *   dy_r = topk_w[t,k] * dOut[t];  dtopk_w[t,k] = dOut[t] . y_r (fp32);
+ *   d act_r = dy_r W_d,e;  dW_d[e] = sum_r dy_r^T act_r;
+ *   d gate = d act * up * s (1 + gate (1 - s)), s = sigmoid(gate);
+ *   d up = d act * silu(gate);
+ *   dW_gu[e] = sum_r [d gate_r ; d up_r]^T x_t;
+ *   dX[t] = sum over t's local picks (k ascending, fp32) of
+ *           d gate_r W_g,e + d up_r W_u,e.
+ * dX [T,Hd] bf16 (zeros for tokens without a local pick); dW_gu
+ * [E_loc,2*Fe,Hd] and dW_d [E_loc,Hd,Fe] fp32, overwritten (zeros for an
+ * expert without rows); dtopk_w [T,topk] fp32 (zero for picks on other
+ * shards).  Weight gradients sum their rows in a fixed order
+ * (deterministic).  ws >= mp_grouped_expert_gemm_bwd_workspace().  Same
+ * shape limits and errors as the forward. */
+int mp_grouped_expert_gemm_bwd(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                               const void* X, const float* topk_w, const void* W_gu,
+                               const void* W_d, const void* dOut, const void* gu_save,
+                               const void* fwd_ws, size_t fwd_ws_bytes, void* dX, float* dW_gu,
+                               float* dW_d, float* dtopk_w, void* ws, size_t ws_bytes,
+                               hipStream_t s);
+
 /* ------------------------------------------------------------------ MXFP8 */
 
 /* MXFP8 block quantisation (MOE-core, technical summary 2.5: expert GEMMs and

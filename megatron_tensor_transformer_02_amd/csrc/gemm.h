@@ -6,7 +6,7 @@
 
 namespace mp {
 
-enum Epilogue { EPI_STORE = 0, EPI_SPLITK = 1, EPI_DACT = 2, EPI_LSE = 3 };
+enum Epilogue { EPI_STORE = 0, EPI_SPLITK = 1, EPI_DACT = 2, EPI_LSE = 3, EPI_SWIGLU_BWD = 4 };
 
 // Operand layouts of C = A * B^T: NT = both K-contiguous; NN = A K-contiguous,
 // B MN-contiguous; TN = both MN-contiguous.
@@ -28,6 +28,22 @@ size_t gemm_splitk_workspace(mp_dtype dt, int64_t M, int64_t N, int64_t K);
 int gemm_lse_slots(int64_t T, int64_t V, int64_t K);
 int gemm_logits_lse(int64_t T, int64_t V, int64_t K, const void* H, const void* E, const int32_t* labels,
                     int64_t v_start, float* part, hipStream_t s);
+
+// Grouped bf16 GEMMs with their shapes on the device (256x256 tiles).
+// GRP_M (layout NN): group e is C[lo:hi, :N] = A[lo:hi, :K] * B_e^T with
+// lo, hi = off[e], off[e+1], B_e = B + e * stride_b, and tiles[e] the first
+// 256-row tile of group e in a flat tile list (tiles[groups] = its length,
+// at most max_mtiles).  epi = EPI_STORE (bf16 out) or EPI_SWIGLU_BWD: C and
+// zin are [rows, 2N]; zin holds the gate (columns [0, N)) and up ([N, 2N))
+// pre-activations, C receives d gate and d up of d act = A * B_e^T.
+// GRP_K (layout TN, fp32 out): group e is C_e[M, N] = sum over k in
+// [lo, hi) of A[k, m] * B[k, n], C_e = C + e * stride_c (zeros when lo = hi).
+int gemm_grouped_m(int epi, int groups, const int32_t* off, const int32_t* tiles, int64_t max_mtiles, int64_t N,
+                   int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b, void* C,
+                   int64_t ldc, const void* zin, hipStream_t s);
+// max_k bounds every group's k-range (for the 2 GiB addressing check).
+int gemm_grouped_k(int groups, const int32_t* off, int64_t max_k, int64_t M, int64_t N, const void* A, int64_t lda,
+                   const void* B, int64_t ldb, float* C, int64_t ldc, int64_t stride_c, hipStream_t s);
 
 // Deterministic column sums of a [rows, cols] matrix into out[cols] (fp32).
 int colsum(mp_dtype dt, int64_t rows, int64_t cols, const void* dy, float* out, void* ws, hipStream_t s);

@@ -46,7 +46,18 @@ struct GemmArgs {
   int64_t v_start;        // first vocabulary row of the shard (EPI_LSE)
   float* lse_part;        // [M, lse_slots, 3] (EPI_LSE)
   int lse_slots;
+  // Grouped GEMMs (one problem per group, shapes on the device).  Group e
+  // owns rows [grp_off[e], grp_off[e+1]) of A and C (GRP_M; its 256-row
+  // tiles start at tile grp_tiles[e] of a flat tile list) or that k-range of
+  // both operands (GRP_K; group e's output at C + e * grp_stride_c).  B of
+  // group e (GRP_M) starts at B + e * grp_stride_b.
+  const int32_t* grp_off;    // [groups + 1]
+  const int32_t* grp_tiles;  // [groups + 1] (GRP_M)
+  int groups;
+  int64_t grp_stride_b, grp_stride_c;
 };
+
+enum GroupMode { GRP_NONE = 0, GRP_M = 1, GRP_K = 2 };
 
 // Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs;
 // renumber so XCD x gets a contiguous range of logical tiles, then walk
@@ -69,8 +80,8 @@ __device__ __forceinline__ void map_tile(int wg, int nwg, int tiles_m, int tiles
 #define MP_GEMM_WARM 2
 #endif
 
-template <int BM, int BN, int NW, int WR, bool AK, bool BKC, int EPI, int ACT>
-__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
+template <int BM, int BN, int NW, int WR, bool AK, bool BKC, int EPI, int ACT, int GRP = GRP_NONE>
+__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g0) {
   // WR x (NW / WR) waves; each wave owns (BM / WR) x (BN / (NW / WR)) of the
   // tile.  Eight waves put two on each SIMD, so one wave's MFMAs run while
   // the other waits at the barrier or on its fragment reads.
@@ -79,12 +90,48 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
   constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;
   __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
   __shared__ uint32_t warm_sink[64];
-  constexpr int WD = MP_GEMM_WARM;
+  // Grouped problems skip the grid-wide warm-up: their grids are sized for
+  // the worst case and most of the workgroups of a group exit at once.
+  constexpr int WD = GRP == GRP_NONE ? MP_GEMM_WARM : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WC, wn = wave % WC;
+  GemmArgs g = g0;
   int tmi, tni;
-  map_tile(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, g.group_m, tmi, tni);
+  if constexpr (GRP == GRP_M) {
+    // Flat list of the groups' tiles (tile-rows of every group back to back,
+    // each tile-row tiles_n wide); workgroups past its end exit.  The list is
+    // dealt to the XCDs in contiguous ranges, as map_tile does.
+    const int n_real = g.grp_tiles[g.groups] * g.tiles_n;
+    const int wg = blockIdx.x;
+    if (wg >= n_real) return;
+    const int per = n_real >> 3, rem = n_real & 7, xcd = wg & 7, idx = wg >> 3;
+    const int lid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+    const int mtg = lid / g.tiles_n;
+    tni = lid - mtg * g.tiles_n;
+    int e = 0;
+    while (e + 1 < g.groups && g.grp_tiles[e + 1] <= mtg) ++e;
+    tmi = mtg - g.grp_tiles[e];
+    const int64_t lo = g.grp_off[e];
+    g.M = g.grp_off[e + 1] - lo;
+    g.A = static_cast<const uint16_t*>(g.A) + lo * g.lda;
+    g.B = static_cast<const uint16_t*>(g.B) + e * g.grp_stride_b;
+    if (g.out_bf16) g.C = static_cast<uint16_t*>(g.C) + lo * g.ldc;
+    else g.C = static_cast<float*>(g.C) + lo * g.ldc;
+    if (g.zin != nullptr) g.zin = static_cast<const uint16_t*>(g.zin) + lo * g.ldc;
+  } else {
+    if constexpr (GRP == GRP_K) {
+      const int e = blockIdx.y;
+      const int64_t lo = g.grp_off[e];
+      g.K = g.grp_off[e + 1] - lo;
+      g.k_split = g.K;
+      g.A = static_cast<const uint16_t*>(g.A) + lo * g.lda;
+      g.B = static_cast<const uint16_t*>(g.B) + lo * g.ldb;
+      if (g.out_bf16) g.C = static_cast<uint16_t*>(g.C) + e * g.grp_stride_c;
+      else g.C = static_cast<float*>(g.C) + e * g.grp_stride_c;
+    }
+    map_tile(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, g.group_m, tmi, tni);
+  }
   const int64_t m0 = static_cast<int64_t>(tmi) * BM, n0 = static_cast<int64_t>(tni) * BN;
   const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * g.k_split;
   const int64_t kend = min(g.K, kbeg + g.k_split);
@@ -291,8 +338,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
     __builtin_amdgcn_wave_barrier();
     // The saved pre-activation of the activation-gradient epilogue, likewise
     // loaded for the whole strip before any of it is used.
-    uint4 zraw[NV];
-    if constexpr (EPI == EPI_DACT) {
+    // EPI_SWIGLU_BWD: the gate pre-activation sits at the output's place and
+    // the up pre-activation N columns further on (rows of ldc values).
+    uint4 zraw[NV], uraw[EPI == EPI_SWIGLU_BWD ? NV : 1];
+    if constexpr (EPI == EPI_DACT || EPI == EPI_SWIGLU_BWD) {
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int v = lane + 64 * it;
@@ -300,6 +349,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
         const int64_t m = m0 + wm * WM + i * 32 + row, n = n0 + wn * WN + c8;
         const int64_t o = (m < g.M && n < g.N) ? m * g.ldc + n : 0;
         zraw[it] = load_stream16(static_cast<const uint16_t*>(g.zin) + o);
+        if constexpr (EPI == EPI_SWIGLU_BWD) uraw[it] = load_stream16(static_cast<const uint16_t*>(g.zin) + o + g.N);
       }
     }
 #pragma unroll
@@ -320,6 +370,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g) {
         for (int e = 0; e < 8; ++e) val[e] *= act_grad_fast(z[e], ACT);
       }
       if (m >= g.M || n >= g.N) continue;
+      if constexpr (EPI == EPI_SWIGLU_BWD) {
+        // act = silu(gate) * up with silu(x) = x s, s = 1 / (1 + e^-x):
+        // d gate = d act * up * s (1 + gate (1 - s)), d up = d act * gate * s.
+        float z[8], u[8], dgv[8], duv[8];
+        unpack8(zraw[it], z);
+        unpack8(uraw[it], u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z[e]));
+          dgv[e] = val[e] * u[e] * sg * (1.0f + z[e] * (1.0f - sg));
+          duv[e] = val[e] * z[e] * sg;
+        }
+        uint16_t* c = static_cast<uint16_t*>(g.C) + m * g.ldc + n;
+        *reinterpret_cast<uint4*>(c) = pack8(dgv);
+        *reinterpret_cast<uint4*>(c + g.N) = pack8(duv);
+        continue;
+      }
       if constexpr (EPI == EPI_SPLITK) {
         float* dst = g.partial + (static_cast<int64_t>(blockIdx.z) * g.M + m) * g.N + n;
         reinterpret_cast<float4*>(dst)[0] = lo;
@@ -634,6 +701,49 @@ int gemm_logits_lse(int64_t T, int64_t V, int64_t K, const void* H, const void* 
   g.lse_slots = g.tiles_n * wave_cols(p);
   launch_bf16(NT, EPI_LSE, MP_ACT_NONE, g, p, s);
   return check_launch("gemm_logits_lse");
+}
+
+int gemm_grouped_m(int epi, int groups, const int32_t* off, const int32_t* tiles, int64_t max_mtiles, int64_t N,
+                   int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b, void* C,
+                   int64_t ldc, const void* zin, hipStream_t s) {
+  if (groups <= 0 || max_mtiles <= 0 || N == 0) return MP_OK;
+  if ((K + 64) * ldb * 2 > 0x7fffffffLL)
+    return fail(MP_ERR_SHAPE, "gemm_grouped_m: an MN-contiguous operand spans more than 2 GiB");
+  GemmArgs g{};
+  g.N = N; g.K = K; g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc; g.zin = zin;
+  g.out_bf16 = 1;
+  g.k_split = ceil_div(K > 0 ? K : 1, 64) * 64;
+  g.tiles_n = static_cast<int>(ceil_div(N, 256));
+  g.group_m = 1;
+  g.grp_off = off;
+  g.grp_tiles = tiles;
+  g.groups = groups;
+  g.grp_stride_b = stride_b;
+  const dim3 grid(static_cast<unsigned>(max_mtiles * g.tiles_n));
+  if (epi == EPI_SWIGLU_BWD)
+    gemm_bf16_kernel<256, 256, 8, 2, true, false, EPI_SWIGLU_BWD, MP_ACT_NONE, GRP_M><<<grid, 512, 0, s>>>(g);
+  else
+    gemm_bf16_kernel<256, 256, 8, 2, true, false, EPI_STORE, MP_ACT_NONE, GRP_M><<<grid, 512, 0, s>>>(g);
+  return check_launch("gemm_grouped_m");
+}
+
+int gemm_grouped_k(int groups, const int32_t* off, int64_t max_k, int64_t M, int64_t N, const void* A, int64_t lda,
+                   const void* B, int64_t ldb, float* C, int64_t ldc, int64_t stride_c, hipStream_t s) {
+  if (groups <= 0 || M == 0 || N == 0) return MP_OK;
+  if ((max_k + 64) * (lda > ldb ? lda : ldb) * 2 > 0x7fffffffLL)
+    return fail(MP_ERR_SHAPE, "gemm_grouped_k: an MN-contiguous operand spans more than 2 GiB");
+  GemmArgs g{};
+  g.M = M; g.N = N; g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
+  g.out_bf16 = 0;
+  g.tiles_m = static_cast<int>(ceil_div(M, 256));
+  g.tiles_n = static_cast<int>(ceil_div(N, 256));
+  g.group_m = 8;
+  g.grp_off = off;
+  g.groups = groups;
+  g.grp_stride_c = stride_c;
+  const dim3 grid(static_cast<unsigned>(g.tiles_m * g.tiles_n), static_cast<unsigned>(groups));
+  gemm_bf16_kernel<256, 256, 8, 2, false, false, EPI_STORE, MP_ACT_NONE, GRP_K><<<grid, 512, 0, s>>>(g);
+  return check_launch("gemm_grouped_k");
 }
 
 static int validate_mat(mp_dtype dt, int64_t contiguous, const char* fn, const char* what) {

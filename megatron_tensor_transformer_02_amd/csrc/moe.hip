@@ -17,6 +17,7 @@
 //
 // The grouped GEMMs launch a worst-case grid; a workgroup finds its expert
 // and tile from the device-side schedule and exits if it has none.
+#include "gemm.h"
 #include "mfma.h"
 
 namespace mp {
@@ -53,6 +54,13 @@ struct MoeArgs {
   const uint8_t* aq;       // [r_cap, Fe]
   const uint8_t* as;       // [r_cap, swf]
   int64_t swh, swf;
+  // Training: the forward keeps each permuted row's gate and up
+  // pre-activations; the backward's operands and outputs.
+  uint16_t* gu_save;       // [r_cap, 2*Fe]: gate in [0, Fe), up in [Fe, 2*Fe)
+  const uint16_t* dout;    // [T, Hd]
+  uint16_t* dy;            // [r_cap, Hd]
+  uint16_t* xp;            // [r_cap, Hd]
+  float* dw;               // [T, topk]
 };
 
 __global__ __launch_bounds__(256) void moe_count_kernel(const MoeArgs a) {
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __rest
 // MX: both operands are MXFP8 (E4M3 codes, k-tiles of 128 codes = the same
 // 128-byte LDS rows), two scaled 32x32x64 MFMA steps per k-tile, each row's
 // four block exponents of a k-tile read as one dword per fragment row.
-template <int MODE, bool MX>
+template <int MODE, bool MX, bool SAVE = false>
 __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   constexpr int BM = MOE_BM, BN = MOE_BN, NT = 512, WC = 4, WM = BM / 2, WN = BN / WC;
   constexpr int TM = WM / 32, TN = WN / 32, A_SLOTS = BM * 8, B_SLOTS = BN * 8;
@@ -478,9 +486,14 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   constexpr int SP = SC + 4;                   // padded strip row (floats)
   constexpr int VPR = SC / 8, NV = 32 * VPR / 64;
   static_assert((32 * VPR) % 64 == 0, "strip vectors must cover the wave evenly");
+  // SAVE (MODE 0): two more passes through the strip first store the gate and
+  // the up pre-activations of the same outputs (for the backward).
+  constexpr int NPASS = MODE == 0 && SAVE ? 3 : 1;
   float* strip = reinterpret_cast<float*>(&lds[0][0]) + wave * 32 * SP;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -490,8 +503,12 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
         // by v_rcp_f32 (about 1 ulp each, far below the bf16 output's
         // resolution); large |g| still gives g or -0.
         const float g = acc[i][0][r];
-        const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
-        strip[srow] = g * __builtin_amdgcn_rcpf(1.0f + e) * acc[i][1][r];
+        if (pass + 1 < NPASS) {
+          strip[srow] = pass == 0 ? g : acc[i][1][r];
+        } else {
+          const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+          strip[srow] = g * __builtin_amdgcn_rcpf(1.0f + e) * acc[i][1][r];
+        }
       } else {
         strip[srow] = acc[i][0][r];
         strip[srow + 32] = acc[i][1][r];
@@ -510,6 +527,10 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
       if constexpr (MODE == 0) {
         const int64_t jcol = static_cast<int64_t>(nt) * (BN / 2) + wn * (WN / 2) + c8;
         if (jcol >= a.Fe) continue;
+        if (pass + 1 < NPASS) {
+          *reinterpret_cast<uint4*>(a.gu_save + grow * 2 * a.Fe + pass * a.Fe + jcol) = pack8(val);
+          continue;
+        }
         if (a.w_on_act) {  // the row's routing weight, before the bf16 rounding
           const float wr = a.w[a.perm[grow]];
 #pragma unroll
@@ -522,6 +543,7 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
         *reinterpret_cast<uint4*>(a.yperm + grow * a.Hd + n) = pack8(val);
       }
     }
+  }
   }
 }
 
@@ -543,6 +565,50 @@ __global__ __launch_bounds__(256) void moe_unpermute_kernel(const MoeArgs a) {
     for (int q = 0; q < 8; ++q) acc[q] += wk * y[q];
   }
   *reinterpret_cast<uint4*>(a.out + t * a.Hd + c) = pack8(acc);
+}
+
+// Backward, one wave per permuted row r < R: with pick p = perm[r] of token
+// t = p / topk, dy[r] = w[p] * dout[t] (bf16), xp[r] = X[t] (the gathered
+// input rows of the gate/up weight gradient) and dw[p] = dout[t] . yperm[r]
+// in fp32 (each lane sums its columns in order, then a fixed shuffle tree).
+__global__ __launch_bounds__(256) void moe_bwd_rows_kernel(const MoeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= a.offsets[a.E_loc]) return;
+  const int32_t p = a.perm[r];
+  const int64_t t = p / a.topk;
+  const float wv = a.w[p];
+  const uint16_t* go = a.dout + t * a.Hd;
+  const uint16_t* yr = a.yperm + r * a.Hd;
+  const uint16_t* xr = a.X + t * a.Hd;
+  float dot = 0.0f;
+  for (int64_t c = lane * 8; c < a.Hd; c += 512) {
+    float gv[8], yv[8];
+    unpack8(*reinterpret_cast<const uint4*>(go + c), gv);
+    unpack8(*reinterpret_cast<const uint4*>(yr + c), yv);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      dot += gv[q] * yv[q];
+      gv[q] *= wv;
+    }
+    *reinterpret_cast<uint4*>(a.dy + r * a.Hd + c) = pack8(gv);
+    *reinterpret_cast<uint4*>(a.xp + r * a.Hd + c) = *reinterpret_cast<const uint4*>(xr + c);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+  if (lane == 0) a.dw[p] = dot;
+}
+
+// n fp32 zeros (a kernel rather than a memset, so the call stays capturable).
+__global__ __launch_bounds__(256) void moe_zero_f32_kernel(float* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// The routing-weight gradient of picks held by other shards is zero.
+__global__ __launch_bounds__(256) void moe_bwd_dw_zero_kernel(const MoeArgs a) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (p < a.T * a.topk && a.pick_row[p] < 0) a.dw[p] = 0.0f;
 }
 
 struct MoeLayout {
@@ -591,7 +657,8 @@ extern "C" size_t mp_grouped_expert_gemm_workspace(int64_t T, int64_t Hd, int64_
 static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t Hd, int64_t Fe, int topk,
                                int E_loc, int e_start, const void* X, const int32_t* topk_ids, const float* topk_w,
                                const void* W_gu, const void* W_d, void* out, int32_t* perm_picks,
-                               int32_t* expert_offsets, void* ws, size_t ws_bytes, hipStream_t s) {
+                               int32_t* expert_offsets, void* ws, size_t ws_bytes, hipStream_t s,
+                               void* gu_save = nullptr) {
   MP_REQUIRE(T >= 0 && Hd > 0 && Fe > 0 && topk > 0 && E_loc > 0 && e_start >= 0, MP_ERR_SHAPE, "%s: bad shape", fn);
   MP_REQUIRE(Hd % 8 == 0 && Fe % 8 == 0, MP_ERR_SHAPE, "%s: Hd and Fe must be multiples of 8", fn);
   MP_REQUIRE(T * Hd * 2 < 0x7fffffffLL && 2 * Fe * Hd * 2 < 0x7fffffffLL && T * topk * Fe * 2 < 0x7fffffffLL,
@@ -634,6 +701,7 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   a.act = reinterpret_cast<uint16_t*>(w + L.act);
   a.yperm = reinterpret_cast<uint16_t*>(w + L.yperm);
   a.w_on_act = w_on_act ? 1 : 0;
+  a.gu_save = static_cast<uint16_t*>(gu_save);
   const unsigned tgrid = static_cast<unsigned>(ceil_div(T, 256));
   moe_count_kernel<<<tgrid, 256, 0, s>>>(a);
   moe_scan_kernel<<<static_cast<unsigned>(E_loc), 1024, 0, s>>>(a);
@@ -641,7 +709,10 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
   const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc;
   a.tiles_n = static_cast<int>(ceil_div(Fe, MOE_BN / 2));
-  moe_gemm_kernel<0, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
+  if (gu_save != nullptr)
+    moe_gemm_kernel<0, false, true><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
+  else
+    moe_gemm_kernel<0, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
   moe_gemm_kernel<1, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a);
@@ -663,6 +734,134 @@ extern "C" int mp_grouped_expert_gemm_weighted_act(int64_t T, int64_t Hd, int64_
                                                    size_t ws_bytes, hipStream_t s) {
   return grouped_expert_gemm("mp_grouped_expert_gemm_weighted_act", true, T, Hd, Fe, topk, E_loc, e_start, X,
                              topk_ids, topk_w, W_gu, W_d, out, perm_picks, expert_offsets, ws, ws_bytes, s);
+}
+
+// ------------------------------------------------------------------ backward
+
+extern "C" int mp_grouped_expert_gemm_fwd_train(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, int e_start,
+                                                const void* X, const int32_t* topk_ids, const float* topk_w,
+                                                const void* W_gu, const void* W_d, void* out, void* gu_save,
+                                                void* ws, size_t ws_bytes, hipStream_t s) {
+  static const char* fn = "mp_grouped_expert_gemm_fwd_train";
+  MP_REQUIRE_PTR(gu_save);
+  MP_REQUIRE_ALIGN(gu_save);
+  return grouped_expert_gemm(fn, false, T, Hd, Fe, topk, E_loc, e_start, X, topk_ids, topk_w, W_gu, W_d, out, nullptr,
+                             nullptr, ws, ws_bytes, s, gu_save);
+}
+
+struct MoeBwdLayout {
+  size_t xp, dy, dgu, total;
+};
+
+static MoeBwdLayout moe_bwd_layout(int64_t T, int64_t Hd, int64_t Fe, int topk) {
+  MoeBwdLayout L{};
+  const int64_t r_cap = T * topk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes, 256);
+    return at;
+  };
+  L.xp = take(static_cast<size_t>(r_cap * Hd) * 2);
+  L.dy = take(static_cast<size_t>(r_cap * Hd) * 2);
+  L.dgu = take(static_cast<size_t>(r_cap * 2 * Fe) * 2);
+  L.total = off;
+  return L;
+}
+
+extern "C" size_t mp_grouped_expert_gemm_bwd_workspace(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc) {
+  if (T < 0 || Hd <= 0 || Fe <= 0 || topk <= 0 || E_loc <= 0) return 0;
+  return moe_bwd_layout(T, Hd, Fe, topk).total;
+}
+
+extern "C" int mp_grouped_expert_gemm_bwd(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, const void* X,
+                                          const float* topk_w, const void* W_gu, const void* W_d, const void* dOut,
+                                          const void* gu_save, const void* fwd_ws, size_t fwd_ws_bytes, void* dX,
+                                          float* dW_gu, float* dW_d, float* dtopk_w, void* ws, size_t ws_bytes,
+                                          hipStream_t s) {
+  static const char* fn = "mp_grouped_expert_gemm_bwd";
+  MP_REQUIRE(T >= 0 && Hd > 0 && Fe > 0 && topk > 0 && E_loc > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  MP_REQUIRE(Hd % 8 == 0 && Fe % 8 == 0, MP_ERR_SHAPE, "%s: Hd and Fe must be multiples of 8", fn);
+  MP_REQUIRE(T * Hd * 2 < 0x7fffffffLL && 2 * Fe * Hd * 2 < 0x7fffffffLL && T * topk * Hd * 2 < 0x7fffffffLL &&
+                 T * topk * 2 * Fe * 2 < 0x7fffffffLL,
+             MP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+  MP_REQUIRE_PTR(X);
+  MP_REQUIRE_PTR(topk_w);
+  MP_REQUIRE_PTR(W_gu);
+  MP_REQUIRE_PTR(W_d);
+  MP_REQUIRE_PTR(dOut);
+  MP_REQUIRE_PTR(gu_save);
+  MP_REQUIRE_PTR(dX);
+  MP_REQUIRE_PTR(dW_gu);
+  MP_REQUIRE_PTR(dW_d);
+  MP_REQUIRE_PTR(dtopk_w);
+  MP_REQUIRE_ALIGN(X);
+  MP_REQUIRE_ALIGN(W_gu);
+  MP_REQUIRE_ALIGN(W_d);
+  MP_REQUIRE_ALIGN(dOut);
+  MP_REQUIRE_ALIGN(gu_save);
+  MP_REQUIRE_ALIGN(dX);
+  MP_REQUIRE_ALIGN(dW_gu);
+  MP_REQUIRE_ALIGN(dW_d);
+  const MoeLayout F = moe_layout(T, Hd, Fe, topk, E_loc);
+  MP_REQUIRE(fwd_ws != nullptr && fwd_ws_bytes >= F.total, MP_ERR_WORKSPACE,
+             "%s: the forward's workspace holds %zu bytes", fn, F.total);
+  MP_REQUIRE_ALIGN(fwd_ws);
+  const MoeBwdLayout L = moe_bwd_layout(T, Hd, Fe, topk);
+  MP_REQUIRE(ws != nullptr && ws_bytes >= L.total, MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, L.total);
+  MP_REQUIRE_ALIGN(ws);
+  if (T == 0) {
+    // No tokens: every expert's weight gradient is zero.
+    const int64_t n = static_cast<int64_t>(E_loc) * 2 * Fe * Hd, m = static_cast<int64_t>(E_loc) * Hd * Fe;
+    moe_zero_f32_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, s>>>(dW_gu, n);
+    moe_zero_f32_kernel<<<static_cast<unsigned>(ceil_div(m, 256)), 256, 0, s>>>(dW_d, m);
+    return check_launch(fn);
+  }
+  char* fw = static_cast<char*>(const_cast<void*>(fwd_ws));
+  char* w = static_cast<char*>(ws);
+  MoeArgs a{};
+  a.T = T;
+  a.Hd = Hd;
+  a.Fe = Fe;
+  a.topk = topk;
+  a.E_loc = E_loc;
+  a.r_cap = T * topk;
+  a.X = static_cast<const uint16_t*>(X);
+  a.w = topk_w;
+  a.pick_row = reinterpret_cast<int32_t*>(fw + F.pick_row);
+  a.perm = reinterpret_cast<int32_t*>(fw + F.perm);
+  a.offsets = reinterpret_cast<int32_t*>(fw + F.offsets);
+  a.tile_start = reinterpret_cast<int32_t*>(fw + F.tile_start);
+  a.act = reinterpret_cast<uint16_t*>(fw + F.act);
+  a.yperm = reinterpret_cast<uint16_t*>(fw + F.yperm);
+  a.dout = static_cast<const uint16_t*>(dOut);
+  a.dy = reinterpret_cast<uint16_t*>(w + L.dy);
+  a.xp = reinterpret_cast<uint16_t*>(w + L.xp);
+  a.dw = dtopk_w;
+  uint16_t* dgu = reinterpret_cast<uint16_t*>(w + L.dgu);
+  const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc;
+  moe_bwd_dw_zero_kernel<<<static_cast<unsigned>(ceil_div(T * topk, 256)), 256, 0, s>>>(a);
+  moe_bwd_rows_kernel<<<static_cast<unsigned>(ceil_div(a.r_cap, 4)), 256, 0, s>>>(a);
+  // d act -> (d gate, d up) through the SwiGLU derivative, per expert.
+  if (int rc = gemm_grouped_m(EPI_SWIGLU_BWD, E_loc, a.offsets, a.tile_start, max_mtiles, Fe, Hd, a.dy, Hd, W_d, Fe,
+                              Hd * Fe, dgu, 2 * Fe, gu_save, s))
+    return rc;
+  // dW_d[e] = dy_e^T act_e.
+  if (int rc = gemm_grouped_k(E_loc, a.offsets, a.r_cap, Hd, Fe, a.dy, Hd, a.act, Fe, dW_d, Fe, Hd * Fe, s)) return rc;
+  // d x_perm = [d gate, d up] W_gu,e, into dy's buffer (dy is consumed).
+  if (int rc = gemm_grouped_m(EPI_STORE, E_loc, a.offsets, a.tile_start, max_mtiles, Hd, 2 * Fe, dgu, 2 * Fe, W_gu,
+                              Hd, 2 * Fe * Hd, a.dy, Hd, nullptr, s))
+    return rc;
+  // dX[t] = sum over t's local picks of d x_perm rows (k ascending).
+  MoeArgs u = a;
+  u.yperm = a.dy;
+  u.w_on_act = 1;
+  u.out = static_cast<uint16_t*>(dX);
+  moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(u);
+  // dW_gu[e] = [d gate, d up]_e^T x_perm,e.
+  if (int rc = gemm_grouped_k(E_loc, a.offsets, a.r_cap, 2 * Fe, Hd, dgu, 2 * Fe, a.xp, Hd, dW_gu, Hd, 2 * Fe * Hd, s))
+    return rc;
+  return check_launch(fn);
 }
 
 // ------------------------------------------------------------------ MXFP8
