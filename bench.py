@@ -32,7 +32,10 @@ the vocab shard's embedding backward (token-order scatter-add, accumulating
 into its fp32 gradient); ``moe_weighted_act_ms`` the MoE shard in its
 memory-efficient permutation form (routing weight on the activation);
 ``moe_mxfp8_ms`` / ``moe_mxfp8_TFLOPS`` the shard with MXFP8 expert GEMMs
-(block-scaled E4M3 operands, fp32 accumulation; the same model FLOPs).
+(block-scaled E4M3 operands, fp32 accumulation; the same model FLOPs);
+``moe_fwd_train_ms`` / ``moe_bwd_ms`` / ``moe_bwd_TFLOPS`` the shard's
+training forward (gate/up pre-activations kept) and its backward (twice the
+forward's expert FLOPs).
 """
 
 import argparse
@@ -372,12 +375,55 @@ def main():
         out["moe_mxfp8_ms"] = round(mx_ms, 4)
         out["moe_mxfp8_TFLOPS"] = round(moe_fl / (mx_ms * 1e-3) / 1e12, 2)
         del gq, gs, dq, ds, mxws
+        # Training form: forward keeping the gate/up pre-activations, then the
+        # backward (routing-weight gradient, grouped input- and weight-gradient
+        # GEMMs), each timed on its own; the backward does twice the forward's
+        # expert FLOPs.
+        gu = torch.empty((wm.T * wm.topk, 2 * wm.Fe), dtype=torch.bfloat16, device="cuda")
+        tws = torch.empty_like(mws)
+        mdout = torch.randn((wm.T, wm.K), generator=torch.Generator().manual_seed(wm.seed + 1)).to(
+            "cuda", torch.bfloat16)
+        mdx = torch.empty_like(mdout)
+        mdwgu = torch.empty(tuple(mwgu.shape), dtype=torch.float32, device="cuda")
+        mdwd = torch.empty(tuple(mwd.shape), dtype=torch.float32, device="cuda")
+        mdtw = torch.empty(tuple(mw.shape), dtype=torch.float32, device="cuda")
+        bws = torch.empty(mp.lib().mp_grouped_expert_gemm_bwd_workspace(wm.T, wm.K, wm.Fe, wm.topk, wm.e_local),
+                          dtype=torch.uint8, device="cuda")
+
+        def moe_fwd_train():
+            mp.mp_grouped_expert_gemm_fwd_train(mx, mids, mw, mwgu, mwd, 0, mout, gu, tws)
+
+        def moe_bwd():
+            mp.mp_grouped_expert_gemm_bwd(mx, mw, mwgu, mwd, mdout, gu, tws, mdx, mdwgu, mdwd, mdtw, bws)
+
+        for _ in range(max(1, args.warmup)):
+            moe_fwd_train()
+            moe_bwd()
+        torch.cuda.synchronize()
+        bev = [(EV(), EV(), EV()) for _ in range(args.steps)]
+        for b_, m_, e_ in bev:
+            b_.record(stream)
+            moe_fwd_train()
+            m_.record(stream)
+            moe_bwd()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        ft_ms = float(np.mean([b_.elapsed_time(m_) for b_, m_, _ in bev]))
+        bw_ms = float(np.mean([m_.elapsed_time(e_) for _, m_, e_ in bev]))
+        out["moe_fwd_train_ms"] = round(ft_ms, 4)
+        out["moe_bwd_ms"] = round(bw_ms, 4)
+        out["moe_bwd_TFLOPS"] = round(2 * moe_fl / (bw_ms * 1e-3) / 1e12, 2)
+        del gu, tws, mdout, mdx, mdwgu, mdwd, mdtw, bws
         # Whole-call rates of the two MoE shard forms against their MFMA peaks
         # (permutation, quantisation and unpermute included in the time).
         roofs.append({"kernel": "MoE hot shard, bf16 grouped expert GEMMs (whole call)", "bound": "mfma",
                       "achieved": out["moe_TFLOPS"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(out["moe_TFLOPS"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
                       "avg_launch_us": round(moe_ms * 1e3, 1), "algorithmic_per_launch": moe_fl})
+        roofs.append({"kernel": "MoE hot shard backward, bf16 grouped expert GEMMs (whole call)", "bound": "mfma",
+                      "achieved": out["moe_bwd_TFLOPS"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(out["moe_bwd_TFLOPS"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                      "avg_launch_us": round(bw_ms * 1e3, 1), "algorithmic_per_launch": 2 * moe_fl})
         roofs.append({"kernel": "MoE hot shard, MXFP8 grouped expert GEMMs (whole call)", "bound": "mfma",
                       "achieved": out["moe_mxfp8_TFLOPS"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(out["moe_mxfp8_TFLOPS"] / PEAK_FP8_TFLOPS, 4), "traffic": None,

@@ -214,3 +214,49 @@ def test_moe_forms_and_mxfp8_validation(lib):
     # The MXFP8 workspace holds the bf16 one plus the quantised rows.
     assert lib.mp_grouped_expert_gemm_mxfp8_workspace(4096, 7168, 2048, 8, 8) >= (
         lib.mp_grouped_expert_gemm_workspace(4096, 7168, 2048, 8, 8) + 4096 * 7168 + 4096 * 8 * 2048)
+
+
+def test_moe_training_validation(lib):
+    T, Hd, Fe, topk, E = 16, 64, 64, 2, 2
+    need = lib.mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E)
+    # Training forward: as the forward, plus a non-NULL, aligned gu_save.
+    fa = [ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ctypes.c_size_t(need), None]
+    bad = list(fa)
+    bad[6] = None
+    rc, msg = call(lib, "mp_grouped_expert_gemm_fwd_train", T, Hd, Fe, topk, E, 0, *bad)
+    assert rc == -1 and "gu_save" in msg
+    bad[6] = ALIGNED + 8
+    rc, _ = call(lib, "mp_grouped_expert_gemm_fwd_train", T, Hd, Fe, topk, E, 0, *bad)
+    assert rc == -5
+    rc, _ = call(lib, "mp_grouped_expert_gemm_fwd_train", T, 60, Fe, topk, E, 0, *fa)
+    assert rc == -2
+    bad = list(fa)
+    bad[8] = ctypes.c_size_t(need - 1)
+    rc, _ = call(lib, "mp_grouped_expert_gemm_fwd_train", T, Hd, Fe, topk, E, 0, *bad)
+    assert rc == -6
+    rc, _ = call(lib, "mp_grouped_expert_gemm_fwd_train", 0, Hd, Fe, topk, E, 0, *fa)
+    assert rc == 0  # no tokens: nothing to do
+    # Backward: its workspace holds x_perm, dy and [d gate, d up] for every possible row.
+    bneed = lib.mp_grouped_expert_gemm_bwd_workspace(T, Hd, Fe, topk, E)
+    assert bneed >= T * topk * (2 * Hd + 2 * Fe) * 2
+    assert bneed == lib.mp_grouped_expert_gemm_bwd_workspace(T, Hd, Fe, topk, E)
+    ba = [ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ctypes.c_size_t(need), ALIGNED, ALIGNED,
+          ALIGNED, ALIGNED, ALIGNED, ctypes.c_size_t(bneed), None]
+    rc, _ = call(lib, "mp_grouped_expert_gemm_bwd", T, Hd, 0, topk, E, *ba)
+    assert rc == -2
+    bad = list(ba)
+    bad[4] = None  # dOut
+    rc, msg = call(lib, "mp_grouped_expert_gemm_bwd", T, Hd, Fe, topk, E, *bad)
+    assert rc == -1 and "dOut" in msg
+    bad = list(ba)
+    bad[7] = ctypes.c_size_t(need - 256)  # the forward's state is smaller than the forward wrote
+    rc, msg = call(lib, "mp_grouped_expert_gemm_bwd", T, Hd, Fe, topk, E, *bad)
+    assert rc == -6 and "forward" in msg
+    bad = list(ba)
+    bad[13] = ctypes.c_size_t(bneed - 1)
+    rc, _ = call(lib, "mp_grouped_expert_gemm_bwd", T, Hd, Fe, topk, E, *bad)
+    assert rc == -6
+    bad = list(ba)
+    bad[9] = ALIGNED + 4  # dW_gu
+    rc, _ = call(lib, "mp_grouped_expert_gemm_bwd", T, Hd, Fe, topk, E, *bad)
+    assert rc == -5
