@@ -211,13 +211,12 @@ def test_moe_backward_central_differences():
     routing weights) against central finite differences of the per-token
     forward definition, at a tiny shape that includes a token with no local
     pick and a local expert nobody picks."""
-    t, hd, fe, experts, topk, e_start, e_local = 7, 5, 4, 8, 2, 2, 4
-    ids, w = routing(t, experts, topk)
-    ids[0] = [0, 7]          # no local pick
-    ids[ids == 5] = 6        # expert 5 (local index 3) is never picked...
-    ids[1] = [6, 1]          # ...and ids stay distinct per token
-    ids[2] = [2, 6]
-    assert not np.any(ids == 5) and all(len(set(r)) == topk for r in ids)
+    t, hd, fe, topk, e_start, e_local = 7, 5, 4, 2, 2, 4
+    # Experts 2..5 are local; token 0 picks none of them and nobody picks
+    # expert 5 (local index 3); ids are distinct per token.
+    ids = np.array([[0, 7], [6, 1], [2, 6], [3, 2], [4, 0], [2, 4], [3, 1]])
+    w = np.random.default_rng(77).random((t, topk))
+    w = w / w.sum(axis=1, keepdims=True)
     x = rnd(t, hd)
     wgu, wd = rnd(e_local, 2 * fe, hd, scale=0.5), rnd(e_local, hd, fe, scale=0.5)
     dout = rnd(t, hd)
