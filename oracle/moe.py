@@ -194,3 +194,58 @@ def moe_backward(x, topk_ids, topk_w, w_gu, w_d, e_start, dout):
         for i, t in enumerate(tok):
             dx[t] += dxe[i]
     return {"x": dx, "w_gu": dw_gu, "w_d": dw_d, "topk_w": dw.reshape(tokens, topk)}
+
+
+def moe_backward_weighted_act(x, topk_ids, topk_w, w_gu, w_d, e_start, dout):
+    """Backward of :func:`moe_forward_weighted_act`, the memory-efficient
+    permutation form (MOE-core, technical summary 2.2: with the routing
+    weight applied before the expert's output is formed, the backward needs
+    no saved expert output).  For a local pick ``(t, k)`` of expert ``e``
+    with ``g``, ``u``, ``s = sigmoid(g)``, the unweighted activation
+    ``a = silu(g) * u`` and the weighted one ``a_w = w[t,k] * a``:
+
+    * ``dy = dout_t`` (the unpermute is an unweighted sum);
+    * ``d a_w = dy W_d`` and ``dW_d += dy^T a_w``;
+    * ``d w[t,k] = d a_w . a`` (the weight's gradient from the activation
+      side), ``d a = w[t,k] * d a_w``;
+    * ``dg``, ``du``, ``dW_gu`` and ``dx`` as in :func:`moe_backward`.
+
+    Equal to :func:`moe_backward` in exact arithmetic (both differentiate the
+    same function).  Returns the same dict.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    tokens, topk = ids.shape
+    w = _f64(topk_w).reshape(-1)
+    x, dout = _f64(x), _f64(dout)
+    w_gu, w_d = _f64(w_gu), _f64(w_d)
+    e_local, _, fe = w_d.shape
+    counts, offsets, picks = moe_permutation(ids, e_start, e_local)
+    dx = np.zeros_like(x)
+    dw_gu = np.zeros_like(w_gu)
+    dw_d = np.zeros_like(w_d)
+    dw = np.zeros(tokens * topk)
+    for e in range(e_local):
+        sel = picks[offsets[e]:offsets[e + 1]]
+        if sel.size == 0:
+            continue
+        tok = sel // topk
+        xe = x[tok]
+        wg, wu, wd = w_gu[e, :fe], w_gu[e, fe:], w_d[e]
+        g = xe @ wg.T
+        u = xe @ wu.T
+        s = _sigmoid(g)
+        a = g * s * u
+        a_w = w[sel][:, None] * a
+        dy = dout[tok]
+        da_w = dy @ wd
+        dw_d[e] = dy.T @ a_w
+        dw[sel] = np.sum(da_w * a, axis=1)
+        da = w[sel][:, None] * da_w
+        dg = da * u * s * (1.0 + g * (1.0 - s))
+        du = da * g * s
+        dw_gu[e, :fe] = dg.T @ xe
+        dw_gu[e, fe:] = du.T @ xe
+        dxe = dg @ wg + du @ wu
+        for i, t in enumerate(tok):
+            dx[t] += dxe[i]
+    return {"x": dx, "w_gu": dw_gu, "w_d": dw_d, "topk_w": dw.reshape(tokens, topk)}

@@ -265,3 +265,40 @@ def test_moe_backward_matches_torch_autograd():
     for name, ref in (("x", tx), ("topk_w", tw), ("w_gu", tgu), ("w_d", td)):
         r = ref.grad.numpy()
         assert np.allclose(g[name], r, rtol=1e-11, atol=1e-12), name
+
+
+def _moe_loss_weighted_act(x, ids, w, wgu, wd, e_start, dout):
+    """sum(dout * out) through the memory-efficient form's forward."""
+    return float(np.sum(dout * O.moe_forward_weighted_act(x, ids, w, wgu, wd, e_start)[0]))
+
+
+def test_moe_backward_weighted_act_central_differences():
+    """The memory-efficient form's backward against central finite
+    differences of its own forward, and against the weighted-unpermute
+    form's backward (the same function, so the same gradients)."""
+    t, hd, fe, topk, e_start, e_local = 7, 5, 4, 2, 2, 4
+    ids = np.array([[0, 7], [6, 1], [2, 6], [3, 2], [4, 0], [2, 4], [3, 1]])
+    w = np.random.default_rng(78).random((t, topk))
+    w = w / w.sum(axis=1, keepdims=True)
+    rng = np.random.default_rng(79)
+    x = rng.standard_normal((t, hd))
+    wgu, wd = rng.standard_normal((e_local, 2 * fe, hd)) * 0.5, rng.standard_normal((e_local, hd, fe)) * 0.5
+    dout = rng.standard_normal((t, hd))
+    g = O.moe_backward_weighted_act(x, ids, w, wgu, wd, e_start, dout)
+    args = {"x": x, "w_gu": wgu, "w_d": wd, "topk_w": w}
+    h = 1e-6
+    for name, arr in args.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + h
+            lp = _moe_loss_weighted_act(args["x"], ids, args["topk_w"], args["w_gu"], args["w_d"], e_start, dout)
+            arr[idx] = keep - h
+            lm = _moe_loss_weighted_act(args["x"], ids, args["topk_w"], args["w_gu"], args["w_d"], e_start, dout)
+            arr[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.linalg.norm(g[name] - fd) / max(np.linalg.norm(fd), 1e-30)
+        assert err <= 1e-6, (name, err)
+    std = O.moe_backward(x, ids, w, wgu, wd, e_start, dout)
+    for name in args:
+        assert np.allclose(g[name], std[name], rtol=1e-11, atol=1e-13), name
