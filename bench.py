@@ -35,7 +35,8 @@ memory-efficient permutation form (routing weight on the activation);
 (block-scaled E4M3 operands, fp32 accumulation; the same model FLOPs);
 ``moe_fwd_train_ms`` / ``moe_bwd_ms`` / ``moe_bwd_TFLOPS`` the shard's
 training forward (gate/up pre-activations kept) and its backward (twice the
-forward's expert FLOPs).
+forward's expert FLOPs); ``moe_weighted_act_train_ms`` the memory-efficient
+form's training forward + backward.
 """
 
 import argparse
@@ -396,6 +397,11 @@ def main():
         def moe_bwd():
             mp.mp_grouped_expert_gemm_bwd(mx, mw, mwgu, mwd, mdout, gu, tws, mdx, mdwgu, mdwd, mdtw, bws)
 
+        def moe_train_wa():
+            mp.mp_grouped_expert_gemm_fwd_train(mx, mids, mw, mwgu, mwd, 0, mout, gu, tws, weighted_act=True)
+            mp.mp_grouped_expert_gemm_bwd(mx, mw, mwgu, mwd, mdout, gu, tws, mdx, mdwgu, mdwd, mdtw, bws,
+                                          weighted_act=True)
+
         for _ in range(max(1, args.warmup)):
             moe_fwd_train()
             moe_bwd()
@@ -413,6 +419,17 @@ def main():
         out["moe_fwd_train_ms"] = round(ft_ms, 4)
         out["moe_bwd_ms"] = round(bw_ms, 4)
         out["moe_bwd_TFLOPS"] = round(2 * moe_fl / (bw_ms * 1e-3) / 1e12, 2)
+        # The memory-efficient form's training forward + backward (no saved
+        # expert output is read by its backward).
+        for _ in range(max(1, args.warmup)):
+            moe_train_wa()
+        torch.cuda.synchronize()
+        for b_, _m, e_ in bev:
+            b_.record(stream)
+            moe_train_wa()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        out["moe_weighted_act_train_ms"] = round(float(np.mean([b_.elapsed_time(e_) for b_, _m, e_ in bev])), 4)
         del gu, tws, mdout, mdx, mdwgu, mdwd, mdtw, bws
         # Whole-call rates of the two MoE shard forms against their MFMA peaks
         # (permutation, quantisation and unpermute included in the time).

@@ -401,6 +401,35 @@ int mp_grouped_expert_gemm_bwd(int64_t T, int64_t Hd, int64_t Fe, int topk, int 
                                float* dW_d, float* dtopk_w, void* ws, size_t ws_bytes,
                                hipStream_t s);
 
+/* Training forward of mp_grouped_expert_gemm_weighted_act (the memory-
+ * efficient form): arguments, outputs, gu_save (unweighted gate and up
+ * pre-activations) and the kept workspace as mp_grouped_expert_gemm_fwd_train;
+ * the activation kept in ws is the weighted one. */
+int mp_grouped_expert_gemm_weighted_act_fwd_train(int64_t T, int64_t Hd, int64_t Fe, int topk,
+                                                  int E_loc, int e_start, const void* X,
+                                                  const int32_t* topk_ids, const float* topk_w,
+                                                  const void* W_gu, const void* W_d, void* out,
+                                                  void* gu_save, void* ws, size_t ws_bytes,
+                                                  hipStream_t s);
+
+/* Backward of the memory-efficient form (MOE-core, technical summary 2.2: the
+ * routing weight sits before the expert's output, so the backward reads no
+ * saved expert output).  With act = silu(gate) * up and act_w = topk_w[t,k] *
+ * act as the forward stored it, for every local pick (t,k) of expert e:
+ *   dy_r = dOut[t];  d act_w = dy_r W_d,e;  dW_d[e] = sum_r dy_r^T act_w,r;
+ *   dtopk_w[t,k] = d act_w . act (fp32, fixed order);
+ *   d act = topk_w[t,k] * d act_w, then d gate, d up, dW_gu and dX as in
+ *   mp_grouped_expert_gemm_bwd.
+ * Needs the state of mp_grouped_expert_gemm_weighted_act_fwd_train; arguments,
+ * outputs, workspace (mp_grouped_expert_gemm_bwd_workspace()) and errors as
+ * mp_grouped_expert_gemm_bwd. */
+int mp_grouped_expert_gemm_weighted_act_bwd(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                                            const void* X, const float* topk_w, const void* W_gu,
+                                            const void* W_d, const void* dOut, const void* gu_save,
+                                            const void* fwd_ws, size_t fwd_ws_bytes, void* dX,
+                                            float* dW_gu, float* dW_d, float* dtopk_w, void* ws,
+                                            size_t ws_bytes, hipStream_t s);
+
 /* ------------------------------------------------------------------ MXFP8 */
 
 /* MXFP8 block quantisation (MOE-core, technical summary 2.5: expert GEMMs and

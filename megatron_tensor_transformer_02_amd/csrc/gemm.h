@@ -35,12 +35,16 @@ int gemm_logits_lse(int64_t T, int64_t V, int64_t K, const void* H, const void* 
 // 256-row tile of group e in a flat tile list (tiles[groups] = its length,
 // at most max_mtiles).  epi = EPI_STORE (bf16 out) or EPI_SWIGLU_BWD: C and
 // zin are [rows, 2N]; zin holds the gate (columns [0, N)) and up ([N, 2N))
-// pre-activations, C receives d gate and d up of d act = A * B_e^T.
+// pre-activations, C receives d gate and d up of d act = A * B_e^T.  With
+// row_w (rows' weights, [rows] fp32), the activation was act_w = w * act:
+// A * B_e^T is d act_w, d act = w * d act_w, and row_part [rows, N/8] gets
+// the sums of d act_w * act over each 8 columns (the weight's gradient).
 // GRP_K (layout TN, fp32 out): group e is C_e[M, N] = sum over k in
 // [lo, hi) of A[k, m] * B[k, n], C_e = C + e * stride_c (zeros when lo = hi).
 int gemm_grouped_m(int epi, int groups, const int32_t* off, const int32_t* tiles, int64_t max_mtiles, int64_t N,
                    int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b, void* C,
-                   int64_t ldc, const void* zin, hipStream_t s);
+                   int64_t ldc, const void* zin, hipStream_t s, const float* row_w = nullptr,
+                   float* row_part = nullptr);
 // max_k bounds every group's k-range (for the 2 GiB addressing check).
 int gemm_grouped_k(int groups, const int32_t* off, int64_t max_k, int64_t M, int64_t N, const void* A, int64_t lda,
                    const void* B, int64_t ldb, float* C, int64_t ldc, int64_t stride_c, hipStream_t s);

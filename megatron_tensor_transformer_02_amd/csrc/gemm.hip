@@ -55,6 +55,12 @@ struct GemmArgs {
   const int32_t* grp_tiles;  // [groups + 1] (GRP_M)
   int groups;
   int64_t grp_stride_b, grp_stride_c;
+  // EPI_SWIGLU_BWD with a weighted activation (act_w = w * silu(gate) * up):
+  // row_w [M] holds each row's weight w; the output d act_w is scaled by it
+  // before the SwiGLU derivative, and row_part [M, N/8] receives, for every
+  // 8 columns, sum d act_w * silu(gate) * up (the weight's gradient, in parts).
+  const float* row_w;
+  float* row_part;
 };
 
 enum GroupMode { GRP_NONE = 0, GRP_M = 1, GRP_K = 2 };
@@ -119,6 +125,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g0) {
     if (g.out_bf16) g.C = static_cast<uint16_t*>(g.C) + lo * g.ldc;
     else g.C = static_cast<float*>(g.C) + lo * g.ldc;
     if (g.zin != nullptr) g.zin = static_cast<const uint16_t*>(g.zin) + lo * g.ldc;
+    if (g.row_w != nullptr) {
+      g.row_w += lo;
+      g.row_part += lo * (g.N / 8);
+    }
   } else {
     if constexpr (GRP == GRP_K) {
       const int e = blockIdx.y;
@@ -373,15 +383,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g0) {
       if constexpr (EPI == EPI_SWIGLU_BWD) {
         // act = silu(gate) * up with silu(x) = x s, s = 1 / (1 + e^-x):
         // d gate = d act * up * s (1 + gate (1 - s)), d up = d act * gate * s.
+        // With row weights, val is d act_w: its dot with the unweighted
+        // activation is the weight's gradient, and d act = w * d act_w.
         float z[8], u[8], dgv[8], duv[8];
         unpack8(zraw[it], z);
         unpack8(uraw[it], u);
+        const bool wt = g.row_w != nullptr;
+        const float wr = wt ? g.row_w[m] : 1.0f;
+        float part = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z[e]));
-          dgv[e] = val[e] * u[e] * sg * (1.0f + z[e] * (1.0f - sg));
-          duv[e] = val[e] * z[e] * sg;
+          part += val[e] * (z[e] * sg * u[e]);
+          const float da = val[e] * wr;
+          dgv[e] = da * u[e] * sg * (1.0f + z[e] * (1.0f - sg));
+          duv[e] = da * z[e] * sg;
         }
+        if (wt) g.row_part[m * (g.N / 8) + n / 8] = part;
         uint16_t* c = static_cast<uint16_t*>(g.C) + m * g.ldc + n;
         *reinterpret_cast<uint4*>(c) = pack8(dgv);
         *reinterpret_cast<uint4*>(c + g.N) = pack8(duv);
@@ -705,7 +723,7 @@ int gemm_logits_lse(int64_t T, int64_t V, int64_t K, const void* H, const void* 
 
 int gemm_grouped_m(int epi, int groups, const int32_t* off, const int32_t* tiles, int64_t max_mtiles, int64_t N,
                    int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b, void* C,
-                   int64_t ldc, const void* zin, hipStream_t s) {
+                   int64_t ldc, const void* zin, hipStream_t s, const float* row_w, float* row_part) {
   if (groups <= 0 || max_mtiles <= 0 || N == 0) return MP_OK;
   if ((K + 64) * ldb * 2 > 0x7fffffffLL)
     return fail(MP_ERR_SHAPE, "gemm_grouped_m: an MN-contiguous operand spans more than 2 GiB");
@@ -719,6 +737,8 @@ int gemm_grouped_m(int epi, int groups, const int32_t* off, const int32_t* tiles
   g.grp_tiles = tiles;
   g.groups = groups;
   g.grp_stride_b = stride_b;
+  g.row_w = row_w;
+  g.row_part = row_part;
   const dim3 grid(static_cast<unsigned>(max_mtiles * g.tiles_n));
   if (epi == EPI_SWIGLU_BWD)
     gemm_bf16_kernel<256, 256, 8, 2, true, false, EPI_SWIGLU_BWD, MP_ACT_NONE, GRP_M><<<grid, 512, 0, s>>>(g);

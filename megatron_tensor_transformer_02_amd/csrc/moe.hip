@@ -61,6 +61,8 @@ struct MoeArgs {
   uint16_t* dy;            // [r_cap, Hd]
   uint16_t* xp;            // [r_cap, Hd]
   float* dw;               // [T, topk]
+  float* wperm;            // [r_cap]: each permuted row's routing weight (weighted-activation form)
+  float* dwp;              // [r_cap, Fe/8]: parts of each row's routing-weight gradient
 };
 
 __global__ __launch_bounds__(256) void moe_count_kernel(const MoeArgs a) {
@@ -571,6 +573,10 @@ __global__ __launch_bounds__(256) void moe_unpermute_kernel(const MoeArgs a) {
 // t = p / topk, dy[r] = w[p] * dout[t] (bf16), xp[r] = X[t] (the gathered
 // input rows of the gate/up weight gradient) and dw[p] = dout[t] . yperm[r]
 // in fp32 (each lane sums its columns in order, then a fixed shuffle tree).
+// W_ON_ACT (the weighted-activation form): the unpermute was unweighted, so
+// dy[r] = dout[t]; the row's weight goes to wperm[r] for the d act GEMM, and
+// dw comes from the activation side there (no expert output is read).
+template <bool W_ON_ACT>
 __global__ __launch_bounds__(256) void moe_bwd_rows_kernel(const MoeArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -578,6 +584,14 @@ __global__ __launch_bounds__(256) void moe_bwd_rows_kernel(const MoeArgs a) {
   const int32_t p = a.perm[r];
   const int64_t t = p / a.topk;
   const float wv = a.w[p];
+  if constexpr (W_ON_ACT) {
+    if (lane == 0) a.wperm[r] = wv;
+    for (int64_t c = lane * 8; c < a.Hd; c += 512) {
+      *reinterpret_cast<uint4*>(a.dy + r * a.Hd + c) = *reinterpret_cast<const uint4*>(a.dout + t * a.Hd + c);
+      *reinterpret_cast<uint4*>(a.xp + r * a.Hd + c) = *reinterpret_cast<const uint4*>(a.X + t * a.Hd + c);
+    }
+    return;
+  }
   const uint16_t* go = a.dout + t * a.Hd;
   const uint16_t* yr = a.yperm + r * a.Hd;
   const uint16_t* xr = a.X + t * a.Hd;
@@ -603,6 +617,20 @@ __global__ __launch_bounds__(256) void moe_bwd_rows_kernel(const MoeArgs a) {
 __global__ __launch_bounds__(256) void moe_zero_f32_kernel(float* p, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
+}
+
+// Weighted-activation form: dw[perm[r]] = sum of row r's Fe/8 parts from the
+// d act GEMM's epilogue (one wave per row; lane order, then a fixed tree).
+__global__ __launch_bounds__(256) void moe_bwd_dw_rows_kernel(const MoeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= a.offsets[a.E_loc]) return;
+  const int64_t np = a.Fe / 8;
+  float acc = 0.0f;
+  for (int64_t c = lane; c < np; c += 64) acc += a.dwp[r * np + c];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) a.dw[a.perm[r]] = acc;
 }
 
 // The routing-weight gradient of picks held by other shards is zero.
@@ -738,19 +766,35 @@ extern "C" int mp_grouped_expert_gemm_weighted_act(int64_t T, int64_t Hd, int64_
 
 // ------------------------------------------------------------------ backward
 
+static int fwd_train(const char* fn, bool w_on_act, int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                     int e_start, const void* X, const int32_t* topk_ids, const float* topk_w, const void* W_gu,
+                     const void* W_d, void* out, void* gu_save, void* ws, size_t ws_bytes, hipStream_t s) {
+  MP_REQUIRE_PTR(gu_save);
+  MP_REQUIRE_ALIGN(gu_save);
+  return grouped_expert_gemm(fn, w_on_act, T, Hd, Fe, topk, E_loc, e_start, X, topk_ids, topk_w, W_gu, W_d, out,
+                             nullptr, nullptr, ws, ws_bytes, s, gu_save);
+}
+
 extern "C" int mp_grouped_expert_gemm_fwd_train(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, int e_start,
                                                 const void* X, const int32_t* topk_ids, const float* topk_w,
                                                 const void* W_gu, const void* W_d, void* out, void* gu_save,
                                                 void* ws, size_t ws_bytes, hipStream_t s) {
-  static const char* fn = "mp_grouped_expert_gemm_fwd_train";
-  MP_REQUIRE_PTR(gu_save);
-  MP_REQUIRE_ALIGN(gu_save);
-  return grouped_expert_gemm(fn, false, T, Hd, Fe, topk, E_loc, e_start, X, topk_ids, topk_w, W_gu, W_d, out, nullptr,
-                             nullptr, ws, ws_bytes, s, gu_save);
+  return fwd_train("mp_grouped_expert_gemm_fwd_train", false, T, Hd, Fe, topk, E_loc, e_start, X, topk_ids, topk_w,
+                   W_gu, W_d, out, gu_save, ws, ws_bytes, s);
+}
+
+extern "C" int mp_grouped_expert_gemm_weighted_act_fwd_train(int64_t T, int64_t Hd, int64_t Fe, int topk,
+                                                             int E_loc, int e_start, const void* X,
+                                                             const int32_t* topk_ids, const float* topk_w,
+                                                             const void* W_gu, const void* W_d, void* out,
+                                                             void* gu_save, void* ws, size_t ws_bytes,
+                                                             hipStream_t s) {
+  return fwd_train("mp_grouped_expert_gemm_weighted_act_fwd_train", true, T, Hd, Fe, topk, E_loc, e_start, X,
+                   topk_ids, topk_w, W_gu, W_d, out, gu_save, ws, ws_bytes, s);
 }
 
 struct MoeBwdLayout {
-  size_t xp, dy, dgu, total;
+  size_t xp, dy, dgu, wperm, dwp, total;
 };
 
 static MoeBwdLayout moe_bwd_layout(int64_t T, int64_t Hd, int64_t Fe, int topk) {
@@ -765,6 +809,8 @@ static MoeBwdLayout moe_bwd_layout(int64_t T, int64_t Hd, int64_t Fe, int topk) 
   L.xp = take(static_cast<size_t>(r_cap * Hd) * 2);
   L.dy = take(static_cast<size_t>(r_cap * Hd) * 2);
   L.dgu = take(static_cast<size_t>(r_cap * 2 * Fe) * 2);
+  L.wperm = take(static_cast<size_t>(r_cap) * 4);
+  L.dwp = take(static_cast<size_t>(r_cap * (Fe / 8)) * 4);
   L.total = off;
   return L;
 }
@@ -774,12 +820,11 @@ extern "C" size_t mp_grouped_expert_gemm_bwd_workspace(int64_t T, int64_t Hd, in
   return moe_bwd_layout(T, Hd, Fe, topk).total;
 }
 
-extern "C" int mp_grouped_expert_gemm_bwd(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, const void* X,
-                                          const float* topk_w, const void* W_gu, const void* W_d, const void* dOut,
-                                          const void* gu_save, const void* fwd_ws, size_t fwd_ws_bytes, void* dX,
-                                          float* dW_gu, float* dW_d, float* dtopk_w, void* ws, size_t ws_bytes,
-                                          hipStream_t s) {
-  static const char* fn = "mp_grouped_expert_gemm_bwd";
+static int grouped_expert_gemm_bwd(const char* fn, bool w_on_act, int64_t T, int64_t Hd, int64_t Fe, int topk,
+                                   int E_loc, const void* X, const float* topk_w, const void* W_gu, const void* W_d,
+                                   const void* dOut, const void* gu_save, const void* fwd_ws, size_t fwd_ws_bytes,
+                                   void* dX, float* dW_gu, float* dW_d, float* dtopk_w, void* ws, size_t ws_bytes,
+                                   hipStream_t s) {
   MP_REQUIRE(T >= 0 && Hd > 0 && Fe > 0 && topk > 0 && E_loc > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
   MP_REQUIRE(Hd % 8 == 0 && Fe % 8 == 0, MP_ERR_SHAPE, "%s: Hd and Fe must be multiples of 8", fn);
   MP_REQUIRE(T * Hd * 2 < 0x7fffffffLL && 2 * Fe * Hd * 2 < 0x7fffffffLL && T * topk * Hd * 2 < 0x7fffffffLL &&
@@ -838,14 +883,21 @@ extern "C" int mp_grouped_expert_gemm_bwd(int64_t T, int64_t Hd, int64_t Fe, int
   a.dy = reinterpret_cast<uint16_t*>(w + L.dy);
   a.xp = reinterpret_cast<uint16_t*>(w + L.xp);
   a.dw = dtopk_w;
+  a.wperm = reinterpret_cast<float*>(w + L.wperm);
+  a.dwp = reinterpret_cast<float*>(w + L.dwp);
   uint16_t* dgu = reinterpret_cast<uint16_t*>(w + L.dgu);
   const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc;
+  const unsigned rgrid = static_cast<unsigned>(ceil_div(a.r_cap, 4));
   moe_bwd_dw_zero_kernel<<<static_cast<unsigned>(ceil_div(T * topk, 256)), 256, 0, s>>>(a);
-  moe_bwd_rows_kernel<<<static_cast<unsigned>(ceil_div(a.r_cap, 4)), 256, 0, s>>>(a);
-  // d act -> (d gate, d up) through the SwiGLU derivative, per expert.
+  if (w_on_act) moe_bwd_rows_kernel<true><<<rgrid, 256, 0, s>>>(a);
+  else moe_bwd_rows_kernel<false><<<rgrid, 256, 0, s>>>(a);
+  // d act -> (d gate, d up) through the SwiGLU derivative, per expert (in the
+  // weighted-activation form, via d act_w, with the weight's gradient parts).
   if (int rc = gemm_grouped_m(EPI_SWIGLU_BWD, E_loc, a.offsets, a.tile_start, max_mtiles, Fe, Hd, a.dy, Hd, W_d, Fe,
-                              Hd * Fe, dgu, 2 * Fe, gu_save, s))
+                              Hd * Fe, dgu, 2 * Fe, gu_save, s, w_on_act ? a.wperm : nullptr,
+                              w_on_act ? a.dwp : nullptr))
     return rc;
+  if (w_on_act) moe_bwd_dw_rows_kernel<<<rgrid, 256, 0, s>>>(a);
   // dW_d[e] = dy_e^T act_e.
   if (int rc = gemm_grouped_k(E_loc, a.offsets, a.r_cap, Hd, Fe, a.dy, Hd, a.act, Fe, dW_d, Fe, Hd * Fe, s)) return rc;
   // d x_perm = [d gate, d up] W_gu,e, into dy's buffer (dy is consumed).
@@ -862,6 +914,26 @@ extern "C" int mp_grouped_expert_gemm_bwd(int64_t T, int64_t Hd, int64_t Fe, int
   if (int rc = gemm_grouped_k(E_loc, a.offsets, a.r_cap, 2 * Fe, Hd, dgu, 2 * Fe, a.xp, Hd, dW_gu, Hd, 2 * Fe * Hd, s))
     return rc;
   return check_launch(fn);
+}
+
+extern "C" int mp_grouped_expert_gemm_bwd(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, const void* X,
+                                          const float* topk_w, const void* W_gu, const void* W_d, const void* dOut,
+                                          const void* gu_save, const void* fwd_ws, size_t fwd_ws_bytes, void* dX,
+                                          float* dW_gu, float* dW_d, float* dtopk_w, void* ws, size_t ws_bytes,
+                                          hipStream_t s) {
+  return grouped_expert_gemm_bwd("mp_grouped_expert_gemm_bwd", false, T, Hd, Fe, topk, E_loc, X, topk_w, W_gu, W_d,
+                                 dOut, gu_save, fwd_ws, fwd_ws_bytes, dX, dW_gu, dW_d, dtopk_w, ws, ws_bytes, s);
+}
+
+extern "C" int mp_grouped_expert_gemm_weighted_act_bwd(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
+                                                       const void* X, const float* topk_w, const void* W_gu,
+                                                       const void* W_d, const void* dOut, const void* gu_save,
+                                                       const void* fwd_ws, size_t fwd_ws_bytes, void* dX,
+                                                       float* dW_gu, float* dW_d, float* dtopk_w, void* ws,
+                                                       size_t ws_bytes, hipStream_t s) {
+  return grouped_expert_gemm_bwd("mp_grouped_expert_gemm_weighted_act_bwd", true, T, Hd, Fe, topk, E_loc, X, topk_w,
+                                 W_gu, W_d, dOut, gu_save, fwd_ws, fwd_ws_bytes, dX, dW_gu, dW_d, dtopk_w, ws,
+                                 ws_bytes, s);
 }
 
 // ------------------------------------------------------------------ MXFP8

@@ -76,6 +76,10 @@ _SIGS = {
                                                     c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "mp_grouped_expert_gemm_fwd_train": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p,
                                                  c_p, c_p, c_p, c_sz, c_p]),
+    "mp_grouped_expert_gemm_weighted_act_fwd_train": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p,
+                                                              c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "mp_grouped_expert_gemm_weighted_act_bwd": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p,
+                                                        c_p, c_p, c_sz, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
     "mp_grouped_expert_gemm_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_i32, c_i32]),
     "mp_grouped_expert_gemm_bwd": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz,
                                            c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
@@ -374,10 +378,13 @@ def mp_grouped_expert_gemm_weighted_act(X, topk_ids, topk_w, W_gu, W_d, e_start,
                          perm_picks, expert_offsets, ws, stream)
 
 
-def mp_grouped_expert_gemm_fwd_train(X, topk_ids, topk_w, W_gu, W_d, e_start, out, gu_save, ws=None, stream=None):
-    """Training forward; returns the workspace, which holds the state
-    mp_grouped_expert_gemm_bwd reads (keep it and gu_save until then).  It is
-    a buffer of its own, not the shared scratch of :func:`workspace`."""
+def mp_grouped_expert_gemm_fwd_train(X, topk_ids, topk_w, W_gu, W_d, e_start, out, gu_save, ws=None, stream=None,
+                                     weighted_act=False):
+    """Training forward (``weighted_act``: the memory-efficient form);
+    returns the workspace, which holds the state the matching backward reads
+    (keep it and gu_save until then).  It is a buffer of its own, not the
+    shared scratch of :func:`workspace`."""
+    name = "mp_grouped_expert_gemm_weighted_act_fwd_train" if weighted_act else "mp_grouped_expert_gemm_fwd_train"
     T, Hd = X.shape
     topk = topk_ids.shape[1]
     E_loc, two_fe, _ = W_gu.shape
@@ -385,21 +392,22 @@ def mp_grouped_expert_gemm_fwd_train(X, topk_ids, topk_w, W_gu, W_d, e_start, ou
     need = lib().mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E_loc)
     if ws is None:
         ws = torch.empty(max(int(need), 1), dtype=torch.uint8, device=X.device)
-    _call("mp_grouped_expert_gemm_fwd_train", T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w),
+    _call(name, T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w),
           _p(W_gu), _p(W_d), _p(out), _p(gu_save), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
           _s(stream))
     return ws
 
 
 def mp_grouped_expert_gemm_bwd(X, topk_w, W_gu, W_d, dOut, gu_save, fwd_ws, dX, dW_gu, dW_d, dtopk_w, ws=None,
-                               stream=None):
+                               stream=None, weighted_act=False):
+    name = "mp_grouped_expert_gemm_weighted_act_bwd" if weighted_act else "mp_grouped_expert_gemm_bwd"
     T, Hd = X.shape
     topk = topk_w.shape[1]
     E_loc, two_fe, _ = W_gu.shape
     Fe = two_fe // 2
     need = lib().mp_grouped_expert_gemm_bwd_workspace(T, Hd, Fe, topk, E_loc)
     ws = ws if ws is not None else workspace(need, X.device)
-    _call("mp_grouped_expert_gemm_bwd", T, Hd, Fe, topk, E_loc, _p(X), _p(topk_w), _p(W_gu), _p(W_d), _p(dOut),
+    _call(name, T, Hd, Fe, topk, E_loc, _p(X), _p(topk_w), _p(W_gu), _p(W_d), _p(dOut),
           _p(gu_save), _p(fwd_ws), fwd_ws.numel() * fwd_ws.element_size() if fwd_ws is not None else 0, _p(dX),
           _p(dW_gu), _p(dW_d), _p(dtopk_w), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
           _s(stream))

@@ -260,3 +260,21 @@ def test_moe_training_validation(lib):
     bad[9] = ALIGNED + 4  # dW_gu
     rc, _ = call(lib, "mp_grouped_expert_gemm_bwd", T, Hd, Fe, topk, E, *bad)
     assert rc == -5
+
+
+def test_moe_weighted_act_training_validation(lib):
+    # The memory-efficient form's training calls validate like the others.
+    T, Hd, Fe, topk, E = 16, 64, 64, 2, 2
+    need = lib.mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E)
+    fa = [ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, ctypes.c_size_t(need), None]
+    rc, msg = call(lib, "mp_grouped_expert_gemm_weighted_act_fwd_train", T, Hd, Fe, topk, E, 0, *fa)
+    assert rc == -1 and "gu_save" in msg
+    bneed = lib.mp_grouped_expert_gemm_bwd_workspace(T, Hd, Fe, topk, E)
+    assert bneed >= T * topk * (2 * Hd + 2 * Fe) * 2 + T * topk * (Fe // 8 + 1) * 4
+    ba = [ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ctypes.c_size_t(need), ALIGNED, ALIGNED,
+          ALIGNED, ALIGNED, ALIGNED, ctypes.c_size_t(bneed - 1), None]
+    rc, _ = call(lib, "mp_grouped_expert_gemm_weighted_act_bwd", T, Hd, Fe, topk, E, *ba)
+    assert rc == -6
+    ba[4] = None  # dOut
+    rc, _ = call(lib, "mp_grouped_expert_gemm_weighted_act_bwd", T, Hd, Fe, topk, E, *ba)
+    assert rc == -1

@@ -2,7 +2,9 @@
 gate/up pre-activations, routing-weight gradient, grouped d act GEMM with the
 SwiGLU derivative in its epilogue, grouped input-gradient GEMM, unpermute of
 the input gradient, grouped weight-gradient GEMMs over each expert's rows)
-against the oracle's backward."""
+against the oracle's backward, in both forms: weighted unpermute, and the
+memory-efficient form (weight on the activation; its weight gradient comes
+from the activation side in the d act GEMM's epilogue)."""
 
 import numpy as np
 import pytest
@@ -22,7 +24,10 @@ def routing(seed, T, experts, topk):
     return torch.from_numpy(ids), torch.from_numpy(w / w.sum(axis=1, keepdims=True))
 
 
-def run(x, ids, w, wgu, wd, e_start, dout):
+FORMS = {"weighted_unpermute": (False, O.moe_backward), "weighted_act": (True, O.moe_backward_weighted_act)}
+
+
+def run(x, ids, w, wgu, wd, e_start, dout, weighted_act=False):
     """Training forward then backward; returns host tensors."""
     T, Hd = x.shape
     topk = ids.shape[1]
@@ -31,14 +36,15 @@ def run(x, ids, w, wgu, wd, e_start, dout):
     x, ids, w, wgu, wd, dout = cu(x), cu(ids), cu(w), cu(wgu), cu(wd), cu(dout)
     out = torch.empty((T, Hd), dtype=torch.bfloat16, device="cuda")
     gu = torch.full((T * topk, 2 * Fe), 7.0, dtype=torch.bfloat16, device="cuda")
-    fws = mp.mp_grouped_expert_gemm_fwd_train(x, ids, w, wgu, wd, e_start, out, gu)
+    fws = mp.mp_grouped_expert_gemm_fwd_train(x, ids, w, wgu, wd, e_start, out, gu, weighted_act=weighted_act)
     dx = torch.full((T, Hd), 7.0, dtype=torch.bfloat16, device="cuda")
     dwgu = torch.full((e_local, 2 * Fe, Hd), 7.0, dtype=torch.float32, device="cuda")
     dwd = torch.full((e_local, Hd, Fe), 7.0, dtype=torch.float32, device="cuda")
     dtw = torch.full((T, topk), 7.0, dtype=torch.float32, device="cuda")
-    mp.mp_grouped_expert_gemm_bwd(x, w, wgu, wd, dout, gu, fws, dx, dwgu, dwd, dtw)
+    mp.mp_grouped_expert_gemm_bwd(x, w, wgu, wd, dout, gu, fws, dx, dwgu, dwd, dtw, weighted_act=weighted_act)
     plain = torch.empty_like(out)
-    mp.mp_grouped_expert_gemm(x, ids, w, wgu, wd, e_start, plain)
+    fwd = mp.mp_grouped_expert_gemm_weighted_act if weighted_act else mp.mp_grouped_expert_gemm
+    fwd(x, ids, w, wgu, wd, e_start, plain)
     sync()
     return {"out": out.cpu(), "plain": plain.cpu(), "gu": gu.cpu(), "x": dx.cpu(), "w_gu": dwgu.cpu(),
             "w_d": dwd.cpu(), "topk_w": dtw.cpu()}
@@ -65,14 +71,16 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("form", list(FORMS))
 @pytest.mark.parametrize("T,Hd,Fe,experts,e_local,e_start,topk", CASES)
-def test_grouped_expert_gemm_bwd(T, Hd, Fe, experts, e_local, e_start, topk):
-    say("moe bwd", T, Hd, Fe, experts, e_local, e_start, topk)
+def test_grouped_expert_gemm_bwd(T, Hd, Fe, experts, e_local, e_start, topk, form):
+    say("moe bwd", form, T, Hd, Fe, experts, e_local, e_start, topk)
+    wa, oracle_bwd = FORMS[form]
     ids, w, x, wgu, wd, dout = inputs(T, Hd, Fe, experts, e_local, topk)
-    got = run(x, ids, w, wgu, wd, e_start, dout)
+    got = run(x, ids, w, wgu, wd, e_start, dout, wa)
     # The training forward's output is the plain forward's, bit for bit.
     assert torch.equal(got["out"], got["plain"])
-    want = O.moe_backward(f64(x), ids.numpy(), w.numpy(), f64(wgu), f64(wd), e_start, f64(dout))
+    want = oracle_bwd(f64(x), ids.numpy(), w.numpy(), f64(wgu), f64(wd), e_start, f64(dout))
     for name in ("x", "w_gu", "w_d", "topk_w"):
         err = rel_frobenius(f64(got[name]), want[name])
         assert err <= TOL["bf16"], (name, err)
@@ -94,41 +102,45 @@ def test_grouped_expert_gemm_bwd(T, Hd, Fe, experts, e_local, e_start, topk):
     assert torch.all(got["x"][torch.from_numpy(~local.any(axis=1))] == 0)
 
 
-def test_bwd_no_local_picks():
-    say("moe bwd empty shard")
+@pytest.mark.parametrize("form", list(FORMS))
+def test_bwd_no_local_picks(form):
+    say("moe bwd empty shard", form)
     ids, w, x, wgu, wd, dout = inputs(20, 64, 64, 8, 2, 2)
-    got = run(x, ids, w, wgu, wd, 100, dout)  # experts 100, 101 are never picked
+    got = run(x, ids, w, wgu, wd, 100, dout, FORMS[form][0])  # experts 100, 101 are never picked
     for name in ("x", "w_gu", "w_d", "topk_w"):
         assert torch.all(got[name] == 0), name
 
 
-def test_bwd_deterministic():
-    say("moe bwd repeat")
+@pytest.mark.parametrize("form", list(FORMS))
+def test_bwd_deterministic(form):
+    say("moe bwd repeat", form)
     ids, w, x, wgu, wd, dout = inputs(300, 256, 136, 32, 8, 8)
-    a = run(x, ids, w, wgu, wd, 0, dout)
-    b = run(x, ids, w, wgu, wd, 0, dout)
+    a = run(x, ids, w, wgu, wd, 0, dout, FORMS[form][0])
+    b = run(x, ids, w, wgu, wd, 0, dout, FORMS[form][0])
     for name in ("x", "w_gu", "w_d", "topk_w"):
         assert torch.equal(a[name], b[name]), name
 
 
-def test_moe_bwd_full_size():
+@pytest.mark.parametrize("form", list(FORMS))
+def test_moe_bwd_full_size(form):
     """The hot expert-parallel shard (experts 0-7 of 256, Zipf(1.1) routing,
     hidden 7168, expert FFN 2048, 4096 tokens top-8): input and routing-weight
     gradients of 48 sampled tokens, and the whole weight gradient of the
     coldest local expert, through the oracle."""
-    say("moe bwd full size")
+    say("moe bwd full size", form)
+    wa, oracle_bwd = FORMS[form]
     wl = S.WORKLOADS["moe"]
     inp = S.moe_inputs(wl)
     rng = np.random.default_rng(11)
     dout = torch.from_numpy(rng.standard_normal((wl.T, wl.K), dtype=np.float32)).to(torch.bfloat16)
-    got = run(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_gu"], inp["w_d"], 0, dout)
+    got = run(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_gu"], inp["w_d"], 0, dout, wa)
     ids, w = inp["topk_ids"].numpy(), inp["topk_w"].numpy()
     x64, wgu64, wd64, d64 = f64(inp["x"]), f64(inp["w_gu"]), f64(inp["w_d"]), f64(dout)
     toks = np.random.default_rng(3).choice(wl.T, 48, replace=False)
-    sub = O.moe_backward(x64[toks], ids[toks], w[toks], wgu64, wd64, 0, d64[toks])
+    sub = oracle_bwd(x64[toks], ids[toks], w[toks], wgu64, wd64, 0, d64[toks])
     assert rel_frobenius(f64(got["x"])[toks], sub["x"]) <= TOL["bf16"]
     assert rel_frobenius(f64(got["topk_w"])[toks], sub["topk_w"]) <= TOL["bf16"]
     e = wl.e_local - 1
-    one = O.moe_backward(x64, ids, w, wgu64[e:e + 1], wd64[e:e + 1], e, d64)
+    one = oracle_bwd(x64, ids, w, wgu64[e:e + 1], wd64[e:e + 1], e, d64)
     assert rel_frobenius(f64(got["w_gu"][e]), one["w_gu"][0]) <= TOL["bf16"]
     assert rel_frobenius(f64(got["w_d"][e]), one["w_d"][0]) <= TOL["bf16"]
