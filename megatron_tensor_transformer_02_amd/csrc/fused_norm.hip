@@ -101,6 +101,28 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// Two independent block sums behind one barrier (each summed exactly as
+// block_sum does, so the results are the same bits).
+template <int NW>
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* red_a, float* red_b) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    red_a[wave] = a;
+    red_b[wave] = b;
+  }
+  __syncthreads();
+  float ta = red_a[0], tb = red_b[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    ta += red_a[w];
+    tb += red_b[w];
+  }
+  a = ta;
+  b = tb;
+}
+
 // out = residual + Drop(sum_j parts[j] + bias); y = LN(out) * gamma + beta.
 // Block = NW waves; thread t owns the 16-byte vector t of every row, and the
 // block walks rows [blockIdx.x * RPB, +RPB).  The loads of row r+1 are issued
@@ -242,8 +264,8 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_bwd_kernel(PartPtrs parts, 
         s2 += g[i] * xh[i];
       }
     }
-    const float m1 = block_sum<NW>(s1, red[slot]) * inv_k;
-    const float m2 = block_sum<NW>(s2, red[slot + 1]) * inv_k;
+    block_sum2<NW>(s1, s2, red[slot], red[slot + 1]);
+    const float m1 = s1 * inv_k, m2 = s2 * inv_k;
     if (act) {
       float o[E], r[E];
       if (dres != nullptr) {
