@@ -146,15 +146,19 @@ def _dt(t):
 _ws_cache = {}
 
 
-def workspace(nbytes, device=None):
-    """A cached device byte buffer of at least ``nbytes`` (per device)."""
+def workspace(nbytes, device=None, stream=None):
+    """A cached device byte buffer of at least ``nbytes``, one per (device,
+    stream): calls enqueued on one stream run in order and may share it; calls
+    on different streams get different buffers.  Its contents do not survive
+    the next call that uses it."""
     if nbytes == 0:
         return None
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    buf = _ws_cache.get(dev)
+    key = (dev, (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream)
+    buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(int(nbytes), dtype=torch.uint8, device=dev)
-        _ws_cache[dev] = buf
+        _ws_cache[key] = buf
     return buf
 
 
@@ -195,7 +199,7 @@ def mp_column_linear_gelu_bwd(X, A_i, Z_save, dY_i, act, dX_partial, dA_i, da_i=
     Fi = A_i.shape[0]
     dt = _dt(X)
     need = lib().mp_column_linear_gelu_bwd_workspace(dt, T, K, Fi)
-    ws = ws if ws is not None else workspace(need, X.device)
+    ws = ws if ws is not None else workspace(need, X.device, stream)
     _call("mp_column_linear_gelu_bwd", dt, T, K, Fi, _p(X), _p(A_i), _p(Z_save), _p(dY_i), _act(act),
           _p(dX_partial), _p(dA_i), _p(da_i), _p(ws), need if ws is not None else 0, _s(stream))
 
@@ -211,7 +215,7 @@ def mp_row_linear_partial_bwd(Y_i, B_i, dOut, dY_i, dB_i, ws=None, stream=None):
     K = B_i.shape[0]
     dt = _dt(Y_i)
     need = lib().mp_row_linear_partial_bwd_workspace(dt, T, Fi, K)
-    ws = ws if ws is not None else workspace(need, Y_i.device)
+    ws = ws if ws is not None else workspace(need, Y_i.device, stream)
     _call("mp_row_linear_partial_bwd", dt, T, Fi, K, _p(Y_i), _p(B_i), _p(dOut), _p(dY_i), _p(dB_i), _p(ws),
           need if ws is not None else 0, _s(stream))
 
@@ -221,7 +225,7 @@ def mp_row_linear_partial_bwd_dact(Y_i, B_i, dOut, Z_save, act, dZ_i, dB_i, ws=N
     K = B_i.shape[0]
     dt = _dt(Y_i)
     need = lib().mp_row_linear_partial_bwd_workspace(dt, T, Fi, K)
-    ws = ws if ws is not None else workspace(need, Y_i.device)
+    ws = ws if ws is not None else workspace(need, Y_i.device, stream)
     _call("mp_row_linear_partial_bwd_dact", dt, T, Fi, K, _p(Y_i), _p(B_i), _p(dOut), _p(Z_save), _act(act),
           _p(dZ_i), _p(dB_i), _p(ws), need if ws is not None else 0, _s(stream))
 
@@ -251,7 +255,7 @@ def mp_shard_reduce_layernorm_bwd(partials, x, gamma, mean, rstd, dx, dres=None,
     arr = _ptr_array(partials)
     need = lib().mp_shard_reduce_layernorm_bwd_workspace(rows, cols) if (dgamma is not None or dbeta is not None) \
         else 0
-    ws = ws if ws is not None else workspace(need, x.device)
+    ws = ws if ws is not None else workspace(need, x.device, stream)
     _call("mp_shard_reduce_layernorm_bwd", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
           _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), _p(ws), need if ws is not None else 0, _s(stream))
 
@@ -262,7 +266,7 @@ def mp_shard_reduce_layernorm_bwd_dropout(partials, x, gamma, mean, rstd, dx, p,
     arr = _ptr_array(partials)
     params = dgamma is not None or dbeta is not None or dbias is not None
     need = lib().mp_shard_reduce_layernorm_bwd_workspace(rows, cols) if params else 0
-    ws = ws if ws is not None else workspace(need, x.device)
+    ws = ws if ws is not None else workspace(need, x.device, stream)
     _call("mp_shard_reduce_layernorm_bwd_dropout", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
           _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), p, _p(keep_bits), _p(ddrop), _p(dbias), _p(ws),
           need if ws is not None else 0, _s(stream))
@@ -283,7 +287,7 @@ def mp_all_gather_rows(slices, out, stream=None):
 def mp_dropout_mask_bwd(dy, keep_bits, p, dx, dbias=None, ws=None, stream=None):
     rows, cols = dy.shape
     need = lib().mp_dropout_mask_bwd_workspace(rows, cols) if dbias is not None else 0
-    ws = ws if ws is not None else workspace(need, dy.device)
+    ws = ws if ws is not None else workspace(need, dy.device, stream)
     _call("mp_dropout_mask_bwd", _dt(dy), rows, cols, _p(dy), _p(keep_bits), p, _p(dx), _p(dbias), _p(ws),
           need if ws is not None else 0, _s(stream))
 
@@ -296,7 +300,7 @@ def mp_shared_seed_dropout(x, y, p, seed, offset, index_base=0, mask_out=None, s
 def mp_bias_grad(dy, db, ws=None, stream=None):
     rows, cols = dy.shape
     need = lib().mp_bias_grad_workspace(rows, cols)
-    ws = ws if ws is not None else workspace(need, dy.device)
+    ws = ws if ws is not None else workspace(need, dy.device, stream)
     _call("mp_bias_grad", _dt(dy), rows, cols, _p(dy), _p(db), _p(ws), need if ws is not None else 0, _s(stream))
 
 
@@ -313,7 +317,7 @@ def mp_head_attention_bwd(X, Wqkv_i, qkv, ctx_i, lse, dctx_i, B, L, h, d, dX_par
     K = X.shape[1]
     dt = _dt(X)
     need = lib().mp_head_attention_bwd_workspace(dt, B, L, K, h, d)
-    ws = ws if ws is not None else workspace(need, X.device)
+    ws = ws if ws is not None else workspace(need, X.device, stream)
     _call("mp_head_attention_bwd", dt, B, L, K, h, d, int(causal), _p(X), _p(Wqkv_i), _p(qkv), _p(ctx_i), _p(lse),
           _p(dctx_i), _p(dX_partial), _p(dWqkv_i), _p(dbqkv_i), _p(ws), need if ws is not None else 0, _s(stream))
 
@@ -335,7 +339,7 @@ def mp_vocab_parallel_logits_xent(H, E_i, labels, v_start, triples, ws=None, str
     T, K = H.shape
     Vi = E_i.shape[0]
     need = lib().mp_vocab_parallel_logits_xent_workspace(T, K, Vi)
-    ws = ws if ws is not None else workspace(need, H.device)
+    ws = ws if ws is not None else workspace(need, H.device, stream)
     _call("mp_vocab_parallel_logits_xent", _dt(H), T, K, Vi, v_start, _p(H), _p(E_i), _p(labels), _p(triples), _p(ws),
           need if ws is not None else 0, _s(stream))
 
@@ -361,7 +365,7 @@ def _grouped_expert_gemm(name, X, topk_ids, topk_w, W_gu, W_d, e_start, out, per
     E_loc, two_fe, _ = W_gu.shape
     Fe = two_fe // 2
     need = lib().mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E_loc)
-    ws = ws if ws is not None else workspace(need, X.device)
+    ws = ws if ws is not None else workspace(need, X.device, stream)
     _call(name, T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w), _p(W_gu),
           _p(W_d), _p(out), _p(perm_picks), _p(expert_offsets), _p(ws), need if ws is not None else 0, _s(stream))
 
@@ -406,7 +410,7 @@ def mp_grouped_expert_gemm_bwd(X, topk_w, W_gu, W_d, dOut, gu_save, fwd_ws, dX, 
     E_loc, two_fe, _ = W_gu.shape
     Fe = two_fe // 2
     need = lib().mp_grouped_expert_gemm_bwd_workspace(T, Hd, Fe, topk, E_loc)
-    ws = ws if ws is not None else workspace(need, X.device)
+    ws = ws if ws is not None else workspace(need, X.device, stream)
     _call(name, T, Hd, Fe, topk, E_loc, _p(X), _p(topk_w), _p(W_gu), _p(W_d), _p(dOut),
           _p(gu_save), _p(fwd_ws), fwd_ws.numel() * fwd_ws.element_size() if fwd_ws is not None else 0, _p(dX),
           _p(dW_gu), _p(dW_d), _p(dtopk_w), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
@@ -431,7 +435,7 @@ def mp_grouped_expert_gemm_mxfp8(X, topk_ids, topk_w, W_gu_q, W_gu_s, W_d_q, W_d
     E_loc, two_fe, _ = W_gu_q.shape
     Fe = two_fe // 2
     need = lib().mp_grouped_expert_gemm_mxfp8_workspace(T, Hd, Fe, topk, E_loc)
-    ws = ws if ws is not None else workspace(need, X.device)
+    ws = ws if ws is not None else workspace(need, X.device, stream)
     _call("mp_grouped_expert_gemm_mxfp8", T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w),
           _p(W_gu_q), _p(W_gu_s), _p(W_d_q), _p(W_d_s), _p(out), _p(perm_picks), _p(expert_offsets), _p(ws),
           need if ws is not None else 0, _s(stream))
@@ -447,6 +451,6 @@ def mp_layernorm(x, gamma, beta, y, mean=None, rstd=None, eps=1e-5, stream=None)
 def mp_layernorm_bwd(x, gamma, mean, rstd, dy, dx, dres=None, dgamma=None, dbeta=None, ws=None, stream=None):
     T, K = x.shape
     need = lib().mp_layernorm_bwd_workspace(T, K) if (dgamma is not None or dbeta is not None) else 0
-    ws = ws if ws is not None else workspace(need, x.device)
+    ws = ws if ws is not None else workspace(need, x.device, stream)
     _call("mp_layernorm_bwd", _dt(x), T, K, _p(x), _p(gamma), _p(mean), _p(rstd), _p(dy), _p(dres), _p(dx),
           _p(dgamma), _p(dbeta), _p(ws), need if ws is not None else 0, _s(stream))
