@@ -336,7 +336,9 @@ size_t mp_grouped_expert_gemm_workspace(int64_t T, int64_t Hd, int64_t Fe, int t
  * X [T,Hd] bf16, topk_ids [T,topk] int32, topk_w [T,topk] fp32,
  * out [T,Hd] bf16, perm_picks [T*topk] int32 or NULL (entries >= R untouched;
  * with distinct ids per token R <= T*min(topk,E_loc)), expert_offsets
- * [E_loc+1] int32 or NULL; ws >= mp_grouped_expert_gemm_workspace(). */
+ * [E_loc+1] int32 or NULL; ws >= mp_grouped_expert_gemm_workspace().  T = 0
+ * (no tokens) returns MP_OK without touching any buffer (all may be NULL);
+ * so do the other MoE forward calls below. */
 int mp_grouped_expert_gemm(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
                            int e_start, const void* X, const int32_t* topk_ids,
                            const float* topk_w, const void* W_gu, const void* W_d, void* out,
@@ -393,7 +395,8 @@ size_t mp_grouped_expert_gemm_bwd_workspace(int64_t T, int64_t Hd, int64_t Fe, i
  * expert without rows); dtopk_w [T,topk] fp32 (zero for picks on other
  * shards).  Weight gradients sum their rows in a fixed order
  * (deterministic).  ws >= mp_grouped_expert_gemm_bwd_workspace().  Same
- * shape limits and errors as the forward. */
+ * shape limits and errors as the forward.  T = 0: only dW_gu and dW_d are
+ * written (zeros); every other buffer may be NULL. */
 int mp_grouped_expert_gemm_bwd(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
                                const void* X, const float* topk_w, const void* W_gu,
                                const void* W_d, const void* dOut, const void* gu_save,

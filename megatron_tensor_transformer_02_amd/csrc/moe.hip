@@ -691,6 +691,7 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   MP_REQUIRE(Hd % 8 == 0 && Fe % 8 == 0, MP_ERR_SHAPE, "%s: Hd and Fe must be multiples of 8", fn);
   MP_REQUIRE(T * Hd * 2 < 0x7fffffffLL && 2 * Fe * Hd * 2 < 0x7fffffffLL && T * topk * Fe * 2 < 0x7fffffffLL,
              MP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+  if (T == 0) return MP_OK;  // no tokens: nothing is read or written
   MP_REQUIRE_PTR(X);
   MP_REQUIRE_PTR(topk_ids);
   MP_REQUIRE_PTR(topk_w);
@@ -704,7 +705,6 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   const MoeLayout L = moe_layout(T, Hd, Fe, topk, E_loc);
   MP_REQUIRE(ws != nullptr && ws_bytes >= L.total, MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, L.total);
   MP_REQUIRE_ALIGN(ws);
-  if (T == 0) return MP_OK;
   char* w = static_cast<char*>(ws);
   MoeArgs a{};
   a.T = T;
@@ -769,8 +769,10 @@ extern "C" int mp_grouped_expert_gemm_weighted_act(int64_t T, int64_t Hd, int64_
 static int fwd_train(const char* fn, bool w_on_act, int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc,
                      int e_start, const void* X, const int32_t* topk_ids, const float* topk_w, const void* W_gu,
                      const void* W_d, void* out, void* gu_save, void* ws, size_t ws_bytes, hipStream_t s) {
-  MP_REQUIRE_PTR(gu_save);
-  MP_REQUIRE_ALIGN(gu_save);
+  if (T != 0) {
+    MP_REQUIRE_PTR(gu_save);
+    MP_REQUIRE_ALIGN(gu_save);
+  }
   return grouped_expert_gemm(fn, w_on_act, T, Hd, Fe, topk, E_loc, e_start, X, topk_ids, topk_w, W_gu, W_d, out,
                              nullptr, nullptr, ws, ws_bytes, s, gu_save);
 }
@@ -830,6 +832,18 @@ static int grouped_expert_gemm_bwd(const char* fn, bool w_on_act, int64_t T, int
   MP_REQUIRE(T * Hd * 2 < 0x7fffffffLL && 2 * Fe * Hd * 2 < 0x7fffffffLL && T * topk * Hd * 2 < 0x7fffffffLL &&
                  T * topk * 2 * Fe * 2 < 0x7fffffffLL,
              MP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+  MP_REQUIRE_PTR(dW_gu);
+  MP_REQUIRE_PTR(dW_d);
+  MP_REQUIRE_ALIGN(dW_gu);
+  MP_REQUIRE_ALIGN(dW_d);
+  if (T == 0) {
+    // No tokens: every expert's weight gradient is zero; the token-sized
+    // buffers are empty and may be NULL.
+    const int64_t n = static_cast<int64_t>(E_loc) * 2 * Fe * Hd, m = static_cast<int64_t>(E_loc) * Hd * Fe;
+    moe_zero_f32_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, s>>>(dW_gu, n);
+    moe_zero_f32_kernel<<<static_cast<unsigned>(ceil_div(m, 256)), 256, 0, s>>>(dW_d, m);
+    return check_launch(fn);
+  }
   MP_REQUIRE_PTR(X);
   MP_REQUIRE_PTR(topk_w);
   MP_REQUIRE_PTR(W_gu);
@@ -837,8 +851,6 @@ static int grouped_expert_gemm_bwd(const char* fn, bool w_on_act, int64_t T, int
   MP_REQUIRE_PTR(dOut);
   MP_REQUIRE_PTR(gu_save);
   MP_REQUIRE_PTR(dX);
-  MP_REQUIRE_PTR(dW_gu);
-  MP_REQUIRE_PTR(dW_d);
   MP_REQUIRE_PTR(dtopk_w);
   MP_REQUIRE_ALIGN(X);
   MP_REQUIRE_ALIGN(W_gu);
@@ -846,8 +858,6 @@ static int grouped_expert_gemm_bwd(const char* fn, bool w_on_act, int64_t T, int
   MP_REQUIRE_ALIGN(dOut);
   MP_REQUIRE_ALIGN(gu_save);
   MP_REQUIRE_ALIGN(dX);
-  MP_REQUIRE_ALIGN(dW_gu);
-  MP_REQUIRE_ALIGN(dW_d);
   const MoeLayout F = moe_layout(T, Hd, Fe, topk, E_loc);
   MP_REQUIRE(fwd_ws != nullptr && fwd_ws_bytes >= F.total, MP_ERR_WORKSPACE,
              "%s: the forward's workspace holds %zu bytes", fn, F.total);
@@ -855,13 +865,6 @@ static int grouped_expert_gemm_bwd(const char* fn, bool w_on_act, int64_t T, int
   const MoeBwdLayout L = moe_bwd_layout(T, Hd, Fe, topk);
   MP_REQUIRE(ws != nullptr && ws_bytes >= L.total, MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, L.total);
   MP_REQUIRE_ALIGN(ws);
-  if (T == 0) {
-    // No tokens: every expert's weight gradient is zero.
-    const int64_t n = static_cast<int64_t>(E_loc) * 2 * Fe * Hd, m = static_cast<int64_t>(E_loc) * Hd * Fe;
-    moe_zero_f32_kernel<<<static_cast<unsigned>(ceil_div(n, 256)), 256, 0, s>>>(dW_gu, n);
-    moe_zero_f32_kernel<<<static_cast<unsigned>(ceil_div(m, 256)), 256, 0, s>>>(dW_d, m);
-    return check_launch(fn);
-  }
   char* fw = static_cast<char*>(const_cast<void*>(fwd_ws));
   char* w = static_cast<char*>(ws);
   MoeArgs a{};
@@ -971,6 +974,7 @@ extern "C" int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, i
   MP_REQUIRE(Hd % 32 == 0 && Fe % 32 == 0, MP_ERR_SHAPE, "%s: Hd and Fe must be multiples of 32 (MX blocks)", fn);
   MP_REQUIRE(T * Hd * 2 < 0x7fffffffLL && 2 * Fe * Hd < 0x7fffffffLL && T * topk * Fe * 2 < 0x7fffffffLL,
              MP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+  if (T == 0) return MP_OK;  // no tokens: nothing is read or written
   MP_REQUIRE_PTR(X);
   MP_REQUIRE_PTR(topk_ids);
   MP_REQUIRE_PTR(topk_w);
@@ -988,7 +992,6 @@ extern "C" int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, i
   const MoeLayout L = moe_layout(T, Hd, Fe, topk, E_loc, true);
   MP_REQUIRE(ws != nullptr && ws_bytes >= L.total, MP_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, L.total);
   MP_REQUIRE_ALIGN(ws);
-  if (T == 0) return MP_OK;
   char* w = static_cast<char*>(ws);
   MoeArgs a{};
   a.T = T;

@@ -278,3 +278,22 @@ def test_moe_weighted_act_training_validation(lib):
     ba[4] = None  # dOut
     rc, _ = call(lib, "mp_grouped_expert_gemm_weighted_act_bwd", T, Hd, Fe, topk, E, *ba)
     assert rc == -1
+
+
+def test_moe_empty_token_buffers_may_be_null(lib):
+    # T = 0: the forward calls touch nothing, so every pointer may be NULL.
+    Hd, Fe, topk, E = 64, 64, 2, 2
+    nulls = [None] * 6
+    rc, msg = call(lib, "mp_grouped_expert_gemm", 0, Hd, Fe, topk, E, 0, *nulls, None, None, None,
+                   ctypes.c_size_t(0), None)
+    assert rc == 0, msg
+    rc, msg = call(lib, "mp_grouped_expert_gemm_fwd_train", 0, Hd, Fe, topk, E, 0, *nulls, None, None,
+                   ctypes.c_size_t(0), None)
+    assert rc == 0, msg
+    rc, msg = call(lib, "mp_grouped_expert_gemm_mxfp8", 0, Hd, Fe, topk, E, 0, None, None, None, None, None, None,
+                   None, None, None, None, None, ctypes.c_size_t(0), None)
+    assert rc == 0, msg
+    # The backward still needs its weight-gradient outputs (it zeroes them).
+    rc, msg = call(lib, "mp_grouped_expert_gemm_bwd", 0, Hd, Fe, topk, E, None, None, None, None, None, None, None,
+                   ctypes.c_size_t(0), None, None, ALIGNED, None, None, ctypes.c_size_t(0), None)
+    assert rc == -1 and "dW" in msg

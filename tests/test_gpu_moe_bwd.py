@@ -144,3 +144,27 @@ def test_moe_bwd_full_size(form):
     one = oracle_bwd(x64, ids, w, wgu64[e:e + 1], wd64[e:e + 1], e, d64)
     assert rel_frobenius(f64(got["w_gu"][e]), one["w_gu"][0]) <= TOL["bf16"]
     assert rel_frobenius(f64(got["w_d"][e]), one["w_d"][0]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("form", list(FORMS))
+def test_bwd_zero_tokens(form):
+    """No tokens at all: the forward does nothing, the backward zeroes every
+    expert's weight gradients (stale values must not survive)."""
+    say("moe bwd zero tokens", form)
+    wa = FORMS[form][0]
+    Hd, Fe, e_local, topk = 64, 72, 3, 2
+    dev = "cuda"
+    x = torch.empty((0, Hd), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((0, topk), dtype=torch.int32, device=dev)
+    w = torch.empty((0, topk), dtype=torch.float32, device=dev)
+    wgu = torch.ones((e_local, 2 * Fe, Hd), dtype=torch.bfloat16, device=dev)
+    wd = torch.ones((e_local, Hd, Fe), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((0, Hd), dtype=torch.bfloat16, device=dev)
+    gu = torch.empty((0, 2 * Fe), dtype=torch.bfloat16, device=dev)
+    fws = mp.mp_grouped_expert_gemm_fwd_train(x, ids, w, wgu, wd, 0, out, gu, weighted_act=wa)
+    dwgu = torch.full((e_local, 2 * Fe, Hd), 7.0, dtype=torch.float32, device=dev)
+    dwd = torch.full((e_local, Hd, Fe), 7.0, dtype=torch.float32, device=dev)
+    mp.mp_grouped_expert_gemm_bwd(x, w, wgu, wd, torch.empty_like(x), gu, fws, torch.empty_like(x), dwgu, dwd,
+                                  torch.empty_like(w), weighted_act=wa)
+    sync()
+    assert torch.all(dwgu == 0) and torch.all(dwd == 0)
