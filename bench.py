@@ -21,7 +21,9 @@ resident in HBM:
 
 ``value`` is the layer's model TFLOP/s (forward + backward = 3x the forward
 FLOPs, attention counted on the causal half); the vocab cross-entropy's GB/s
-is reported beside it.  After the timed steps, the sequence-parallel form of
+is reported beside it (``xent_GBps``; ``xent_bwd_GBps`` and
+``xent_fwd_bwd_GBps`` add the cross-entropy backward timed in the same
+steps).  After the timed steps, the sequence-parallel form of
 the same layer share (each 8-way reduce on the rank's 1024 tokens only, an
 all-gather before each column-parallel GEMM) is timed on its own and reported
 as ``sp_layer_ms`` / ``sp_layer_TFLOPS`` (``--no-sp`` skips it).  Prints one
@@ -181,7 +183,7 @@ def main():
         torch.cuda.synchronize()
         log(f"vocab setup {time.time() - t0:.1f}s")
 
-        def vocab_step(ev=None):
+        def vocab_step(ev=None, evb=None):
             e0 = v0.embed_partial(ids)
             v0.embed_reduce([e0] + emb_sib[1:])
             v0.logits(hidden)
@@ -191,7 +193,11 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
             v0.combine([t0_] + tri_sib[1:])
+            if evb is not None:
+                evb[0].record(stream)
             v0.xent_bwd(labels, 1.0 / Tv)
+            if evb is not None:
+                evb[1].record(stream)
 
     # --------------------------------------------------------------- moe setup
     wm = S.WORKLOADS["moe"]
@@ -229,14 +235,14 @@ def main():
             rec["layer"][1].record(stream)
         if "vocab" in parts:
             rec["vocab"][0].record(stream)
-            vocab_step(rec["xent"])
+            vocab_step(rec["xent"], rec["xent_bwd"])
             rec["vocab"][1].record(stream)
         if "moe" in parts:
             rec["moe"][0].record(stream)
             moe_step()
             rec["moe"][1].record(stream)
 
-    mk = lambda: {k: (EV(), EV()) for k in ("layer", "vocab", "moe", "xent")}  # noqa: E731
+    mk = lambda: {k: (EV(), EV()) for k in ("layer", "vocab", "moe", "xent", "xent_bwd")}  # noqa: E731
     for _ in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -291,6 +297,13 @@ def main():
         out["vocab_ms"] = round(seg_ms("vocab"), 4)
         out["xent_GBps"] = round(gbps, 1)
         out["xent_pct_hbm"] = round(100 * gbps / PEAK_HBM_GBPS, 2)
+        # The cross-entropy backward in the same steps (fp32 gradient written
+        # over the logits: read Z + write dZ + labels + (M, S) statistics), and
+        # the statistics pass + backward together.
+        xb_ms = float(np.mean([r["xent_bwd"][0].elapsed_time(r["xent_bwd"][1]) for r in recs]))
+        bbytes = 2.0 * Tv * Vi * 4 + Tv * 4 + Tv * 8
+        out["xent_bwd_GBps"] = round(bbytes / (xb_ms * 1e-3) / 1e9, 1)
+        out["xent_fwd_bwd_GBps"] = round((xbytes + bbytes) / ((x_ms + xb_ms) * 1e-3) / 1e9, 1)
         # The logits (210 MB) are written just before by the logits GEMM and may be
         # served from the 256 MB Infinity Cache; also time the pass cold.
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
