@@ -21,7 +21,8 @@ resident in HBM:
 
 ``value`` is the layer's model TFLOP/s (forward + backward = 3x the forward
 FLOPs, attention counted on the causal half); the vocab cross-entropy's GB/s
-is reported beside it (``xent_GBps``; ``xent_bwd_GBps`` and
+is reported beside it (``xent_GBps``; ``shard_reduce_GBps`` is the MLP's
+8-way shard reduce in the same steps; ``xent_bwd_GBps`` and
 ``xent_fwd_bwd_GBps`` add the cross-entropy backward timed in the same
 steps).  After the timed steps, the sequence-parallel form of
 the same layer share (each 8-way reduce on the rank's 1024 tokens only, an
@@ -157,7 +158,11 @@ def main():
             pa = r0.attn_partial(xd)
             r0.attn_reduce([pa] + sib["attn"][1:], xd)
             pm = r0.mlp_partial()
+            if r0.probe is not None:
+                r0.probe("reduce_begin")
             r0.mlp_reduce([pm] + sib["mlp"][1:])
+            if r0.probe is not None:
+                r0.probe("reduce_end")
             pb = r0.mlp_bwd_partial(dd)
             r0.mlp_bwd_reduce([pb] + sib["mlp_bwd"][1:], dd)
             pq = r0.attn_bwd_partial()
@@ -281,7 +286,8 @@ def main():
         out["value"] = round(fl / (lay_ms * 1e-3) / 1e12, 2)
         out["layer_ms"] = round(lay_ms, 4)
         out["layer_pct_bf16_peak"] = round(100 * out["value"] / PEAK_BF16_TFLOPS, 2)
-        col = [b.elapsed_time(e) for (tb, b), (te, e) in zip(col_events[0::2], col_events[1::2])]
+        ev_of = lambda tag: [e for t, e in col_events if t == tag]  # noqa: E731
+        col = [b.elapsed_time(e) for b, e in zip(ev_of("col_begin"), ev_of("col_end"))]
         col_ms = float(np.mean(col))
         col_fl = 2.0 * B * L * K * Fi
         ach = col_fl / (col_ms * 1e-3) / 1e12
@@ -289,6 +295,19 @@ def main():
                       "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
                       "avg_launch_us": round(col_ms * 1e3, 2), "algorithmic_per_launch": col_fl})
+        # The MLP's 8-way shard reduce (+ bias, dropout with its keep bits
+        # saved, residual): 8 bf16 partials and the residual read, the output
+        # and the keep bits written.
+        red = [b.elapsed_time(e) for b, e in zip(ev_of("reduce_begin"), ev_of("reduce_end"))]
+        red_ms = float(np.mean(red))
+        n_el = B * L * K
+        red_bytes = 8 * 2.0 * n_el + 2 * n_el + 2 * n_el + n_el / 8 + 2 * K
+        red_gbps = red_bytes / (red_ms * 1e-3) / 1e9
+        out["shard_reduce_GBps"] = round(red_gbps, 1)
+        roofs.append({"kernel": "8-way shard reduce + bias + dropout + residual (shard_reduce_kernel) [8192x3072] bf16",
+                      "bound": "hbm", "achieved": round(red_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(red_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                      "avg_launch_us": round(red_ms * 1e3, 2), "algorithmic_per_launch": red_bytes})
     if "vocab" in parts:
         xs = [r["xent"][0].elapsed_time(r["xent"][1]) for r in recs]
         x_ms = float(np.mean(xs))
