@@ -27,7 +27,9 @@ is reported beside it (``xent_GBps``; ``shard_reduce_GBps`` is the MLP's
 steps).  After the timed steps, the sequence-parallel form of
 the same layer share (each 8-way reduce on the rank's 1024 tokens only, an
 all-gather before each column-parallel GEMM) is timed on its own and reported
-as ``sp_layer_ms`` / ``sp_layer_TFLOPS`` (``--no-sp`` skips it).  Prints one
+as ``sp_layer_ms`` / ``sp_layer_TFLOPS`` (``--no-sp`` skips it), and the
+GPT-2-medium-shaped full layer at N = 1 as ``gpt2m_layer_ms`` /
+``gpt2m_layer_TFLOPS``.  Prints one
 JSON line.  ``logits_xent_fused_us`` / ``logits_xent_unfused_us`` time the
 vocab shard's logits GEMM + statistics with the statistics fused into the
 GEMM's epilogue (no logits stored) and as two passes; ``embedding_bwd_us``
@@ -521,6 +523,33 @@ def main():
         sp_ms = float(np.mean([b_.elapsed_time(e_) for b_, e_ in sev]))
         out["sp_layer_ms"] = round(sp_ms, 4)
         out["sp_layer_TFLOPS"] = round(3 * layer_flops(B, L, K, hi, d, Fi) / (sp_ms * 1e-3) / 1e12, 2)
+
+    if "layer" in parts:
+        # The GPT-2-medium-shaped full layer at N = 1 (hidden 1024, 16 heads of
+        # 64, FFN 4096, causal L = 1024, micro-batch 8), forward + backward,
+        # timed on its own after the main steps.
+        wg = S.WORKLOADS["gpt2m"]
+        prm_g = S.layer_params(wg)
+        xg, dg = S.layer_activations(wg)
+        shared_g = {k: cu(prm_g[k]) for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "b_o", "b_b")}
+        shard_g = {k: cu(v) for k, v in S.rank_shard(prm_g, 0, 1, wg.heads, wg.d).items() if k != "heads"}
+        del prm_g
+        rg = make_ranks([shard_g], shared_g, wg.B, wg.L, wg.heads, wg.d, p=wg.p, seed=wg.seed, offsets=(1, 2))
+        xgd, dgd = cu(xg), cu(dg)
+        for _ in range(max(1, args.warmup)):
+            run_ranks(rg, xgd, dgd)
+        torch.cuda.synchronize()
+        gev = [(EV(), EV()) for _ in range(args.steps)]
+        for b_, e_ in gev:
+            b_.record(stream)
+            run_ranks(rg, xgd, dgd)
+            e_.record(stream)
+        torch.cuda.synchronize()
+        g_ms = float(np.mean([b_.elapsed_time(e_) for b_, e_ in gev]))
+        out["gpt2m_layer_ms"] = round(g_ms, 4)
+        out["gpt2m_layer_TFLOPS"] = round(3 * layer_flops(wg.B, wg.L, wg.K, wg.heads, wg.d, wg.F) / (g_ms * 1e-3)
+                                          / 1e12, 2)
+        del rg, shard_g, shared_g, xgd, dgd
 
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
