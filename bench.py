@@ -34,7 +34,9 @@ JSON line.  ``logits_xent_fused_us`` / ``logits_xent_unfused_us`` time the
 vocab shard's logits GEMM + statistics with the statistics fused into the
 GEMM's epilogue (no logits stored) and as two passes; ``embedding_bwd_us``
 the vocab shard's embedding backward (token-order scatter-add, accumulating
-into its fp32 gradient); ``moe_weighted_act_ms`` the MoE shard in its
+into its fp32 gradient); ``moe_median_shard_ms`` / ``moe_median_weight_GBps`` the median
+expert-parallel shard of the same routing (weight-stream bound);
+``moe_weighted_act_ms`` the MoE shard in its
 memory-efficient permutation form (routing weight on the activation);
 ``moe_mxfp8_ms`` / ``moe_mxfp8_TFLOPS`` the shard with MXFP8 expert GEMMs
 (block-scaled E4M3 operands, fp32 accumulation; the same model FLOPs);
@@ -382,6 +384,25 @@ def main():
             e_.record(stream)
         torch.cuda.synchronize()
         out["moe_weighted_act_ms"] = round(float(np.mean([b_.elapsed_time(e_) for b_, e_ in mev])), 4)
+        # The median expert-parallel shard of the same routing (experts
+        # 128-135 of 256, a few hundred routed rows): the grouped GEMMs stream
+        # the 8 experts' weights (705 MB) and do little arithmetic, so this
+        # call is bound by HBM; timed on its own.
+        e_med = wm.experts // 2
+        R_med = int(((ids_np >= e_med) & (ids_np < e_med + wm.e_local)).sum())
+        for _ in range(max(1, args.warmup)):
+            mp.mp_grouped_expert_gemm(mx, mids, mw, mwgu, mwd, e_med, mout, mperm, moffs, mws)
+        torch.cuda.synchronize()
+        for b_, e_ in mev:
+            b_.record(stream)
+            mp.mp_grouped_expert_gemm(mx, mids, mw, mwgu, mwd, e_med, mout, mperm, moffs, mws)
+            e_.record(stream)
+        torch.cuda.synchronize()
+        med_ms = float(np.mean([b_.elapsed_time(e_) for b_, e_ in mev]))
+        wbytes = (mwgu.numel() + mwd.numel()) * 2.0
+        out["moe_median_shard_ms"] = round(med_ms, 4)
+        out["moe_median_shard_rows"] = R_med
+        out["moe_median_weight_GBps"] = round(wbytes / (med_ms * 1e-3) / 1e9, 1)
         # The same shard with MXFP8 expert GEMMs (weights quantised once in
         # untimed setup; token rows and activations quantised inside the call).
         sw_h, sw_f = mp.mxfp8_scale_width(wm.K), mp.mxfp8_scale_width(wm.Fe)
@@ -475,6 +496,11 @@ def main():
                       "achieved": out["moe_bwd_TFLOPS"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(out["moe_bwd_TFLOPS"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
                       "avg_launch_us": round(bw_ms * 1e3, 1), "algorithmic_per_launch": 2 * moe_fl})
+        roofs.append({"kernel": "MoE median shard (experts 128-135), bf16 grouped expert GEMMs, weight stream "
+                                "(whole call)", "bound": "hbm", "achieved": out["moe_median_weight_GBps"],
+                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(out["moe_median_weight_GBps"] /
+                                                                            PEAK_HBM_GBPS, 4),
+                      "traffic": None, "avg_launch_us": round(med_ms * 1e3, 1), "algorithmic_per_launch": wbytes})
         roofs.append({"kernel": "MoE hot shard, MXFP8 grouped expert GEMMs (whole call)", "bound": "mfma",
                       "achieved": out["moe_mxfp8_TFLOPS"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(out["moe_mxfp8_TFLOPS"] / PEAK_FP8_TFLOPS, 4), "traffic": None,
