@@ -1,0 +1,49 @@
+"""Calls on two streams at once, each with the binding's default scratch
+workspace: the cached workspace is kept per (device, stream), so two
+weight-gradient GEMMs whose split-K partials use it can run concurrently and
+give exactly what they give one after the other."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import say, sync
+from megatron_tensor_transformer_02_amd import mp
+
+pytestmark = pytest.mark.gpu
+
+
+def test_concurrent_streams_use_separate_workspaces():
+    say("two streams, default workspaces")
+    T, Fi, K = 8192, 384, 3072  # the out-projection's backward (split-K weight gradient)
+    g = torch.Generator().manual_seed(3)
+    mk = lambda *s, sc=1.0: (torch.randn(*s, generator=g) * sc).to("cuda", torch.bfloat16)  # noqa: E731
+    jobs = []
+    for _ in range(2):
+        jobs.append(dict(Y=mk(T, Fi), B=mk(K, Fi, sc=0.02), dO=mk(T, K),
+                         dY=torch.empty(T, Fi, dtype=torch.bfloat16, device="cuda"),
+                         dB=torch.empty(K, Fi, dtype=torch.float32, device="cuda")))
+    assert mp.lib().mp_row_linear_partial_bwd_workspace(mp.MP_BF16, T, Fi, K) > 0  # scratch is used
+
+    def run(j, stream=None):
+        mp.mp_row_linear_partial_bwd(j["Y"], j["B"], j["dO"], j["dY"], j["dB"], stream=stream)
+
+    want = []
+    for j in jobs:
+        run(j)
+        sync()
+        want.append((j["dY"].clone(), j["dB"].clone()))
+        j["dY"].fill_(0)
+        j["dB"].fill_(0)
+    sync()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        run(jobs[0], s1)
+        run(jobs[1], s2)
+        torch.cuda.current_stream().wait_stream(s1)
+        torch.cuda.current_stream().wait_stream(s2)
+        sync()
+        for j, (dy, db) in zip(jobs, want):
+            assert torch.equal(j["dY"], dy) and torch.equal(j["dB"], db)
