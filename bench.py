@@ -29,7 +29,8 @@ the same layer share (each 8-way reduce on the rank's 1024 tokens only, an
 all-gather before each column-parallel GEMM) is timed on its own and reported
 as ``sp_layer_ms`` / ``sp_layer_TFLOPS`` (``--no-sp`` skips it), and the
 GPT-2-medium-shaped full layer at N = 1 as ``gpt2m_layer_ms`` /
-``gpt2m_layer_TFLOPS``.  Prints one
+``gpt2m_layer_TFLOPS``.  ``hbm_copy_GBps`` is a 256 MiB device copy's
+rate (read + write), the measured context for the HBM-bound kernels.  Prints one
 JSON line.  ``logits_xent_fused_us`` / ``logits_xent_unfused_us`` time the
 vocab shard's logits GEMM + statistics with the statistics fused into the
 GEMM's epilogue (no logits stored) and as two passes; ``embedding_bwd_us``
@@ -576,6 +577,22 @@ def main():
         out["gpt2m_layer_TFLOPS"] = round(3 * layer_flops(wg.B, wg.L, wg.K, wg.heads, wg.d, wg.F) / (g_ms * 1e-3)
                                           / 1e12, 2)
         del rg, shard_g, shared_g, xgd, dgd
+
+    # Context for the HBM-bound kernels: a 256 MiB device-to-device copy
+    # (the runtime's copy kernel; bytes read + written) on this GPU.
+    csrc = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    cev = [(EV(), EV()) for _ in range(10)]
+    for b_, e_ in cev:
+        b_.record(stream)
+        cdst.copy_(csrc)
+        e_.record(stream)
+    torch.cuda.synchronize()
+    c_ms = float(np.median([b_.elapsed_time(e_) for b_, e_ in cev]))
+    out["hbm_copy_GBps"] = round(2.0 * csrc.numel() / (c_ms * 1e-3) / 1e9, 1)
+    del csrc, cdst
 
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
