@@ -323,7 +323,8 @@ size_t mp_grouped_expert_gemm_workspace(int64_t T, int64_t Hd, int64_t Fe, int t
  * grouped GEMM and sync-free kernels, 2.2 permutation; 1: small per-expert
  * GEMMs and dynamic shapes).  Local experts are e_start .. e_start+E_loc-1.
  *  1. permutation: list the local picks (t,k) with topk_ids[t,k] local,
- *     ordered by expert, then token, then slot; perm_picks[r] = t*topk + k;
+ *     ordered by expert, then token, then slot (a token that picks one
+ *     expert in two slots gets two rows); perm_picks[r] = t*topk + k;
  *     expert_offsets[e] = first row of local expert e (exclusive scan of the
  *     per-expert counts; expert_offsets[E_loc] = R).  Shapes stay on the
  *     device: nothing is copied back to the host.

@@ -168,3 +168,29 @@ def test_bwd_zero_tokens(form):
                                   torch.empty_like(w), weighted_act=wa)
     sync()
     assert torch.all(dwgu == 0) and torch.all(dwd == 0)
+
+
+@pytest.mark.parametrize("form", list(FORMS))
+def test_bwd_duplicate_picks(form):
+    """A token may pick one expert in two slots: both picks get their own
+    permuted row (slot order), and forward and backward still match the
+    oracle, which enumerates (token, slot) pairs."""
+    say("moe bwd duplicate picks", form)
+    wa, oracle_bwd = FORMS[form]
+    T, Hd, Fe, e_local, topk = 60, 64, 72, 4, 3
+    rng = np.random.default_rng(21)
+    ids = torch.from_numpy(rng.integers(0, 6, size=(T, topk)).astype(np.int32))  # duplicates are common
+    w = torch.from_numpy(rng.random((T, topk)).astype(np.float32))
+    x = torch.from_numpy(rng.standard_normal((T, Hd), dtype=np.float32)).to(torch.bfloat16)
+    wgu = torch.from_numpy(rng.standard_normal((e_local, 2 * Fe, Hd), dtype=np.float32) * 0.1).to(torch.bfloat16)
+    wd = torch.from_numpy(rng.standard_normal((e_local, Hd, Fe), dtype=np.float32) * 0.1).to(torch.bfloat16)
+    dout = torch.from_numpy(rng.standard_normal((T, Hd), dtype=np.float32)).to(torch.bfloat16)
+    assert any(len(set(r)) < topk for r in ids.numpy())
+    got = run(x, ids, w, wgu, wd, 0, dout, wa)
+    fwd = O.moe_forward_weighted_act if wa else O.moe_forward
+    want_out = fwd(f64(x), ids.numpy(), w.numpy(), f64(wgu), f64(wd), 0)[0]
+    assert rel_frobenius(f64(got["out"]), want_out) <= TOL["bf16"]
+    want = oracle_bwd(f64(x), ids.numpy(), w.numpy(), f64(wgu), f64(wd), 0, f64(dout))
+    for name in ("x", "w_gu", "w_d", "topk_w"):
+        err = rel_frobenius(f64(got[name]), want[name])
+        assert err <= TOL["bf16"], (name, err)
