@@ -27,7 +27,7 @@ def declared_symbols():
     return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mp_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_north_star_calls():
+def test_header_declares_the_hot_path_calls():
     names = declared_symbols()
     for want in ["mp_column_linear_gelu", "mp_row_linear_partial", "mp_shard_reduce", "mp_head_attention",
                  "mp_vocab_parallel_xent", "mp_shared_seed_dropout", "mp_grouped_expert_gemm"]:
