@@ -386,9 +386,9 @@ def main():
         torch.cuda.synchronize()
         out["moe_weighted_act_ms"] = round(float(np.mean([b_.elapsed_time(e_) for b_, e_ in mev])), 4)
         # The median expert-parallel shard of the same routing (experts
-        # 128-135 of 256, a few hundred routed rows): the grouped GEMMs stream
-        # the 8 experts' weights (705 MB) and do little arithmetic, so this
-        # call is bound by HBM; timed on its own.
+        # 128-135 of 256, a few hundred routed rows): little useful arithmetic
+        # per byte of the 8 experts' weights (705 MB), so its rate is reported
+        # against HBM; timed on its own.
         e_med = wm.experts // 2
         R_med = int(((ids_np >= e_med) & (ids_np < e_med + wm.e_local)).sum())
         for _ in range(max(1, args.warmup)):
