@@ -23,6 +23,9 @@
 namespace mp {
 
 constexpr int MOE_BM = 256, MOE_BN = 256;
+// bf16 forward: an expert with fewer rows than this is "sparse" and runs on
+// 64-row tiles (a 256-row tile would spend most of its MFMA work on padding).
+constexpr int MOE_BM_SPARSE = 64, MOE_SPARSE_ROWS = 192;
 
 struct MoeArgs {
   int64_t T, Hd, Fe;
@@ -36,7 +39,9 @@ struct MoeArgs {
   uint16_t* out;           // [T, Hd]
   int32_t* perm;           // [r_cap]
   int32_t* offsets;        // [E_loc + 1]
-  int32_t* tile_start;     // [E_loc + 1]
+  int32_t* tile_start;     // [E_loc + 1]: 256-row tiles of every expert
+  int32_t* tile_start_d;   // [E_loc + 1]: 256-row tiles of the dense experts only
+  int32_t* tile_start_s;   // [E_loc + 1]: 64-row tiles of the sparse experts only
   int32_t* counts;         // [E_loc]
   int32_t* cnt;            // [T, E_loc] per-token counts, then per-token ranks
   int32_t* pick_row;       // [T * topk]
@@ -109,15 +114,26 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(const MoeArgs a) {
 
 __global__ void moe_offsets_kernel(const MoeArgs a) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int off = 0, tiles = 0;
+  int off = 0, tiles = 0, dense = 0, sparse = 0;
   for (int e = 0; e < a.E_loc; ++e) {
+    const int c = a.counts[e];
     a.offsets[e] = off;
     a.tile_start[e] = tiles;
-    off += a.counts[e];
-    tiles += (a.counts[e] + MOE_BM - 1) / MOE_BM;
+    off += c;
+    tiles += (c + MOE_BM - 1) / MOE_BM;
+    if (a.tile_start_d != nullptr) {
+      a.tile_start_d[e] = dense;
+      a.tile_start_s[e] = sparse;
+      if (c < MOE_SPARSE_ROWS) sparse += (c + MOE_BM_SPARSE - 1) / MOE_BM_SPARSE;
+      else dense += (c + MOE_BM - 1) / MOE_BM;
+    }
   }
   a.offsets[a.E_loc] = off;
   a.tile_start[a.E_loc] = tiles;
+  if (a.tile_start_d != nullptr) {
+    a.tile_start_d[a.E_loc] = dense;
+    a.tile_start_s[a.E_loc] = sparse;
+  }
 }
 
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const MoeArgs a) {
@@ -252,24 +268,27 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __rest
 // MX: both operands are MXFP8 (E4M3 codes, k-tiles of 128 codes = the same
 // 128-byte LDS rows), two scaled 32x32x64 MFMA steps per k-tile, each row's
 // four block exponents of a k-tile read as one dword per fragment row.
-template <int MODE, bool MX, bool SAVE = false>
+template <int MODE, bool MX, bool SAVE = false, int BMT = MOE_BM>
 __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
-  constexpr int BM = MOE_BM, BN = MOE_BN, NT = 512, WC = 4, WM = BM / 2, WN = BN / WC;
+  constexpr int BM = BMT, BN = MOE_BN, NT = 512, WC = 4, WM = BM / 2, WN = BN / WC;
   constexpr int TM = WM / 32, TN = WN / 32, A_SLOTS = BM * 8, B_SLOTS = BN * 8;
   static_assert(TN == 2, "the SwiGLU epilogue pairs the gate and up 32-column tiles of a wave");
   __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / WC, wn = wave % WC;
 
-  // Device-side schedule: real tiles = tile_start[E_loc] * tiles_n.
-  const int n_real = a.tile_start[a.E_loc] * a.tiles_n;
+  // Device-side schedule: real tiles = ts[E_loc] * tiles_n.  MXFP8 runs every
+  // expert on 256-row tiles; bf16 splits them into dense experts (256-row
+  // tiles) and sparse ones (64-row tiles, a launch of their own).
+  const int32_t* ts = MX ? a.tile_start : (BM == MOE_BM ? a.tile_start_d : a.tile_start_s);
+  const int n_real = ts[a.E_loc] * a.tiles_n;
   const int wg = blockIdx.x;
   if (wg >= n_real) return;
   const int per = n_real >> 3, rem = n_real & 7, xcd = wg & 7, idx = wg >> 3;
   const int lid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
   const int mtg = lid / a.tiles_n, nt = lid - mtg * a.tiles_n;
   int e = 0;
-  while (e + 1 < a.E_loc && a.tile_start[e + 1] <= mtg) ++e;
-  const int64_t row0 = a.offsets[e] + static_cast<int64_t>(mtg - a.tile_start[e]) * BM;
+  while (e + 1 < a.E_loc && ts[e + 1] <= mtg) ++e;
+  const int64_t row0 = a.offsets[e] + static_cast<int64_t>(mtg - ts[e]) * BM;
   const int64_t row_end = a.offsets[e + 1];
   const int64_t K = MODE == 0 ? a.Hd : a.Fe;
   // The loaders count 2-byte units: bf16 values, or pairs of E4M3 codes.
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   wait_vmcnt<NI>();
   __syncthreads();
 
-  constexpr int NR = TM + TN, NM = TM * TN, H = TM / 2;
+  constexpr int NR = TM + TN, NM = TM * TN, H = TM / 2;  // H = 0 for 64-row tiles: all after the barrier
   uint4 fa[2][TM], fb[2][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) fa[0][i] = lds_frag<true>(lds[0], ar0 + 32 * i, 0, lane);
@@ -640,7 +659,8 @@ __global__ __launch_bounds__(256) void moe_bwd_dw_zero_kernel(const MoeArgs a) {
 }
 
 struct MoeLayout {
-  size_t cnt, pick_row, perm, offsets, tile_start, counts, act, yperm, xq, xs, aq, as, total;
+  size_t cnt, pick_row, perm, offsets, tile_start, tile_start_d, tile_start_s, counts, act, yperm, xq, xs, aq, as,
+      total;
 };
 
 static int64_t mx_scale_width(int64_t K) { return 4 * ceil_div(K, 128); }
@@ -660,6 +680,8 @@ static MoeLayout moe_layout(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_l
   L.perm = take(static_cast<size_t>(r_cap) * 4);
   L.offsets = take(static_cast<size_t>(E_loc + 1) * 4);
   L.tile_start = take(static_cast<size_t>(E_loc + 1) * 4);
+  L.tile_start_d = take(static_cast<size_t>(E_loc + 1) * 4);
+  L.tile_start_s = take(static_cast<size_t>(E_loc + 1) * 4);
   L.counts = take(static_cast<size_t>(E_loc) * 4);
   L.act = take(static_cast<size_t>(r_cap * Fe) * 2);
   L.yperm = take(static_cast<size_t>(r_cap * Hd) * 2);
@@ -725,6 +747,8 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   a.perm = perm_picks != nullptr ? perm_picks : reinterpret_cast<int32_t*>(w + L.perm);
   a.offsets = expert_offsets != nullptr ? expert_offsets : reinterpret_cast<int32_t*>(w + L.offsets);
   a.tile_start = reinterpret_cast<int32_t*>(w + L.tile_start);
+  a.tile_start_d = reinterpret_cast<int32_t*>(w + L.tile_start_d);
+  a.tile_start_s = reinterpret_cast<int32_t*>(w + L.tile_start_s);
   a.counts = reinterpret_cast<int32_t*>(w + L.counts);
   a.act = reinterpret_cast<uint16_t*>(w + L.act);
   a.yperm = reinterpret_cast<uint16_t*>(w + L.yperm);
@@ -735,14 +759,22 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   moe_scan_kernel<<<static_cast<unsigned>(E_loc), 1024, 0, s>>>(a);
   moe_offsets_kernel<<<1, 64, 0, s>>>(a);
   moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
-  const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc;
+  // Dense experts' 256-row tiles and sparse experts' 64-row tiles (each
+  // sparse expert has at most 3); the two launches cover disjoint rows.
+  const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc, max_stiles = 3LL * E_loc;
+  constexpr int SB = MOE_BM_SPARSE;
   a.tiles_n = static_cast<int>(ceil_div(Fe, MOE_BN / 2));
-  if (gu_save != nullptr)
-    moe_gemm_kernel<0, false, true><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
-  else
-    moe_gemm_kernel<0, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
+  const unsigned gd0 = static_cast<unsigned>(max_mtiles * a.tiles_n), gs0 = static_cast<unsigned>(max_stiles * a.tiles_n);
+  if (gu_save != nullptr) {
+    moe_gemm_kernel<0, false, true><<<gd0, 512, 0, s>>>(a);
+    moe_gemm_kernel<0, false, true, SB><<<gs0, 512, 0, s>>>(a);
+  } else {
+    moe_gemm_kernel<0, false><<<gd0, 512, 0, s>>>(a);
+    moe_gemm_kernel<0, false, false, SB><<<gs0, 512, 0, s>>>(a);
+  }
   a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
   moe_gemm_kernel<1, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
+  moe_gemm_kernel<1, false, false, SB><<<static_cast<unsigned>(max_stiles * a.tiles_n), 512, 0, s>>>(a);
   moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a);
   return check_launch(fn);
 }
