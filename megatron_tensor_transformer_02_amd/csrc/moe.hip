@@ -569,13 +569,37 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
 }
 
 // out[t, 8c..8c+7] = sum_k w[t,k] * yperm[row(t,k), 8c..8c+7] (k ascending;
-// w = 1 when the weights were applied to the activation).
+// w = 1 when the weights were applied to the activation).  With KMAX > 0
+// (topk <= KMAX) every pick's row index and row chunk is loaded before the
+// sum, so the loads of one token overlap; the sum keeps the k order.
+template <int KMAX>
 __global__ __launch_bounds__(256) void moe_unpermute_kernel(const MoeArgs a) {
   const int64_t vpr = a.Hd / 8;
   const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (v >= a.T * vpr) return;
   const int64_t t = v / vpr, c = (v - t * vpr) * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (KMAX > 0) {
+    int32_t rows[KMAX];
+    uint4 yv[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) rows[k] = k < a.topk ? a.pick_row[t * a.topk + k] : -1;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      yv[k] = rows[k] >= 0 ? *reinterpret_cast<const uint4*>(a.yperm + static_cast<int64_t>(rows[k]) * a.Hd + c)
+                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (rows[k] < 0) continue;
+      const float wk = a.w_on_act ? 1.0f : a.w[t * a.topk + k];
+      float y[8];
+      unpack8(yv[k], y);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += wk * y[q];
+    }
+    *reinterpret_cast<uint4*>(a.out + t * a.Hd + c) = pack8(acc);
+    return;
+  }
   for (int k = 0; k < a.topk; ++k) {
     const int32_t row = a.pick_row[t * a.topk + k];
     if (row < 0) continue;
@@ -656,6 +680,12 @@ __global__ __launch_bounds__(256) void moe_bwd_dw_rows_kernel(const MoeArgs a) {
 __global__ __launch_bounds__(256) void moe_bwd_dw_zero_kernel(const MoeArgs a) {
   const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (p < a.T * a.topk && a.pick_row[p] < 0) a.dw[p] = 0.0f;
+}
+
+static void launch_unpermute(const MoeArgs& a, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(ceil_div(a.T * (a.Hd / 8), 256));
+  if (a.topk <= 8) moe_unpermute_kernel<8><<<grid, 256, 0, s>>>(a);
+  else moe_unpermute_kernel<0><<<grid, 256, 0, s>>>(a);
 }
 
 struct MoeLayout {
@@ -775,7 +805,7 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
   moe_gemm_kernel<1, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   moe_gemm_kernel<1, false, false, SB><<<static_cast<unsigned>(max_stiles * a.tiles_n), 512, 0, s>>>(a);
-  moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a);
+  launch_unpermute(a, s);
   return check_launch(fn);
 }
 
@@ -944,7 +974,7 @@ static int grouped_expert_gemm_bwd(const char* fn, bool w_on_act, int64_t T, int
   u.yperm = a.dy;
   u.w_on_act = 1;
   u.out = static_cast<uint16_t*>(dX);
-  moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(u);
+  launch_unpermute(u, s);
   // dW_gu[e] = [d gate, d up]_e^T x_perm,e.
   if (int rc = gemm_grouped_k(E_loc, a.offsets, a.r_cap, 2 * Fe, Hd, dgu, 2 * Fe, a.xp, Hd, dW_gu, Hd, 2 * Fe * Hd, s))
     return rc;
@@ -1076,6 +1106,6 @@ extern "C" int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, i
       a.act, Fe, a.r_cap, a.offsets + E_loc, Fe, aq, as, a.swf);
   a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
   moe_gemm_kernel<1, true><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
-  moe_unpermute_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a);
+  launch_unpermute(a, s);
   return check_launch(fn);
 }
