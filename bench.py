@@ -176,7 +176,7 @@ def main():
     # ------------------------------------------------------------- vocab setup
     wv = S.WORKLOADS["vocab"]
     Tv, V, Kv, nv = wv.T, wv.V, wv.K, wv.N
-    Vi = V // nv
+    Vi = S.vocab_shard_rows(V, nv)
     if "vocab" in parts:
         t0 = time.time()
         vin = S.vocab_inputs(wv)

@@ -195,11 +195,14 @@ int mp_dropout_mask_bwd(mp_dtype dtype, int64_t rows, int64_t cols, const void* 
                         const uint8_t* keep_bits, float p, void* dx, float* dbias, void* ws,
                         size_t ws_bytes, hipStream_t s);
 
-/* All-gather stand-in for the sequence-parallel layer (MLM-notes, "Model
- * Parallel Transformers": the per-block all-reduce splits into a
- * reduce-scatter, after which LayerNorm, dropout and the residual work on the
- * rank's token slice, and an all-gather that restores the full sequence
- * before the next column-parallel GEMM).  out [N*rows, cols] receives slice j
+/* All-gather stand-in for the sequence-parallel layer (PAR-survey,
+ * "Achievement" item 4 and the sequence-parallelism bullet of "How": with
+ * TP+SP the operations outside the tensor-parallel GEMMs -- LayerNorm,
+ * dropout, the residual -- are spread over the ranks along the sequence).
+ * Reading (the page names no collective): each per-block all-reduce splits
+ * into a reduce-scatter, after which those operations work on the rank's
+ * token slice, and an all-gather that restores the full sequence before the
+ * next column-parallel GEMM.  out [N*rows, cols] receives slice j
  * (a host array of N device pointers, each [rows, cols] dtype) in rows
  * [j*rows, (j+1)*rows); slices[j] may be those very rows of out.  The
  * reduce-scatter side needs no call of its own: it is mp_shard_reduce,

@@ -26,6 +26,13 @@ constexpr int MOE_BM = 256, MOE_BN = 256;
 // bf16 forward: an expert with fewer rows than this is "sparse" and runs on
 // 64-row tiles (a 256-row tile would spend most of its MFMA work on padding).
 constexpr int MOE_BM_SPARSE = 64, MOE_SPARSE_ROWS = 192;
+// Most 64-row tiles a sparse expert (at most MOE_SPARSE_ROWS - 1 rows) needs:
+// the bound the sparse launches' grids are sized by, derived from the same
+// constants the offsets kernel counts tiles with.
+constexpr int MOE_MAX_STILES = (MOE_SPARSE_ROWS - 1 + MOE_BM_SPARSE - 1) / MOE_BM_SPARSE;
+static_assert(MOE_MAX_STILES * MOE_BM_SPARSE >= MOE_SPARSE_ROWS - 1 &&
+                  (MOE_MAX_STILES - 1) * MOE_BM_SPARSE < MOE_SPARSE_ROWS - 1,
+              "MOE_MAX_STILES is ceil((MOE_SPARSE_ROWS - 1) / MOE_BM_SPARSE)");
 
 struct MoeArgs {
   int64_t T, Hd, Fe;
@@ -790,8 +797,10 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   moe_offsets_kernel<<<1, 64, 0, s>>>(a);
   moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
   // Dense experts' 256-row tiles and sparse experts' 64-row tiles (each
-  // sparse expert has at most 3); the two launches cover disjoint rows.
-  const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc, max_stiles = 3LL * E_loc;
+  // sparse expert has at most MOE_MAX_STILES); the two launches cover
+  // disjoint rows.
+  const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc,
+                max_stiles = static_cast<int64_t>(MOE_MAX_STILES) * E_loc;
   constexpr int SB = MOE_BM_SPARSE;
   a.tiles_n = static_cast<int>(ceil_div(Fe, MOE_BN / 2));
   const unsigned gd0 = static_cast<unsigned>(max_mtiles * a.tiles_n), gs0 = static_cast<unsigned>(max_stiles * a.tiles_n);

@@ -153,9 +153,10 @@ class RankLayer:
 
 class SPRankLayer(RankLayer):
     """Rank ``r`` of ``n`` in the sequence-parallel form of the same layer
-    (MLM-notes, "Model Parallel Transformers": each all-reduce becomes a
-    reduce-scatter followed, before the next column-parallel GEMM, by an
-    all-gather).  The rank owns tokens ``[r*T/n, (r+1)*T/n)`` for LayerNorm,
+    (PAR-survey, "Achievement" item 4 and "How": TP+SP spreads LayerNorm,
+    dropout and the residual over the ranks along the sequence; read here as
+    each all-reduce becoming a reduce-scatter followed, before the next
+    column-parallel GEMM, by an all-gather).  The rank owns tokens ``[r*T/n, (r+1)*T/n)`` for LayerNorm,
     dropout and the residual; its attention and MLP work on the gathered
     full sequence exactly as in :class:`RankLayer`.  The reduce-scatter is a
     shard reduce over the rank's rows of every partial, with the dropout

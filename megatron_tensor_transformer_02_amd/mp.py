@@ -9,6 +9,7 @@ byte buffers obtained through torch's allocator.
 All calls are asynchronous on ``stream`` (default: torch's current stream).
 """
 
+import collections
 import ctypes
 import os
 
@@ -143,23 +144,49 @@ def _dt(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-_ws_cache = {}
+# Cached scratch buffers, one per (device, stream handle), least recently
+# used first; at most _WS_ENTRIES are kept.
+_WS_ENTRIES = 8
+_ws_cache = collections.OrderedDict()
+
+
+def _stream_of(stream, dev):
+    return stream if stream is not None else torch.cuda.current_stream(dev)
 
 
 def workspace(nbytes, device=None, stream=None):
     """A cached device byte buffer of at least ``nbytes``, one per (device,
     stream): calls enqueued on one stream run in order and may share it; calls
     on different streams get different buffers.  Its contents do not survive
-    the next call that uses it."""
+    the next call that uses it.
+
+    The buffer is allocated while ``stream`` is torch's current stream, so
+    the caching allocator files it under that stream: when a larger request
+    replaces it (or it is evicted), its memory is reused only by later work
+    on the same stream, never while kernels enqueued there may still use it.
+    A stream handle destroyed with work pending and issued again to a new
+    stream would share the old entry, as with any tensor torch allocated on
+    it."""
     if nbytes == 0:
         return None
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    key = (dev, (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream)
-    buf = _ws_cache.get(key)
+    strm = _stream_of(stream, dev)
+    key = (dev, strm.cuda_stream)
+    buf = _ws_cache.pop(key, None)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(int(nbytes), dtype=torch.uint8, device=dev)
-        _ws_cache[key] = buf
+        buf = None
+        with torch.cuda.stream(strm):
+            buf = torch.empty(int(nbytes), dtype=torch.uint8, device=dev)
+    _ws_cache[key] = buf
+    while len(_ws_cache) > _WS_ENTRIES:
+        _ws_cache.popitem(last=False)
     return buf
+
+
+def _nbytes(t):
+    """Byte size of a caller's (or cached) buffer, passed to the library so
+    its workspace check sees the real size."""
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _act(act):
@@ -201,7 +228,7 @@ def mp_column_linear_gelu_bwd(X, A_i, Z_save, dY_i, act, dX_partial, dA_i, da_i=
     need = lib().mp_column_linear_gelu_bwd_workspace(dt, T, K, Fi)
     ws = ws if ws is not None else workspace(need, X.device, stream)
     _call("mp_column_linear_gelu_bwd", dt, T, K, Fi, _p(X), _p(A_i), _p(Z_save), _p(dY_i), _act(act),
-          _p(dX_partial), _p(dA_i), _p(da_i), _p(ws), need if ws is not None else 0, _s(stream))
+          _p(dX_partial), _p(dA_i), _p(da_i), _p(ws), _nbytes(ws), _s(stream))
 
 
 def mp_row_linear_partial(Y_i, B_i, P_i, stream=None):
@@ -217,7 +244,7 @@ def mp_row_linear_partial_bwd(Y_i, B_i, dOut, dY_i, dB_i, ws=None, stream=None):
     need = lib().mp_row_linear_partial_bwd_workspace(dt, T, Fi, K)
     ws = ws if ws is not None else workspace(need, Y_i.device, stream)
     _call("mp_row_linear_partial_bwd", dt, T, Fi, K, _p(Y_i), _p(B_i), _p(dOut), _p(dY_i), _p(dB_i), _p(ws),
-          need if ws is not None else 0, _s(stream))
+          _nbytes(ws), _s(stream))
 
 
 def mp_row_linear_partial_bwd_dact(Y_i, B_i, dOut, Z_save, act, dZ_i, dB_i, ws=None, stream=None):
@@ -227,7 +254,7 @@ def mp_row_linear_partial_bwd_dact(Y_i, B_i, dOut, Z_save, act, dZ_i, dB_i, ws=N
     need = lib().mp_row_linear_partial_bwd_workspace(dt, T, Fi, K)
     ws = ws if ws is not None else workspace(need, Y_i.device, stream)
     _call("mp_row_linear_partial_bwd_dact", dt, T, Fi, K, _p(Y_i), _p(B_i), _p(dOut), _p(Z_save), _act(act),
-          _p(dZ_i), _p(dB_i), _p(ws), need if ws is not None else 0, _s(stream))
+          _p(dZ_i), _p(dB_i), _p(ws), _nbytes(ws), _s(stream))
 
 
 # ------------------------------------------------------- reduce and dropout
@@ -257,7 +284,7 @@ def mp_shard_reduce_layernorm_bwd(partials, x, gamma, mean, rstd, dx, dres=None,
         else 0
     ws = ws if ws is not None else workspace(need, x.device, stream)
     _call("mp_shard_reduce_layernorm_bwd", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
-          _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), _p(ws), need if ws is not None else 0, _s(stream))
+          _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), _p(ws), _nbytes(ws), _s(stream))
 
 
 def mp_shard_reduce_layernorm_bwd_dropout(partials, x, gamma, mean, rstd, dx, p, keep_bits, ddrop, dres=None,
@@ -269,7 +296,7 @@ def mp_shard_reduce_layernorm_bwd_dropout(partials, x, gamma, mean, rstd, dx, p,
     ws = ws if ws is not None else workspace(need, x.device, stream)
     _call("mp_shard_reduce_layernorm_bwd_dropout", _dt(x), len(partials), rows, cols, arr, _p(x), _p(gamma), _p(mean),
           _p(rstd), _p(dres), _p(dx), _p(dgamma), _p(dbeta), p, _p(keep_bits), _p(ddrop), _p(dbias), _p(ws),
-          need if ws is not None else 0, _s(stream))
+          _nbytes(ws), _s(stream))
 
 
 def mp_vocab_parallel_embedding_bwd(ids, dOut, v_start, dE_i, accumulate=False, stream=None):
@@ -289,7 +316,7 @@ def mp_dropout_mask_bwd(dy, keep_bits, p, dx, dbias=None, ws=None, stream=None):
     need = lib().mp_dropout_mask_bwd_workspace(rows, cols) if dbias is not None else 0
     ws = ws if ws is not None else workspace(need, dy.device, stream)
     _call("mp_dropout_mask_bwd", _dt(dy), rows, cols, _p(dy), _p(keep_bits), p, _p(dx), _p(dbias), _p(ws),
-          need if ws is not None else 0, _s(stream))
+          _nbytes(ws), _s(stream))
 
 
 def mp_shared_seed_dropout(x, y, p, seed, offset, index_base=0, mask_out=None, stream=None):
@@ -301,7 +328,7 @@ def mp_bias_grad(dy, db, ws=None, stream=None):
     rows, cols = dy.shape
     need = lib().mp_bias_grad_workspace(rows, cols)
     ws = ws if ws is not None else workspace(need, dy.device, stream)
-    _call("mp_bias_grad", _dt(dy), rows, cols, _p(dy), _p(db), _p(ws), need if ws is not None else 0, _s(stream))
+    _call("mp_bias_grad", _dt(dy), rows, cols, _p(dy), _p(db), _p(ws), _nbytes(ws), _s(stream))
 
 
 # ---------------------------------------------------------------- attention
@@ -319,7 +346,7 @@ def mp_head_attention_bwd(X, Wqkv_i, qkv, ctx_i, lse, dctx_i, B, L, h, d, dX_par
     need = lib().mp_head_attention_bwd_workspace(dt, B, L, K, h, d)
     ws = ws if ws is not None else workspace(need, X.device, stream)
     _call("mp_head_attention_bwd", dt, B, L, K, h, d, int(causal), _p(X), _p(Wqkv_i), _p(qkv), _p(ctx_i), _p(lse),
-          _p(dctx_i), _p(dX_partial), _p(dWqkv_i), _p(dbqkv_i), _p(ws), need if ws is not None else 0, _s(stream))
+          _p(dctx_i), _p(dX_partial), _p(dWqkv_i), _p(dbqkv_i), _p(ws), _nbytes(ws), _s(stream))
 
 
 # ------------------------------------------------------------- vocab path
@@ -341,7 +368,7 @@ def mp_vocab_parallel_logits_xent(H, E_i, labels, v_start, triples, ws=None, str
     need = lib().mp_vocab_parallel_logits_xent_workspace(T, K, Vi)
     ws = ws if ws is not None else workspace(need, H.device, stream)
     _call("mp_vocab_parallel_logits_xent", _dt(H), T, K, Vi, v_start, _p(H), _p(E_i), _p(labels), _p(triples), _p(ws),
-          need if ws is not None else 0, _s(stream))
+          _nbytes(ws), _s(stream))
 
 
 def mp_vocab_xent_combine(triples, loss, stats=None, mean_loss=None, stream=None):
@@ -367,7 +394,7 @@ def _grouped_expert_gemm(name, X, topk_ids, topk_w, W_gu, W_d, e_start, out, per
     need = lib().mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E_loc)
     ws = ws if ws is not None else workspace(need, X.device, stream)
     _call(name, T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w), _p(W_gu),
-          _p(W_d), _p(out), _p(perm_picks), _p(expert_offsets), _p(ws), need if ws is not None else 0, _s(stream))
+          _p(W_d), _p(out), _p(perm_picks), _p(expert_offsets), _p(ws), _nbytes(ws), _s(stream))
 
 
 def mp_grouped_expert_gemm(X, topk_ids, topk_w, W_gu, W_d, e_start, out, perm_picks=None, expert_offsets=None,
@@ -395,9 +422,10 @@ def mp_grouped_expert_gemm_fwd_train(X, topk_ids, topk_w, W_gu, W_d, e_start, ou
     Fe = two_fe // 2
     need = lib().mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E_loc)
     if ws is None:
-        ws = torch.empty(max(int(need), 1), dtype=torch.uint8, device=X.device)
+        with torch.cuda.stream(_stream_of(stream, X.device)):
+            ws = torch.empty(max(int(need), 1), dtype=torch.uint8, device=X.device)
     _call(name, T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w),
-          _p(W_gu), _p(W_d), _p(out), _p(gu_save), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+          _p(W_gu), _p(W_d), _p(out), _p(gu_save), _p(ws), _nbytes(ws),
           _s(stream))
     return ws
 
@@ -412,8 +440,8 @@ def mp_grouped_expert_gemm_bwd(X, topk_w, W_gu, W_d, dOut, gu_save, fwd_ws, dX, 
     need = lib().mp_grouped_expert_gemm_bwd_workspace(T, Hd, Fe, topk, E_loc)
     ws = ws if ws is not None else workspace(need, X.device, stream)
     _call(name, T, Hd, Fe, topk, E_loc, _p(X), _p(topk_w), _p(W_gu), _p(W_d), _p(dOut),
-          _p(gu_save), _p(fwd_ws), fwd_ws.numel() * fwd_ws.element_size() if fwd_ws is not None else 0, _p(dX),
-          _p(dW_gu), _p(dW_d), _p(dtopk_w), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+          _p(gu_save), _p(fwd_ws), _nbytes(fwd_ws), _p(dX),
+          _p(dW_gu), _p(dW_d), _p(dtopk_w), _p(ws), _nbytes(ws),
           _s(stream))
 
 
@@ -438,7 +466,7 @@ def mp_grouped_expert_gemm_mxfp8(X, topk_ids, topk_w, W_gu_q, W_gu_s, W_d_q, W_d
     ws = ws if ws is not None else workspace(need, X.device, stream)
     _call("mp_grouped_expert_gemm_mxfp8", T, Hd, Fe, topk, E_loc, e_start, _p(X), _p(topk_ids), _p(topk_w),
           _p(W_gu_q), _p(W_gu_s), _p(W_d_q), _p(W_d_s), _p(out), _p(perm_picks), _p(expert_offsets), _p(ws),
-          need if ws is not None else 0, _s(stream))
+          _nbytes(ws), _s(stream))
 
 
 # ---------------------------------------------------------------- LayerNorm
@@ -453,4 +481,4 @@ def mp_layernorm_bwd(x, gamma, mean, rstd, dy, dx, dres=None, dgamma=None, dbeta
     need = lib().mp_layernorm_bwd_workspace(T, K) if (dgamma is not None or dbeta is not None) else 0
     ws = ws if ws is not None else workspace(need, x.device, stream)
     _call("mp_layernorm_bwd", _dt(x), T, K, _p(x), _p(gamma), _p(mean), _p(rstd), _p(dy), _p(dres), _p(dx),
-          _p(dgamma), _p(dbeta), _p(ws), need if ws is not None else 0, _s(stream))
+          _p(dgamma), _p(dbeta), _p(ws), _nbytes(ws), _s(stream))

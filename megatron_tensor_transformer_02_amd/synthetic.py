@@ -137,14 +137,24 @@ def rank_shard(prm, rank, n, heads, d):
     """Rank ``rank`` of ``n``: its heads' rows of the fused QKV weight (Q, K, V
     blocks kept in that order), the matching columns of ``w_o``, rows of
     ``w_a``/``b_a`` and columns of ``w_b``, each as a contiguous tensor.  The
-    replicated biases ``b_o``/``b_b`` and LayerNorm parameters are shared."""
+    replicated biases ``b_o``/``b_b`` and LayerNorm parameters are shared.
+    ``n`` must divide the head count and the FFN width (MLM-notes, "Model
+    Parallel Transformers": the GPU count has to divide the attention heads);
+    a remainder raises ValueError."""
+    F = prm["w_a"].shape[0]
+    if n < 1 or not 0 <= rank < n:
+        raise ValueError(f"rank {rank} of {n} ranks")
+    if heads % n:
+        raise ValueError(f"{n} ranks do not divide {heads} attention heads")
+    if F % n:
+        raise ValueError(f"{n} ranks do not divide the FFN width {F}")
     hi = heads // n
     hd = heads * d
     rows = []
     for blk in range(3):
         rows.append(torch.arange(blk * hd + rank * hi * d, blk * hd + (rank + 1) * hi * d))
     rows = torch.cat(rows)
-    fi = prm["w_a"].shape[0] // n
+    fi = F // n
     fs = slice(rank * fi, (rank + 1) * fi)
     cs = slice(rank * hi * d, (rank + 1) * hi * d)
     return {
@@ -159,6 +169,13 @@ def rank_shard(prm, rank, n, heads, d):
 # --------------------------------------------------------------------------
 # Vocab tensors
 # --------------------------------------------------------------------------
+
+def vocab_shard_rows(V, n):
+    """Rows of each of ``n`` vocabulary shards; ``n`` must divide ``V``."""
+    if n < 1 or V % n:
+        raise ValueError(f"{n} ranks do not divide the vocabulary of {V}")
+    return V // n
+
 
 def vocab_inputs(wl, T=None, V=None, K=None, std=0.02):
     """Embedding ``[V, K]`` (~N(0, std)), hidden states ``[T, K]`` (~N(0,1)),

@@ -47,4 +47,6 @@ from .moe import (
     moe_permutation, expert_swiglu_ffn, moe_forward, moe_forward_rows, moe_forward_weighted_act, moe_backward,
     moe_backward_weighted_act,
 )
-from .mxfp8 import e4m3_value, e4m3_round, shared_exponent, scale_width, mx_quantize, mx_dequantize, moe_forward_mxfp8
+from .mxfp8 import (
+    e4m3_value, e4m3_round, shared_exponent, scale_width, mx_quantize, mx_dequantize, bf16_round, moe_forward_mxfp8,
+)

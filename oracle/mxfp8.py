@@ -99,12 +99,19 @@ def _silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def _bf16(v):
-    """Round fp64 values to bfloat16 (nearest, ties to even), back to fp64."""
-    f = np.asarray(v, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+def bf16_round(v):
+    """Round values to bfloat16 (8 significant bits, exponent range of fp32),
+    to the nearest representable value with ties to the even significand,
+    returned as fp64.  The exact input is rounded once (no fp32 step): write
+    |v| = m 2^e with m in [0.5, 1); the spacing of bf16 values there is
+    2^(e-8), or 2^-133 below the smallest normal 2^-126; v / spacing is exact
+    in fp64 and np.rint rounds it half to even.  A magnitude that rounds past
+    the largest finite bf16, 2^128 (1 - 2^-8), becomes infinite."""
+    v = _f64(v)
+    _, e = np.frexp(v)
+    spacing = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    r = np.rint(v / spacing) * spacing
+    return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)
 
 
 def moe_forward_mxfp8(x, topk_ids, topk_w, w_gu_q, w_gu_s, w_d_q, w_d_s, e_start, act_round=True,
@@ -113,10 +120,10 @@ def moe_forward_mxfp8(x, topk_ids, topk_w, w_gu_q, w_gu_s, w_d_q, w_d_s, e_start
     along the hidden dimension, the weights arrive quantised (``w_gu_q/_s``
     per expert [2Fe, Hd], ``w_d_q/_s`` per expert [Hd, Fe]); each expert
     computes ``act = silu(g) * u`` from the dequantised operands (exact
-    products, fp64 sums), rounds it to bf16 (the stored activation;
-    ``act_round``), quantises it along Fe (``act_quant``), and projects it
-    down; the unpermute sums ``w[t,k] * y`` per token (k ascending).  Returns
-    ``out [T, Hd]``."""
+    products, fp64 sums), rounds that value once to the nearest bf16 (the
+    stored activation; ``act_round``), quantises it along Fe
+    (``act_quant``), and projects it down; the unpermute sums ``w[t,k] * y``
+    per token (k ascending).  Returns ``out [T, Hd]``."""
     ids = np.asarray(topk_ids, dtype=np.int64)
     tokens, topk = ids.shape
     w = _f64(topk_w)
@@ -134,7 +141,7 @@ def moe_forward_mxfp8(x, topk_ids, topk_w, w_gu_q, w_gu_s, w_d_q, w_d_s, e_start
         xe = xd[rows]
         act = _silu(xe @ wgu[:fe].T) * (xe @ wgu[fe:].T)
         if act_round:
-            act = _bf16(act)
+            act = bf16_round(act)
         if act_quant:
             act = mx_dequantize(*mx_quantize(act))
         y = act @ mx_dequantize(w_d_q[e], w_d_s[e]).T

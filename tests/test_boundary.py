@@ -297,3 +297,92 @@ def test_moe_empty_token_buffers_may_be_null(lib):
     rc, msg = call(lib, "mp_grouped_expert_gemm_bwd", 0, Hd, Fe, topk, E, None, None, None, None, None, None, None,
                    ctypes.c_size_t(0), None, None, ALIGNED, None, None, ctypes.c_size_t(0), None)
     assert rc == -1 and "dW" in msg
+
+
+def test_head_attention_validation(lib):
+    """mp_head_attention / _bwd reject, before any launch: a head dim outside
+    {64, 128} (MP_ERR_UNSUPPORTED), fp32 (MP_ERR_DTYPE), K not a multiple
+    of 8 or a non-positive size (MP_ERR_SHAPE), NULL and misaligned
+    pointers, and a missing or short backward workspace."""
+    A = ALIGNED
+    fwd = lambda *a: call(lib, "mp_head_attention", *a)  # noqa: E731
+    ok = (mp.MP_BF16, 2, 64, 128, 2, 64, 1, A, A, None, A, A, A, None)
+    assert fwd(mp.MP_BF16, 2, 64, 128, 2, 96, 1, A, A, None, A, A, A, None)[0] == -4
+    assert fwd(mp.MP_BF16, 2, 64, 128, 2, 32, 1, A, A, None, A, A, A, None)[0] == -4
+    assert fwd(mp.MP_F32, *ok[1:])[0] == -3
+    assert fwd(mp.MP_BF16, 2, 64, 132, 2, 64, 1, A, A, None, A, A, A, None)[0] == -2
+    assert fwd(mp.MP_BF16, 0, 64, 128, 2, 64, 1, A, A, None, A, A, A, None)[0] == -2
+    assert fwd(mp.MP_BF16, 2, 64, 128, 0, 64, 1, A, A, None, A, A, A, None)[0] == -2
+    assert fwd(mp.MP_BF16, 2, 64, 128, 2, 64, 1, None, A, None, A, A, A, None)[0] == -1
+    assert fwd(mp.MP_BF16, 2, 64, 128, 2, 64, 1, A, A, None, A, None, A, None)[0] == -1
+    assert fwd(mp.MP_BF16, 2, 64, 128, 2, 64, 1, A + 8, A, None, A, A, A, None)[0] == -5
+    assert fwd(mp.MP_BF16, 2, 64, 128, 2, 64, 1, A, A, A + 4, A, A, A, None)[0] == -5
+    assert fwd(mp.MP_BF16, 2, 64, 128, 2, 64, 1, A, A, None, A + 2, A, A, None)[0] == -5
+    need = lib.mp_head_attention_bwd_workspace(mp.MP_BF16, 2, 64, 128, 2, 64)
+    assert need > 0 and lib.mp_head_attention_bwd_workspace(mp.MP_BF16, 2, 64, 128, 2, 96) == 0
+    bwd = lambda *a: call(lib, "mp_head_attention_bwd", *a)  # noqa: E731
+    args = [mp.MP_BF16, 2, 64, 128, 2, 64, 1, A, A, A, A, A, A, A, A, None, A, need, None]
+    a = list(args); a[5] = 128 + 64
+    assert bwd(*a)[0] == -4
+    a = list(args); a[16] = None
+    assert bwd(*a)[0] == -6
+    a = list(args); a[17] = need - 1
+    rc, msg = bwd(*a)
+    assert rc == -6 and str(need) in msg
+    a = list(args); a[16] = A + 8
+    assert bwd(*a)[0] == -5
+    a = list(args); a[13] = A + 4  # dWqkv_i
+    assert bwd(*a)[0] == -5
+    a = list(args); a[12] = None  # dX_partial
+    assert bwd(*a)[0] == -1
+
+
+class _HostStream:
+    """Stands in for a torch stream object on the CPU (handle 0): the calls
+    below fail validation before anything is enqueued on it."""
+    cuda_stream = 0
+
+
+def test_binding_passes_the_callers_workspace_size():
+    """A caller's workspace smaller than the call needs must be reported as
+    MP_ERR_WORKSPACE: the binding passes the buffer's real byte size, not the
+    size the call asked for.  Host tensors are used (only their addresses
+    cross the ABI, and validation fails before any kernel is enqueued)."""
+    import torch
+    T, K, Fi = 64, 64, 64
+    bf = torch.bfloat16
+    X, A, Z, dY = (torch.zeros(*s, dtype=bf) for s in [(T, K), (Fi, K), (T, Fi), (T, Fi)])
+    dX, dA = torch.zeros(T, K, dtype=bf), torch.zeros(Fi, K)
+    need = mp.lib().mp_column_linear_gelu_bwd_workspace(mp.MP_BF16, T, K, Fi)
+    ws = torch.zeros(need - 16, dtype=torch.uint8)
+    with pytest.raises(mp.MPError) as e:
+        mp.mp_column_linear_gelu_bwd(X, A, Z, dY, "erf", dX, dA, ws=ws, stream=_HostStream())
+    assert e.value.code == -6
+    Y, Bw, dO = torch.zeros(2048, Fi, dtype=bf), torch.zeros(3072, Fi, dtype=bf), torch.zeros(2048, 3072, dtype=bf)
+    dYr, dBr = torch.zeros(2048, Fi, dtype=bf), torch.zeros(3072, Fi)
+    need = mp.lib().mp_row_linear_partial_bwd_workspace(mp.MP_BF16, 2048, Fi, 3072)
+    assert need > 0  # split-K partials
+    with pytest.raises(mp.MPError) as e:
+        mp.mp_row_linear_partial_bwd(Y, Bw, dO, dYr, dBr, ws=torch.zeros(need // 2, dtype=torch.uint8),
+                                     stream=_HostStream())
+    assert e.value.code == -6
+
+
+def test_rank_shards_reject_indivisible_counts():
+    """The GPU count must divide the heads (MLM-notes, "Model Parallel
+    Transformers", the drawback bullet), and the FFN width and vocabulary it
+    splits; a remainder is an error, never a floored shard."""
+    import torch
+    from megatron_tensor_transformer_02_amd import synthetic as S
+    prm = {"w_qkv": torch.zeros(3 * 6 * 8, 16), "b_qkv": torch.zeros(3 * 6 * 8), "w_o": torch.zeros(16, 48),
+           "w_a": torch.zeros(40, 16), "b_a": torch.zeros(40), "w_b": torch.zeros(16, 40)}
+    assert S.rank_shard(prm, 1, 2, 6, 8)["heads"] == 3
+    with pytest.raises(ValueError, match="heads"):
+        S.rank_shard(prm, 0, 4, 6, 8)
+    with pytest.raises(ValueError, match="FFN"):
+        S.rank_shard(dict(prm, w_a=torch.zeros(41, 16)), 0, 2, 6, 8)
+    with pytest.raises(ValueError):
+        S.rank_shard(prm, 2, 2, 6, 8)
+    assert S.vocab_shard_rows(51200, 8) == 6400
+    with pytest.raises(ValueError, match="vocabulary"):
+        S.vocab_shard_rows(51201, 8)

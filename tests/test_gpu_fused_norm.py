@@ -55,7 +55,9 @@ def test_reduce_layernorm_fwd(dtype, n, rows, cols, p):
     assert rel_frobenius(f64(out), want_pre + f64(res)) <= TOL[dtype]
     wy, wm, wr = O.layernorm(f64(out), f64(gamma), f64(beta))
     assert rel_frobenius(f64(y), wy) <= TOL[dtype]
-    assert np.max(np.abs(f64(mean) - wm)) <= 1e-4 * (1 + np.max(np.abs(wm)))
+    # A row mean of values of either sign cancels: fp32 summation error is
+    # bounded relative to the mean magnitude of the row's values.
+    assert np.all(np.abs(f64(mean) - wm) <= 1e-5 * np.abs(f64(out)).mean(axis=1))
     assert rel_frobenius(f64(rstd), wr) <= 1e-5
 
 

@@ -72,7 +72,8 @@ def test_column_linear_bwd(dtype, T, K, Fi, act):
     assert rel_frobenius(f64(dab), wdab) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,T,Fi,K", [("f32", 32, 128, 64), ("bf16", 300, 136, 264), ("bf16", 2048, 384, 3072)])
+@pytest.mark.parametrize("dtype,T,Fi,K", [("f32", 32, 128, 64), ("bf16", 300, 136, 264), ("bf16", 2048, 384, 3072),
+                                          ("bf16", 8192, 384, 3072)])  # the 8.3B shard's out-projection, full T
 def test_row_linear_bwd(dtype, T, Fi, K):
     say("row bwd", dtype, T, Fi, K)
     y = randn(10, (T, Fi), dtype)
@@ -114,10 +115,13 @@ def test_row_linear_bwd_dact(dtype, T, Fi, K, act):
     assert torch.equal(db, db2)
 
 
-@pytest.mark.parametrize("plan", ["256,256,1", "256,192,1", "256,128,1", "128,128,3", "128,192,1", "256,192,2"])
+@pytest.mark.parametrize("plan", ["256,256,1", "256,192,1", "256,128,1", "128,128,3", "128,192,1", "256,192,2",
+                                  "128,128,16", "256,256,16"])
 def test_forced_tile_plans_ragged(plan, monkeypatch):
     """Every tile shape and a split-K whose last split is ragged, on ragged
-    M, N and K in all three layouts (forward NT; backward NN and TN)."""
+    M, N and K in all three layouts (forward NT; backward NN and TN).  The
+    16-way splits are the planner's largest (one 64-deep k-tile per split
+    here, the last one 40 deep)."""
     say("forced plan", plan)
     monkeypatch.setenv("MP_GEMM_PLAN", plan)
     T, Fi, K = 1000, 200, 264
@@ -188,3 +192,26 @@ def test_vocab_logits_gemm_full_size_sampled_rows():
     rows = np.random.default_rng(1).choice(T, 64, replace=False)
     want = f64(h)[rows] @ f64(e).T
     assert rel_frobenius(f64(z)[rows], want) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("splits", [2, 7, 16])
+def test_weight_gradient_split_k_full_tokens(splits, monkeypatch):
+    """The out-projection's weight gradient of the 8.3B shard, dW_o [3072,
+    384] = dOut^T ctx over all 8192 tokens, with the K split forced to 2, 7
+    (the planner's choice) and 16 (its largest) pieces, against the oracle;
+    the fixed-order reduce of the fp32 partials makes every plan
+    deterministic (two runs equal)."""
+    say("wgrad split-K full T", splits)
+    monkeypatch.setenv("MP_GEMM_PLAN", f"128,128,{splits}")
+    T, Fi, K = 8192, 384, 3072
+    y, dout = randn(40, (T, Fi), "bf16"), randn(41, (T, K), "bf16")
+    b = randn(42, (K, Fi), "bf16", 0.02)
+    yd, bd, dd = cu(y), cu(b), cu(dout)
+    dy = torch.empty((T, Fi), dtype=torch.bfloat16, device="cuda")
+    db = torch.empty((K, Fi), dtype=torch.float32, device="cuda")
+    mp.mp_row_linear_partial_bwd(yd, bd, dd, dy, db)
+    db2 = torch.empty_like(db)
+    mp.mp_row_linear_partial_bwd(yd, bd, dd, dy, db2)
+    sync()
+    assert torch.equal(db, db2)
+    assert rel_frobenius(f64(db), f64(dout).T @ f64(y)) <= TOL["bf16"]

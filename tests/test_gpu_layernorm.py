@@ -38,5 +38,11 @@ def test_layernorm_fwd_bwd(dtype, T, K):
     sync()
     wdx, wdg, wdb = O.layernorm_bwd(f64(dy), f64(x), f64(g), wm, wr)
     assert rel_frobenius(f64(dx), wdx + f64(dres)) <= TOL[dtype]
-    assert rel_frobenius(f64(dg), wdg) <= 1e-4
+    # dgamma and dbeta are fp32 sums over T rows of terms of either sign:
+    # fp32 summation error scales with the sum of the terms' magnitudes, not
+    # with the (cancelling) sum, so each column is held to 1e-5 of that.
+    xhat = (f64(x) - wm[:, None]) * wr[:, None]
+    assert np.all(np.abs(f64(dg) - wdg) <= 1e-5 * np.abs(f64(dy) * xhat).sum(axis=0))
+    assert np.all(np.abs(f64(db) - wdb) <= 1e-5 * np.abs(f64(dy)).sum(axis=0))
     assert rel_frobenius(f64(db), wdb) <= 1e-5
+    assert rel_frobenius(f64(dg), wdg) <= TOL[dtype]
