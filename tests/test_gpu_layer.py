@@ -211,21 +211,34 @@ def test_sequence_parallel_equals_tensor_parallel(wname, n):
 @pytest.mark.parametrize("wname,n,B", [("gpt2m", 4, 2), ("mlm8b", 8, 1)])
 def test_sequence_parallel_against_oracle(wname, n, B):
     """The sequence-parallel form against the unpartitioned oracle layer
-    (PAR-survey, "Achievement" item 4 and "How": TP+SP): the ranks' output
-    and input-gradient slices, concatenated, give the layer's; each rank's
-    weight-shard gradients are that rank's cut of the oracle's full
-    gradients; the replicated parameters' gradients (LayerNorm, the two
-    reduced biases), summed over the ranks' token slices, give the full ones.
-    Whole batch (B sequences) through the oracle."""
+    (PAR-survey, "Achievement" item 4 and "How": TP+SP), whole batch:
+
+    * end to end: the ranks' output and input-gradient slices, concatenated,
+      give the layer's; the MLP-side weight-shard gradients are each rank's
+      cut of the oracle's full gradients; the replicated parameters'
+      gradients (LayerNorm, the two reduced biases), summed over the ranks'
+      token slices, give the full ones -- all within the bf16 bound;
+    * per step, for the attention side (w_qkv, b_qkv, w_o, and LayerNorm 1
+      behind it): each rank's gradients against the oracle's attention,
+      out-projection and LayerNorm backward on the bf16 tensors that rank's
+      kernels read (LN1 output, QKV, context, upstream gradients), the
+      oracle's convention of taking the path's rounded inputs as exact,
+      within the bf16 bound.  End to end these gradients sit behind about
+      eight stored bf16 intermediates whose rounding the softmax amplifies
+      (measured on the 8.3B layer: context 4.8e-3, its gradient 4.5e-3,
+      w_qkv 7.1e-3, LayerNorm 1 gamma 7.4e-3, while the attention kernels
+      on their own inputs give 2.4e-3); they are held to 1e-2 there."""
     say("sequence parallel vs oracle", wname, n, B)
     wl = S.WORKLOADS[wname]
     L, K, H, d = wl.L, wl.K, wl.heads, wl.d
+    hi = H // n
     prm = S.layer_params(wl)
     x, dout = S.layer_activations(wl, T=B * L)
     shared = shared_params(prm)
-    shards = [{k: cu(v) for k, v in S.rank_shard(prm, i, n, H, d).items() if k != "heads"} for i in range(n)]
+    cut = [S.rank_shard(prm, i, n, H, d) for i in range(n)]
+    shards = [{k: cu(v) for k, v in sh.items() if k != "heads"} for sh in cut]
     kw = dict(p=max(wl.p, 0.1), seed=wl.seed, offsets=(1, 2))
-    sp = make_sp_ranks(shards, shared, B, L, H // n, d, **kw)
+    sp = make_sp_ranks(shards, shared, B, L, hi, d, **kw)
     run_ranks_sp(sp, cu(x), cu(dout))
     sync()
     out = torch.cat([r._rows(r.out) for r in sp])
@@ -238,8 +251,25 @@ def test_sequence_parallel_against_oracle(wname, n, B):
     full = {k: torch.from_numpy(gr[k]) for k in ("w_qkv", "b_qkv", "w_o", "w_a", "b_a", "w_b")}
     for i, r in enumerate(sp):
         want = S.rank_shard(full, i, n, H, d)
-        for k in ("w_qkv", "b_qkv", "w_o", "w_a", "b_a", "w_b"):
+        for k in ("w_a", "b_a", "w_b"):
             assert rel_frobenius(f64(r.g[k]), want[k].numpy()) <= TOL["bf16"], (i, k)
-    for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "b_o", "b_b"):
+        for k in ("w_qkv", "b_qkv", "w_o"):
+            assert rel_frobenius(f64(r.g[k]), want[k].numpy()) <= 1e-2, (i, k)
+        # per step, on the tensors this rank's kernels read
+        _, wdo = O.row_linear_partial_bwd(f64(r.ctx), f64(cut[i]["w_o"]), f64(r.d_attn))
+        assert rel_frobenius(f64(r.g["w_o"]), wdo) <= TOL["bf16"], (i, "w_o step")
+        _, wdw, wdb = O.head_attention_bwd(f64(r.h), f64(cut[i]["w_qkv"]), f64(r.qkv), f64(r.dctx), B, L, hi, d)
+        assert rel_frobenius(f64(r.g["w_qkv"]), wdw) <= TOL["bf16"], (i, "w_qkv step")
+        assert rel_frobenius(f64(r.g["b_qkv"]), wdb) <= TOL["bf16"], (i, "b_qkv step")
+    for k in ("ln2_g", "ln2_b", "b_o", "b_b"):
         total = sum(f64(r.g[k]) for r in sp)
         assert rel_frobenius(total, gr[k]) <= TOL["bf16"], k
+    # LayerNorm 1 sits behind the attention backward: end to end as the
+    # attention side; per step, its backward on the summed input-gradient
+    # partials the ranks' kernels read (the reduce-scatter's inputs).
+    dh = sum(f64(r.dhp) for r in sp)
+    _, wdg, wdb = O.layernorm_bwd(dh, f64(x), op["ln1_g"], c["mu1"], c["rs1"])
+    for k, want in (("ln1_g", wdg), ("ln1_b", wdb)):
+        total = sum(f64(r.g[k]) for r in sp)
+        assert rel_frobenius(total, gr[k]) <= 1e-2, k
+        assert rel_frobenius(total, want) <= TOL["bf16"], (k, "step")
