@@ -132,6 +132,25 @@ int mp_row_linear_partial_bwd(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K,
                               const void* Y_i, const void* B_i, const void* dOut, void* dY_i,
                               float* dB_i, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* mp_row_linear_partial_bwd without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results (bit for
+ * bit) and errors as mp_row_linear_partial_bwd, minus ws/ws_bytes: the
+ * split-K partials of the weight gradient go to a static scratch array of
+ * mp_row_linear_partial_bwd_static_max_bytes() bytes (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends.  A shape
+ * whose partials need more (mp_row_linear_partial_bwd_workspace > that)
+ * fails with MP_ERR_WORKSPACE before anything is enqueued.  The call
+ * allocates nothing; the first call on a device looks up the array's
+ * address there.  Every call on one GPU shares the array: calls that
+ * overlap in time on one GPU (different streams, or threads) race on it
+ * and must be serialised by the caller.  Nothing in it needs clearing: each
+ * call writes every partial it reads. */
+size_t mp_row_linear_partial_bwd_static_max_bytes(void);
+int mp_row_linear_partial_bwd_static(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K,
+                                     const void* Y_i, const void* B_i, const void* dOut,
+                                     void* dY_i, float* dB_i, hipStream_t s);
+
 /* mp_row_linear_partial_bwd for the second GEMM of the MLP block, whose input
  * Y_i = act(Z_save) came from mp_column_linear_gelu (MLM-notes, "Model
  * Parallel Transformers": the GeLU sits between the column- and the

@@ -20,6 +20,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "gemm.h"
 #include "mfma.h"
 
@@ -925,4 +927,81 @@ extern "C" int mp_row_linear_partial_bwd_dact(mp_dtype dtype, int64_t T, int64_t
   MP_REQUIRE_PTR(Z_save);
   MP_REQUIRE_ALIGN(Z_save);
   return row_linear_bwd(fn, dtype, T, Fi, K, Y_i, B_i, dOut, Z_save, act, dZ_i, dB_i, ws, ws_bytes, s);
+}
+
+// ------------------------------------------------ no-allocation variant
+// Scratch of mp_row_linear_partial_bwd_static: a file-scope device array, so
+// the call needs no caller workspace and allocates nothing.  The runtime
+// places one copy on every GPU that loads this code object and keeps it
+// until the process ends.  In host code `scratch` names a host-side stand-in:
+// its device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and only that address is ever passed to a kernel.
+namespace mp {
+
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device that runs stream `s`.
+static int static_scratch(hipStream_t s, void** out, const char* fn) {
+  int dev = 0;
+  hipError_t e = s == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(s, &dev);
+  if (e != hipSuccess) return fail(MP_ERR_HIP, "%s: cannot find the stream's device: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MP_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(MP_ERR_HIP, "%s: no device address for the static scratch on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MP_OK;
+}
+
+}  // namespace mp
+
+extern "C" size_t mp_row_linear_partial_bwd_static_max_bytes(void) { return mp::kStaticScratchBytes; }
+
+extern "C" int mp_row_linear_partial_bwd_static(mp_dtype dtype, int64_t T, int64_t Fi, int64_t K, const void* Y_i,
+                                                const void* B_i, const void* dOut, void* dY_i, float* dB_i,
+                                                hipStream_t s) {
+  static const char* fn = "mp_row_linear_partial_bwd_static";
+  MP_REQUIRE(dtype_ok(dtype), MP_ERR_DTYPE, "%s: bad dtype", fn);
+  MP_REQUIRE(T >= 0 && K > 0 && Fi > 0, MP_ERR_SHAPE, "%s: bad shape", fn);
+  // Host-visible checks first, so a bad call fails before the address lookup.
+  if (int rc = validate_mat(dtype, K, fn, "K")) return rc;
+  if (int rc = validate_mat(dtype, Fi, fn, "Fi")) return rc;
+  MP_REQUIRE_PTR(Y_i);
+  MP_REQUIRE_PTR(B_i);
+  MP_REQUIRE_PTR(dOut);
+  MP_REQUIRE_PTR(dY_i);
+  MP_REQUIRE_PTR(dB_i);
+  MP_REQUIRE_ALIGN(Y_i);
+  MP_REQUIRE_ALIGN(B_i);
+  MP_REQUIRE_ALIGN(dOut);
+  MP_REQUIRE_ALIGN(dY_i);
+  MP_REQUIRE_ALIGN(dB_i);
+  const size_t need = mp_row_linear_partial_bwd_workspace(dtype, T, Fi, K);
+  MP_REQUIRE(need <= kStaticScratchBytes, MP_ERR_WORKSPACE,
+             "%s: this shape needs %zu scratch bytes, more than the static %zu; use mp_row_linear_partial_bwd", fn,
+             need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    if (int rc = static_scratch(s, &ws, fn)) return rc;
+  }
+  return row_linear_bwd(fn, dtype, T, Fi, K, Y_i, B_i, dOut, nullptr, MP_ACT_NONE, dY_i, dB_i, ws,
+                        need > 0 ? kStaticScratchBytes : 0, s);
 }

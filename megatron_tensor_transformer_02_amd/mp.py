@@ -41,6 +41,8 @@ _SIGS = {
     "mp_row_linear_partial": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p]),
     "mp_row_linear_partial_bwd_workspace": (c_sz, [c_i32, c_i64, c_i64, c_i64]),
     "mp_row_linear_partial_bwd": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]),
+    "mp_row_linear_partial_bwd_static_max_bytes": (c_sz, []),
+    "mp_row_linear_partial_bwd_static": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p]),
     "mp_row_linear_partial_bwd_dact": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_p,
                                                c_sz, c_p]),
     "mp_shard_reduce": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_p, c_p, c_p, c_f32, c_u64, c_u64, c_u64, c_p, c_p,
@@ -245,6 +247,16 @@ def mp_row_linear_partial_bwd(Y_i, B_i, dOut, dY_i, dB_i, ws=None, stream=None):
     ws = ws if ws is not None else workspace(need, Y_i.device, stream)
     _call("mp_row_linear_partial_bwd", dt, T, Fi, K, _p(Y_i), _p(B_i), _p(dOut), _p(dY_i), _p(dB_i), _p(ws),
           _nbytes(ws), _s(stream))
+
+
+def mp_row_linear_partial_bwd_static(Y_i, B_i, dOut, dY_i, dB_i, stream=None):
+    """mp_row_linear_partial_bwd on the library's static scratch: no
+    workspace argument, nothing allocated (for code under graph capture or
+    other callers that cannot allocate).  Calls overlapping on one GPU race."""
+    T, Fi = Y_i.shape
+    K = B_i.shape[0]
+    _call("mp_row_linear_partial_bwd_static", _dt(Y_i), T, Fi, K, _p(Y_i), _p(B_i), _p(dOut), _p(dY_i), _p(dB_i),
+          _s(stream))
 
 
 def mp_row_linear_partial_bwd_dact(Y_i, B_i, dOut, Z_save, act, dZ_i, dB_i, ws=None, stream=None):
