@@ -270,8 +270,16 @@ def main():
     if "layer" in parts:
         r0.probe = None
 
+    def seg_times(name):
+        return [r[name][0].elapsed_time(r[name][1]) for r in recs]
+
     def seg_ms(name):
-        return float(np.mean([r[name][0].elapsed_time(r[name][1]) for r in recs]))
+        return float(np.mean(seg_times(name)))
+
+    def stats(vals):
+        """Median and minimum beside the mean (the whole-job figures use the
+        mean, i.e. total time over the steps)."""
+        return round(float(np.median(vals)), 4), round(float(np.min(vals)), 4)
 
     ms_step = wall * 1e3 / args.steps
     out = {"metric": "TP-shard layer fwd+bwd TFLOPS (% bf16 MFMA peak); vocab-xent GB/s (% HBM)",
@@ -290,6 +298,7 @@ def main():
         lay_ms = seg_ms("layer")
         out["value"] = round(fl / (lay_ms * 1e-3) / 1e12, 2)
         out["layer_ms"] = round(lay_ms, 4)
+        out["layer_ms_median"], out["layer_ms_min"] = stats(seg_times("layer"))
         out["layer_pct_bf16_peak"] = round(100 * out["value"] / PEAK_BF16_TFLOPS, 2)
         ev_of = lambda tag: [e for t, e in col_events if t == tag]  # noqa: E731
         col = [b.elapsed_time(e) for b, e in zip(ev_of("col_begin"), ev_of("col_end"))]
@@ -299,7 +308,8 @@ def main():
         roofs.append({"kernel": "column-parallel GEMM + GeLU (gemm_bf16_kernel, act=erf) [8192x3072]x[1536x3072]^T",
                       "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
-                      "avg_launch_us": round(col_ms * 1e3, 2), "algorithmic_per_launch": col_fl})
+                      "avg_launch_us": round(col_ms * 1e3, 2),
+                      "median_launch_us": round(float(np.median(col)) * 1e3, 2), "algorithmic_per_launch": col_fl})
         # The MLP's 8-way shard reduce (+ bias, dropout with its keep bits
         # saved, residual): 8 bf16 partials and the residual read, the output
         # and the keep bits written.
@@ -312,14 +322,17 @@ def main():
         roofs.append({"kernel": "8-way shard reduce + bias + dropout + residual (shard_reduce_kernel) [8192x3072] bf16",
                       "bound": "hbm", "achieved": round(red_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                       "frac": round(red_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                      "avg_launch_us": round(red_ms * 1e3, 2), "algorithmic_per_launch": red_bytes})
+                      "avg_launch_us": round(red_ms * 1e3, 2),
+                      "median_launch_us": round(float(np.median(red)) * 1e3, 2), "algorithmic_per_launch": red_bytes})
     if "vocab" in parts:
         xs = [r["xent"][0].elapsed_time(r["xent"][1]) for r in recs]
         x_ms = float(np.mean(xs))
         xbytes = Tv * Vi * 4.0 + Tv * 4 + Tv * 12
         gbps = xbytes / (x_ms * 1e-3) / 1e9
         out["vocab_ms"] = round(seg_ms("vocab"), 4)
+        out["vocab_ms_median"], out["vocab_ms_min"] = stats(seg_times("vocab"))
         out["xent_GBps"] = round(gbps, 1)
+        out["xent_GBps_median"] = round(xbytes / (float(np.median(xs)) * 1e-3) / 1e9, 1)
         out["xent_pct_hbm"] = round(100 * gbps / PEAK_HBM_GBPS, 2)
         # The cross-entropy backward in the same steps (fp32 gradient written
         # over the logits: read Z + write dZ + labels + (M, S) statistics), and
@@ -371,6 +384,7 @@ def main():
         moe_ms = seg_ms("moe")
         moe_fl = R_hot * 2.0 * (wm.K * 2 * wm.Fe + wm.Fe * wm.K)
         out["moe_ms"] = round(moe_ms, 4)
+        out["moe_ms_median"], out["moe_ms_min"] = stats(seg_times("moe"))
         out["moe_TFLOPS"] = round(moe_fl / (moe_ms * 1e-3) / 1e12, 2)
         out["moe_rows"] = R_hot
         # The memory-efficient permutation form (routing weight on the
@@ -616,6 +630,15 @@ def cpu_baseline(wl, hi, Fi, budget_s=20.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     L, K, d = wl.L, wl.K, wl.d
     prm = S.layer_params(wl, heads=hi, d=d, F=Fi)
     op = {k: v.double().numpy() for k, v in prm.items()}
@@ -633,6 +656,7 @@ def cpu_baseline(wl, hi, Fi, budget_s=20.0):
     t = run(nseq) if nseq > 1 else t1
     fl = 3 * layer_flops(nseq, L, K, hi, d, Fi)
     return {"value": round(fl / t / 1e12, 4), "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model, "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"rank-share layer fwd+bwd on {nseq} of {wl.B} sequences (L={L}), fp64 numpy, {t:.1f}s"}
 
 

@@ -36,8 +36,13 @@
  *   the contiguous dimension of every bf16 matrix must be a multiple of 8
  *   and of every fp32 matrix a multiple of 4 (MP_ERR_SHAPE), so rows stay
  *   16-byte aligned.
- * - Device-data preconditions (labels in [0, V), expert ids in [0, E) and
- *   distinct within a token) are documented, not checked.
+ * - Device-data preconditions (labels and token ids in [0, V), expert ids
+ *   in [0, E)) are documented, not checked on the fast path.  With the
+ *   environment variable MP_DEBUG_CHECKS set (to anything but "0"), every
+ *   call that reads labels, token ids or expert ids first copies them to the
+ *   host (synchronising its stream) and fails with MP_ERR_DATA if one is
+ *   negative -- the one bound a single shard can check, since it is not told
+ *   V or E.  mp_check_indices checks a full range on the device.
  * - Only gfx950 is supported; mp_device_supported() says so per device.
  */
 #ifndef MP_H
@@ -53,12 +58,26 @@ extern "C" {
 
 /* ------------------------------------------------------------------ types */
 
-typedef enum { MP_F32 = 0, MP_BF16 = 1 } mp_dtype;
+/* The two range sentinels make every int a valid mp_dtype value, so a bad
+ * value from a caller is rejected with MP_ERR_DTYPE rather than being
+ * undefined behaviour once it is read as the enum type. */
+typedef enum {
+  MP_F32 = 0,
+  MP_BF16 = 1,
+  MP_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  MP_DTYPE_RANGE_MAX_ = 2147483647
+} mp_dtype;
 
 /* Activation of the column-parallel linear.  GeLU is not defined on the
  * pages; MP_ACT_GELU_ERF is the exact z*Phi(z) (via erf), MP_ACT_GELU_TANH the
  * tanh approximation. */
-typedef enum { MP_ACT_NONE = 0, MP_ACT_GELU_ERF = 1, MP_ACT_GELU_TANH = 2 } mp_act;
+typedef enum {
+  MP_ACT_NONE = 0,
+  MP_ACT_GELU_ERF = 1,
+  MP_ACT_GELU_TANH = 2,
+  MP_ACT_RANGE_MIN_ = -2147483647 - 1,
+  MP_ACT_RANGE_MAX_ = 2147483647
+} mp_act;
 
 #define MP_OK              0
 #define MP_ERR_NULL       -1  /* a required pointer is NULL                     */
@@ -69,6 +88,7 @@ typedef enum { MP_ACT_NONE = 0, MP_ACT_GELU_ERF = 1, MP_ACT_GELU_TANH = 2 } mp_a
 #define MP_ERR_WORKSPACE  -6  /* workspace NULL or smaller than required        */
 #define MP_ERR_HIP        -7  /* a HIP runtime call or kernel launch failed     */
 #define MP_ERR_ARG        -8  /* an argument value is out of range (e.g. p)     */
+#define MP_ERR_DATA       -9  /* device data violates a precondition (debug)    */
 
 #define MP_MAX_SHARDS 16      /* largest N accepted by the reduce/combine calls */
 
@@ -76,6 +96,16 @@ typedef enum { MP_ACT_NONE = 0, MP_ACT_GELU_ERF = 1, MP_ACT_GELU_TANH = 2 } mp_a
 
 /* Library version, major*10000 + minor*100 + patch. */
 int mp_version(void);
+
+/* Data check of an index array (labels or token ids against [0, V), expert
+ * ids against [0, E)), for callers that validate inputs before the hot path:
+ * *bad_count (device memory, 8-byte aligned) receives the number of
+ * idx[0..n) outside [lo, hi), enqueued on s (no synchronisation; read it
+ * after the stream reaches this point).  The count is exact (integer
+ * atomics).  Errors: MP_ERR_SHAPE (n < 0 or lo > hi), MP_ERR_NULL,
+ * MP_ERR_ALIGN. */
+int mp_check_indices(const int32_t* idx, int64_t n, int64_t lo, int64_t hi, uint64_t* bad_count,
+                     hipStream_t s);
 
 /* MP_OK if device `device` is a gfx950 part, MP_ERR_UNSUPPORTED otherwise,
  * MP_ERR_HIP if the device cannot be queried. */

@@ -4,6 +4,13 @@ Each translation unit is compiled with ``hipcc --offload-arch=gfx950`` in
 parallel into ``_build/`` at the repository root, then linked into
 ``megatron_tensor_transformer_02_amd/libmp.so``.  Packed fp32 instructions
 are disabled (``-packed-fp32-ops``) for every GPU object.
+
+``build(sanitize=True)`` builds a test-only variant whose host code carries
+AddressSanitizer and UndefinedBehaviorSanitizer instrumentation (each
+``-fsanitize=`` flag is passed for the host compilation only; the device code
+is built as usual and is never run from it) into
+``_build/asan/libmp_asan.so``, for exercising the argument validation layer
+on the CPU under the sanitizers' runtime.
 """
 
 import concurrent.futures as cf
@@ -30,8 +37,14 @@ CFLAGS = [
 ]
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libmp_asan.so")
+
+
+def _compile(src, extra, out_dir=BUILD):
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -39,25 +52,38 @@ def _compile(src, extra):
     return obj, res.stderr
 
 
-def build(verbose=False, extra=(), jobs=None):
-    """Compile and link libmp.so; returns its path.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, extra=(), jobs=None, sanitize=False):
+    """Compile and link libmp.so (or, with ``sanitize``, the host-sanitized
+    test build); returns its path.  Always rebuilds."""
+    out_dir = ASAN_DIR if sanitize else BUILD
+    lib = ASAN_LIB if sanitize else LIB
+    extra = list(extra) + (SANITIZE_FLAGS + ["-O1"] if sanitize else [])
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
+        results = list(ex.map(lambda s: _compile(s, extra, out_dir), srcs))
     objs = []
     for obj, err in results:
         objs.append(obj)
         if verbose and err.strip():
             sys.stderr.write(err)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = lib + ".tmp"
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-shared-libasan"] if sanitize else []
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def asan_runtime():
+    """Path of the compiler's AddressSanitizer runtime (to preload into a
+    process that loads the sanitized build)."""
+    res = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return res.stdout.strip()
 
 
 if __name__ == "__main__":

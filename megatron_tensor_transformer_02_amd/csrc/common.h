@@ -21,6 +21,14 @@ int ok();
 // Translates the result of a kernel launch into a status.
 int check_launch(const char* what);
 
+// Debug-mode data check, active when MP_DEBUG_CHECKS is set to a value other
+// than "0": copies the n int32 indices at idx (device memory) to the host
+// after the work already queued on s, and returns MP_ERR_DATA naming the
+// first index outside [lo, hi).  Synchronises s, so it is for debugging
+// (and not for code under graph capture).  MP_OK when the variable is unset.
+int debug_check_range(const char* fn, const char* what, const int32_t* idx, int64_t n, int64_t lo, int64_t hi,
+                      hipStream_t s);
+
 #define MP_REQUIRE(cond, code, ...) \
   do {                              \
     if (!(cond)) return ::mp::fail(code, __VA_ARGS__); \

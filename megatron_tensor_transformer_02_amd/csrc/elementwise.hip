@@ -461,6 +461,7 @@ extern "C" int mp_vocab_parallel_embedding_bwd(mp_dtype dtype, int64_t T, int64_
   MP_REQUIRE_PTR(dE_i);
   MP_REQUIRE_OPT_ALIGN(dOut);
   MP_REQUIRE_ALIGN(dE_i);
+  if (int rc = debug_check_range(fn, "ids", ids, T, 0, INT32_MAX + 1LL, s)) return rc;
   const unsigned grid = static_cast<unsigned>(ceil_div(Vi, 16));
   if (dtype == MP_BF16)
     embedding_bwd_kernel<true><<<grid, 256, 0, s>>>(T, Vi, v_start, K, ids, dOut, dE_i, accumulate);
@@ -505,6 +506,7 @@ extern "C" int mp_vocab_parallel_embedding(mp_dtype dtype, int64_t T, int64_t Vi
   MP_REQUIRE_ALIGN(E_i);
   MP_REQUIRE_ALIGN(out_partial);
   if (T == 0) return MP_OK;
+  if (int rc = debug_check_range("mp_vocab_parallel_embedding", "ids", ids, T, 0, INT32_MAX + 1LL, s)) return rc;
   const int64_t vpr = K / vec_elems(dtype);
   const int64_t nvec = T * vpr;
   embedding_kernel<<<static_cast<unsigned>(ceil_div(nvec, 256)), 256, 0, s>>>(

@@ -239,6 +239,8 @@ struct DmaTile {
     rows = rows_;
     if constexpr (KC) desc = make_desc(base + row0 * ld, (rows - row0) * ld * 2);
     else desc = make_desc(base + row0, (kdim * ld - row0) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) desc[i] = __builtin_amdgcn_readfirstlane(desc[i]);  // uniform: scalar registers
     // Slot (q * NWV + w) * 64 + l holds row/k-row wave*8 + l/8 (+ a per-copy
     // step), chunk (l % 8) ^ swz(row): the swizzle term does not depend on q.
     const int r = wave * 8 + (lane >> 3), c = (lane & 7) ^ lds_swz(r);

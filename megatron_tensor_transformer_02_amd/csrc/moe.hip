@@ -757,6 +757,7 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   MP_REQUIRE_PTR(W_gu);
   MP_REQUIRE_PTR(W_d);
   MP_REQUIRE_PTR(out);
+  if (int rc = debug_check_range(fn, "topk_ids", topk_ids, T * topk, 0, INT32_MAX + 1LL, s)) return rc;
   MP_REQUIRE_ALIGN(X);
   MP_REQUIRE_ALIGN(W_gu);
   MP_REQUIRE_ALIGN(W_d);
@@ -1054,6 +1055,7 @@ extern "C" int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, i
   MP_REQUIRE_PTR(W_d_q);
   MP_REQUIRE_PTR(W_d_s);
   MP_REQUIRE_PTR(out);
+  if (int rc = debug_check_range(fn, "topk_ids", topk_ids, T * topk, 0, INT32_MAX + 1LL, s)) return rc;
   MP_REQUIRE_ALIGN(X);
   MP_REQUIRE_ALIGN(W_gu_q);
   MP_REQUIRE_ALIGN(W_d_q);

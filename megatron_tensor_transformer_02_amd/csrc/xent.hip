@@ -183,6 +183,7 @@ extern "C" int mp_vocab_parallel_xent(int64_t T, int64_t Vi, int64_t v_start, co
   MP_REQUIRE_PTR(triples);
   MP_REQUIRE_ALIGN(Z_i);
   if (T == 0) return MP_OK;
+  if (int rc = debug_check_range("mp_vocab_parallel_xent", "labels", labels, T, 0, INT32_MAX + 1LL, s)) return rc;
 #ifndef MP_XENT_UNROLL
 #define MP_XENT_UNROLL 25
 #endif
@@ -214,6 +215,7 @@ extern "C" int mp_vocab_parallel_logits_xent(mp_dtype dtype, int64_t T, int64_t 
              need);
   MP_REQUIRE_OPT_ALIGN(ws);
   if (T == 0) return MP_OK;
+  if (int rc = debug_check_range(fn, "labels", labels, T, 0, INT32_MAX + 1LL, s)) return rc;
   float* part = static_cast<float*>(ws);
   if (int rc = gemm_logits_lse(T, Vi, K, H, E_i, labels, v_start, part, s)) return rc;
   lse_fold_kernel<<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(T, gemm_lse_slots(T, Vi, K), part, triples);
@@ -253,6 +255,7 @@ extern "C" int mp_vocab_parallel_xent_bwd(int64_t T, int64_t Vi, int64_t v_start
   MP_REQUIRE(out_dtype == MP_F32 || static_cast<const void*>(Z_i) != dZ_i, MP_ERR_ARG,
              "mp_vocab_parallel_xent_bwd: in-place only for fp32 output");
   if (T == 0) return MP_OK;
+  if (int rc = debug_check_range("mp_vocab_parallel_xent_bwd", "labels", labels, T, 0, INT32_MAX + 1LL, s)) return rc;
   const int64_t nvec = T * (Vi / 4);
   const unsigned grid = static_cast<unsigned>(ceil_div(nvec, 256));
   if (out_dtype == MP_BF16)

@@ -15,7 +15,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmp.so")
+# MP_LIB may name another build of the library (e.g. the host-sanitized test
+# build); a missing library is an error either way.
+_LIB_PATH = os.environ.get("MP_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmp.so")
 _lib = None
 
 MP_F32, MP_BF16 = 0, 1
@@ -24,7 +26,7 @@ ACTS = {"none": MP_ACT_NONE, "erf": MP_ACT_GELU_ERF, "tanh": MP_ACT_GELU_TANH}
 MP_MAX_SHARDS = 16
 
 ERRORS = {0: "MP_OK", -1: "MP_ERR_NULL", -2: "MP_ERR_SHAPE", -3: "MP_ERR_DTYPE", -4: "MP_ERR_UNSUPPORTED",
-          -5: "MP_ERR_ALIGN", -6: "MP_ERR_WORKSPACE", -7: "MP_ERR_HIP", -8: "MP_ERR_ARG"}
+          -5: "MP_ERR_ALIGN", -6: "MP_ERR_WORKSPACE", -7: "MP_ERR_HIP", -8: "MP_ERR_ARG", -9: "MP_ERR_DATA"}
 
 c_i64, c_i32, c_u64, c_f32, c_p, c_sz = (ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t)
@@ -34,6 +36,7 @@ _SIGS = {
     "mp_version": (c_i32, []),
     "mp_device_supported": (c_i32, [c_i32]),
     "mp_last_error": (ctypes.c_char_p, []),
+    "mp_check_indices": (c_i32, [c_p, c_i64, c_i64, c_i64, c_p, c_p]),
     "mp_column_linear_gelu": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_i32, c_p, c_p, c_p]),
     "mp_column_linear_gelu_bwd_workspace": (c_sz, [c_i32, c_i64, c_i64, c_i64]),
     "mp_column_linear_gelu_bwd": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_p,
@@ -212,6 +215,13 @@ def mp_device_supported(device=0):
 
 def mp_last_error():
     return lib().mp_last_error().decode()
+
+
+def mp_check_indices(idx, lo, hi, bad_count, stream=None):
+    """Counts the entries of the int32 device tensor ``idx`` outside
+    [lo, hi) into ``bad_count`` (a one-element int64 device tensor),
+    asynchronously on ``stream``."""
+    _call("mp_check_indices", _p(idx), idx.numel(), lo, hi, _p(bad_count), _s(stream))
 
 
 # -------------------------------------------------------------- MLP pieces

@@ -386,3 +386,17 @@ def test_rank_shards_reject_indivisible_counts():
     assert S.vocab_shard_rows(51200, 8) == 6400
     with pytest.raises(ValueError, match="vocabulary"):
         S.vocab_shard_rows(51201, 8)
+
+
+def test_check_indices_validation(lib):
+    rc, _ = call(lib, "mp_check_indices", ALIGNED, -1, 0, 10, ALIGNED, None)
+    assert rc == -2
+    rc, _ = call(lib, "mp_check_indices", ALIGNED, 5, 10, 0, ALIGNED, None)
+    assert rc == -2  # lo > hi
+    rc, _ = call(lib, "mp_check_indices", None, 5, 0, 10, ALIGNED, None)
+    assert rc == -1
+    rc, _ = call(lib, "mp_check_indices", ALIGNED, 5, 0, 10, None, None)
+    assert rc == -1
+    rc, _ = call(lib, "mp_check_indices", ALIGNED, 5, 0, 10, ALIGNED + 4, None)
+    assert rc == -5
+    assert mp.ERRORS[-9] == "MP_ERR_DATA"
