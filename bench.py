@@ -21,7 +21,11 @@ resident in HBM:
 
 ``value`` is the layer's model TFLOP/s (forward + backward = 3x the forward
 FLOPs, attention counted on the causal half); the vocab cross-entropy's GB/s
-is reported beside it (``xent_GBps``; ``shard_reduce_GBps`` is the MLP's
+is reported beside it (``xent_GBps``: the statistics pass reading the
+logits from HBM, a 512 MB write before each rep evicting them from the
+last-level cache as the protocol for HBM kernels prescribes;
+``xent_step_GBps`` the same pass inside the timed steps, right after the
+logits GEMM; ``shard_reduce_GBps`` is the MLP's
 8-way shard reduce in the same steps; ``xent_bwd_GBps`` and
 ``xent_fwd_bwd_GBps`` add the cross-entropy backward timed in the same
 steps).  After the timed steps, the sequence-parallel form of
@@ -325,15 +329,17 @@ def main():
                       "avg_launch_us": round(red_ms * 1e3, 2),
                       "median_launch_us": round(float(np.median(red)) * 1e3, 2), "algorithmic_per_launch": red_bytes})
     if "vocab" in parts:
+        # In-step figures (the pass right after the logits GEMM, whose 210 MB of
+        # output may still sit in the 256 MB last-level cache or be on its way
+        # back to HBM).
         xs = [r["xent"][0].elapsed_time(r["xent"][1]) for r in recs]
         x_ms = float(np.mean(xs))
         xbytes = Tv * Vi * 4.0 + Tv * 4 + Tv * 12
-        gbps = xbytes / (x_ms * 1e-3) / 1e9
+        step_gbps = xbytes / (x_ms * 1e-3) / 1e9
         out["vocab_ms"] = round(seg_ms("vocab"), 4)
         out["vocab_ms_median"], out["vocab_ms_min"] = stats(seg_times("vocab"))
-        out["xent_GBps"] = round(gbps, 1)
-        out["xent_GBps_median"] = round(xbytes / (float(np.median(xs)) * 1e-3) / 1e9, 1)
-        out["xent_pct_hbm"] = round(100 * gbps / PEAK_HBM_GBPS, 2)
+        out["xent_step_GBps"] = round(step_gbps, 1)
+        out["xent_step_GBps_median"] = round(xbytes / (float(np.median(xs)) * 1e-3) / 1e9, 1)
         # The cross-entropy backward in the same steps (fp32 gradient written
         # over the logits: read Z + write dZ + labels + (M, S) statistics), and
         # the statistics pass + backward together.
@@ -341,11 +347,12 @@ def main():
         bbytes = 2.0 * Tv * Vi * 4 + Tv * 4 + Tv * 8
         out["xent_bwd_GBps"] = round(bbytes / (xb_ms * 1e-3) / 1e9, 1)
         out["xent_fwd_bwd_GBps"] = round((xbytes + bbytes) / ((x_ms + xb_ms) * 1e-3) / 1e9, 1)
-        # The logits (210 MB) are written just before by the logits GEMM and may be
-        # served from the 256 MB Infinity Cache; also time the pass cold.
+        # The HBM-bound statistics pass by the measurement protocol for HBM
+        # kernels: a 512 MB write before each rep evicts the logits from the
+        # last-level cache, so the pass reads them from HBM; median of 20 reps.
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         cold = []
-        for _ in range(10):
+        for _ in range(20):
             flush.fill_(1)
             b_, e_ = EV(), EV()
             b_.record(stream)
@@ -355,7 +362,10 @@ def main():
             cold.append(b_.elapsed_time(e_))
         del flush
         cold_ms = float(np.median(cold))
-        out["xent_cold_GBps"] = round(xbytes / (cold_ms * 1e-3) / 1e9, 1)
+        gbps = xbytes / (cold_ms * 1e-3) / 1e9
+        out["xent_GBps"] = round(gbps, 1)
+        out["xent_pct_hbm"] = round(100 * gbps / PEAK_HBM_GBPS, 2)
+        out["xent_protocol"] = "512 MB write before each of 20 reps (logits read from HBM), median"
         # The logits GEMM with the statistics fused into its epilogue, against
         # the unfused pair (logits GEMM writing the fp32 logits + the triples
         # pass reading them back), each timed on its own.
@@ -376,10 +386,12 @@ def main():
         out["embedding_bwd_us"] = round(timed_us(lambda: mp.mp_vocab_parallel_embedding_bwd(
             ids, hidden, v0.v0, de, accumulate=True)), 1)
         del de
-        roofs.append({"kernel": "vocab xent triples (xent_triples_kernel) [8192x6400] fp32", "bound": "hbm",
-                      "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "avg_launch_us": round(x_ms * 1e3, 2),
-                      "cold_GBps": out["xent_cold_GBps"], "algorithmic_per_launch": xbytes})
+        roofs.append({"kernel": "vocab xent triples (xent_triples_kernel) [8192x6400] fp32, logits read from HBM",
+                      "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                      "avg_launch_us": round(float(np.mean(cold)) * 1e3, 2),
+                      "median_launch_us": round(cold_ms * 1e3, 2), "in_step_GBps": out["xent_step_GBps"],
+                      "algorithmic_per_launch": xbytes})
     if "moe" in parts:
         moe_ms = seg_ms("moe")
         moe_fl = R_hot * 2.0 * (wm.K * 2 * wm.Fe + wm.Fe * wm.K)
