@@ -280,7 +280,11 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   constexpr int BM = BMT, BN = MOE_BN, NT = 512, WC = 4, WM = BM / 2, WN = BN / WC;
   constexpr int TM = WM / 32, TN = WN / 32, A_SLOTS = BM * 8, B_SLOTS = BN * 8;
   static_assert(TN == 2, "the SwiGLU epilogue pairs the gate and up 32-column tiles of a wave");
-  __shared__ uint4 lds[2][A_SLOTS + B_SLOTS];
+  // MXFP8: each k-tile buffer also holds the k-tile's exponent dword of every
+  // A row (256) and B row (256), 2 KiB, loaded with the tile.
+  constexpr int S_SLOTS = MX ? 128 : 0;
+  static_assert(!MX || (BM == 256 && BN == 256), "the exponent region covers 256 + 256 rows");
+  __shared__ uint4 lds[2][A_SLOTS + B_SLOTS + S_SLOTS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / WC, wn = wave % WC;
 
   // Device-side schedule: real tiles = ts[E_loc] * tiles_n.  MXFP8 runs every
@@ -350,51 +354,63 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
 
   const int ar0 = wm * WM, br0 = wn * WN;
   if constexpr (MX) {
-    // Scale rows of this lane's fragment rows.  A padding row (codes read as
-    // zeros) borrows a real row's exponents, which are finite (never 0xFF),
-    // so every load is unconditional and nothing waits for it before use.
-    const uint32_t* sra[TM];
-    const uint32_t* srb[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      int64_t grow = row0 + ar0 + 32 * i + (lane & 31);
-      if (grow >= row_end) grow = row0;
-      const uint8_t* p =
-          MODE == 0 ? a.xs + static_cast<int64_t>(a.perm[grow] / a.topk) * a.swh : a.as + grow * a.swf;
-      sra[i] = reinterpret_cast<const uint32_t*>(p);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = br0 + 32 * j + (lane & 31);
-      const uint8_t* p;
-      if constexpr (MODE == 0) {
-        int64_t w = gu_row(r);
-        if (w < 0) w = 0;
-        p = a.gs + (static_cast<int64_t>(e) * 2 * a.Fe + w) * a.swh;
+    // Exponents travel with their k-tile: the dword of k-tile t of each A and
+    // B row goes global -> LDS by the same direct loads as the codes (wave w
+    // fills dwords w*64 .. +63 of the buffer's exponent region: A rows, then
+    // B rows), so they are complete at the same barrier and are read from LDS
+    // like the fragments, never waited for as separate loads.  A row with no
+    // data (past the expert's rows, or a gate/up row past Fe) reads zeros:
+    // its codes are zeros too, so its products are 0 whatever the scale.
+    i32x4_t sdesc;
+    uint32_t svoff;
+    {
+      const int r = (wave & 3) * 64 + lane;
+      int64_t off = -1;
+      if (wave < 4) {
+        const int64_t grow = row0 + r;
+        if (grow < row_end)
+          off = MODE == 0 ? static_cast<int64_t>(a.perm[grow] / a.topk) * a.swh : grow * a.swf;
+        sdesc = MODE == 0 ? make_desc(a.xs, a.T * a.swh) : make_desc(a.as, a.r_cap * a.swf);
       } else {
-        const int64_t n = n0 + r < a.Hd ? n0 + r : 0;
-        p = a.ds + (static_cast<int64_t>(e) * a.Hd + n) * a.swf;
+        if constexpr (MODE == 0) {
+          const int64_t w = gu_row(r);
+          if (w >= 0) off = (static_cast<int64_t>(e) * 2 * a.Fe + w) * a.swh;
+          sdesc = make_desc(a.gs, static_cast<int64_t>(a.E_loc) * 2 * a.Fe * a.swh);
+        } else {
+          if (n0 + r < a.Hd) off = (static_cast<int64_t>(e) * a.Hd + n0 + r) * a.swf;
+          sdesc = make_desc(a.ds, static_cast<int64_t>(a.E_loc) * a.Hd * a.swf);
+        }
       }
-      srb[j] = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sdesc[i] = __builtin_amdgcn_readfirstlane(sdesc[i]);
+      svoff = off < 0 ? 0x80000000u : static_cast<uint32_t>(off);
     }
+    auto sfill = [&](uint4* buf, int t) {
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(buf + A_SLOTS + B_SLOTS) + wave * 256);
+      const uint32_t so = __builtin_amdgcn_readfirstlane(t < nk ? static_cast<uint32_t>(4 * t) : 0x80000000u);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %3 offen lds" ::"v"(svoff), "s"(sdesc),
+                   "s"(m0v), "s"(so)
+                   : "memory", "m0");
+    };
     // Lane l < 32 supplies block 0 of each 64-code step, lane l + 32 block 1:
     // shifting the k-tile's dword by a byte for the upper lanes makes byte 0
-    // (step 0) and byte 2 (step 1) the right exponents for every lane.  The
-    // shift is applied after the barrier that waits for the load.
+    // (step 0) and byte 2 (step 1) the right exponents for every lane.
     const int shift = 8 * (lane >> 5);
     uint32_t sa[TM], sb[TN];
+    auto read_scales = [&](const uint4* buf) {
+      const uint32_t* sd = reinterpret_cast<const uint32_t*>(buf + A_SLOTS + B_SLOTS);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = sra[i][0];
+      for (int i = 0; i < TM; ++i) sa[i] = sd[ar0 + 32 * i + (lane & 31)] >> shift;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sb[j] = srb[j][0];
+      for (int j = 0; j < TN; ++j) sb[j] = sd[256 + br0 + 32 * j + (lane & 31)] >> shift;
+    };
     fill(lds[0], 0);
+    sfill(lds[0], 0);
     fill(lds[1], 1);
+    sfill(lds[1], 1);
     wait_vm_lds();
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] >>= shift;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sb[j] >>= shift;
+    read_scales(lds[0]);
     // Software pipeline in registers: a fragment is reloaded as soon as its
     // last MFMA of the step is issued (step 0's A fragments become step 1's,
     // step 1's become the next k-tile's step 0), and the barrier sits after
@@ -416,12 +432,6 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
     for (int kt = 0; kt < nk; ++kt) {
       uint4* cur = lds[kt & 1];
       const uint4* nxt = lds[(kt & 1) ^ 1];
-      uint32_t na[TM], nb[TN];
-      const int tn = kt + 1 < nk ? kt + 1 : kt;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) na[i] = sra[i][tn];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) nb[j] = srb[j][tn];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -439,6 +449,7 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
       wait_vm_lds();  // k-tile kt+1 and its exponents have landed; reads of kt retired
       __syncthreads();
       fill(cur, kt + 2);
+      sfill(cur, kt + 2);
 #pragma unroll
       for (int i = 0; i < H; ++i) load_a(nxt, i, 0);
 #pragma unroll
@@ -450,10 +461,7 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) load_b(nxt, j, 0);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) sa[i] = na[i] >> shift;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sb[j] = nb[j] >> shift;
+      read_scales(nxt);
     }
   } else {
   fill(lds[0], 0);
