@@ -397,12 +397,12 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
     // (step 0) and byte 2 (step 1) the right exponents for every lane.
     const int shift = 8 * (lane >> 5);
     uint32_t sa[TM], sb[TN];
-    auto read_scales = [&](const uint4* buf) {
+    auto read_scales = [&](const uint4* buf, uint32_t* ra, uint32_t* rb) {
       const uint32_t* sd = reinterpret_cast<const uint32_t*>(buf + A_SLOTS + B_SLOTS);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) sa[i] = sd[ar0 + 32 * i + (lane & 31)] >> shift;
+      for (int i = 0; i < TM; ++i) ra[i] = sd[ar0 + 32 * i + (lane & 31)];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sb[j] = sd[256 + br0 + 32 * j + (lane & 31)] >> shift;
+      for (int j = 0; j < TN; ++j) rb[j] = sd[256 + br0 + 32 * j + (lane & 31)];
     };
     fill(lds[0], 0);
     sfill(lds[0], 0);
@@ -410,7 +410,11 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
     sfill(lds[1], 1);
     wait_vm_lds();
     __syncthreads();
-    read_scales(lds[0]);
+    read_scales(lds[0], sa, sb);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] >>= shift;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] >>= shift;
     // Software pipeline in registers: a fragment is reloaded as soon as its
     // last MFMA of the step is issued (step 0's A fragments become step 1's,
     // step 1's become the next k-tile's step 0), and the barrier sits after
@@ -448,6 +452,8 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
           acc[i][j] = mfma_mx_32x32x64<2>(fa0[i], fa1[i], fb0[j], fb1[j], sa[i], sb[j], acc[i][j]);
       wait_vm_lds();  // k-tile kt+1 and its exponents have landed; reads of kt retired
       __syncthreads();
+      uint32_t na[TM], nb[TN];  // the next k-tile's exponents, read under this step's MFMAs
+      read_scales(nxt, na, nb);
       fill(cur, kt + 2);
       sfill(cur, kt + 2);
 #pragma unroll
@@ -461,7 +467,10 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) load_b(nxt, j, 0);
-      read_scales(nxt);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa[i] = na[i] >> shift;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb[j] = nb[j] >> shift;
     }
   } else {
   fill(lds[0], 0);
