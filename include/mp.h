@@ -512,8 +512,9 @@ size_t mp_grouped_expert_gemm_mxfp8_workspace(int64_t T, int64_t Hd, int64_t Fe,
  * W_gu_q [E_loc, 2*Fe, Hd] with W_gu_s [E_loc, 2*Fe, 4*ceil(Hd/128)], W_d_q
  * [E_loc, Hd, Fe] with W_d_s [E_loc, Hd, 4*ceil(Fe/128)] (scale arrays 4-byte
  * aligned).  Each expert's gate/up products accumulate in fp32 on gfx950's
- * block-scaled MFMA; the SwiGLU activation is stored as bf16, quantised along
- * Fe, and projected down the same way; the unpermute is the weighted fp32
+ * block-scaled MFMA; the SwiGLU activation is rounded to bf16 and quantised
+ * along Fe (the gate/up GEMM's epilogue writes only its codes and scales),
+ * then projected down the same way; the unpermute is the weighted fp32
  * sum of mp_grouped_expert_gemm.  Hd % 32 == 0, Fe % 32 == 0; other arguments,
  * outputs and errors as mp_grouped_expert_gemm, with the workspace from
  * mp_grouped_expert_gemm_mxfp8_workspace(). */

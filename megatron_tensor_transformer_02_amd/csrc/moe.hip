@@ -230,37 +230,45 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return code | sign;
 }
 
-// Rows of x (bf16, row stride ld) to codes q [rows, K] and scales sc
-// [rows, sw] (bytes past the last block set to 127); four lanes per block,
-// eight values each.  With rows_dev the row count is read from the device
-// (rows is then its upper bound).
-__global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __restrict__ x, int64_t ld, int64_t rows,
-                                                          const int32_t* rows_dev, int64_t K,
-                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
-                                                          int64_t sw) {
-  const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t gpr = K / 8;  // a multiple of 4: the four lanes of a block share a row
-  const int64_t r = v / gpr;
-  const int64_t nrows = rows_dev != nullptr ? min(rows, static_cast<int64_t>(*rows_dev)) : rows;
-  if (r >= nrows) return;
-  const int64_t c = (v - r * gpr) * 8;
-  float f[8];
-  unpack8(*reinterpret_cast<const uint4*>(x + r * ld + c), f);
+// One 32-value MX block held by four consecutive lanes (aligned to 4), eight
+// values each: the block's shared exponent se (E8M0 byte se + 127) is the
+// largest one that keeps the block's maximum magnitude finite in E4M3 (the
+// maximum's exponent minus 8, at least -127), and each value becomes the
+// E4M3 code of value * 2^-se (exact scaling).  Returns the eight codes
+// (value i in byte i % 4 of word i / 4).  All four lanes must be active.
+__device__ __forceinline__ uint2 mx_block8(const float* f, int& se) {
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(f[i]));
   mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
   const int e8 = static_cast<int>(__float_as_uint(mx) >> 23);
-  const int se = e8 == 0 ? -127 : max(e8 - 135, -127);
-  const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);  // 2^-se, exact scaling
+  se = e8 == 0 ? -127 : max(e8 - 135, -127);
+  const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);  // 2^-se
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     lo |= e4m3_code(f[i] * inv) << (8 * i);
     hi |= e4m3_code(f[4 + i] * inv) << (8 * i);
   }
-  *reinterpret_cast<uint2*>(q + r * K + c) = make_uint2(lo, hi);
+  return make_uint2(lo, hi);
+}
+
+// Rows of x (bf16, row stride ld) to codes q [rows, K] and scales sc
+// [rows, sw] (bytes past the last block set to 127); four lanes per block,
+// eight values each.
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __restrict__ x, int64_t ld, int64_t rows,
+                                                          int64_t K, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ sc, int64_t sw) {
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t gpr = K / 8;  // a multiple of 4: the four lanes of a block share a row
+  const int64_t r = v / gpr;
+  if (r >= rows) return;
+  const int64_t c = (v - r * gpr) * 8;
+  float f[8];
+  unpack8(*reinterpret_cast<const uint4*>(x + r * ld + c), f);
+  int se;
+  *reinterpret_cast<uint2*>(q + r * K + c) = mx_block8(f, se);
   if ((c & 31) == 0) sc[r * sw + c / 32] = static_cast<uint8_t>(se + 127);
   if (c == 0)
     for (int64_t bk = K / 32; bk < sw; ++bk) sc[r * sw + bk] = 127;
@@ -581,7 +589,25 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) val[q] *= wr;
         }
-        *reinterpret_cast<uint4*>(a.act + grow * a.Fe + jcol) = pack8(val);
+        if constexpr (MX) {
+          // The activation is rounded to bf16, then quantised: the wave's 32
+          // columns are one MX block of the row (Fe is a multiple of 32), held
+          // by the row's four consecutive lanes.  The lane of the block's
+          // first 8 values writes its exponent, and, for the row's last
+          // block, the padding bytes of the row's scale record.
+          float f[8];
+          unpack8(pack8(val), f);
+          int se;
+          *reinterpret_cast<uint2*>(const_cast<uint8_t*>(a.aq) + grow * a.Fe + jcol) = mx_block8(f, se);
+          if (c8 == 0) {
+            uint8_t* srow = const_cast<uint8_t*>(a.as) + grow * a.swf;
+            srow[jcol / 32] = static_cast<uint8_t>(se + 127);
+            if (jcol + 32 == a.Fe)
+              for (int64_t bk = a.Fe / 32; bk < a.swf; ++bk) srow[bk] = 127;
+          }
+        } else {
+          *reinterpret_cast<uint4*>(a.act + grow * a.Fe + jcol) = pack8(val);
+        }
       } else {
         const int64_t n = static_cast<int64_t>(nt) * BN + wn * WN + c8;
         if (n >= a.Hd) continue;
@@ -737,7 +763,7 @@ static MoeLayout moe_layout(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_l
   L.tile_start_d = take(static_cast<size_t>(E_loc + 1) * 4);
   L.tile_start_s = take(static_cast<size_t>(E_loc + 1) * 4);
   L.counts = take(static_cast<size_t>(E_loc) * 4);
-  L.act = take(static_cast<size_t>(r_cap * Fe) * 2);
+  L.act = take(mx ? 0 : static_cast<size_t>(r_cap * Fe) * 2);  // MXFP8 keeps only the quantised activation
   L.yperm = take(static_cast<size_t>(r_cap * Hd) * 2);
   if (mx) {
     L.xq = take(static_cast<size_t>(T * Hd));
@@ -1044,7 +1070,7 @@ extern "C" int mp_mxfp8_quantize(int64_t rows, int64_t K, const void* x, int64_t
   MP_REQUIRE(reinterpret_cast<uintptr_t>(q) % 8 == 0, MP_ERR_ALIGN, "%s: q must be 8-byte aligned", fn);
   const int64_t groups = rows * (K / 8);
   mx_quantize_kernel<<<static_cast<unsigned>(ceil_div(groups, 256)), 256, 0, s>>>(
-      static_cast<const uint16_t*>(x), ld, rows, nullptr, K, q, scales, mx_scale_width(K));
+      static_cast<const uint16_t*>(x), ld, rows, K, q, scales, mx_scale_width(K));
   return check_launch(fn);
 }
 
@@ -1101,7 +1127,7 @@ extern "C" int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, i
   a.offsets = expert_offsets != nullptr ? expert_offsets : reinterpret_cast<int32_t*>(w + L.offsets);
   a.tile_start = reinterpret_cast<int32_t*>(w + L.tile_start);
   a.counts = reinterpret_cast<int32_t*>(w + L.counts);
-  a.act = reinterpret_cast<uint16_t*>(w + L.act);
+  a.act = nullptr;  // the gate/up GEMM writes the quantised activation only
   a.yperm = reinterpret_cast<uint16_t*>(w + L.yperm);
   a.swh = mx_scale_width(Hd);
   a.swf = mx_scale_width(Fe);
@@ -1124,14 +1150,13 @@ extern "C" int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, i
   moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
   // Token rows quantised once along the hidden dimension (the expert GEMMs'
   // reduction dimension); the weights arrive quantised.
-  mx_quantize_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a.X, Hd, T, nullptr, Hd, xq,
-                                                                                          xs, a.swh);
+  mx_quantize_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a.X, Hd, T, Hd, xq, xs,
+                                                                                          a.swh);
   const int64_t max_mtiles = ceil_div(a.r_cap, MOE_BM) + E_loc;
   a.tiles_n = static_cast<int>(ceil_div(Fe, MOE_BN / 2));
+  // The gate/up GEMM quantises the bf16-rounded activation along Fe in its
+  // epilogue (aq, as), the down GEMM's A operand.
   moe_gemm_kernel<0, true><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
-  // The bf16 activation rows (R of them, known on the device) quantised along Fe.
-  mx_quantize_kernel<<<static_cast<unsigned>(ceil_div(a.r_cap * (Fe / 8), 256)), 256, 0, s>>>(
-      a.act, Fe, a.r_cap, a.offsets + E_loc, Fe, aq, as, a.swf);
   a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
   moe_gemm_kernel<1, true><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
   launch_unpermute(a, s);
