@@ -75,6 +75,13 @@ struct MoeArgs {
   float* dw;               // [T, topk]
   float* wperm;            // [r_cap]: each permuted row's routing weight (weighted-activation form)
   float* dwp;              // [r_cap, Fe/8]: parts of each row's routing-weight gradient
+  // Split-K sparse launches: k-range split s covers [s * k_per, (s+1) * k_per)
+  // (2-byte units, a multiple of 64); its fp32 sums of sparse tile slot row q
+  // (64-row tile mtg of the sparse list, row r: q = 64 * mtg + r) go to
+  // part[(s * part_rows + q) * width + column], width 2*Fe (gate/up, gate
+  // columns first) or Hd (down).
+  float* part;
+  int64_t part_rows, k_per;
 };
 
 __global__ __launch_bounds__(256) void moe_count_kernel(const MoeArgs a) {
@@ -157,6 +164,133 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const MoeArgs a) {
     }
     a.pick_row[t * a.topk + k] = row;
   }
+}
+
+// Two-kernel routing (T <= MOE_ROUTE_TOKENS, E_loc <= MOE_ROUTE_EXPERTS),
+// with the results of the four kernels above.  Blocks of 256 tokens:
+//  1. each block counts its tokens' picks per local expert in LDS (one
+//     column per thread), scans every expert's column in token order, and
+//     gives each pick its rank among the block's picks of that expert (in
+//     (token, slot) order), kept in pick_row; the block's totals go to
+//     cnt[block, expert];
+//  2. each block sums the totals of the blocks before it (its base per
+//     expert) and of all blocks (the expert's row count), scans those over
+//     experts (offsets; block 0 writes offsets, counts and tile starts) and
+//     places every local pick at row offset + base + rank.
+constexpr int MOE_ROUTE_TOKENS = 65536, MOE_ROUTE_EXPERTS = 64;
+
+__global__ __launch_bounds__(256) void moe_route_rank_kernel(const MoeArgs a) {
+  __shared__ int sc[MOE_ROUTE_EXPERTS][257];  // padded: a wave's 4-value runs fall in distinct banks
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + tid;
+  for (int e = 0; e < a.E_loc; ++e) sc[e][tid] = 0;
+  const int64_t tc = t < a.T ? t : a.T - 1;  // every load issued, values of t >= T unused
+  for (int k = 0; k < a.topk; ++k) {
+    const int e = a.ids[tc * a.topk + k] - a.e_start;
+    if (t < a.T && e >= 0 && e < a.E_loc) sc[e][tid] += 1;
+  }
+  __syncthreads();
+  // Exclusive scan of each expert's 256 counts: wave w takes experts w, w+4,
+  // ...; lane l sums values 4l .. 4l+3, the wave scans the lane sums.
+  for (int e = wave; e < a.E_loc; e += 4) {
+    int v[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = sc[e][4 * lane + i];
+      sum += v[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += n;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[e][4 * lane + i] = run;
+      run += v[i];
+    }
+    if (lane == 63) a.cnt[static_cast<int64_t>(blockIdx.x) * a.E_loc + e] = incl;
+  }
+  __syncthreads();
+  if (t >= a.T) return;
+  for (int k = 0; k < a.topk; ++k) {
+    const int e = a.ids[t * a.topk + k] - a.e_start;
+    if (e >= 0 && e < a.E_loc) a.pick_row[t * a.topk + k] = sc[e][tid]++;  // a token's repeats in slot order
+  }
+}
+
+__global__ __launch_bounds__(256) void moe_route_place_kernel(const MoeArgs a) {
+  __shared__ int base[MOE_ROUTE_EXPERTS], off[MOE_ROUTE_EXPERTS], tot[MOE_ROUTE_EXPERTS];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x, nb = gridDim.x;
+  if (tid < a.E_loc) {
+    int before = 0, all = 0;
+    for (int b2 = 0; b2 < nb; ++b2) {
+      const int c = a.cnt[static_cast<int64_t>(b2) * a.E_loc + tid];
+      before += b2 < b ? c : 0;
+      all += c;
+    }
+    base[tid] = before;
+    tot[tid] = all;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, tiles = 0, dense = 0, sparse = 0;
+    for (int e = 0; e < a.E_loc; ++e) {
+      const int c = tot[e];
+      off[e] = o;
+      if (b == 0) {
+        a.offsets[e] = o;
+        a.counts[e] = c;
+        a.tile_start[e] = tiles;
+        if (a.tile_start_d != nullptr) {
+          a.tile_start_d[e] = dense;
+          a.tile_start_s[e] = sparse;
+        }
+      }
+      o += c;
+      tiles += (c + MOE_BM - 1) / MOE_BM;
+      if (c < MOE_SPARSE_ROWS) sparse += (c + MOE_BM_SPARSE - 1) / MOE_BM_SPARSE;
+      else dense += (c + MOE_BM - 1) / MOE_BM;
+    }
+    if (b == 0) {
+      a.offsets[a.E_loc] = o;
+      a.tile_start[a.E_loc] = tiles;
+      if (a.tile_start_d != nullptr) {
+        a.tile_start_d[a.E_loc] = dense;
+        a.tile_start_s[a.E_loc] = sparse;
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(b) * 256 + tid;
+  if (t >= a.T) return;
+  for (int k = 0; k < a.topk; ++k) {
+    const int64_t p = t * a.topk + k;
+    const int e = a.ids[p] - a.e_start;
+    int32_t row = -1;
+    if (e >= 0 && e < a.E_loc) {
+      row = off[e] + base[e] + a.pick_row[p];
+      a.perm[row] = static_cast<int32_t>(p);
+    }
+    a.pick_row[p] = row;
+  }
+}
+
+static void launch_routing(const MoeArgs& a, hipStream_t s) {
+  if (a.T <= MOE_ROUTE_TOKENS && a.E_loc <= MOE_ROUTE_EXPERTS) {
+    const unsigned nb = static_cast<unsigned>(ceil_div(a.T, 256));
+    moe_route_rank_kernel<<<nb, 256, 0, s>>>(a);
+    moe_route_place_kernel<<<nb, 256, 0, s>>>(a);
+    return;
+  }
+  const unsigned tgrid = static_cast<unsigned>(ceil_div(a.T, 256));
+  moe_count_kernel<<<tgrid, 256, 0, s>>>(a);
+  moe_scan_kernel<<<static_cast<unsigned>(a.E_loc), 1024, 0, s>>>(a);
+  moe_offsets_kernel<<<1, 64, 0, s>>>(a);
+  moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
 }
 
 // Direct global -> LDS loader for a 256-row x 64-k operand tile whose rows
@@ -283,7 +417,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __rest
 // MX: both operands are MXFP8 (E4M3 codes, k-tiles of 128 codes = the same
 // 128-byte LDS rows), two scaled 32x32x64 MFMA steps per k-tile, each row's
 // four block exponents of a k-tile read as one dword per fragment row.
-template <int MODE, bool MX, bool SAVE = false, int BMT = MOE_BM>
+template <int MODE, bool MX, bool SAVE = false, int BMT = MOE_BM, bool SPLIT = false>
 __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   constexpr int BM = BMT, BN = MOE_BN, NT = 512, WC = 4, WM = BM / 2, WN = BN / WC;
   constexpr int TM = WM / 32, TN = WN / 32, A_SLOTS = BM * 8, B_SLOTS = BN * 8;
@@ -292,6 +426,7 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   // A row (256) and B row (256), 2 KiB, loaded with the tile.
   constexpr int S_SLOTS = MX ? 128 : 0;
   static_assert(!MX || (BM == 256 && BN == 256), "the exponent region covers 256 + 256 rows");
+  static_assert(!SPLIT || (!MX && !SAVE && BM == MOE_BM_SPARSE), "split-K runs the bf16 sparse launches");
   __shared__ uint4 lds[2][A_SLOTS + B_SLOTS + S_SLOTS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / WC, wn = wave % WC;
 
@@ -345,11 +480,14 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
             [&](int r) -> int64_t { return n0 + r < a.Hd ? static_cast<int64_t>(r) * KU : -1; });
   }
   constexpr int NI = GatherDma<BM, NT>::NI + GatherDma<BN, NT>::NI;
-  const int nk = static_cast<int>((KU + 63) / 64);
+  // This workgroup's k-range (all of K, or split blockIdx.y's share).
+  const int64_t kb = SPLIT ? static_cast<int64_t>(blockIdx.y) * a.k_per : 0;
+  const int64_t ke = SPLIT ? min(KU, kb + a.k_per) : KU;
+  const int nk = ke > kb ? static_cast<int>((ke - kb + 63) / 64) : 0;
   auto fill = [&](uint4* buf, int t) {
-    const int64_t k0 = 64 * static_cast<int64_t>(t);
-    da.issue(buf, k0, KU, t < nk);
-    db.issue(buf + A_SLOTS, k0, KU, t < nk);
+    const int64_t k0 = kb + 64 * static_cast<int64_t>(t);
+    da.issue(buf, k0, ke, t < nk);
+    db.issue(buf + A_SLOTS, k0, ke, t < nk);
   };
 
   f32x16_t acc[TM][TN];
@@ -531,6 +669,34 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   wait_vm_lds();  // the trailing (all-zero) loads write LDS the epilogue reuses
   __syncthreads();
 
+  if constexpr (SPLIT) {
+    // fp32 sums of this k-range straight from the accumulators (lane l holds
+    // column l % 32 of each 32x32 tile: 128 contiguous bytes per tile row);
+    // the reduce applies the epilogue.
+    const int64_t width = MODE == 0 ? 2 * a.Fe : a.Hd;
+    float* P = a.part + (static_cast<int64_t>(blockIdx.y) * a.part_rows + static_cast<int64_t>(mtg) * BM) * width;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      int64_t col;
+      if constexpr (MODE == 0) {
+        const int64_t jcol = static_cast<int64_t>(nt) * (BN / 2) + wn * (WN / 2) + (lane & 31);
+        col = jcol < a.Fe ? jcol + j * a.Fe : -1;
+      } else {
+        const int64_t n = n0 + wn * WN + j * 32 + (lane & 31);
+        col = n < a.Hd ? n : -1;
+      }
+      if (col < 0) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = wm * WM + i * 32 + mfma_row(r, lane);
+          if (row0 + rr < row_end) P[rr * width + col] = acc[i][j][r];
+        }
+    }
+    return;
+  }
+
   // Epilogue through a wave-private LDS strip, one 32-row strip at a time (as
   // in the dense GEMM; no barrier needed).  MODE 0: lane l holds the gate and
   // the up value of the same output column (l % 32) in its two accumulator
@@ -615,6 +781,67 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
       }
     }
   }
+  }
+}
+
+__device__ __forceinline__ void unpack_f32x8(const float* p, float* f) {
+  const float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+}
+
+// Reduce of the split-K sparse launches: the row's fp32 sums over the splits
+// in split order, then the epilogue the unsplit kernel applies.  MODE 0:
+// act = silu(gate) * up (times the routing weight with w_on_act), bf16, and
+// with SAVE the gate and up sums as bf16 pre-activations; MODE 1: yperm in
+// bf16.  Thread: 8 columns of one slot row; slots without a row exit.
+template <int MODE, bool SAVE>
+__global__ __launch_bounds__(256) void moe_splitk_reduce_kernel(const MoeArgs a, int splits) {
+  constexpr int SB = MOE_BM_SPARSE;
+  const int64_t nc = MODE == 0 ? a.Fe : a.Hd, width = MODE == 0 ? 2 * a.Fe : a.Hd, vpr = nc / 8;
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t q = v / vpr;
+  if (q >= a.part_rows) return;
+  const int64_t c = (v - q * vpr) * 8;
+  const int32_t* ts = a.tile_start_s;
+  const int mtg = static_cast<int>(q / SB);
+  if (mtg >= ts[a.E_loc]) return;
+  int e = 0;
+  while (e + 1 < a.E_loc && ts[e + 1] <= mtg) ++e;
+  const int64_t grow = a.offsets[e] + static_cast<int64_t>(mtg - ts[e]) * SB + (q - static_cast<int64_t>(mtg) * SB);
+  if (grow >= a.offsets[e + 1]) return;
+  float x[8], u[8];
+  for (int sp = 0; sp < splits; ++sp) {
+    const float* p = a.part + (static_cast<int64_t>(sp) * a.part_rows + q) * width + c;
+    float px[8], pu[8];
+    unpack_f32x8(p, px);
+    if constexpr (MODE == 0) unpack_f32x8(p + a.Fe, pu);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = sp == 0 ? px[i] : x[i] + px[i];
+      if constexpr (MODE == 0) u[i] = sp == 0 ? pu[i] : u[i] + pu[i];
+    }
+  }
+  if constexpr (MODE == 0) {
+    if constexpr (SAVE) {
+      *reinterpret_cast<uint4*>(a.gu_save + grow * 2 * a.Fe + c) = pack8(x);
+      *reinterpret_cast<uint4*>(a.gu_save + grow * 2 * a.Fe + a.Fe + c) = pack8(u);
+    }
+    // The same SwiGLU evaluation as the grouped GEMM's epilogue.
+    float val[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float ex = __builtin_amdgcn_exp2f(-1.4426950408889634f * x[i]);
+      val[i] = x[i] * __builtin_amdgcn_rcpf(1.0f + ex) * u[i];
+    }
+    if (a.w_on_act) {
+      const float wr = a.w[a.perm[grow]];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) val[i] *= wr;
+    }
+    *reinterpret_cast<uint4*>(a.act + grow * a.Fe + c) = pack8(val);
+  } else {
+    *reinterpret_cast<uint4*>(a.yperm + grow * a.Hd + c) = pack8(x);
   }
 }
 
@@ -740,10 +967,24 @@ static void launch_unpermute(const MoeArgs& a, hipStream_t s) {
 
 struct MoeLayout {
   size_t cnt, pick_row, perm, offsets, tile_start, tile_start_d, tile_start_s, counts, act, yperm, xq, xs, aq, as,
-      total;
+      part, total;
 };
 
 static int64_t mx_scale_width(int64_t K) { return 4 * ceil_div(K, 128); }
+
+// k-range splits of a bf16 sparse launch (64-row tiles) over a reduction of
+// K values.  A sparse shard has one tile-row per expert, so its launches have
+// few workgroups, each streaming a slice of the experts' weights; every split
+// adds a full set of them.  Each split keeps at least 8 k-tiles.
+#ifndef MP_MOE_SPARSE_KSPLIT
+#define MP_MOE_SPARSE_KSPLIT 2
+#endif
+static int sparse_splits(int64_t K) {
+  const int64_t nk = ceil_div(K, 64);
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(MP_MOE_SPARSE_KSPLIT, nk / 8)));
+}
+// Slot rows of the sparse tiles (MOE_MAX_STILES per expert).
+static int64_t sparse_slot_rows(int E_loc) { return static_cast<int64_t>(MOE_MAX_STILES) * E_loc * MOE_BM_SPARSE; }
 
 // With mx, the quantised token rows and activations follow the bf16 buffers.
 static MoeLayout moe_layout(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_loc, bool mx = false) {
@@ -765,6 +1006,11 @@ static MoeLayout moe_layout(int64_t T, int64_t Hd, int64_t Fe, int topk, int E_l
   L.counts = take(static_cast<size_t>(E_loc) * 4);
   L.act = take(mx ? 0 : static_cast<size_t>(r_cap * Fe) * 2);  // MXFP8 keeps only the quantised activation
   L.yperm = take(static_cast<size_t>(r_cap * Hd) * 2);
+  // fp32 partial sums of the split sparse launches (one launch at a time).
+  const int64_t part_w = mx ? 0
+                            : std::max<int64_t>(sparse_splits(Hd) > 1 ? sparse_splits(Hd) * 2 * Fe : 0,
+                                                sparse_splits(Fe) > 1 ? sparse_splits(Fe) * Hd : 0);
+  L.part = take(static_cast<size_t>(part_w * sparse_slot_rows(E_loc)) * 4);
   if (mx) {
     L.xq = take(static_cast<size_t>(T * Hd));
     L.xs = take(static_cast<size_t>(T * mx_scale_width(Hd)));
@@ -835,11 +1081,9 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   a.yperm = reinterpret_cast<uint16_t*>(w + L.yperm);
   a.w_on_act = w_on_act ? 1 : 0;
   a.gu_save = static_cast<uint16_t*>(gu_save);
-  const unsigned tgrid = static_cast<unsigned>(ceil_div(T, 256));
-  moe_count_kernel<<<tgrid, 256, 0, s>>>(a);
-  moe_scan_kernel<<<static_cast<unsigned>(E_loc), 1024, 0, s>>>(a);
-  moe_offsets_kernel<<<1, 64, 0, s>>>(a);
-  moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
+  a.part = reinterpret_cast<float*>(w + L.part);
+  a.part_rows = sparse_slot_rows(E_loc);
+  launch_routing(a, s);
   // Dense experts' 256-row tiles and sparse experts' 64-row tiles (each
   // sparse expert has at most MOE_MAX_STILES); the two launches cover
   // disjoint rows.
@@ -848,16 +1092,33 @@ static int grouped_expert_gemm(const char* fn, bool w_on_act, int64_t T, int64_t
   constexpr int SB = MOE_BM_SPARSE;
   a.tiles_n = static_cast<int>(ceil_div(Fe, MOE_BN / 2));
   const unsigned gd0 = static_cast<unsigned>(max_mtiles * a.tiles_n), gs0 = static_cast<unsigned>(max_stiles * a.tiles_n);
-  if (gu_save != nullptr) {
-    moe_gemm_kernel<0, false, true><<<gd0, 512, 0, s>>>(a);
+  // A split sparse launch writes fp32 partial sums; its reduce (one thread per
+  // 8 columns of every sparse slot row) applies the epilogue.
+  auto split_launch = [&](auto gemm, auto reduce, unsigned grid, int64_t K, int64_t nc) {
+    const int ks = sparse_splits(K);
+    a.k_per = ceil_div(ceil_div(K, 64), ks) * 64;
+    gemm<<<dim3(grid, static_cast<unsigned>(ks)), 512, 0, s>>>(a);
+    reduce<<<static_cast<unsigned>(ceil_div(a.part_rows * (nc / 8), 256)), 256, 0, s>>>(a, ks);
+  };
+  if (gu_save != nullptr) moe_gemm_kernel<0, false, true><<<gd0, 512, 0, s>>>(a);
+  else moe_gemm_kernel<0, false><<<gd0, 512, 0, s>>>(a);
+  if (sparse_splits(Hd) > 1) {
+    if (gu_save != nullptr)
+      split_launch(moe_gemm_kernel<0, false, false, SB, true>, moe_splitk_reduce_kernel<0, true>, gs0, Hd, Fe);
+    else
+      split_launch(moe_gemm_kernel<0, false, false, SB, true>, moe_splitk_reduce_kernel<0, false>, gs0, Hd, Fe);
+  } else if (gu_save != nullptr) {
     moe_gemm_kernel<0, false, true, SB><<<gs0, 512, 0, s>>>(a);
   } else {
-    moe_gemm_kernel<0, false><<<gd0, 512, 0, s>>>(a);
     moe_gemm_kernel<0, false, false, SB><<<gs0, 512, 0, s>>>(a);
   }
   a.tiles_n = static_cast<int>(ceil_div(Hd, MOE_BN));
-  moe_gemm_kernel<1, false><<<static_cast<unsigned>(max_mtiles * a.tiles_n), 512, 0, s>>>(a);
-  moe_gemm_kernel<1, false, false, SB><<<static_cast<unsigned>(max_stiles * a.tiles_n), 512, 0, s>>>(a);
+  const unsigned gd1 = static_cast<unsigned>(max_mtiles * a.tiles_n), gs1 = static_cast<unsigned>(max_stiles * a.tiles_n);
+  moe_gemm_kernel<1, false><<<gd1, 512, 0, s>>>(a);
+  if (sparse_splits(Fe) > 1)
+    split_launch(moe_gemm_kernel<1, false, false, SB, true>, moe_splitk_reduce_kernel<1, false>, gs1, Fe, Hd);
+  else
+    moe_gemm_kernel<1, false, false, SB><<<gs1, 512, 0, s>>>(a);
   launch_unpermute(a, s);
   return check_launch(fn);
 }
@@ -1143,11 +1404,7 @@ extern "C" int mp_grouped_expert_gemm_mxfp8(int64_t T, int64_t Hd, int64_t Fe, i
   a.ds = W_d_s;
   a.aq = aq;
   a.as = as;
-  const unsigned tgrid = static_cast<unsigned>(ceil_div(T, 256));
-  moe_count_kernel<<<tgrid, 256, 0, s>>>(a);
-  moe_scan_kernel<<<static_cast<unsigned>(E_loc), 1024, 0, s>>>(a);
-  moe_offsets_kernel<<<1, 64, 0, s>>>(a);
-  moe_scatter_kernel<<<tgrid, 256, 0, s>>>(a);
+  launch_routing(a, s);
   // Token rows quantised once along the hidden dimension (the expert GEMMs'
   // reduction dimension); the weights arrive quantised.
   mx_quantize_kernel<<<static_cast<unsigned>(ceil_div(T * (Hd / 8), 256)), 256, 0, s>>>(a.X, Hd, T, Hd, xq, xs,

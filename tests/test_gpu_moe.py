@@ -43,6 +43,9 @@ CASES = [
     (33, 64, 64, 16, 4, 12, 1),     # top-1
     (700, 200, 264, 4, 2, 1, 2),    # >256 rows per expert, ragged k-tiles in both GEMMs
     (513, 72, 520, 8, 3, 2, 4),     # K = 72 (one full and one 8-wide k-tile), 5 act tiles
+    (300, 1096, 1032, 32, 8, 0, 2), # sparse experts with both GEMMs split over k (ragged last k-tiles)
+    (8500, 64, 64, 16, 4, 2, 8),    # 34 blocks of 256 tokens in the two-kernel routing
+    (200, 64, 64, 80, 70, 3, 4),    # 70 local experts: more than the two-kernel routing takes (four kernels)
 ]
 FORMS = {"weighted_unpermute": (lambda: mp.mp_grouped_expert_gemm, O.moe_forward),
          "weighted_act": (lambda: mp.mp_grouped_expert_gemm_weighted_act, O.moe_forward_weighted_act)}
@@ -97,3 +100,61 @@ def test_moe_shard_full_size(form):
     sub_out = oracle_fn(f64(inp["x"])[toks], inp["topk_ids"].numpy()[toks], inp["topk_w"].numpy()[toks],
                         f64(inp["w_gu"]), f64(inp["w_d"]), 0)[0]
     assert rel_frobenius(f64(out)[toks], sub_out) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("form", list(FORMS))
+def test_split_sparse_experts_beside_dense(form):
+    """One dense expert (300 rows: a full and a partial 256-row tile) beside
+    sparse ones (about 60 rows) whose 64-row launches are split over k; the
+    two kinds of launch write disjoint rows."""
+    say("moe dense + split sparse", form)
+    T, Hd, Fe, experts, e_local, topk = 600, 1024, 1024, 16, 4, 2
+    rng = np.random.default_rng(11)
+    ids = np.empty((T, topk), dtype=np.int32)
+    for t in range(T):
+        first = 0 if t < 300 else int(rng.integers(1, experts))
+        rest = rng.permutation([e for e in range(experts) if e != first])[: topk - 1]
+        ids[t] = [first, *rest]
+    wts = rng.random((T, topk)).astype(np.float32)
+    w = torch.from_numpy(wts / wts.sum(axis=1, keepdims=True))
+    ids = torch.from_numpy(ids)
+    x = torch.from_numpy(rng.standard_normal((T, Hd), dtype=np.float32)).to(torch.bfloat16)
+    wgu = torch.from_numpy(rng.standard_normal((e_local, 2 * Fe, Hd), dtype=np.float32) * 0.05).to(torch.bfloat16)
+    wd = torch.from_numpy(rng.standard_normal((e_local, Hd, Fe), dtype=np.float32) * 0.05).to(torch.bfloat16)
+    fn, oracle_fn = FORMS[form]
+    out, perm, offs = run(x, ids, w, wgu, wd, 0, fn())
+    want, counts, woffs, picks, _ = oracle_fn(f64(x), ids.numpy(), w.numpy(), f64(wgu), f64(wd), 0)
+    assert counts[0] >= 256 and 0 < counts[1:].max() < 192  # one dense expert, the rest sparse
+    assert np.array_equal(offs, woffs) and np.array_equal(perm[:picks.size], picks)
+    assert rel_frobenius(f64(out), want) <= TOL["bf16"]
+    # Rows of each expert separately: a wrong sparse slot would misplace whole rows.
+    for e in range(e_local):
+        toks = np.nonzero((ids.numpy() == e).any(axis=1))[0]
+        if toks.size:
+            assert rel_frobenius(f64(out)[toks], want[toks]) <= TOL["bf16"], e
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("form", list(FORMS))
+def test_moe_median_shard_full_size(form):
+    """The median expert-parallel shard of the full-size routing (experts
+    128-135 of 256: a few hundred rows, every expert sparse, both GEMMs split
+    over k) with the timed configuration's weights; outputs of 48 sampled
+    tokens that have a pick in the shard, through the oracle."""
+    say("moe median shard full size", form)
+    fn, oracle_fn = FORMS[form]
+    wl = S.WORKLOADS["moe"]
+    inp = S.moe_inputs(wl)
+    e_med = wl.experts // 2
+    out, perm, offs = run(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_gu"], inp["w_d"], e_med, fn())
+    ids = inp["topk_ids"].numpy()
+    counts, woffs, picks = O.moe_permutation(ids, e_med, wl.e_local)
+    assert 0 < counts.max() < 192
+    assert np.array_equal(offs, woffs) and np.array_equal(perm[:picks.size], picks)
+    hit = np.nonzero(((ids >= e_med) & (ids < e_med + wl.e_local)).any(axis=1))[0]
+    toks = np.random.default_rng(4).choice(hit, min(48, hit.size), replace=False)
+    sub_out = oracle_fn(f64(inp["x"])[toks], ids[toks], inp["topk_w"].numpy()[toks],
+                        f64(inp["w_gu"]), f64(inp["w_d"]), e_med)[0]
+    assert rel_frobenius(f64(out)[toks], sub_out) <= TOL["bf16"]
+    miss = np.setdiff1d(np.arange(wl.T), hit)
+    assert torch.all(out.float()[torch.from_numpy(miss)] == 0)

@@ -68,6 +68,7 @@ CASES = [
     (33, 64, 64, 16, 4, 12, 1),     # top-1
     (700, 200, 264, 4, 2, 1, 2),    # >256 rows per expert: several row tiles and ragged k-tiles
     (513, 72, 520, 8, 3, 2, 4),     # Hd = 72 (one full and one 8-wide k-tile), 3 column tiles of d act
+    (300, 1096, 1032, 32, 8, 0, 2), # sparse experts: split-K training forward (pre-activations from the reduce)
 ]
 
 
