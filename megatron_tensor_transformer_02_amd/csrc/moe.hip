@@ -184,10 +184,19 @@ __global__ __launch_bounds__(256) void moe_route_rank_kernel(const MoeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + tid;
   for (int e = 0; e < a.E_loc; ++e) sc[e][tid] = 0;
-  const int64_t tc = t < a.T ? t : a.T - 1;  // every load issued, values of t >= T unused
-  for (int k = 0; k < a.topk; ++k) {
-    const int e = a.ids[tc * a.topk + k] - a.e_start;
-    if (t < a.T && e >= 0 && e < a.E_loc) sc[e][tid] += 1;
+  // A token's picks are loaded 8 at a time before any is used (every load
+  // issued: indexes clamped in range, values past the token's picks unused).
+  const int64_t tc = t < a.T ? t : a.T - 1;
+  const int64_t plast = a.T * a.topk - 1;
+  int le[8];  // local expert of picks k0 .. k0+7 of this token, or -1
+  for (int k0 = 0; k0 < a.topk; k0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) le[u] = a.ids[min(tc * a.topk + k0 + u, plast)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = le[u] - a.e_start;
+      if (t < a.T && k0 + u < a.topk && e >= 0 && e < a.E_loc) sc[e][tid] += 1;
+    }
   }
   __syncthreads();
   // Exclusive scan of each expert's 256 counts: wave w takes experts w, w+4,
@@ -215,9 +224,15 @@ __global__ __launch_bounds__(256) void moe_route_rank_kernel(const MoeArgs a) {
   }
   __syncthreads();
   if (t >= a.T) return;
-  for (int k = 0; k < a.topk; ++k) {
-    const int e = a.ids[t * a.topk + k] - a.e_start;
-    if (e >= 0 && e < a.E_loc) a.pick_row[t * a.topk + k] = sc[e][tid]++;  // a token's repeats in slot order
+  for (int k0 = 0; k0 < a.topk; k0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) le[u] = a.ids[min(t * a.topk + k0 + u, plast)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = le[u] - a.e_start;
+      if (k0 + u < a.topk && e >= 0 && e < a.E_loc)
+        a.pick_row[t * a.topk + k0 + u] = sc[e][tid]++;  // a token's repeats in slot order
+    }
   }
 }
 
@@ -227,10 +242,16 @@ __global__ __launch_bounds__(256) void moe_route_place_kernel(const MoeArgs a) {
   const int b = blockIdx.x, nb = gridDim.x;
   if (tid < a.E_loc) {
     int before = 0, all = 0;
-    for (int b2 = 0; b2 < nb; ++b2) {
-      const int c = a.cnt[static_cast<int64_t>(b2) * a.E_loc + tid];
-      before += b2 < b ? c : 0;
-      all += c;
+    for (int b0 = 0; b0 < nb; b0 += 8) {  // 8 blocks' totals loaded before any is used
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = a.cnt[static_cast<int64_t>(min(b0 + u, nb - 1)) * a.E_loc + tid];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cu = b0 + u < nb ? c[u] : 0;
+        before += b0 + u < b ? cu : 0;
+        all += cu;
+      }
     }
     base[tid] = before;
     tot[tid] = all;
@@ -267,15 +288,27 @@ __global__ __launch_bounds__(256) void moe_route_place_kernel(const MoeArgs a) {
   __syncthreads();
   const int64_t t = static_cast<int64_t>(b) * 256 + tid;
   if (t >= a.T) return;
-  for (int k = 0; k < a.topk; ++k) {
-    const int64_t p = t * a.topk + k;
-    const int e = a.ids[p] - a.e_start;
-    int32_t row = -1;
-    if (e >= 0 && e < a.E_loc) {
-      row = off[e] + base[e] + a.pick_row[p];
-      a.perm[row] = static_cast<int32_t>(p);
+  const int64_t plast = a.T * a.topk - 1;
+  for (int k0 = 0; k0 < a.topk; k0 += 8) {
+    int id[8], rk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t p = min(t * a.topk + k0 + u, plast);
+      id[u] = a.ids[p];
+      rk[u] = a.pick_row[p];
     }
-    a.pick_row[p] = row;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (k0 + u >= a.topk) break;
+      const int64_t p = t * a.topk + k0 + u;
+      const int e = id[u] - a.e_start;
+      int32_t row = -1;
+      if (e >= 0 && e < a.E_loc) {
+        row = off[e] + base[e] + rk[u];
+        a.perm[row] = static_cast<int32_t>(p);
+      }
+      a.pick_row[p] = row;
+    }
   }
 }
 
@@ -846,47 +879,73 @@ __global__ __launch_bounds__(256) void moe_splitk_reduce_kernel(const MoeArgs a,
 }
 
 // out[t, 8c..8c+7] = sum_k w[t,k] * yperm[row(t,k), 8c..8c+7] (k ascending;
-// w = 1 when the weights were applied to the activation).  With KMAX > 0
-// (topk <= KMAX) every pick's row index and row chunk is loaded before the
-// sum, so the loads of one token overlap; the sum keeps the k order.
+// w = 1 when the weights were applied to the activation).  A token's row is
+// split over tpt = ceil(Hd / 32) threads, thread i owning chunks i, i + tpt,
+// i + 2 tpt, i + 3 tpt of 8 columns (consecutive threads, consecutive
+// chunks), so the token's pick rows and weights are loaded once for four
+// chunks.  With KMAX > 0 (topk <= KMAX) every pick's row index, weight and
+// row chunks are loaded before the sum, so the loads of one token overlap;
+// the sum keeps the k order.
+#ifndef MP_UNPERM_CH
+#define MP_UNPERM_CH 4
+#endif
+constexpr int UNPERM_CH = MP_UNPERM_CH;
 template <int KMAX>
 __global__ __launch_bounds__(256) void moe_unpermute_kernel(const MoeArgs a) {
-  const int64_t vpr = a.Hd / 8;
+  const int64_t vpr = a.Hd / 8, tpt = (vpr + UNPERM_CH - 1) / UNPERM_CH;
   const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (v >= a.T * vpr) return;
-  const int64_t t = v / vpr, c = (v - t * vpr) * 8;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (v >= a.T * tpt) return;
+  const int64_t t = v / tpt, i = v - t * tpt;
+  float acc[UNPERM_CH][8] = {};
   if constexpr (KMAX > 0) {
     int32_t rows[KMAX];
-    uint4 yv[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) rows[k] = k < a.topk ? a.pick_row[t * a.topk + k] : -1;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      yv[k] = rows[k] >= 0 ? *reinterpret_cast<const uint4*>(a.yperm + static_cast<int64_t>(rows[k]) * a.Hd + c)
-                           : make_uint4(0, 0, 0, 0);
+    float wk[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-      if (rows[k] < 0) continue;
-      const float wk = a.w_on_act ? 1.0f : a.w[t * a.topk + k];
-      float y[8];
-      unpack8(yv[k], y);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += wk * y[q];
+      rows[k] = k < a.topk ? a.pick_row[t * a.topk + k] : -1;
+      wk[k] = k < a.topk && !a.w_on_act ? a.w[t * a.topk + k] : 1.0f;
     }
-    *reinterpret_cast<uint4*>(a.out + t * a.Hd + c) = pack8(acc);
-    return;
-  }
-  for (int k = 0; k < a.topk; ++k) {
-    const int32_t row = a.pick_row[t * a.topk + k];
-    if (row < 0) continue;
-    const float wk = a.w_on_act ? 1.0f : a.w[t * a.topk + k];
-    float y[8];
-    unpack8(*reinterpret_cast<const uint4*>(a.yperm + static_cast<int64_t>(row) * a.Hd + c), y);
+    uint4 yv[UNPERM_CH][KMAX];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += wk * y[q];
+    for (int j = 0; j < UNPERM_CH; ++j) {
+      const int64_t ch = i + j * tpt;
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        yv[j][k] = rows[k] >= 0 && ch < vpr
+                       ? *reinterpret_cast<const uint4*>(a.yperm + static_cast<int64_t>(rows[k]) * a.Hd + ch * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < UNPERM_CH; ++j)
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        if (rows[k] < 0) continue;
+        float y[8];
+        unpack8(yv[j][k], y);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[j][q] += wk[k] * y[q];
+      }
+  } else {
+    for (int k = 0; k < a.topk; ++k) {
+      const int32_t row = a.pick_row[t * a.topk + k];
+      if (row < 0) continue;
+      const float wk = a.w_on_act ? 1.0f : a.w[t * a.topk + k];
+#pragma unroll
+      for (int j = 0; j < UNPERM_CH; ++j) {
+        const int64_t ch = i + j * tpt;
+        if (ch >= vpr) break;
+        float y[8];
+        unpack8(*reinterpret_cast<const uint4*>(a.yperm + static_cast<int64_t>(row) * a.Hd + ch * 8), y);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[j][q] += wk * y[q];
+      }
+    }
   }
-  *reinterpret_cast<uint4*>(a.out + t * a.Hd + c) = pack8(acc);
+#pragma unroll
+  for (int j = 0; j < UNPERM_CH; ++j) {
+    const int64_t ch = i + j * tpt;
+    if (ch < vpr) *reinterpret_cast<uint4*>(a.out + t * a.Hd + ch * 8) = pack8(acc[j]);
+  }
 }
 
 // Backward, one wave per permuted row r < R: with pick p = perm[r] of token
@@ -960,7 +1019,7 @@ __global__ __launch_bounds__(256) void moe_bwd_dw_zero_kernel(const MoeArgs a) {
 }
 
 static void launch_unpermute(const MoeArgs& a, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>(ceil_div(a.T * (a.Hd / 8), 256));
+  const unsigned grid = static_cast<unsigned>(ceil_div(a.T * ceil_div(a.Hd / 8, UNPERM_CH), 256));
   if (a.topk <= 8) moe_unpermute_kernel<8><<<grid, 256, 0, s>>>(a);
   else moe_unpermute_kernel<0><<<grid, 256, 0, s>>>(a);
 }
