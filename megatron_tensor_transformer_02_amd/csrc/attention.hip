@@ -65,10 +65,20 @@ struct RowTile {
   }
 };
 
+// Column group of k-group g (lane / 16) in a 32-column step: 8 * kgrp(g),
+// kgrp = (0, 3, 1, 2).  The MFMA sums over the step's 32 columns in any
+// order, so both operands only have to agree on it.  A 16-byte LDS read
+// serves lanes {0-3, 12-15, 20-27} (and the matching sets) in one cycle
+// (measured on gfx950), which pairs rows of k-groups 0 and 1 (and 2 and 3)
+// whose swizzles differ by an odd-weight value; chunks whose indexes differ
+// by 3 then fall in distinct banks, where the plain order (chunks 0, 1)
+// put every such pair in the same banks: 4 conflict cycles per read.
+__device__ __forceinline__ int kgrp(int g) { return (0x2130 >> (4 * g)) & 3; }
+
 // Row fragment (A or B operand) of a row tile: row r0 + lane%16, columns
-// 32*st + 8*(lane/16) .. +7.
+// 32*st + 8*kgrp(lane/16) .. +7.
 __device__ __forceinline__ uint4 row_frag(const uint4* tile, int r0, int st, int lane) {
-  const int c = 32 * st + 8 * (lane >> 4);
+  const int c = 32 * st + 8 * kgrp(lane >> 4);
   return tile[(c >> 6) * 512 + lds_slot(r0 + (lane & 15), (c & 63) >> 3)];
 }
 
@@ -121,9 +131,9 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
   const int q0 = qb * BQ, qw0 = q0 + wave * 16, qi = qw0 + qc;
   const bool qvalid = qi < a.L;
 
-  uint4 qf[KS];  // Q^T as the B operand: query qi, d = 32 st + 8 g .. +7
+  uint4 qf[KS];  // Q^T as the B operand: query qi, d = 32 st + 8 kgrp(g) .. +7
 #pragma unroll
-  for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * g, qvalid);
+  for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * kgrp(g), qvalid);
 
   const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
   const BufRes rk = make_bufres(base + HD + hh * D, batch_bytes - (HD + hh * D) * 2);
@@ -240,9 +250,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
   const int q0 = qb * BQ, qw0 = q0 + qt * 16, qi = qw0 + qc;
   const bool qvalid = qi < a.L;
 
-  uint4 qf[KS];  // Q^T as the B operand: query qi, d = 32 st + 8 g .. +7
+  uint4 qf[KS];  // Q^T as the B operand: query qi, d = 32 st + 8 kgrp(g) .. +7
 #pragma unroll
-  for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * g, qvalid);
+  for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * kgrp(g), qvalid);
 
   const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
   const BufRes rk = make_bufres(base + HD + hh * D, batch_bytes - (HD + hh * D) * 2);
@@ -436,8 +446,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
   uint4 qf[KS], dof[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
-    qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * g, qvalid);
-    dof[st] = ld16_or_zero(a.dctx + trow * HD + hh * D + 32 * st + 8 * g, qvalid);
+    qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * kgrp(g), qvalid);
+    dof[st] = ld16_or_zero(a.dctx + trow * HD + hh * D + 32 * st + 8 * kgrp(g), qvalid);
   }
   const int64_t sidx = (static_cast<int64_t>(b) * a.h + hh) * a.L + qi;
   const float lse2 = qvalid ? a.lse[sidx] * kLog2eA : 0.0f;
@@ -541,11 +551,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int k0 = kb * BK, kw0 = k0 + grp * 16, kj = kw0 + kc;
   const bool kvalid = kj < a.L;
 
-  uint4 kf[KS], vf[KS];  // K^T, V^T as B operands: key kj, d = 32 st + 8 g .. +7
+  uint4 kf[KS], vf[KS];  // K^T, V^T as B operands: key kj, d = 32 st + 8 kgrp(g) .. +7
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
-    kf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + HD + hh * D + 32 * st + 8 * g, kvalid);
-    vf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + 2 * HD + hh * D + 32 * st + 8 * g, kvalid);
+    kf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + HD + hh * D + 32 * st + 8 * kgrp(g), kvalid);
+    vf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + 2 * HD + hh * D + 32 * st + 8 * kgrp(g), kvalid);
   }
   const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
   const BufRes rq = make_bufres(base + hh * D, batch_bytes - hh * D * 2);
