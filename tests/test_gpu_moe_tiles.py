@@ -116,3 +116,17 @@ def test_topk_beyond_eight_uses_generic_unpermute(form):
     x, wgu, wd, dout = tensors(T, Hd, Fe, len(counts), seed=42)
     got = check_shard(ids, w, x, wgu, wd, dout, form)
     assert list(got) == counts
+
+
+@pytest.mark.parametrize("form", list(FWD))
+def test_tile_edges_with_split_sparse_launches(form):
+    """The same tile edges with Hd and Fe large enough (18 and 17 k-tiles,
+    both ragged) that the sparse experts' launches split their k-range in
+    two: fp32 partials per sparse tile slot, then the reduce that applies
+    SwiGLU (and, in the training forward, saves the pre-activations)."""
+    say("moe tile edges, split sparse launches", form, COUNTS)
+    T, topk, Hd, Fe = 264, 8, 1096, 1032
+    ids, w = explicit_routing(COUNTS, T, topk, remote=16, seed=33)
+    x, wgu, wd, dout = tensors(T, Hd, Fe, len(COUNTS), seed=34)
+    counts = check_shard(ids, w, x, wgu, wd, dout, form)
+    assert list(counts) == COUNTS
