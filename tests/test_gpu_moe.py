@@ -46,6 +46,9 @@ CASES = [
     (300, 1096, 1032, 32, 8, 0, 2), # sparse experts with both GEMMs split over k (ragged last k-tiles)
     (8500, 64, 64, 16, 4, 2, 8),    # 34 blocks of 256 tokens in the two-kernel routing
     (200, 64, 64, 80, 70, 3, 4),    # 70 local experts: more than the two-kernel routing takes (four kernels)
+    (200, 64, 64, 80, 64, 3, 4),    # 64 local experts: the most the two-kernel routing takes
+    (65536, 64, 64, 8, 4, 2, 2),    # 65536 tokens: the most the two-kernel routing takes (256 blocks)
+    (65537, 64, 64, 8, 4, 2, 2),    # one token more: the four-kernel routing
 ]
 FORMS = {"weighted_unpermute": (lambda: mp.mp_grouped_expert_gemm, O.moe_forward),
          "weighted_act": (lambda: mp.mp_grouped_expert_gemm_weighted_act, O.moe_forward_weighted_act)}
