@@ -211,9 +211,14 @@ def test_moe_forms_and_mxfp8_validation(lib):
     rc, _ = call(lib, "mp_grouped_expert_gemm_weighted_act", T, 12, Fe, topk, E, 0, ALIGNED, ALIGNED, ALIGNED,
                  ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, ctypes.c_size_t(need), None)
     assert rc == -2
-    # The MXFP8 workspace holds the bf16 one plus the quantised rows.
-    assert lib.mp_grouped_expert_gemm_mxfp8_workspace(4096, 7168, 2048, 8, 8) >= (
-        lib.mp_grouped_expert_gemm_workspace(4096, 7168, 2048, 8, 8) + 4096 * 7168 + 4096 * 8 * 2048)
+    # The MXFP8 workspace holds the expert outputs (bf16), the quantised token
+    # rows and the quantised activation, but no bf16 activation and no split
+    # partials: smaller than the bf16 workspace.
+    T, Hd, Fe, topk, E = 4096, 7168, 2048, 8, 8
+    r = T * topk
+    mx = lib.mp_grouped_expert_gemm_mxfp8_workspace(T, Hd, Fe, topk, E)
+    assert mx >= r * Hd * 2 + T * Hd + r * Fe
+    assert mx < lib.mp_grouped_expert_gemm_workspace(T, Hd, Fe, topk, E)
 
 
 def test_moe_training_validation(lib):
