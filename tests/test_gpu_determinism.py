@@ -152,8 +152,8 @@ def _moe_inputs(T=300, Hd=256, Fe=136, experts=32, e_local=8, topk=8, seed=5):
     return ids, w, x, wgu, wd, dout
 
 
-def case_moe():
-    ids, w, x, wgu, wd, dout = _moe_inputs()
+def case_moe(shape=None):
+    ids, w, x, wgu, wd, dout = _moe_inputs(**(shape or {}))
     T, Hd = x.shape
     topk = ids.shape[1]
     e_local, two_fe, _ = wgu.shape
@@ -170,6 +170,11 @@ def case_moe():
         mp.mp_grouped_expert_gemm_bwd(x, w, wgu, wd, dout, gu, fws, dx, dwgu, dwd, dtw, weighted_act=wa)
         res += [out, gu, dx, dwgu, dwd, dtw]
     return res
+
+
+def case_moe_split_sparse():
+    # Sparse experts whose launches split the k-range (fp32 partials + reduce).
+    return case_moe(dict(T=300, Hd=1096, Fe=1032, experts=32, e_local=8, topk=2))
 
 
 def case_moe_mxfp8():
