@@ -23,6 +23,13 @@
 namespace mp {
 
 constexpr int MOE_BM = 256, MOE_BN = 256;
+// Tiles per band of the grouped GEMMs' tile order: one round of workgroups
+// (the 256-row kernel's 128 KiB of LDS fit once on each of 256 CUs).
+#ifndef MP_MOE_BAND
+#define MP_MOE_BAND 256
+#endif
+constexpr int MOE_BAND = MP_MOE_BAND;
+static_assert(MOE_BAND % 8 == 0, "bands start on the first XCD");
 // bf16 forward: an expert with fewer rows than this is "sparse" and runs on
 // 64-row tiles (a 256-row tile would spend most of its MFMA work on padding).
 constexpr int MOE_BM_SPARSE = 64, MOE_SPARSE_ROWS = 192;
@@ -470,8 +477,16 @@ __global__ __launch_bounds__(512) void moe_gemm_kernel(const MoeArgs a) {
   const int n_real = ts[a.E_loc] * a.tiles_n;
   const int wg = blockIdx.x;
   if (wg >= n_real) return;
-  const int per = n_real >> 3, rem = n_real & 7, xcd = wg & 7, idx = wg >> 3;
-  const int lid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  // Workgroups are dealt round-robin to the 8 XCDs and start in dispatch
+  // order, 256 at a time (one per CU).  The tile list is cut into bands of
+  // MOE_BAND consecutive tiles taken in that order, and inside a band each
+  // XCD takes a contiguous run: in every round all XCDs work on neighbouring
+  // tiles (mostly one expert, whose weight panels they then share through the
+  // last-level cache), the workgroups of one XCD on two or three m-tiles
+  // (their token rows shared in its L2).
+  const int b0 = wg - wg % MOE_BAND, nb = min(MOE_BAND, n_real - b0), w = wg - b0;
+  const int per = nb >> 3, rem = nb & 7, xcd = w & 7, idx = w >> 3;
+  const int lid = b0 + (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
   const int mtg = lid / a.tiles_n, nt = lid - mtg * a.tiles_n;
   int e = 0;
   while (e + 1 < a.E_loc && ts[e + 1] <= mtg) ++e;
