@@ -66,6 +66,13 @@ struct GemmArgs {
 };
 
 enum GroupMode { GRP_NONE = 0, GRP_M = 1, GRP_K = 2 };
+// Tiles per band of the GRP_M tile order: one round of 256-row workgroups
+// (one per CU).
+#ifndef MP_GRP_BAND
+#define MP_GRP_BAND 256
+#endif
+constexpr int GRP_BAND = MP_GRP_BAND;
+static_assert(GRP_BAND % 8 == 0, "bands start on the first XCD");
 
 // Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs;
 // renumber so XCD x gets a contiguous range of logical tiles, then walk
@@ -109,12 +116,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(const GemmArgs g0) {
   if constexpr (GRP == GRP_M) {
     // Flat list of the groups' tiles (tile-rows of every group back to back,
     // each tile-row tiles_n wide); workgroups past its end exit.  The list is
-    // dealt to the XCDs in contiguous ranges, as map_tile does.
+    // taken in bands of one round of workgroups (GRP_BAND tiles), each band
+    // dealt to the XCDs in contiguous runs, so every round works on
+    // neighbouring tiles: mostly one group, whose B panels the XCDs then
+    // share through the last-level cache.
     const int n_real = g.grp_tiles[g.groups] * g.tiles_n;
     const int wg = blockIdx.x;
     if (wg >= n_real) return;
-    const int per = n_real >> 3, rem = n_real & 7, xcd = wg & 7, idx = wg >> 3;
-    const int lid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+    const int b0 = wg - wg % GRP_BAND, nb = min(GRP_BAND, n_real - b0), w = wg - b0;
+    const int per = nb >> 3, rem = nb & 7, xcd = w & 7, idx = w >> 3;
+    const int lid = b0 + (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
     const int mtg = lid / g.tiles_n;
     tni = lid - mtg * g.tiles_n;
     int e = 0;
