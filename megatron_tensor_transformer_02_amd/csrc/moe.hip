@@ -1,22 +1,25 @@
 // One expert-parallel shard of a MoE layer, with every dynamic shape kept on
 // the device (no host synchronisation):
 //
-//  1. count   -- per token, how many of its top-k picks hit each local expert;
-//  2. scan    -- per expert, exclusive prefix of those counts over tokens
-//                (deterministic; gives each pick its rank inside its expert);
-//  3. offsets -- exclusive scan over experts of the row counts, and of their
-//                256-row tile counts (the grouped GEMMs' schedule);
-//  4. scatter -- perm_picks[row] = t*topk + k in (expert, token, slot) order,
-//                plus the inverse map pick -> row;
-//  5. grouped gate/up GEMM -- A rows are gathered straight from X through the
+//  1. routing -- per expert, each pick's rank among the expert's picks in
+//                (token, slot) order (deterministic), the row counts and their
+//                exclusive scan over experts (offsets), the 256-row and 64-row
+//                tile lists (the grouped GEMMs' schedule), and
+//                perm_picks[row] = t*topk + k in (expert, token, slot) order
+//                with the inverse map pick -> row: two kernels over blocks of
+//                256 tokens, or count / scan / offsets / scatter kernels for
+//                larger shards;
+//  2. grouped gate/up GEMM -- A rows are gathered straight from X through the
 //                permutation (no permuted copy of X), each wave's B rows
 //                interleave gate and up rows of the same output columns so
 //                the SwiGLU epilogue is local: act = silu(gate) * up;
-//  6. grouped down GEMM  -- y = act * W_d^T for each expert's rows;
-//  7. unpermute -- out[t] = sum_k w[t,k] * y[row(t,k)], fp32, k ascending.
+//  3. grouped down GEMM  -- y = act * W_d^T for each expert's rows;
+//  4. unpermute -- out[t] = sum_k w[t,k] * y[row(t,k)], fp32, k ascending.
 //
 // The grouped GEMMs launch a worst-case grid; a workgroup finds its expert
-// and tile from the device-side schedule and exits if it has none.
+// and tile from the device-side schedule and exits if it has none.  Experts
+// with few rows run on 64-row tiles in launches of their own, split over k
+// with a fixed-order reduce.
 #include "gemm.h"
 #include "mfma.h"
 
