@@ -22,9 +22,10 @@ def routing(seed, T, experts, topk):
     return torch.from_numpy(ids), torch.from_numpy(w / w.sum(axis=1, keepdims=True))
 
 
-def test_moe_train_step_graph_replay():
-    say("moe graph capture")
-    T, Hd, Fe, experts, e_local, topk = 300, 256, 136, 32, 8, 8
+@pytest.mark.parametrize("Hd,Fe", [(256, 136), (1096, 1032)])  # the second splits the sparse launches over k
+def test_moe_train_step_graph_replay(Hd, Fe):
+    say("moe graph capture", Hd, Fe)
+    T, experts, e_local, topk = 300, 32, 8, 8
     rng = np.random.default_rng(9)
     dev = "cuda"
     x = torch.from_numpy(rng.standard_normal((T, Hd), dtype=np.float32)).to(dev, torch.bfloat16)
