@@ -393,18 +393,18 @@ struct GatherDma {
 // E4M3's largest exponent), clamped to [-127, 127], -127 for blocks below
 // 2^-126; values become E4M3 codes of x / 2^exponent.
 
-// E4M3 code of v (|v| < 2^9): nearest, ties to the even code, saturating at
-// 448 (0x7E); the sign bit is kept, so a value rounding to zero gives +-0.
-// Below 2^-6 the grid is the multiples of 2^-9 (codes 0..8, 8 = 2^-6).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t sign = (bits >> 24) & 0x80u, b = bits & 0x7fffffffu;
-  const float m = __uint_as_float(b);
-  uint32_t code;
-  if (m >= 448.0f) code = 0x7eu;
-  else if (m < 0.015625f) code = static_cast<uint32_t>(__builtin_rintf(m * 512.0f));
-  else code = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);  // keep 3 mantissa bits, rebias 127 -> 7
-  return code | sign;
+// E4M3 codes of four values (|v| < 2^9), value i in byte i: nearest, ties to
+// the even code, saturating at 448 (0x7E); the sign bit is kept, so a value
+// rounding to zero gives +-0, and below 2^-6 the grid is the multiples of
+// 2^-9.  gfx950's v_cvt_pk_fp8_f32 converts to the OCP E4M3 format with that
+// rounding; its out-of-range results are not the saturated code, so values
+// are clamped to +-448 first.  Checked against a bit-level encoder of the
+// format over every f32 of magnitude below 2^9, both signs: identical codes.
+__device__ __forceinline__ uint32_t e4m3x4(float v0, float v1, float v2, float v3) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v0, -448.0f, 448.0f),
+                                                __builtin_amdgcn_fmed3f(v1, -448.0f, 448.0f), 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v2, -448.0f, 448.0f),
+                                                               __builtin_amdgcn_fmed3f(v3, -448.0f, 448.0f), w, true));
 }
 
 // One 32-value MX block held by four consecutive lanes (aligned to 4), eight
@@ -422,13 +422,8 @@ __device__ __forceinline__ uint2 mx_block8(const float* f, int& se) {
   const int e8 = static_cast<int>(__float_as_uint(mx) >> 23);
   se = e8 == 0 ? -127 : max(e8 - 135, -127);
   const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);  // 2^-se
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo |= e4m3_code(f[i] * inv) << (8 * i);
-    hi |= e4m3_code(f[4 + i] * inv) << (8 * i);
-  }
-  return make_uint2(lo, hi);
+  return make_uint2(e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                    e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
 }
 
 // Rows of x (bf16, row stride ld) to codes q [rows, K] and scales sc
