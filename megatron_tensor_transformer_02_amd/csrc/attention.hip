@@ -14,9 +14,9 @@
 // Sixteen rows per wave keep the register footprint small enough for two or
 // more waves per SIMD and give short sequences with few heads enough waves.
 //
-// Every kernel streams 64-row tiles through two LDS buffers: the next tile is
-// loaded into registers while the current one is multiplied, then written to
-// the other buffer (one barrier per tile).
+// Every kernel streams 64-row tiles through two LDS buffers: direct global ->
+// LDS loads fill the other buffer while the current one is multiplied (no
+// staging registers, no LDS stores; one wait and one barrier per tile).
 //
 // Backward (P recomputed from the saved log-sum-exp, no atomics):
 //  * dQ kernel -- lanes own queries: S^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
@@ -50,18 +50,20 @@ __device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
 
 // A 64-row x D-column tile of a [L, ld] bf16 matrix (a head slice), held in
 // D/64 LDS sub-tiles of the GEMM tile format (64 rows x 64 columns, rows of
-// eight swizzled 16-byte chunks).  load() fetches rows r0..r0+63 into
-// registers (rows >= L read as zeros), store() writes them to LDS.
+// eight swizzled 16-byte chunks) and filled by direct global -> LDS loads (no
+// registers, no LDS stores): `issue` starts the copy of rows r0..r0+63,
+// which lands asynchronously; wait_vm_lds() and a barrier make it visible.
+// The resource covers rows [0, L) of the head slice, so rows >= L arrive as
+// zeros.
 template <int D, int NT>
-struct RowTile {
-  TileLoader<64, true, NT> part[D / 64];
-  __device__ __forceinline__ void load(const BufRes& rs, int64_t ld, int r0, int L, int tid) {
-#pragma unroll
-    for (int hf = 0; hf < D / 64; ++hf) part[hf].load(rs, ld, r0, L, 64 * hf, D, tid, r0);
+struct RowTileDma {
+  DmaTile<64, true, NT> part;
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int L, int tid) {
+    part.init(base, ld, 0, L, D, tid);
   }
-  __device__ __forceinline__ void store(uint4* lds, int tid) const {
+  __device__ __forceinline__ void issue(uint4* lds, int r0) const {
 #pragma unroll
-    for (int hf = 0; hf < D / 64; ++hf) part[hf].store(lds + hf * 512, tid);
+    for (int hf = 0; hf < D / 64; ++hf) part.issue_rows(lds + hf * 512, r0, 64 * hf);
   }
 };
 
@@ -135,9 +137,9 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
   for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * kgrp(g), qvalid);
 
-  const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
-  const BufRes rk = make_bufres(base + HD + hh * D, batch_bytes - (HD + hh * D) * 2);
-  const BufRes rv = make_bufres(base + 2 * HD + hh * D, batch_bytes - (2 * HD + hh * D) * 2);
+  RowTileDma<D, NT> tk, tv;
+  tk.init(base + HD + hh * D, S3, a.L, tid);
+  tv.init(base + 2 * HD + hh * D, S3, a.L, tid);
 
   float m = -INFINITY, l = 0.0f;
   f32x4_t o[DB];
@@ -146,18 +148,17 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
 
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
   const int nkb = (kv_end + 63) / 64;
-  RowTile<D, NT> tk, tv;
-  tk.load(rk, S3, 0, a.L, tid);
-  tv.load(rv, S3, 0, a.L, tid);
-  tk.store(lds_k[0], tid);
-  tv.store(lds_v[0], tid);
+  tk.issue(lds_k[0], 0);
+  tv.issue(lds_v[0], 0);
+  wait_compiler_loads();  // the Q fragments
+  wait_vm_lds();
   __syncthreads();
   for (int it = 0; it < nkb; ++it) {
     const int kv0 = it * 64, cur = it & 1;
     const bool more = it + 1 < nkb;
-    if (more) {
-      tk.load(rk, S3, kv0 + 64, a.L, tid);
-      tv.load(rv, S3, kv0 + 64, a.L, tid);
+    if (more) {  // the other buffer's reads retired before the last barrier
+      tk.issue(lds_k[cur ^ 1], kv0 + 64);
+      tv.issue(lds_v[cur ^ 1], kv0 + 64);
     }
     if (!(a.causal && kv0 > qw0 + 15)) {  // else every key of the tile is in this wave's future
       const uint4* kt_ = lds_k[cur];
@@ -207,10 +208,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
       }
       m = mn;
     }
-    if (more) {
-      tk.store(lds_k[cur ^ 1], tid);
-      tv.store(lds_v[cur ^ 1], tid);
-    }
+    wait_vm_lds();  // this wave's copies of the next tile landed; its reads of this one retired
     __syncthreads();
   }
   const float lt = sum4(l);
@@ -254,9 +252,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
 #pragma unroll
   for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * kgrp(g), qvalid);
 
-  const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
-  const BufRes rk = make_bufres(base + HD + hh * D, batch_bytes - (HD + hh * D) * 2);
-  const BufRes rv = make_bufres(base + 2 * HD + hh * D, batch_bytes - (2 * HD + hh * D) * 2);
+  RowTileDma<D, NT> tk, tv;
+  tk.init(base + HD + hh * D, S3, a.L, tid);
+  tv.init(base + 2 * HD + hh * D, S3, a.L, tid);
 
   float m = -INFINITY, l = 0.0f;
   f32x4_t o[DB];
@@ -265,18 +263,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
 
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
   const int nkb = (kv_end + 63) / 64;
-  RowTile<D, NT> tk, tv;
-  tk.load(rk, S3, 0, a.L, tid);
-  tv.load(rv, S3, 0, a.L, tid);
-  tk.store(lds[0], tid);
-  tv.store(lds[2], tid);
+  tk.issue(lds[0], 0);
+  tv.issue(lds[2], 0);
+  wait_compiler_loads();  // the Q fragments
+  wait_vm_lds();
   __syncthreads();
   for (int it = 0; it < nkb; ++it) {
     const int kv0 = it * 64, cur = it & 1;
     const bool more = it + 1 < nkb;
-    if (more) {
-      tk.load(rk, S3, kv0 + 64, a.L, tid);
-      tv.load(rv, S3, kv0 + 64, a.L, tid);
+    if (more) {  // the other buffer's reads retired before the last barrier
+      tk.issue(lds[cur ^ 1], kv0 + 64);
+      tv.issue(lds[2 + (cur ^ 1)], kv0 + 64);
     }
     const int k0h = kv0 + 32 * hf;  // this wave's 32 keys
     if (k0h < a.L && !(a.causal && k0h > qw0 + 15)) {
@@ -320,16 +317,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
       l = l * alpha + ps;
       const uint4 pb = pack_pair(s[0], s[1]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        o[db] *= alpha;
-        o[db] = mfma_16x16x32(tr_frag(vt_, 16 * db, hf, lane), pb, o[db]);
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      // V^T fragments four at a time: their transpose reads are in flight
+      // together instead of one before each MFMA.
+#pragma unroll
+      for (int d4 = 0; d4 < DB; d4 += 4) {
+        uint4 vf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vf[j] = tr_frag(vt_, 16 * (d4 + j), hf, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[d4 + j] = mfma_16x16x32(vf[j], pb, o[d4 + j]);
       }
       m = mn;
     }
-    if (more) {
-      tk.store(lds[cur ^ 1], tid);
-      tv.store(lds[2 + (cur ^ 1)], tid);
-    }
+    wait_vm_lds();  // this wave's copies of the next tile landed; its reads of this one retired
     __syncthreads();
   }
   // Merge the key halves: the second half's wave leaves (m, l, O) in LDS,
@@ -453,9 +454,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
   const float lse2 = qvalid ? a.lse[sidx] * kLog2eA : 0.0f;
   const float dq_d = qvalid ? a.dvec[sidx] : 0.0f;
 
-  const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
-  const BufRes rk = make_bufres(base + HD + hh * D, batch_bytes - (HD + hh * D) * 2);
-  const BufRes rv = make_bufres(base + 2 * HD + hh * D, batch_bytes - (2 * HD + hh * D) * 2);
+  RowTileDma<D, NT> tk, tv;
+  tk.init(base + HD + hh * D, S3, a.L, tid);
+  tv.init(base + 2 * HD + hh * D, S3, a.L, tid);
 
   f32x4_t dq[DB];
 #pragma unroll
@@ -463,19 +464,18 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
 
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
   const int nkb = (kv_end + 63) / 64;
-  RowTile<D, NT> tk, tv;
-  tk.load(rk, S3, 0, a.L, tid);
-  tv.load(rv, S3, 0, a.L, tid);
-  tk.store(lds_k[0], tid);
-  tv.store(lds_v[0], tid);
+  tk.issue(lds_k[0], 0);
+  tv.issue(lds_v[0], 0);
+  wait_compiler_loads();  // the Q and dO fragments, lse, dvec
+  wait_vm_lds();
   __syncthreads();
   for (int it = 0; it < nkb; ++it) {
     const int kv0 = it * 64, cur = it & 1;
     const int ks0 = kv0 + 16 * SUB * half;  // first key of this wave's part of the tile
     const bool more = it + 1 < nkb;
-    if (more) {
-      tk.load(rk, S3, kv0 + 64, a.L, tid);
-      tv.load(rv, S3, kv0 + 64, a.L, tid);
+    if (more) {  // the other buffer's reads retired before the last barrier
+      tk.issue(lds_k[cur ^ 1], kv0 + 64);
+      tv.issue(lds_v[cur ^ 1], kv0 + 64);
     }
     if (!(a.causal && ks0 > qw0 + 15)) {
       const uint4* kt_ = lds_k[cur];
@@ -507,10 +507,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
           dq[db] = mfma_16x16x32(tr_frag(kt_, 16 * db, (SUB / 2) * half + t2, lane), d, dq[db]);
       }
     }
-    if (more) {
-      tk.store(lds_k[cur ^ 1], tid);
-      tv.store(lds_v[cur ^ 1], tid);
-    }
+    wait_vm_lds();  // this wave's copies of the next tile landed; its reads of this one retired
     __syncthreads();
   }
   if constexpr (NH == 2) {
@@ -557,10 +554,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     kf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + HD + hh * D + 32 * st + 8 * kgrp(g), kvalid);
     vf[st] = ld16_or_zero(base + static_cast<int64_t>(kj) * S3 + 2 * HD + hh * D + 32 * st + 8 * kgrp(g), kvalid);
   }
-  const int64_t batch_bytes = static_cast<int64_t>(a.L) * S3 * 2;
-  const BufRes rq = make_bufres(base + hh * D, batch_bytes - hh * D * 2);
   const uint16_t* dbase = a.dctx + static_cast<int64_t>(b) * a.L * HD;
-  const BufRes rdo = make_bufres(dbase + hh * D, (static_cast<int64_t>(a.L) * HD - hh * D) * 2);
   const int64_t sbase = (static_cast<int64_t>(b) * a.h + hh) * a.L;
 
   f32x4_t dkv[2 * DB];  // dK in [0, DB), dV in [DB, 2 DB)
@@ -569,11 +563,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   const int q_begin = a.causal ? (k0 / 64) * 64 : 0;
   const int nqb = (a.L - q_begin + 63) / 64;
-  RowTile<D, NT> tq, tdo;
+  RowTileDma<D, NT> tq, tdo;
+  tq.init(base + hh * D, S3, a.L, tid);
+  tdo.init(dbase + hh * D, HD, a.L, tid);
   float lse_r = 0.0f, dv_r = 0.0f;
-  auto fetch = [&](int q0) {
-    tq.load(rq, S3, q0, a.L, tid);
-    tdo.load(rdo, HD, q0, a.L, tid);
+  auto fetch = [&](int buf, int q0) {
+    tq.issue(lds_q[buf], q0);
+    tdo.issue(lds_do[buf], q0);
     if (tid < 64) {
       const int q = q0 + tid;
       lse_r = q < a.L ? a.lse[sbase + q] * kLog2eA : 0.0f;
@@ -581,23 +577,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
   auto commit = [&](int buf) {
-    tq.store(lds_q[buf], tid);
-    tdo.store(lds_do[buf], tid);
     if (tid < 64) {
       lds_lse[buf][tid] = lse_r;
       lds_dv[buf][tid] = dv_r;
     }
   };
   if (nqb > 0) {
-    fetch(q_begin);
+    fetch(0, q_begin);
     commit(0);
   }
+  wait_compiler_loads();  // the K and V fragments
+  wait_vm_lds();
   __syncthreads();
   for (int it = 0; it < nqb; ++it) {
     const int q0 = q_begin + it * 64, cur = it & 1;
     const int qs0 = q0 + 16 * SUB * half;  // first query of this wave's part of the tile
     const bool more = it + 1 < nqb;
-    if (more) fetch(q0 + 64);
+    if (more) fetch(cur ^ 1, q0 + 64);  // the other buffer's reads retired before the last barrier
     if (!(a.causal && qs0 + 16 * SUB - 1 < kw0)) {  // else every such query precedes this wave's keys
       const uint4* qt_ = lds_q[cur];
       const uint4* dot_ = lds_do[cur];
@@ -632,6 +628,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
     if (more) commit(cur ^ 1);
+    wait_vm_lds();  // this wave's copies of the next tiles landed; its reads of these retired
     __syncthreads();
   }
   if constexpr (NH == 2) {

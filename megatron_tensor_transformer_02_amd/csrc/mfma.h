@@ -59,24 +59,6 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b,
                                                  0, 0, 0);
 }
 
-// ------------------------------------------------------------ buffer loads
-// A buffer resource covers [base, base + bytes); a load at an offset outside
-// it returns zeros, which the tile loaders use for every out-of-range element.
-typedef __amdgpu_buffer_rsrc_t BufRes;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-constexpr uint32_t kBufOOB = 0x80000000u;  // offset past any resource (<= 2 GiB)
-
-__device__ __forceinline__ BufRes make_bufres(const void* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(n),
-                                           0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_load16(const BufRes& r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 __device__ __forceinline__ int lds_swz(int row) {
   const int t = (row >> 1) & 7;
   return t ^ ((t & 1) << 2);
@@ -99,59 +81,6 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
       (__attribute__((address_space(3))) i16x4_t*)(const_cast<void*>(p)));
   return __builtin_bit_cast(uint2, v);
 }
-
-// Global -> register -> LDS loader of one operand tile of R operand rows x 64
-// k-values, NT threads.  Loads go through a buffer resource whose base is the
-// tile's first row (K-contiguous) or first column (MN-contiguous); an element
-// outside the matrix or past the k-range gets an out-of-range offset, which
-// the hardware returns as zeros.  Eight consecutive threads read 128
-// contiguous bytes: one operand row (K-contiguous) or 64 columns of one
-// k-row (MN-contiguous); the latter are stored as they are, in the
-// sub-tile format, and read back with transpose reads.
-template <int R, bool KC, int NT>
-struct TileLoader {
-  static_assert((R * 8) % NT == 0, "tile chunks must cover the threads");
-  static_assert(KC || R % 64 == 0, "MN-contiguous tiles are whole 64-column sub-tiles");
-  static constexpr int NREG = R * 8 / NT;
-  uint4 reg[NREG];
-
-  // Resource for rows [row0, rows) of a K-contiguous matrix with row stride
-  // `ld`, or for columns [row0, ld) of an MN-contiguous matrix of `kdim` rows.
-  __device__ __forceinline__ static BufRes resource(const uint16_t* base, int64_t ld, int64_t row0, int64_t rows,
-                                                    int64_t kdim) {
-    if constexpr (KC) return make_bufres(base + row0 * ld, (rows - row0) * ld * 2);
-    else return make_bufres(base + row0, (kdim * ld - row0) * 2);
-  }
-
-  // `res_row` = rows between the resource base and row0 (K-contiguous only).
-  __device__ __forceinline__ void load(const BufRes& rs, int64_t ld, int64_t row0, int64_t rows, int64_t k0,
-                                       int64_t kend, int tid, int64_t res_row = 0) {
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int idx = tid + NT * i;
-      if constexpr (KC) {
-        const int64_t r = idx >> 3;
-        const int64_t gk = k0 + (idx & 7) * 8;
-        const bool ok = row0 + r < rows && gk < kend;
-        reg[i] = buf_load16(rs, ok ? static_cast<uint32_t>(((res_row + r) * ld + gk) * 2) : kBufOOB);
-      } else {
-        const int64_t mm = (idx >> 9) * 64 + (idx & 7) * 8;
-        const int64_t gk = k0 + ((idx >> 3) & 63);
-        const bool ok = row0 + mm < rows && gk < kend;
-        reg[i] = buf_load16(rs, ok ? static_cast<uint32_t>((gk * ld + mm) * 2) : kBufOOB);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint4* __restrict__ tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int idx = tid + NT * i;
-      if constexpr (KC) tile[lds_slot(idx >> 3, idx & 7)] = reg[i];
-      else tile[(idx >> 9) * 512 + lds_slot((idx >> 3) & 63, idx & 7)] = reg[i];
-    }
-  }
-};
 
 // ------------------------------------------------ direct global -> LDS
 // buffer_load_dwordx4 with the LDS flag writes the 16 bytes each lane fetches
@@ -199,6 +128,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // loads, this retires the wave's own reads of it: a plain __syncthreads()
 // only waits for LDS writes.
 __device__ __forceinline__ void wait_vm_lds() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+
+// vmcnt(0) as the builtin, which the compiler's wait-count tracking sees:
+// loads it issued before count as complete afterwards.  Without it, a loop
+// whose first use of such a load's value lies inside it gets a vmcnt(0) at
+// that use on every iteration, which also waits for the direct loads just
+// issued for the next tile.
+__device__ __forceinline__ void wait_compiler_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Direct loader of one operand tile (R operand rows x 64 k-values, NT
 // threads) into the LDS tile format.  Wave instruction q of wave w fills
@@ -266,6 +202,23 @@ struct DmaTile {
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
       const uint32_t so = live ? soff(q, k0) : kOOB;
+      const uint32_t m0v = lb + q * NWV * 1024;
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(desc),
+                   "s"(m0v), "s"(so)
+                   : "memory", "m0");
+    }
+  }
+
+  // K-contiguous operand whose resource starts at row 0: fills `tile` with
+  // rows row_off .. row_off + R - 1 at k-values k0 .. k0 + 63; rows past the
+  // resource's end arrive as zeros.
+  __device__ __forceinline__ void issue_rows(uint4* tile, int64_t row_off, int64_t k0) const {
+    static_assert(KC, "row offsets are for K-contiguous operands");
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(tile)) + wave * 1024;
+    const uint32_t ro = static_cast<uint32_t>(row_off * ld * 2);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const uint32_t so = soff(q, k0) + ro;
       const uint32_t m0v = lb + q * NWV * 1024;
       asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(desc),
                    "s"(m0v), "s"(so)
@@ -357,7 +310,7 @@ struct GridWarm {
 };
 
 // MFMA operand fragment of k-step ks (16 k-values) for operand rows
-// r0 .. r0+31 (r0 % 32 == 0) of a tile stored by TileLoader: lane l gets row
+// r0 .. r0+31 (r0 % 32 == 0) of a tile in the LDS tile format: lane l gets row
 // r0 + l%32, k-values 16*ks + 8*(l/32) .. +7.  An MN-contiguous tile is read
 // with two transpose reads of four k-rows each.
 template <bool KC>
