@@ -67,6 +67,26 @@ struct RowTileDma {
   }
 };
 
+// 64 consecutive floats [q0, q0 + 64) of a per-row vector copied into LDS by
+// one wave's direct loads (lane l fills lds[l]); entries past the vector's
+// end arrive as zeros.  No compiler-visible load stays in the tile loop, so
+// the compiler places no wait there that would also wait for the tiles.
+struct VecDma {
+  i32x4_t desc;
+  __device__ __forceinline__ void init(const float* base, int64_t n) {
+    desc = make_desc(base, n * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) desc[i] = __builtin_amdgcn_readfirstlane(desc[i]);
+  }
+  __device__ __forceinline__ void issue(float* lds, int q0, int lane) const {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(q0) * 4u);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %3 offen lds" ::"v"(lane * 4), "s"(desc),
+                 "s"(m0v), "s"(so)
+                 : "memory", "m0");
+  }
+};
+
 // Column group of k-group g (lane / 16) in a 32-column step: 8 * kgrp(g),
 // kgrp = (0, 3, 1, 2).  The MFMA sums over the step's 32 columns in any
 // order, so both operands only have to agree on it.  A 16-byte LDS read
@@ -566,26 +586,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   RowTileDma<D, NT> tq, tdo;
   tq.init(base + hh * D, S3, a.L, tid);
   tdo.init(dbase + hh * D, HD, a.L, tid);
-  float lse_r = 0.0f, dv_r = 0.0f;
+  VecDma vl, vd;  // lse and dvec of the tile's queries (zeros past L)
+  vl.init(a.lse + sbase, a.L);
+  vd.init(a.dvec + sbase, a.L);
   auto fetch = [&](int buf, int q0) {
     tq.issue(lds_q[buf], q0);
     tdo.issue(lds_do[buf], q0);
-    if (tid < 64) {
-      const int q = q0 + tid;
-      lse_r = q < a.L ? a.lse[sbase + q] * kLog2eA : 0.0f;
-      dv_r = q < a.L ? a.dvec[sbase + q] : 0.0f;
+    if (wave == 0) {
+      vl.issue(lds_lse[buf], q0, lane);
+      vd.issue(lds_dv[buf], q0, lane);
     }
   };
-  auto commit = [&](int buf) {
-    if (tid < 64) {
-      lds_lse[buf][tid] = lse_r;
-      lds_dv[buf][tid] = dv_r;
-    }
-  };
-  if (nqb > 0) {
-    fetch(0, q_begin);
-    commit(0);
-  }
+  if (nqb > 0) fetch(0, q_begin);
   wait_compiler_loads();  // the K and V fragments
   wait_vm_lds();
   __syncthreads();
@@ -612,7 +624,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int r = 0; r < 4; ++r) {
           const int ql = 16 * qb4 + 4 * g + r, q = q0 + ql;
           const bool vis = kvalid && (!edge || (q < a.L && (!a.causal || kj <= q)));
-          p[j][r] = vis ? exp2_fast(fmaf(sv[r], a.scale_log2, -lds_lse[cur][ql])) : 0.0f;
+          p[j][r] = vis ? exp2_fast(fmaf(sv[r], a.scale_log2, -(lds_lse[cur][ql] * kLog2eA))) : 0.0f;
           ds[j][r] = p[j][r] * (dp[r] - lds_dv[cur][ql]);
         }
       }
@@ -627,7 +639,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
       }
     }
-    if (more) commit(cur ^ 1);
     wait_vm_lds();  // this wave's copies of the next tiles landed; its reads of these retired
     __syncthreads();
   }
@@ -659,12 +670,19 @@ static int attn_waves(int B, int L, int h) {
   return blocks8 >= 512 ? 8 : 4;
 }
 
+// Unused dynamic LDS that keeps a causal split-kernel block alone on its CU
+// (static LDS D*512 bytes + the pad > 80 KiB, half the CU's 160 KiB).  The
+// heaviest causal blocks decide the kernel's time, and a block that shares
+// its CU runs slower; lighter blocks then queue behind finished ones.
+static unsigned causal_pad(const AttnArgs& a, int D) { return a.causal ? 96u * 1024u - 512u * D : 0u; }
+
 // With 4-wave blocks (few (batch, head) pairs) the forward runs the split-key
 // kernel instead: the same 64-query blocks on 8 waves.
 template <int D, int NW>
 static void launch_fwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
-  if constexpr (NW == 4) attn_fwd_split_kernel<D><<<static_cast<unsigned>(a.nblk * a.B * a.h), 512, 0, s>>>(a);
+  if constexpr (NW == 4)
+    attn_fwd_split_kernel<D><<<static_cast<unsigned>(a.nblk * a.B * a.h), 512, causal_pad(a, D), s>>>(a);
   else attn_fwd_kernel<D, NW><<<static_cast<unsigned>(a.nblk * a.B * a.h), 64 * NW, 0, s>>>(a);
 }
 
@@ -675,7 +693,7 @@ static void launch_bwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
   const unsigned grid = static_cast<unsigned>(a.nblk * a.B * a.h);
   if constexpr (NW == 4) {
-    attn_bwd_dq_kernel<D, 8, 2><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dq_kernel<D, 8, 2><<<grid, 512, causal_pad(a, D), s>>>(a);
     attn_bwd_dkv_kernel<D, 8, 2><<<grid, 512, 0, s>>>(a);
   } else {
     attn_bwd_dq_kernel<D, NW, 1><<<grid, 64 * NW, 0, s>>>(a);
