@@ -556,7 +556,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   static_assert(NH == 1 || NH == 2, "one or two waves per row group");
   __shared__ uint4 lds_q[2][TS];
   __shared__ uint4 lds_do[2][TS];
-  __shared__ float lds_lse[2][64], lds_dv[2][64];
+  __shared__ __align__(16) float lds_lse[2][64];
+  __shared__ __align__(16) float lds_dv[2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kc = lane & 15, g = lane >> 4;
   const int grp = wave % NG, half = wave / NG;
   const int nbh = a.B * a.h;
@@ -611,6 +612,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       const uint4* dot_ = lds_do[cur];
       const bool edge = qs0 + 16 * SUB - 1 >= a.L || (a.causal && qs0 < kw0 + 15);
       f32x4_t p[SUB], ds[SUB];
+      // lse and dvec of this lane's queries 16 qb4 + 4 g .. +3, one 16-byte
+      // read each, issued before the MFMAs that they wait for.
+      f32x4_t lse4[SUB], dv4[SUB];
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) {
+        const int ql0 = 16 * (SUB * half + j) + 4 * g;
+        lse4[j] = *reinterpret_cast<const f32x4_t*>(&lds_lse[cur][ql0]);
+        dv4[j] = *reinterpret_cast<const f32x4_t*>(&lds_dv[cur][ql0]);
+      }
 #pragma unroll
       for (int j = 0; j < SUB; ++j) {
         const int qb4 = SUB * half + j;
@@ -624,8 +634,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int r = 0; r < 4; ++r) {
           const int ql = 16 * qb4 + 4 * g + r, q = q0 + ql;
           const bool vis = kvalid && (!edge || (q < a.L && (!a.causal || kj <= q)));
-          p[j][r] = vis ? exp2_fast(fmaf(sv[r], a.scale_log2, -(lds_lse[cur][ql] * kLog2eA))) : 0.0f;
-          ds[j][r] = p[j][r] * (dp[r] - lds_dv[cur][ql]);
+          p[j][r] = vis ? exp2_fast(fmaf(sv[r], a.scale_log2, -(lse4[j][r] * kLog2eA))) : 0.0f;
+          ds[j][r] = p[j][r] * (dp[r] - dv4[j][r]);
         }
       }
 #pragma unroll
