@@ -445,8 +445,11 @@ __device__ __forceinline__ void merge_halves(f32x4_t* x, f32x4_t* buf, int grp, 
   }
 }
 
-template <int D, int NW, int NH>
-__global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) {
+// WPE: at least this many waves per SIMD (a register cap: 4 keeps two 8-wave
+// blocks on a CU, which pays when every block carries the same work).
+template <int D, int NW, int NH, int WPE = 1>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) void attn_bwd_dq_kernel(
+    const AttnArgs a) {
   constexpr int NT = 64 * NW, NG = NW / NH, BQ = 16 * NG, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
   constexpr int SUB = 4 / NH;  // 16-key sub-blocks per wave per tile
   static_assert(NH == 1 || NH == 2, "one or two waves per row group");
@@ -506,10 +509,16 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(const AttnArgs a) 
       for (int j = 0; j < SUB; ++j) {
         const int kb = SUB * half + j;
         f32x4_t sv = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
+        uint4 kfr[KS], vfr[KS];  // all of the step's K and V fragments in flight together
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
-          sv = mfma_16x16x32(row_frag(kt_, 16 * kb, st, lane), qf[st], sv);
-          dp = mfma_16x16x32(row_frag(vt_, 16 * kb, st, lane), dof[st], dp);
+          kfr[st] = row_frag(kt_, 16 * kb, st, lane);
+          vfr[st] = row_frag(vt_, 16 * kb, st, lane);
+        }
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          sv = mfma_16x16x32(kfr[st], qf[st], sv);
+          dp = mfma_16x16x32(vfr[st], dof[st], dp);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -703,7 +712,8 @@ static void launch_bwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
   const unsigned grid = static_cast<unsigned>(a.nblk * a.B * a.h);
   if constexpr (NW == 4) {
-    attn_bwd_dq_kernel<D, 8, 2><<<grid, 512, causal_pad(a, D), s>>>(a);
+    if (a.causal) attn_bwd_dq_kernel<D, 8, 2><<<grid, 512, causal_pad(a, D), s>>>(a);
+    else attn_bwd_dq_kernel<D, 8, 2, 4><<<grid, 512, 0, s>>>(a);
     attn_bwd_dkv_kernel<D, 8, 2><<<grid, 512, 0, s>>>(a);
   } else {
     attn_bwd_dq_kernel<D, NW, 1><<<grid, 64 * NW, 0, s>>>(a);
