@@ -19,7 +19,8 @@
 // staging registers, no LDS stores; one wait and one barrier per tile).
 //
 // Backward (P recomputed from the saved log-sum-exp, no atomics):
-//  * dQ kernel -- lanes own queries: S^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
+//  * dQ kernel -- lanes own queries: rowsum(dO * O) (also left for the next
+//    kernel), S^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
 //  * dK/dV kernel -- lanes own keys: S = Q K^T, dP = dO V^T, dS,
 //    dV^T += dO^T P, dK^T += Q^T dS.
 // The QKV GEMM's input and weight gradients then run on the GEMM family.
@@ -35,7 +36,7 @@ struct AttnArgs {
   uint16_t* ctx;         // [B*L, h*D]
   float* lse;            // [B, h, L]
   const uint16_t* dctx;  // [B*L, h*D]        (backward)
-  const float* dvec;     // [B, h, L] rowsum(dO * O)
+  const float* dvec;     // [B, h, L] rowsum(dO * O), written by the dQ kernel
   uint16_t* dqkv;        // [B*L, 3*h*D]      (backward)
   int B, L, h, causal;
   int nblk;              // query (or key) blocks per (batch, head)
@@ -394,30 +395,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void a
   if (g == 0) a.lse[(static_cast<int64_t>(b) * a.h + hh) * a.L + qi] = m * a.scale + logf(lt);
 }
 
-// dvec[b, h, l] = sum_d dctx[t, h*D + d] * ctx[t, h*D + d]; one thread per (t, head).
-template <int D>
-__global__ __launch_bounds__(256) void attn_dvec_kernel(const AttnArgs a) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t T = static_cast<int64_t>(a.B) * a.L;
-  if (idx >= T * a.h) return;
-  const int64_t t = idx / a.h;
-  const int hh = static_cast<int>(idx - t * a.h);
-  const int64_t HD = static_cast<int64_t>(a.h) * D;
-  const uint16_t* o = a.ctx + t * HD + hh * D;
-  const uint16_t* dO = a.dctx + t * HD + hh * D;
-  float acc = 0.0f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    float x[8], y[8];
-    unpack8(*reinterpret_cast<const uint4*>(o + 8 * c), x);
-    unpack8(*reinterpret_cast<const uint4*>(dO + 8 * c), y);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
-  }
-  const int64_t b = t / a.L, l = t - b * a.L;
-  const_cast<float*>(a.dvec)[(b * a.h + hh) * a.L + l] = acc;
-}
-
 // Backward kernels.  NH = 1: each wave owns 16 rows (queries for dQ, keys
 // for dK/dV) and walks every visible 64-row tile of the other side.  NH = 2
 // (few (batch, head) pairs): two waves share each 16-row group and take one
@@ -467,19 +444,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   const bool qvalid = qi < a.L;
   const int64_t trow = static_cast<int64_t>(b) * a.L + qi;
 
+  // The first K and V tiles are in flight while the rows below load.
+  RowTileDma<D, NT> tk, tv;
+  tk.init(base + HD + hh * D, S3, a.L, tid);
+  tv.init(base + 2 * HD + hh * D, S3, a.L, tid);
+  tk.issue(lds_k[0], 0);
+  tv.issue(lds_v[0], 0);
+
+  const int64_t sidx = (static_cast<int64_t>(b) * a.h + hh) * a.L + qi;
+  const float lse2 = qvalid ? a.lse[sidx] * kLog2eA : 0.0f;  // loaded before the dvec store below
   uint4 qf[KS], dof[KS];
+  float dq_d = 0.0f;  // rowsum(dO * O) of query qi: this lane's 32 columns, then the 4 lanes of the query
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
     qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * kgrp(g), qvalid);
     dof[st] = ld16_or_zero(a.dctx + trow * HD + hh * D + 32 * st + 8 * kgrp(g), qvalid);
+    float x[8], y[8];
+    unpack8(dof[st], x);
+    unpack8(ld16_or_zero(a.ctx + trow * HD + hh * D + 32 * st + 8 * kgrp(g), qvalid), y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dq_d = fmaf(x[e], y[e], dq_d);
   }
-  const int64_t sidx = (static_cast<int64_t>(b) * a.h + hh) * a.L + qi;
-  const float lse2 = qvalid ? a.lse[sidx] * kLog2eA : 0.0f;
-  const float dq_d = qvalid ? a.dvec[sidx] : 0.0f;
-
-  RowTileDma<D, NT> tk, tv;
-  tk.init(base + HD + hh * D, S3, a.L, tid);
-  tv.init(base + 2 * HD + hh * D, S3, a.L, tid);
+  dq_d = sum4(dq_d);
+  // The dK/dV kernel, launched next, reads it back.
+  if (qvalid && g == 0 && half == 0) const_cast<float*>(a.dvec)[sidx] = dq_d;
 
   f32x4_t dq[DB];
 #pragma unroll
@@ -487,9 +475,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
   const int nkb = (kv_end + 63) / 64;
-  tk.issue(lds_k[0], 0);
-  tv.issue(lds_v[0], 0);
-  wait_compiler_loads();  // the Q and dO fragments, lse, dvec
+  wait_compiler_loads();  // the Q, dO and O rows, lse
   wait_vm_lds();
   __syncthreads();
   for (int it = 0; it < nkb; ++it) {
@@ -826,9 +812,6 @@ extern "C" int mp_head_attention_bwd(mp_dtype dtype, int B, int L, int K, int h,
   a.dctx = static_cast<const uint16_t*>(dctx_i);
   a.dvec = dvec;
   a.dqkv = dqkv;
-  const unsigned dgrid = static_cast<unsigned>(ceil_div(T * h, 256));
-  if (d == 64) attn_dvec_kernel<64><<<dgrid, 256, 0, s>>>(a);
-  else attn_dvec_kernel<128><<<dgrid, 256, 0, s>>>(a);
   const int nw = attn_waves(B, L, h);
   if (d == 64) nw == 8 ? launch_bwd<64, 8>(a, s) : launch_bwd<64, 4>(a, s);
   else nw == 8 ? launch_bwd<128, 8>(a, s) : launch_bwd<128, 4>(a, s);
