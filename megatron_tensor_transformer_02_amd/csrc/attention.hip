@@ -518,8 +518,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
       for (int t2 = 0; t2 < SUB / 2; ++t2) {
         const uint4 d = pack_pair(ds[2 * t2], ds[2 * t2 + 1]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dq[db] = mfma_16x16x32(tr_frag(kt_, 16 * db, (SUB / 2) * half + t2, lane), d, dq[db]);
+        for (int d4 = 0; d4 < DB; d4 += 4) {  // K^T fragments four at a time, in flight together
+          uint4 fk[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) fk[j] = tr_frag(kt_, 16 * (d4 + j), (SUB / 2) * half + t2, lane);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dq[d4 + j] = mfma_16x16x32(fk[j], d, dq[d4 + j]);
+        }
       }
     }
     wait_vm_lds();  // this wave's copies of the next tile landed; its reads of this one retired
@@ -638,9 +643,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int t = (SUB / 2) * half + t2;
         const uint4 pp = pack_pair(p[2 * t2], p[2 * t2 + 1]), dd = pack_pair(ds[2 * t2], ds[2 * t2 + 1]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dkv[DB + db] = mfma_16x16x32(tr_frag(dot_, 16 * db, t, lane), pp, dkv[DB + db]);
-          dkv[db] = mfma_16x16x32(tr_frag(qt_, 16 * db, t, lane), dd, dkv[db]);
+        for (int d4 = 0; d4 < DB; d4 += 4) {  // fragments four at a time, in flight together
+          uint4 fo[4], fq[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            fo[j] = tr_frag(dot_, 16 * (d4 + j), t, lane);
+            fq[j] = tr_frag(qt_, 16 * (d4 + j), t, lane);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dkv[DB + d4 + j] = mfma_16x16x32(fo[j], pp, dkv[DB + d4 + j]);
+            dkv[d4 + j] = mfma_16x16x32(fq[j], dd, dkv[d4 + j]);
+          }
         }
       }
     }
