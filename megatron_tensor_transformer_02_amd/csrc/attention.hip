@@ -246,6 +246,162 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
   if (g == 0) a.lse[(static_cast<int64_t>(b) * a.h + hh) * a.L + qi] = m * a.scale + logf(lt);
 }
 
+// Causal forward for few (batch, head) pairs: a block holds 4 query tiles of
+// 16 rows x 2 waves (8 waves, two per SIMD, one block per CU), and the two
+// waves of a query tile take alternate 64-key tiles (wave (qt, p) the tiles of
+// parity p): each step multiplies a whole tile per wave, with four
+// independent S^T chains and one max / rescale per 64 keys, and the heaviest
+// block runs ceil(n/2) steps for its n key tiles.  Both tiles of a step are
+// in LDS together.  At the end the two waves' (running max, exp-sum, O) are
+// merged through LDS, rescaled to the common max.
+template <int D>
+__global__ __launch_bounds__(512) void attn_fwd_par_kernel(const AttnArgs a) {
+  constexpr int NT = 512, BQ = 64, DB = D / 16, KS = D / 32, TS = D / 64 * 512;
+  __shared__ uint4 lds[2][4][TS];  // [buffer][K even, K odd, V even, V odd]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qt = wave & 3, par = wave >> 2;
+  const int qc = lane & 15, g = lane >> 4;
+  const int nbh = a.B * a.h;
+  const int bh = blockIdx.x % nbh;
+  const int qb = a.nblk - 1 - static_cast<int>(blockIdx.x / nbh);  // heavy (late) query blocks first
+  const int b = bh / a.h, hh = bh % a.h;
+  const int64_t S3 = 3LL * a.h * D, HD = static_cast<int64_t>(a.h) * D;
+  const uint16_t* base = a.qkv + static_cast<int64_t>(b) * a.L * S3;
+  const int q0 = qb * BQ, qw0 = q0 + qt * 16, qi = qw0 + qc;
+  const bool qvalid = qi < a.L;
+
+  RowTileDma<D, NT> tk, tv;
+  tk.init(base + HD + hh * D, S3, a.L, tid);
+  tv.init(base + 2 * HD + hh * D, S3, a.L, tid);
+  auto fetch = [&](int buf, int kt0) {  // key tiles kt0 and kt0 + 1
+    tk.issue(lds[buf][0], 64 * kt0);
+    tk.issue(lds[buf][1], 64 * kt0 + 64);
+    tv.issue(lds[buf][2], 64 * kt0);
+    tv.issue(lds[buf][3], 64 * kt0 + 64);
+  };
+  fetch(0, 0);
+
+  uint4 qf[KS];  // Q^T as the B operand: query qi, d = 32 st + 8 kgrp(g) .. +7
+#pragma unroll
+  for (int st = 0; st < KS; ++st) qf[st] = ld16_or_zero(base + static_cast<int64_t>(qi) * S3 + hh * D + 32 * st + 8 * kgrp(g), qvalid);
+
+  float m = -INFINITY, l = 0.0f;
+  f32x4_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nkb = (min(a.L, q0 + BQ) + 63) / 64, nit = (nkb + 1) / 2;
+  wait_compiler_loads();  // the Q fragments
+  wait_vm_lds();
+  __syncthreads();
+  for (int it = 0; it < nit; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < nit) fetch(cur ^ 1, 2 * it + 2);  // the other buffer's reads retired before the last barrier
+    const int kv0 = 128 * it + 64 * par;  // this wave's tile
+    if (kv0 < a.L && kv0 <= qw0 + 15) {
+      const uint4* kt_ = lds[cur][par];
+      const uint4* vt_ = lds[cur][2 + par];
+      f32x4_t s[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        uint4 kfr[4];  // the step's four K fragments in flight together
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) kfr[kb] = row_frag(kt_, 16 * kb, st, lane);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s[kb] = mfma_16x16x32(kfr[kb], qf[st], s[kb]);
+      }
+      // Keys of this lane: kv0 + 16 kb + 4 g + r.
+      if (kv0 + 63 >= a.L || kv0 + 63 > qw0) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kv0 + 16 * kb + 4 * g + r;
+            if (key >= a.L || key > qi) s[kb][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max4(mx);
+      const float mn = fmaxf(m, mx);
+      const float ms = mn == -INFINITY ? 0.0f : mn;
+      const float alpha = exp2_fast((m - ms) * a.scale_log2);
+      const float msc = ms * a.scale_log2;
+      float ps = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[kb][r] = exp2_fast(fmaf(s[kb][r], a.scale_log2, -msc));
+          ps += s[kb][r];
+        }
+      l = l * alpha + ps;
+      const uint4 pb0 = pack_pair(s[0], s[1]), pb1 = pack_pair(s[2], s[3]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+#pragma unroll
+      for (int d4 = 0; d4 < DB; d4 += 4) {  // V^T fragments four at a time, in flight together
+        uint4 v0[4], v1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v0[j] = tr_frag(vt_, 16 * (d4 + j), 0, lane);
+          v1[j] = tr_frag(vt_, 16 * (d4 + j), 1, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[d4 + j] = mfma_16x16x32(v0[j], pb0, o[d4 + j]);
+          o[d4 + j] = mfma_16x16x32(v1[j], pb1, o[d4 + j]);
+        }
+      }
+      m = mn;
+    }
+    wait_vm_lds();  // this wave's copies of the next tiles landed; its reads of these retired
+    __syncthreads();
+  }
+  // The parity-1 wave leaves (m, l, O) in LDS, laid out [tile][value][lane]
+  // (conflict-free); the parity-0 wave rescales both to the common max.
+  constexpr int MS = 4 * DB + 2;
+  float* mrg = reinterpret_cast<float*>(&lds[0][0][0]) + qt * MS * 64 + lane;
+  if (par == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mrg[(4 * db + r) * 64] = o[db][r];
+    mrg[(4 * DB) * 64] = m;
+    mrg[(4 * DB + 1) * 64] = l;
+  }
+  __syncthreads();
+  if (par == 1) return;
+  {
+    const float m1 = mrg[(4 * DB) * 64], l1 = mrg[(4 * DB + 1) * 64];
+    const float mn = fmaxf(m, m1);
+    const float ms = mn == -INFINITY ? 0.0f : mn;
+    const float a0 = exp2_fast((m - ms) * a.scale_log2), a1 = exp2_fast((m1 - ms) * a.scale_log2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[db][r] = o[db][r] * a0 + mrg[(4 * db + r) * 64] * a1;
+    l = l * a0 + l1 * a1;
+    m = mn;
+  }
+  const float lt = sum4(l);
+  if (!qvalid) return;
+  const float inv = 1.0f / lt;
+  uint16_t* crow = a.ctx + (static_cast<int64_t>(b) * a.L + qi) * HD + hh * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    uint2 v;
+    v.x = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
+    v.y = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
+    *reinterpret_cast<uint2*>(crow + 16 * db + 4 * g) = v;
+  }
+  if (g == 0) a.lse[(static_cast<int64_t>(b) * a.h + hh) * a.L + qi] = m * a.scale + logf(lt);
+}
+
 // Forward with the keys of each query tile split between two waves: a block
 // holds 4 query tiles of 16 rows x 2 key halves (8 waves, two per SIMD).
 // Wave (qt, hf) multiplies keys 32*hf .. 32*hf+31 of every 64-key tile, so
@@ -700,8 +856,11 @@ static unsigned causal_pad(const AttnArgs& a, int D) { return a.causal ? 96u * 1
 template <int D, int NW>
 static void launch_fwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
-  if constexpr (NW == 4)
-    attn_fwd_split_kernel<D><<<static_cast<unsigned>(a.nblk * a.B * a.h), 512, causal_pad(a, D), s>>>(a);
+  if constexpr (NW == 4) {
+    const unsigned grid = static_cast<unsigned>(a.nblk * a.B * a.h);
+    if (a.causal) attn_fwd_par_kernel<D><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_split_kernel<D><<<grid, 512, 0, s>>>(a);
+  }
   else attn_fwd_kernel<D, NW><<<static_cast<unsigned>(a.nblk * a.B * a.h), 64 * NW, 0, s>>>(a);
 }
 
