@@ -845,11 +845,13 @@ static int attn_waves(int B, int L, int h) {
   return blocks8 >= 512 ? 8 : 4;
 }
 
-// Unused dynamic LDS that keeps a causal split-kernel block alone on its CU
-// (static LDS D*512 bytes + the pad > 80 KiB, half the CU's 160 KiB).  The
+// Unused dynamic LDS that keeps a causal block with `lds` bytes of static LDS
+// alone on its CU (static + pad > 80 KiB, half the CU's 160 KiB).  The
 // heaviest causal blocks decide the kernel's time, and a block that shares
 // its CU runs slower; lighter blocks then queue behind finished ones.
-static unsigned causal_pad(const AttnArgs& a, int D) { return a.causal ? 96u * 1024u - 512u * D : 0u; }
+static unsigned causal_pad(const AttnArgs& a, unsigned lds) {
+  return a.causal && lds < 96u * 1024u ? 96u * 1024u - lds : 0u;
+}
 
 // With 4-wave blocks (few (batch, head) pairs) the forward runs the split-key
 // kernel instead: the same 64-query blocks on 8 waves.
@@ -858,7 +860,7 @@ static void launch_fwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
   if constexpr (NW == 4) {
     const unsigned grid = static_cast<unsigned>(a.nblk * a.B * a.h);
-    if (a.causal) attn_fwd_par_kernel<D><<<grid, 512, 0, s>>>(a);
+    if (a.causal) attn_fwd_par_kernel<D><<<grid, 512, causal_pad(a, 1024u * D), s>>>(a);
     else attn_fwd_split_kernel<D><<<grid, 512, 0, s>>>(a);
   }
   else attn_fwd_kernel<D, NW><<<static_cast<unsigned>(a.nblk * a.B * a.h), 64 * NW, 0, s>>>(a);
@@ -871,7 +873,7 @@ static void launch_bwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
   const unsigned grid = static_cast<unsigned>(a.nblk * a.B * a.h);
   if constexpr (NW == 4) {
-    if (a.causal) attn_bwd_dq_kernel<D, 8, 2><<<grid, 512, causal_pad(a, D), s>>>(a);
+    if (a.causal) attn_bwd_dq_kernel<D, 8, 2><<<grid, 512, causal_pad(a, 512u * D), s>>>(a);
     else attn_bwd_dq_kernel<D, 8, 2, 4><<<grid, 512, 0, s>>>(a);
     attn_bwd_dkv_kernel<D, 8, 2><<<grid, 512, 0, s>>>(a);
   } else {
