@@ -629,6 +629,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Keys 0 .. key_lim are visible to query qi (none past L, none after qi
+  // when causal, none for a query past L): one compare per score, no
+  // branches (a short-circuit test here compiled to per-element branches).
+  const int key_lim = !qvalid ? -1 : (a.causal ? min(a.L - 1, qi) : a.L - 1);
   const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
   const int nkb = (kv_end + 63) / 64;
   wait_compiler_loads();  // the Q, dO and O rows, lse
@@ -645,7 +649,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
     if (!(a.causal && ks0 > qw0 + 15)) {
       const uint4* kt_ = lds_k[cur];
       const uint4* vt_ = lds_v[cur];
-      const bool edge = ks0 + 16 * SUB - 1 >= a.L || (a.causal && ks0 + 16 * SUB - 1 > qw0);
       f32x4_t ds[SUB];
 #pragma unroll
       for (int j = 0; j < SUB; ++j) {
@@ -665,8 +668,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = kv0 + 16 * kb + 4 * g + r;
-          const bool vis = qvalid && (!edge || (key < a.L && (!a.causal || key <= qi)));
-          const float p = vis ? exp2_fast(fmaf(sv[r], a.scale_log2, -lse2)) : 0.0f;
+          const bool vis = key <= key_lim;
+          // exp2(-inf) = 0: a select on the argument, not on the exponential, keeps
+          // the loop free of per-element branches.
+          const float p = exp2_fast(vis ? fmaf(sv[r], a.scale_log2, -lse2) : -INFINITY);
           ds[j][r] = p * (dp[r] - dq_d);
         }
       }
@@ -738,6 +743,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
   for (int v = 0; v < 2 * DB; ++v) dkv[v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Queries q_lo .. L-1 see key kj (as key_lim in dQ).
+  const int q_lo = !kvalid ? 0x7fffffff : (a.causal ? kj : 0);
   const int q_begin = a.causal ? (k0 / 64) * 64 : 0;
   const int nqb = (a.L - q_begin + 63) / 64;
   RowTileDma<D, NT> tq, tdo;
@@ -766,7 +773,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (!(a.causal && qs0 + 16 * SUB - 1 < kw0)) {  // else every such query precedes this wave's keys
       const uint4* qt_ = lds_q[cur];
       const uint4* dot_ = lds_do[cur];
-      const bool edge = qs0 + 16 * SUB - 1 >= a.L || (a.causal && qs0 < kw0 + 15);
       f32x4_t p[SUB], ds[SUB];
       // lse and dvec of this lane's queries 16 qb4 + 4 g .. +3, one 16-byte
       // read each, issued before the MFMAs that they wait for.
@@ -789,8 +795,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ql = 16 * qb4 + 4 * g + r, q = q0 + ql;
-          const bool vis = kvalid && (!edge || (q < a.L && (!a.causal || kj <= q)));
-          p[j][r] = vis ? exp2_fast(fmaf(sv[r], a.scale_log2, -(lse4[j][r] * kLog2eA))) : 0.0f;
+          const bool vis = (q >= q_lo) & (q < a.L);
+          p[j][r] = exp2_fast(vis ? fmaf(sv[r], a.scale_log2, -(lse4[j][r] * kLog2eA)) : -INFINITY);  // as in dQ
           ds[j][r] = p[j][r] * (dp[r] - dv4[j][r]);
         }
       }
