@@ -283,6 +283,12 @@ int mp_head_attention(mp_dtype dtype, int B, int L, int K, int h, int d, int cau
                       const void* X, const void* Wqkv_i, const void* bqkv_i, void* ctx_i,
                       void* qkv, float* lse, hipStream_t s);
 
+/* Workspace bytes of mp_head_attention_bwd (0 for an unsupported shape):
+ * dQKV, the per-query rowsum(dO * O), and one region shared by the weight
+ * products' scratch and, when B * h * ceil(L/128) < 512 and L <= 4096, the
+ * bf16 dS^T of every (batch, head) pair in 64 x 64 tiles
+ * (B * h * ceil(L/64)^2 * 8 KiB), which the dQ kernel reads back instead of
+ * recomputing S and dP. */
 size_t mp_head_attention_bwd_workspace(mp_dtype dtype, int B, int L, int K, int h, int d);
 
 /* Backward of mp_head_attention (P recomputed from lse).  Inputs as saved by

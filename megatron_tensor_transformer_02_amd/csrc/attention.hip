@@ -38,6 +38,7 @@ struct AttnArgs {
   const uint16_t* dctx;  // [B*L, h*D]        (backward)
   const float* dvec;     // [B, h, L] rowsum(dO * O), written by the dQ kernel
   uint16_t* dqkv;        // [B*L, 3*h*D]      (backward)
+  uint16_t* dst;         // [B, h, L keys, L queries] dS^T (backward, stored-dS form) or null
   int B, L, h, causal;
   int nblk;              // query (or key) blocks per (batch, head)
   float scale;           // 1/sqrt(D)
@@ -578,6 +579,101 @@ __device__ __forceinline__ void merge_halves(f32x4_t* x, f32x4_t* buf, int grp, 
   }
 }
 
+// dvec[b, h, l] = rowsum(dO * O) of query row l: D/8 lanes per row, one
+// 16-byte chunk of dO and of O each, then a fixed-order butterfly.
+template <int D>
+__global__ __launch_bounds__(256) void attn_dvec_kernel(const AttnArgs a) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per (token, head) row, rows per block
+  const int64_t T = static_cast<int64_t>(a.B) * a.L, HD = static_cast<int64_t>(a.h) * D;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  const bool ok = idx < T * a.h;
+  const int64_t t = ok ? idx / a.h : 0;
+  const int hh = ok ? static_cast<int>(idx - t * a.h) : 0;
+  float x[8], y[8];
+  unpack8(ld16_or_zero(a.ctx + t * HD + hh * D + 8 * c, ok), x);
+  unpack8(ld16_or_zero(a.dctx + t * HD + hh * D + 8 * c, ok), y);
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (ok && c == 0) {
+    const int64_t b = t / a.L, l = t - b * a.L;
+    const_cast<float*>(a.dvec)[(b * a.h + hh) * a.L + l] = acc;
+  }
+}
+
+// dQ from the stored dS^T (the dK/dV kernel of this form writes it): per
+// 64-query block, dQ^T += K^T dS^T over the visible 64-key tiles, with no
+// recomputation of S and dP.  Waves (grp, half): 16 queries, keys 32*half ..
+// +31 of each tile; both operands are transposed LDS reads of row tiles (K
+// rows; dS^T rows are keys, columns queries).  The halves' sums are added
+// through LDS at the end.  Each tile costs a fixed chain (barrier, LDS reads,
+// products) of about a microsecond; a deeper tile ring and 4-wave blocks
+// with a third of the LDS reads both measured slower.
+template <int D>
+__global__ __launch_bounds__(512) void attn_bwd_dq_ds_kernel(const AttnArgs a) {
+  constexpr int NT = 512, NG = 4, BQ = 64, DB = D / 16, TS = D / 64 * 512;
+  __shared__ uint4 lds_k[2][TS];
+  __shared__ uint4 lds_s[2][512];  // one 64 x 64 tile of dS^T
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qc = lane & 15;
+  const int grp = wave % NG, half = wave / NG;
+  const int nbh = a.B * a.h;
+  const int bh = blockIdx.x % nbh;
+  const int qb = a.nblk - 1 - static_cast<int>(blockIdx.x / nbh);  // heavy (late) query blocks first
+  const int b = bh / a.h, hh = bh % a.h;
+  const int64_t S3 = 3LL * a.h * D;
+  const uint16_t* base = a.qkv + static_cast<int64_t>(b) * a.L * S3;
+  const int q0 = qb * BQ, qi = q0 + grp * 16 + qc;
+
+  RowTileDma<D, NT> tk;
+  RowTileDma<64, NT> ts_;  // dS^T tile (key tile, query tile qb): keys as rows, queries as columns
+  tk.init(base + static_cast<int64_t>(a.h) * D + hh * D, S3, a.L, tid);
+  const int nt = (a.L + 63) / 64;
+  ts_.init(a.dst + static_cast<int64_t>(bh) * nt * nt * 4096, 64, nt * nt * 64, tid);
+  f32x4_t dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int kv_end = a.causal ? min(a.L, q0 + BQ) : a.L;
+  const int nkb = (kv_end + 63) / 64;
+  tk.issue(lds_k[0], 0);
+  ts_.issue(lds_s[0], 64 * qb);
+  wait_vm_lds();
+  __syncthreads();
+  for (int it = 0; it < nkb; ++it) {
+    const int kv0 = it * 64, cur = it & 1;
+    if (it + 1 < nkb) {  // the other buffer's reads retired before the last barrier
+      tk.issue(lds_k[cur ^ 1], kv0 + 64);
+      ts_.issue(lds_s[cur ^ 1], 64 * ((it + 1) * nt + qb));
+    }
+    if (!(a.causal && kv0 + 32 * half > q0 + grp * 16 + 15)) {  // else dS is zero for these keys
+      const uint4 d = tr_frag(lds_s[cur], 16 * grp, half, lane);
+#pragma unroll
+      for (int d4 = 0; d4 < DB; d4 += 4) {  // K^T fragments four at a time, in flight together
+        uint4 fk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fk[j] = tr_frag(lds_k[cur], 16 * (d4 + j), half, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dq[d4 + j] = mfma_16x16x32(fk[j], d, dq[d4 + j]);
+      }
+    }
+    wait_vm_lds();  // this wave's copies of the next tiles landed; its reads of these retired
+    __syncthreads();
+  }
+  static_assert(NG * DB * 64 * 16 <= sizeof(lds_k), "merge buffer exceeds the tile buffers");
+  merge_halves<DB, NG>(dq, reinterpret_cast<f32x4_t*>(&lds_k[0][0]), grp, half, lane);
+  if (half != 0 || qi >= a.L) return;
+  uint16_t* row = a.dqkv + (static_cast<int64_t>(b) * a.L + qi) * S3 + hh * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    uint2 v;
+    v.x = pack_bf16x2(dq[db][0] * a.scale, dq[db][1] * a.scale);
+    v.y = pack_bf16x2(dq[db][2] * a.scale, dq[db][3] * a.scale);
+    *reinterpret_cast<uint2*>(row + 16 * db + 4 * (lane >> 4)) = v;
+  }
+}
+
 // WPE: at least this many waves per SIMD (a register cap: 4 keeps two 8-wave
 // blocks on a CU, which pays when every block carries the same work).
 template <int D, int NW, int NH, int WPE = 1>
@@ -800,6 +896,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           ds[j][r] = p[j][r] * (dp[r] - dv4[j][r]);
         }
       }
+      if (a.dst != nullptr) {
+        // dS^T in 64 x 64 tiles, each 8 KiB contiguous ([B h][key tile][query
+        // tile][key][query]), bf16 as the dK product takes them: this lane's 4
+        // consecutive queries per 16-query block.  Keys and queries past L
+        // carry zeros (p is zero there), so every tile that the dQ kernel
+        // reads is fully defined.
+        const int nt = (a.L + 63) / 64;
+        uint16_t* tile = a.dst + ((static_cast<int64_t>(bh) * nt + kb) * nt + q0 / 64) * 4096 + (kj - k0) * 64;
+#pragma unroll
+        for (int j = 0; j < SUB; ++j)
+          *reinterpret_cast<uint2*>(tile + 16 * (SUB * half + j) + 4 * g) =
+              make_uint2(pack_bf16x2(ds[j][0], ds[j][1]), pack_bf16x2(ds[j][2], ds[j][3]));
+      }
 #pragma unroll
       for (int t2 = 0; t2 < SUB / 2; ++t2) {
         const int t = (SUB / 2) * half + t2;
@@ -879,6 +988,13 @@ static void launch_bwd(AttnArgs a, hipStream_t s) {
   a.nblk = static_cast<int>(ceil_div(a.L, 16 * NW));
   const unsigned grid = static_cast<unsigned>(a.nblk * a.B * a.h);
   if constexpr (NW == 4) {
+    if (a.dst != nullptr) {  // stored-dS form: dvec, dK/dV writing dS^T, dQ from it
+      attn_dvec_kernel<D><<<static_cast<unsigned>(ceil_div(static_cast<int64_t>(a.B) * a.L * a.h, 256 / (D / 8))),
+                             256, 0, s>>>(a);
+      attn_bwd_dkv_kernel<D, 8, 2><<<grid, 512, 0, s>>>(a);
+      attn_bwd_dq_ds_kernel<D><<<grid, 512, 0, s>>>(a);
+      return;
+    }
     if (a.causal) attn_bwd_dq_kernel<D, 8, 2><<<grid, 512, causal_pad(a, 512u * D), s>>>(a);
     else attn_bwd_dq_kernel<D, 8, 2, 4><<<grid, 512, 0, s>>>(a);
     attn_bwd_dkv_kernel<D, 8, 2><<<grid, 512, 0, s>>>(a);
@@ -942,13 +1058,24 @@ extern "C" int mp_head_attention(mp_dtype dtype, int B, int L, int K, int h, int
   return check_launch(fn);
 }
 
+// Bytes of the stored dS^T (64 x 64 bf16 tiles over [B h][L][L]) when the
+// backward takes that form (4-wave blocks, at most 4096 keys), else 0.
+static size_t attn_ds_bytes(int B, int L, int h) {
+  if (attn_waves(B, L, h) != 4 || L > 4096) return 0;
+  const size_t nt = static_cast<size_t>(ceil_div(L, 64));
+  return static_cast<size_t>(B) * h * nt * nt * 8192;
+}
+
+// Workspace: dQKV, dvec, then one region that first holds dS^T (read by the
+// dQ kernel) and then the split-k / column-sum scratch of the products after.
 static size_t attn_bwd_parts(int B, int L, int K, int h, int d, size_t* dqkv_bytes, size_t* dvec_bytes) {
   const int64_t T = static_cast<int64_t>(B) * L, N3 = 3LL * h * d;
   *dqkv_bytes = align_up(static_cast<size_t>(T * N3) * 2, 256);
   *dvec_bytes = align_up(static_cast<size_t>(T * h) * 4, 256);
   const size_t sk = gemm_splitk_workspace(MP_BF16, N3, K, T);
   const size_t cs = colsum_workspace(T, N3);
-  return *dqkv_bytes + *dvec_bytes + (sk > cs ? sk : cs);
+  const size_t ds = attn_ds_bytes(B, L, h);
+  return *dqkv_bytes + *dvec_bytes + std::max(ds, std::max(sk, cs));
 }
 
 extern "C" size_t mp_head_attention_bwd_workspace(mp_dtype dtype, int B, int L, int K, int h, int d) {
@@ -993,6 +1120,7 @@ extern "C" int mp_head_attention_bwd(mp_dtype dtype, int B, int L, int K, int h,
   a.dctx = static_cast<const uint16_t*>(dctx_i);
   a.dvec = dvec;
   a.dqkv = dqkv;
+  if (attn_ds_bytes(B, L, h) != 0) a.dst = static_cast<uint16_t*>(ws2);
   const int nw = attn_waves(B, L, h);
   if (d == 64) nw == 8 ? launch_bwd<64, 8>(a, s) : launch_bwd<64, 4>(a, s);
   else nw == 8 ? launch_bwd<128, 8>(a, s) : launch_bwd<128, 4>(a, s);
