@@ -896,7 +896,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           ds[j][r] = p[j][r] * (dp[r] - dv4[j][r]);
         }
       }
-      if (a.dst != nullptr) {
+      // Compiled out of the one-wave-per-row form, which never stores dS^T:
+      // there the store's registers took it past 128 VGPRs, one block per CU.
+      if (NH == 2 && a.dst != nullptr) {
         // dS^T in 64 x 64 tiles, each 8 KiB contiguous ([B h][key tile][query
         // tile][key][query]), bf16 as the dK product takes them: this lane's 4
         // consecutive queries per 16-query block.  Keys and queries past L
