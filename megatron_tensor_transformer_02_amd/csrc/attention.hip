@@ -23,6 +23,10 @@
 //    kernel), S^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
 //  * dK/dV kernel -- lanes own keys: S = Q K^T, dP = dO V^T, dS,
 //    dV^T += dO^T P, dK^T += Q^T dS.
+// With few (batch, head) pairs and at most 4096 keys the order turns round:
+// rowsum(dO * O) by a small kernel, then the dK/dV kernel, which also writes
+// dS^T (bf16, 64 x 64 tiles) to the workspace, then a dQ kernel that forms
+// dQ^T = K^T dS^T from the stored tiles without recomputing S and dP.
 // The QKV GEMM's input and weight gradients then run on the GEMM family.
 #include "gemm.h"
 #include "mfma.h"
