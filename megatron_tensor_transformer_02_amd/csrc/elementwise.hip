@@ -6,6 +6,7 @@
 // Every thread moves whole 16-byte vectors (8 bf16 or 4 fp32), so a wave reads
 // 1 KiB contiguous per load instruction.
 #include "common.h"
+#include "slab_sum.h"
 
 namespace mp {
 
@@ -175,30 +176,13 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const void* __restr
   }
 }
 
-// Column-sum stage 2: out[c] = sum over slabs.  A block owns 64 columns;
-// thread group q (of 4) sums slabs q, q+4, ... in ascending order (4 loads in
-// flight), then the 4 group sums are added in group order (deterministic).
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ partial, int64_t slabs,
-                                                           int64_t cols, float* __restrict__ out) {
-  __shared__ float red[4][64];
-  const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
-  float t = 0.0f;
-  if (c < cols) {
-    int64_t s = q;
-    for (; s + 12 < slabs; s += 16) {
-      const float a0 = partial[s * cols + c], a1 = partial[(s + 4) * cols + c];
-      const float a2 = partial[(s + 8) * cols + c], a3 = partial[(s + 12) * cols + c];
-      t += a0;
-      t += a1;
-      t += a2;
-      t += a3;
-    }
-    for (; s < slabs; s += 4) t += partial[s * cols + c];
-  }
-  red[q][cl] = t;
-  __syncthreads();
-  if (q == 0 && c < cols) out[c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
+// Column-sum stage 2: out[c] = sum over slabs (fixed order, slab_sum.h).
+__global__ __launch_bounds__(SLAB_THREADS) void colsum_final_kernel(const float* __restrict__ partial, int64_t slabs,
+                                                                    int64_t cols, float* __restrict__ out) {
+  __shared__ float red[SLAB_GROUPS][SLAB_COLS];
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * SLAB_COLS + threadIdx.x % SLAB_COLS;
+  const float v = slab_column_sum(partial, slabs, cols, c, red);
+  if (threadIdx.x < SLAB_COLS && c < cols) out[c] = v;
 }
 
 static void colsum_plan(int64_t rows, int64_t& slab_rows, int64_t& slabs) {
@@ -227,8 +211,8 @@ int colsum(mp_dtype dt, int64_t rows, int64_t cols, const void* dy, float* out, 
     else
       colsum_partial_kernel<false><<<grid, 256, 0, s>>>(dy, rows, cols, slab_rows, static_cast<float*>(ws));
   }
-  colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, 64)), 256, 0, s>>>(static_cast<const float*>(ws), slabs,
-                                                                                cols, out);
+  colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, SLAB_COLS)), SLAB_THREADS, 0, s>>>(
+      static_cast<const float*>(ws), slabs, cols, out);
   return check_launch("colsum");
 }
 
@@ -427,7 +411,8 @@ extern "C" int mp_dropout_mask_bwd(mp_dtype dtype, int64_t rows, int64_t cols, c
     }
   }
   if (dbias != nullptr)
-    colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, 64)), 256, 0, s>>>(partial, slabs, cols, dbias);
+    colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, SLAB_COLS)), SLAB_THREADS, 0, s>>>(partial, slabs,
+                                                                                                 cols, dbias);
   return check_launch(fn);
 }
 

@@ -5,6 +5,7 @@
 // barriers.  The gamma/beta gradients are deterministic column sums over
 // row slabs (partials in the workspace, then a fixed-order final pass).
 #include "common.h"
+#include "slab_sum.h"
 
 namespace mp {
 
@@ -176,37 +177,18 @@ __global__ __launch_bounds__(256) void layernorm_bwd_param_kernel(int64_t T, int
   }
 }
 
-// Sums the slab partials of dgamma (columns [0, K)) and dbeta ([K, 2K)).
-// 64 columns x 16 slab lanes per block: lane q sums slabs q, q+16, ... in
-// ascending order (4 loads in flight), then the 16 lane sums are added in
-// lane order (deterministic).
-__global__ __launch_bounds__(1024) void layernorm_param_final_kernel(const float* __restrict__ partial, int64_t slabs,
-                                                                     int64_t K, int64_t w, float* __restrict__ dgamma,
-                                                                     float* __restrict__ dbeta,
-                                                                     float* __restrict__ dthird) {
-  constexpr int Q = 16;
-  __shared__ float red[Q][64];
-  const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
-  float t = 0.0f;
-  if (c < w) {
-    int64_t s = q;
-    for (; s + 3 * Q < slabs; s += 4 * Q) {
-      const float a0 = partial[s * w + c], a1 = partial[(s + Q) * w + c];
-      const float a2 = partial[(s + 2 * Q) * w + c], a3 = partial[(s + 3 * Q) * w + c];
-      t += a0;
-      t += a1;
-      t += a2;
-      t += a3;
-    }
-    for (; s < slabs; s += Q) t += partial[s * w + c];
-  }
-  red[q][cl] = t;
-  __syncthreads();
-  if (q != 0 || c >= w) return;
-  float v = red[0][cl];
-#pragma unroll
-  for (int i = 1; i < Q; ++i) v += red[i][cl];
+// Sums the slab partials of dgamma (columns [0, K)), dbeta ([K, 2K)) and,
+// with partial rows 3K wide, a third vector ([2K, 3K)) in the fixed order of
+// slab_sum.h.
+__global__ __launch_bounds__(SLAB_THREADS) void layernorm_param_final_kernel(const float* __restrict__ partial,
+                                                                             int64_t slabs, int64_t K, int64_t w,
+                                                                             float* __restrict__ dgamma,
+                                                                             float* __restrict__ dbeta,
+                                                                             float* __restrict__ dthird) {
+  __shared__ float red[SLAB_GROUPS][SLAB_COLS];
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * SLAB_COLS + threadIdx.x % SLAB_COLS;
+  const float v = slab_column_sum(partial, slabs, w, c, red);
+  if (threadIdx.x >= SLAB_COLS || c >= w) return;
   if (c < K) {
     if (dgamma) dgamma[c] = v;
   } else if (c < 2 * K) {
@@ -222,8 +204,8 @@ __global__ __launch_bounds__(1024) void layernorm_param_final_kernel(const float
 void layernorm_param_final(const float* partial, int64_t slabs, int64_t K, float* dgamma, float* dbeta,
                            hipStream_t s, float* dthird = nullptr) {
   const int64_t w = (dthird != nullptr ? 3 : 2) * K;
-  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(w, 64)), 1024, 0, s>>>(partial, slabs, K, w, dgamma,
-                                                                                     dbeta, dthird);
+  layernorm_param_final_kernel<<<static_cast<unsigned>(ceil_div(w, SLAB_COLS)), SLAB_THREADS, 0, s>>>(
+      partial, slabs, K, w, dgamma, dbeta, dthird);
 }
 
 static void ln_slabs(int64_t T, int64_t& slab_rows, int64_t& slabs) {
