@@ -12,6 +12,17 @@ namespace mp {
 int colsum(mp_dtype dt, int64_t rows, int64_t cols, const void* dy, float* out, void* ws, hipStream_t s);
 size_t colsum_workspace(int64_t rows, int64_t cols);
 
+// The 16-byte vector at element offset `elem` of a bf16 / fp32 array, raw.
+template <bool BF16>
+__device__ __forceinline__ uint4 ld_vec(const void* base, int64_t elem) {
+  return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem * (BF16 ? 2 : 4));
+}
+
+// Every load of a row (and of gamma / beta) is issued unconditionally, at a
+// clamped index, all before the first use, and kept raw (16 bytes) until
+// used; values past the row's end are selected away.  With the loads inside
+// a per-lane `if`, the compiler waited for each one before the next branch,
+// so a wave made one memory round trip per 16-byte vector.
 template <bool BF16, int CPL>
 __global__ __launch_bounds__(256) void layernorm_fwd_kernel(int64_t T, int64_t K, const void* __restrict__ x,
                                                             const void* __restrict__ gamma,
@@ -24,42 +35,47 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(int64_t T, int64_t K
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
   const int64_t nvec = K / E;
-  float v[CPL][E];
+  uint4 rx[CPL], rg[CPL], rb[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int64_t vi = lane + 64 * c, vs = vi < nvec ? vi : 0;
+    rx[c] = ld_vec<BF16>(x, row * K + vs * E);
+    rg[c] = ld_vec<BF16>(gamma, vs * E);
+    rb[c] = ld_vec<BF16>(beta, vs * E);
+  }
   float sum = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int64_t vi = lane + 64 * c;
-    if (vi < nvec) {
-      V::load(x, row * K + vi * E, v[c]);
+    const bool ok = lane + 64 * c < nvec;
+    float f[E];
+    V::unpack(rx[c], f);
 #pragma unroll
-      for (int i = 0; i < E; ++i) sum += v[c][i];
-    }
+    for (int i = 0; i < E; ++i) sum += ok ? f[i] : 0.0f;
   }
   const float mean = wave_sum(sum) / static_cast<float>(K);
   float sq = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int64_t vi = lane + 64 * c;
-    if (vi < nvec) {
+    const bool ok = lane + 64 * c < nvec;
+    float f[E];
+    V::unpack(rx[c], f);
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const float dlt = v[c][i] - mean;
-        sq += dlt * dlt;
-      }
+    for (int i = 0; i < E; ++i) {
+      const float dlt = ok ? f[i] - mean : 0.0f;
+      sq += dlt * dlt;
     }
   }
   const float rstd = rsqrtf(wave_sum(sq) / static_cast<float>(K) + eps);
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int64_t vi = lane + 64 * c;
-    if (vi < nvec) {
-      float g[E], b[E], o[E];
-      V::load(gamma, vi * E, g);
-      V::load(beta, vi * E, b);
+    float f[E], g[E], b[E], o[E];
+    V::unpack(rx[c], f);
+    V::unpack(rg[c], g);
+    V::unpack(rb[c], b);
 #pragma unroll
-      for (int i = 0; i < E; ++i) o[i] = (v[c][i] - mean) * rstd * g[i] + b[i];
-      V::store(y, row * K + vi * E, o);
-    }
+    for (int i = 0; i < E; ++i) o[i] = (f[i] - mean) * rstd * g[i] + b[i];
+    if (vi < nvec) V::store(y, row * K + vi * E, o);
   }
   if (lane == 0) {
     if (mean_out) mean_out[row] = mean;
@@ -68,6 +84,8 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(int64_t T, int64_t K
 }
 
 // dx = dres + rstd * (g - mean(g) - xhat * mean(g * xhat)), g = dy * gamma.
+// Loads at clamped indices, with no per-lane branch around them, as in the
+// forward.
 template <bool BF16, int CPL>
 __global__ __launch_bounds__(256) void layernorm_bwd_dx_kernel(int64_t T, int64_t K, const void* __restrict__ x,
                                                                const void* __restrict__ gamma,
@@ -87,19 +105,18 @@ __global__ __launch_bounds__(256) void layernorm_bwd_dx_kernel(int64_t T, int64_
   float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int64_t vi = lane + 64 * c;
-    if (vi < nvec) {
-      float gm[E];
-      V::load(x, row * K + vi * E, xh[c]);
-      V::load(dy, row * K + vi * E, g[c]);
-      V::load(gamma, vi * E, gm);
+    const int64_t vi = lane + 64 * c, vs = vi < nvec ? vi : 0;
+    const bool ok = vi < nvec;
+    float gm[E];
+    V::load(x, row * K + vs * E, xh[c]);
+    V::load(dy, row * K + vs * E, g[c]);
+    V::load(gamma, vs * E, gm);
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        xh[c][i] = (xh[c][i] - mean) * rstd;
-        g[c][i] *= gm[i];
-        s1 += g[c][i];
-        s2 += g[c][i] * xh[c][i];
-      }
+    for (int i = 0; i < E; ++i) {
+      xh[c][i] = (xh[c][i] - mean) * rstd;
+      g[c][i] = ok ? g[c][i] * gm[i] : 0.0f;
+      s1 += g[c][i];
+      s2 += g[c][i] * xh[c][i];
     }
   }
   const float inv_k = 1.0f / static_cast<float>(K);
@@ -108,18 +125,16 @@ __global__ __launch_bounds__(256) void layernorm_bwd_dx_kernel(int64_t T, int64_
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int64_t vi = lane + 64 * c;
-    if (vi < nvec) {
-      float o[E], r[E];
-      if (dres != nullptr) {
-        V::load(dres, row * K + vi * E, r);
-      } else {
+    float o[E], r[E];
+    if (dres != nullptr) {
+      V::load(dres, row * K + (vi < nvec ? vi : 0) * E, r);
+    } else {
 #pragma unroll
-        for (int i = 0; i < E; ++i) r[i] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < E; ++i) o[i] = r[i] + rstd * (g[c][i] - m1 - xh[c][i] * m2);
-      V::store(dx, row * K + vi * E, o);
+      for (int i = 0; i < E; ++i) r[i] = 0.0f;
     }
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = r[i] + rstd * (g[c][i] - m1 - xh[c][i] * m2);
+    if (vi < nvec) V::store(dx, row * K + vi * E, o);
   }
 }
 
@@ -220,8 +235,11 @@ static int dispatch_cpl(int64_t nvec, Args... args) {
   const int64_t cpl = ceil_div(nvec, 64);
   if (cpl <= 1) return Launcher<BF16, 1>::run(args...);
   if (cpl <= 2) return Launcher<BF16, 2>::run(args...);
+  if (cpl <= 3) return Launcher<BF16, 3>::run(args...);
   if (cpl <= 4) return Launcher<BF16, 4>::run(args...);
+  if (cpl <= 6) return Launcher<BF16, 6>::run(args...);
   if (cpl <= 8) return Launcher<BF16, 8>::run(args...);
+  if (cpl <= 12) return Launcher<BF16, 12>::run(args...);
   return Launcher<BF16, 16>::run(args...);
 }
 
