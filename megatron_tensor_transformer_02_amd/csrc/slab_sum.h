@@ -10,9 +10,8 @@ namespace mp {
 // columns.  Group q sums slabs q, q + SLAB_GROUPS, ... in ascending order,
 // eight loads in flight per thread; the group sums are then added in group
 // order.  With few slabs per group the loads of a column are all in flight
-// at once (the previous layout, four groups walking 128 or 512 slabs four
-// loads at a time, was bound by the load latency).  The order depends only
-// on the slab count, so results are identical run to run.
+// at once.  The order depends only on the slab count, so results are
+// identical run to run.
 constexpr int SLAB_COLS = 32, SLAB_GROUPS = 32, SLAB_THREADS = SLAB_COLS * SLAB_GROUPS;
 
 // Returns the sum of column c in threads of group 0 (0 elsewhere); every
