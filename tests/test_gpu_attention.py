@@ -46,6 +46,9 @@ def check_core_grads(ws, qkv, dctx, B, L, h, d, causal, seqs=None):
 @pytest.mark.parametrize("B,L,K,h,d,causal", [
     (2, 100, 64, 2, 64, True), (1, 257, 128, 3, 128, True), (2, 70, 96, 1, 64, False),
     (3, 1, 64, 2, 128, True), (1, 200, 256, 2, 128, False),
+    # stored-dS backward edges: one whole 64 x 64 tile, one key past a tile,
+    # exactly two tiles
+    (1, 64, 64, 1, 64, True), (2, 65, 64, 1, 128, False), (1, 128, 64, 2, 128, True),
     # past 4096 keys the few-pairs backward recomputes dS instead of storing it
     (1, 4104, 64, 1, 64, True)])
 def test_head_attention_fwd_bwd(B, L, K, h, d, causal):
