@@ -325,6 +325,16 @@ def test_head_attention_validation(lib):
     assert fwd(mp.MP_BF16, 2, 64, 128, 2, 64, 1, A, A, None, A + 2, A, A, None)[0] == -5
     need = lib.mp_head_attention_bwd_workspace(mp.MP_BF16, 2, 64, 128, 2, 64)
     assert need > 0 and lib.mp_head_attention_bwd_workspace(mp.MP_BF16, 2, 64, 128, 2, 96) == 0
+    # Few (batch, head) pairs and at most 4096 keys: the workspace holds the
+    # bf16 dS^T of every pair in 64 x 64 tiles (the stored-dS backward); past
+    # 4096 keys, or with many pairs, it does not.
+    def ds_tiles(B, L, h):
+        nt = -(-L // 64)
+        return B * h * nt * nt * 8192
+    for B, L, h in ((8, 1024, 3), (1, 4096, 1), (2, 65, 1)):
+        assert lib.mp_head_attention_bwd_workspace(mp.MP_BF16, B, L, 3072, h, 128) >= ds_tiles(B, L, h)
+    assert lib.mp_head_attention_bwd_workspace(mp.MP_BF16, 1, 4104, 64, 1, 64) < ds_tiles(1, 4104, 1)
+    assert lib.mp_head_attention_bwd_workspace(mp.MP_BF16, 8, 1024, 1024, 16, 64) < ds_tiles(8, 1024, 16)
     bwd = lambda *a: call(lib, "mp_head_attention_bwd", *a)  # noqa: E731
     args = [mp.MP_BF16, 2, 64, 128, 2, 64, 1, A, A, A, A, A, A, A, A, None, A, need, None]
     a = list(args); a[5] = 128 + 64
