@@ -314,6 +314,26 @@ def main():
                       "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
                       "avg_launch_us": round(col_ms * 1e3, 2),
                       "median_launch_us": round(float(np.median(col)) * 1e3, 2), "algorithmic_per_launch": col_fl})
+        # The attention calls as a whole (mp_head_attention: the fused QKV
+        # GEMM + causal attention; mp_head_attention_bwd: attention backward +
+        # the QKV input- and weight-gradient GEMMs + the bias column sums),
+        # counted as layer_flops counts them (attention on the causal half,
+        # its backward 2.5x the forward).
+        T_ = B * L
+        qkv_fl = 2.0 * T_ * K * 3 * hi * d
+        att_fl = 2 * 2 * B * hi * (L * (L + 1) / 2) * d
+        for tag, what, fl in (("attn_fwd", "mp_head_attention: fused QKV GEMM + causal attention forward",
+                               qkv_fl + att_fl),
+                              ("attn_bwd", "mp_head_attention_bwd: attention backward + QKV input/weight-gradient "
+                                           "GEMMs", 2 * qkv_fl + 2.5 * att_fl)):
+            tms = [b.elapsed_time(e) for b, e in zip(ev_of(tag + "_begin"), ev_of(tag + "_end"))]
+            t_ms = float(np.mean(tms))
+            a_tf = fl / (t_ms * 1e-3) / 1e12
+            roofs.append({"kernel": f"{what} (whole call, 3 of 24 heads x 128, causal L {L})", "bound": "mfma",
+                          "achieved": round(a_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                          "avg_launch_us": round(t_ms * 1e3, 2),
+                          "median_launch_us": round(float(np.median(tms)) * 1e3, 2), "algorithmic_per_launch": fl})
         # The MLP's 8-way shard reduce (+ bias, dropout with its keep bits
         # saved, residual): 8 bf16 partials and the residual read, the output
         # and the keep bits written.

@@ -83,8 +83,12 @@ class RankLayer:
         # Attention over this rank's heads of LN1(X) (in self.h), then the
         # out-projection's partial sum.
         s = self.s
+        if self.probe is not None:
+            self.probe("attn_fwd_begin")
         mp.mp_head_attention(self.h, s["w_qkv"], s["b_qkv"], self.B, self.L, self.nh, self.d, self.ctx,
                              self.qkv, self.lse, self.causal)
+        if self.probe is not None:
+            self.probe("attn_fwd_end")
         mp.mp_row_linear_partial(self.ctx, s["w_o"], self.p_attn)
         return self.p_attn
 
@@ -140,8 +144,12 @@ class RankLayer:
     def attn_bwd_partial(self):
         s, g = self.s, self.g
         mp.mp_row_linear_partial_bwd(self.ctx, s["w_o"], self.d_attn, self.dctx, g["w_o"])
+        if self.probe is not None:
+            self.probe("attn_bwd_begin")
         mp.mp_head_attention_bwd(self.h, s["w_qkv"], self.qkv, self.ctx, self.lse, self.dctx, self.B, self.L,
                                  self.nh, self.d, self.dhp, g["w_qkv"], g["b_qkv"], self.causal)
+        if self.probe is not None:
+            self.probe("attn_bwd_end")
         return self.dhp
 
     def attn_bwd_reduce(self, partials, x):
