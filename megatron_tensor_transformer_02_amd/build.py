@@ -15,6 +15,8 @@ on the CPU under the sanitizers' runtime.
 
 import concurrent.futures as cf
 import glob
+import json
+import re
 import os
 import shutil
 import subprocess
@@ -34,7 +36,44 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument", "-Wno-unknown-warning-option",
+    # The compiler's per-kernel register / scratch / occupancy remarks,
+    # collected into kernel_resources.json beside the objects.
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+_REMARK_NAME = re.compile(r"remark: Function Name: (\S+)")
+_REMARK_FIELD = re.compile(r"remark:\s+(.+?):\s+(\S+) \[-Rpass-analysis=kernel-resource-usage\]")
+
+
+def _resources(stderr):
+    """{kernel symbol: {field: value}} from the resource-usage remarks."""
+    out, cur = {}, None
+    for line in stderr.splitlines():
+        m = _REMARK_NAME.search(line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = _REMARK_FIELD.search(line)
+        if m and cur is not None:
+            v = m.group(2)
+            cur[m.group(1).strip()] = int(v) if v.lstrip("-").isdigit() else v
+    return out
+
+
+def _without_remarks(stderr):
+    """The compiler's messages other than the resource remarks (and their
+    source excerpts)."""
+    keep, skip = [], 0
+    for line in stderr.splitlines():
+        if "[-Rpass-analysis=kernel-resource-usage]" in line:
+            skip = 2  # the source line and caret the first remark of a kernel quotes
+            continue
+        if skip and (line.startswith(" ") or not line.strip()):
+            skip -= 1
+            continue
+        skip = 0
+        keep.append(line)
+    return "\n".join(keep)
 
 
 SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
@@ -63,11 +102,15 @@ def build(verbose=False, extra=(), jobs=None, sanitize=False):
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(lambda s: _compile(s, extra, out_dir), srcs))
-    objs = []
+    objs, resources = [], {}
     for obj, err in results:
         objs.append(obj)
-        if verbose and err.strip():
-            sys.stderr.write(err)
+        resources.update(_resources(err))
+        msgs = _without_remarks(err)
+        if verbose and msgs.strip():
+            sys.stderr.write(msgs + "\n")
+    with open(os.path.join(out_dir, "kernel_resources.json"), "w") as f:
+        json.dump(resources, f, indent=1, sort_keys=True)
     tmp = lib + ".tmp"
     link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
                   "-shared-libasan"] if sanitize else []

@@ -1,0 +1,74 @@
+"""Registers, scratch and occupancy of the library's kernels, from the
+compiler's resource-usage remarks that the build collects into
+_build/kernel_resources.json (no GPU needed).
+
+Two guards: no kernel spills to scratch (apart from the listed rare variants),
+and the kernels whose speed was tuned to a number of waves per SIMD keep it.
+The second caught a real regression once: code compiled into the one-wave-per-
+row dK/dV kernel, though never run there, took it from 124 to 149 VGPRs and
+from four to three waves per SIMD, and the GPT-2-medium dK/dV from 66 to 84 us.
+"""
+import json
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+REPORT = os.path.join(ROOT, "_build", "kernel_resources.json")
+
+
+@pytest.fixture(scope="module")
+def report():
+    if not os.path.exists(REPORT):
+        pytest.skip("no kernel resource report: build the library first (__graft_entry__.build())")
+    with open(REPORT) as f:
+        rep = json.load(f)
+    if not rep:
+        pytest.skip("empty kernel resource report")
+    return rep
+
+
+# The fused shard reduce + LayerNorm with up to 16 partials (NMAX 16: more than
+# 8 shards, or fp32) or rows of more than 4096 bf16 values (16 waves, 1024
+# threads, a 128-register cap): two rows of 16 + 2 sixteen-byte vectors in
+# flight do not fit, and these variants spill.  Neither shape is on the
+# benchmarked path (8 shards, rows of 3072 or 1024 values).
+SPILL_ALLOWED = ("reduce_ln_fwd_kernelILb1ELi16ELi16E", "reduce_ln_fwd_kernelILb0ELi16ELi16E",
+                 "reduce_ln_bwd_kernelILb1ELi8ELi16E", "reduce_ln_bwd_kernelILb1ELi16ELi16E",
+                 "reduce_ln_bwd_kernelILb0ELi16ELi16E")
+
+# Kernel (mangled-name fragment) -> the fewest waves per SIMD it must keep.
+OCCUPANCY_FLOORS = {
+    "attn_bwd_dkv_kernelILi64ELi8ELi1E": 4,      # GPT-2-medium dK/dV: two 8-wave blocks per CU
+    "attn_bwd_dq_kernelILi64ELi8ELi1ELi1E": 4,   # GPT-2-medium dQ
+    "attn_fwd_kernelILi64ELi8E": 4,              # GPT-2-medium forward
+    "attn_bwd_dkv_kernelILi128ELi8ELi2E": 2,     # few-pairs dK/dV held to 256 registers
+    "attn_bwd_dq_kernelILi128ELi8ELi2ELi4E": 4,  # non-causal few-pairs dQ: two blocks per CU
+    "attn_bwd_dq_ds_kernelILi128E": 4,           # dQ from the stored dS^T
+    "layernorm_fwd_kernelILb1ELi6E": 4,          # LayerNorm forward, rows of 3072 bf16
+    "reduce_ln_fwd_kernelILb1ELi8ELi6E": 4,      # fused reduce + LN2 forward (8 shards, 3072)
+    "reduce_ln_bwd_kernelILb1ELi8ELi6E": 3,      # fused reduce + LN backward
+}
+
+
+def test_report_covers_the_hot_path(report):
+    for frag in ("gemm_bf16_kernel", "attn_fwd_par_kernel", "attn_bwd_dq_ds_kernel", "moe_gemm_kernel",
+                 "xent_triples_kernel", "shard_reduce_kernel"):
+        assert any(frag in k for k in report), frag
+
+
+def test_no_scratch(report):
+    # Scratch memory and VGPR spills only: SGPR spills land in VGPR lanes
+    # (v_writelane / v_readlane) and cost no memory traffic.
+    bad = [(k, v.get("ScratchSize [bytes/lane]"), v.get("VGPRs Spill")) for k, v in report.items()
+           if (v.get("ScratchSize [bytes/lane]", 0) or v.get("VGPRs Spill", 0))
+           and not any(a in k for a in SPILL_ALLOWED)]
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("frag,floor", sorted(OCCUPANCY_FLOORS.items()))
+def test_occupancy_floor(report, frag, floor):
+    hits = {k: v for k, v in report.items() if frag in k}
+    assert hits, f"no kernel matches {frag}"
+    for k, v in hits.items():
+        assert v["Occupancy [waves/SIMD]"] >= floor, (k, v["VGPRs"], v["Occupancy [waves/SIMD]"])
