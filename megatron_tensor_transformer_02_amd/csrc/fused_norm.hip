@@ -153,13 +153,22 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_fwd_kernel(PartPtrs parts, 
     V::load(beta, vi * E, be);
   }
   const float inv_k = 1.0f / static_cast<float>(K);
+  // The next row's inputs are loaded before the current row's reductions,
+  // except in 16-wave blocks, whose 128-register cap does not hold two rows
+  // of up to 16 + 2 vectors (they spilled).
+  constexpr bool PF = NW < 16;
   RowIn<NMAX> nxt;
-  if (act && r0 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, r0 * K + vi * E, residual, nullptr);
+  if (PF && act && r0 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, r0 * K + vi * E, residual, nullptr);
   int slot = 0;
   for (int64_t row = r0; row < r1; ++row, slot ^= 2) {
     const int64_t e0 = row * K + vi * E;
-    const RowIn<NMAX> cur = nxt;
-    if (act && row + 1 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, e0 + K, residual, nullptr);
+    RowIn<NMAX> cur;
+    if constexpr (PF) {
+      cur = nxt;
+      if (act && row + 1 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, e0 + K, residual, nullptr);
+    } else {
+      if (act) load_row<BF16, NMAX>(cur, parts, n_parts, e0, residual, nullptr);
+    }
     float h[E];
     float sum = 0.0f;
     uint8_t keep[E];
@@ -239,13 +248,19 @@ __global__ __launch_bounds__(64 * NW) void reduce_ln_bwd_kernel(PartPtrs parts, 
   for (int i = 0; i < E; ++i) pg[i] = pb[i] = pd[i] = 0.0f;
   if (act) V::load(gamma, vi * E, gm);
   const float inv_k = 1.0f / static_cast<float>(K);
+  constexpr bool PF = NW < 16;  // prefetch of the next row, as in the forward
   RowIn<NMAX> nxt;
-  if (act && r0 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, r0 * K + vi * E, x, dres);
+  if (PF && act && r0 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, r0 * K + vi * E, x, dres);
   int slot = 0;
   for (int64_t row = r0; row < r1; ++row, slot ^= 2) {
     const int64_t e0 = row * K + vi * E;
-    const RowIn<NMAX> cur = nxt;
-    if (act && row + 1 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, e0 + K, x, dres);
+    RowIn<NMAX> cur;
+    if constexpr (PF) {
+      cur = nxt;
+      if (act && row + 1 < r1) load_row<BF16, NMAX>(nxt, parts, n_parts, e0 + K, x, dres);
+    } else {
+      if (act) load_row<BF16, NMAX>(cur, parts, n_parts, e0, x, dres);
+    }
     const float mean = mean_in[row];
     const float rstd = rstd_in[row];
     float g[E], xh[E];

@@ -22,6 +22,8 @@ CASES = [
     ("bf16", 1, 5, 8, 0.5),         # N=1, one vector per row
     ("bf16", 16, 33, 1024, 0.9),    # maximum N, heavy dropout
     ("bf16", 8, 2048, 3072, 0.1),   # a quarter of the full token count
+    # rows wider than 4096 values: 16-wave blocks, no next-row prefetch
+    ("bf16", 8, 40, 7168, 0.1), ("f32", 3, 24, 4096, 0.0), ("bf16", 12, 20, 8192, 0.1),
 ]
 
 
