@@ -76,8 +76,17 @@ __global__ __launch_bounds__(256) void dropout_mask_bwd_kernel(const void* __res
   __shared__ float red[SUM ? 8 : 1][SUM ? 32 * E : 1];
   const int cv = threadIdx.x & 31;
   const int rl = threadIdx.x >> 5;
-  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 32 + cv) * E;
-  const int64_t r_begin = static_cast<int64_t>(blockIdx.y) * slab_rows;
+  // Blocks are dealt to the 8 XCDs round-robin by their linear id; each XCD
+  // instead gets a contiguous run of (column block, slab) pairs, so the four
+  // column-neighbour blocks that read one 128-byte line of keep bits (32
+  // vectors x 8 bits each) share its L2 instead of fetching it four times.
+  // Runs cover whole groups of four when the block count is a multiple of 32
+  // and a slab's column blocks a multiple of 4; otherwise the plain order.
+  const unsigned gx = gridDim.x, nb = gx * gridDim.y, hw = blockIdx.x + gx * blockIdx.y;
+  const unsigned lid = (nb % 32 == 0 && gx % 4 == 0) ? (hw % 8) * (nb / 8) + hw / 8 : hw;
+  const unsigned bx = lid % gx, by = lid / gx;
+  const int64_t c0 = (static_cast<int64_t>(bx) * 32 + cv) * E;
+  const int64_t r_begin = static_cast<int64_t>(by) * slab_rows;
   const int64_t r_end = r_begin + slab_rows < rows ? r_begin + slab_rows : rows;
   float acc[E];
 #pragma unroll
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(256) void dropout_mask_bwd_kernel(const void* __res
         float t = red[0][cv * E + i];
 #pragma unroll
         for (int l = 1; l < 8; ++l) t += red[l][cv * E + i];
-        partial[static_cast<int64_t>(blockIdx.y) * cols + c0 + i] = t;
+        partial[static_cast<int64_t>(by) * cols + c0 + i] = t;
       }
     }
   }
