@@ -50,7 +50,10 @@ def check_core_grads(ws, qkv, dctx, B, L, h, d, causal, seqs=None):
     # exactly two tiles
     (1, 64, 64, 1, 64, True), (2, 65, 64, 1, 128, False), (1, 128, 64, 2, 128, True),
     # past 4096 keys the few-pairs backward recomputes dS instead of storing it
-    (1, 4104, 64, 1, 64, True)])
+    (1, 4104, 64, 1, 64, True),
+    # either side of the block-count threshold (B h ceil(L/128) = 510 and 512)
+    # between 4-wave blocks with the stored dS^T and 8-wave blocks
+    (1, 130, 64, 255, 64, True), (1, 130, 64, 256, 64, True)])
 def test_head_attention_fwd_bwd(B, L, K, h, d, causal):
     say("attention", B, L, K, h, d, causal)
     x, w, bq, xd, wd, ctx, qkv, lse = run_fwd(B, L, K, h, d, causal, 10)
